@@ -1,0 +1,175 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) decode-time MoE layer library with a
+ * router-following LRU cache of expert slots.
+ *
+ * The method (FreeToken's offload backend, as the pages describe it):
+ *   pirouter.ai, "FreeToken x RTX 5090 -- 120B MoE が 127 tok/s、その請求書",
+ *   section on how 65 GB runs on a 32 GB GPU: every expert lives in pinned
+ *   host RAM, the GPU keeps an LRU cache of expert slots, and a miss is
+ *   streamed over PCIe; the cache follows the router.
+ *   ai-hardware-zukan.com, "VRAMに収まらないMoEモデルのデコードが約2倍になった",
+ *   section on how misses are made up for: cache unit = (layer, expert),
+ *   replacement = least recently used.
+ *   gaming-st.com DeepSeek page, section on the role of VRAM: one global LRU
+ *   expert cache.
+ *   ai.holude.com preflight page, section on long prompts: the next layer's
+ *   experts are loaded over PCIe while the GPU computes the current layer.
+ *
+ * Per token and layer the library runs: router logits + top-k + softmax over
+ * the selected logits (K1), resolution of the selected (layer, expert) pairs
+ * to cache slots with a miss list (K2), one host-to-device copy per miss on the
+ * copy stream, the selected experts' MXFP4 SwiGLU FFNs (K3: gate/up + SwiGLU;
+ * K4: down projection fused with the weighted combine and the shared expert).
+ *
+ * Conventions
+ *  - Every call returns moe_status; nothing throws or aborts across the ABI.
+ *  - Pointers named *_dev are device pointers; the others are host pointers.
+ *  - Streams are hipStream_t passed as void*; calls are ordered on the
+ *    compute stream.  Calls that resolve the cache block the calling host
+ *    thread until the step's miss list is readable (the host issues the copies).
+ *  - After a HIP error the context is failed: every later call returns
+ *    MOE_ESTATE; moe_last_error() tells what happened; destroy and re-create.
+ *  - One context per host thread; calls on one context must not overlap.
+ *
+ * Data formats
+ *  - bf16 = IEEE binary32 upper 16 bits, little-endian uint16.
+ *  - Logical expert blob (what the fill callback writes; 3*H*I*17/32 bytes):
+ *      gate codes [I][H/2], gate scales [I][H/32],
+ *      up   codes [I][H/2], up   scales [I][H/32],
+ *      down codes [H][I/2], down scales [H][I/32].
+ *    MXFP4: a code byte holds element 2j (low nibble) and 2j+1 (high nibble),
+ *    each an E2M1 value; a scale byte is the E8M0 exponent (2^(E-127)) shared
+ *    by 32 consecutive elements along the row.  The library repacks blobs into
+ *    its own kernel layout when it fills the pool; slots hold that layout.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,     /* bad argument or unsupported shape */
+    MOE_ENOMEM = -2,     /* host (pinned) or device allocation failed, or a caller buffer is too small */
+    MOE_EHIP = -3,       /* a HIP call failed; the context is now failed */
+    MOE_ECAPACITY = -4,  /* cache_slots < 2 * largest distinct expert set one step can request */
+    MOE_ESTATE = -5,     /* context already failed */
+} moe_status;
+
+enum {
+    MOE_FLAG_PROFILE = 1,  /* time every K3 and K4 launch and every layer's miss copies with HIP
+                              events (read via moe_stats) */
+};
+
+typedef struct {
+    int32_t n_layers;       /* L */
+    int32_t n_experts;      /* E routed experts per layer, 1..1024 */
+    int32_t top_k;          /* k, 1..16 and <= E */
+    int32_t hidden;         /* H, multiple of 32, <= 16384 */
+    int32_t inter;          /* I, multiple of 32, <= 16384 */
+    int32_t n_shared;       /* always-on shared experts per layer (0 or 1), resident in HBM */
+    int32_t cache_slots;    /* C: GPU expert slots; must be >= 2 * min(max_tokens * k, E) */
+    int32_t max_tokens;     /* largest n_tokens of any call */
+    int32_t lookahead;      /* moe_stack_forward: 1 = resolve and copy layer l+1 while layer l's
+                               FFN runs; 0 = causal (each layer's copies before its FFN) */
+    int32_t trace_capacity; /* cache trace records kept on the device (0 = none) */
+    int32_t fill_threads;   /* host threads calling the fill callback (0 = all cores) */
+    int32_t flags;          /* MOE_FLAG_* */
+} moe_config;
+
+/* Writes the logical blob of routed expert (layer, expert >= 0) or of shared
+ * expert s (expert = -1 - s) into dst.  May be called from several threads at
+ * once with different dst buffers. */
+typedef void (*moe_fill_fn)(void* user, int32_t layer, int32_t expert, uint8_t* dst_blob);
+
+typedef struct moe_ctx moe_ctx;
+
+/* Sizes the caller must provide: bytes of one expert blob, of the slot arena
+ * (C blobs) and of the workspace.  Any pointer may be NULL.  Checks cfg. */
+moe_status moe_query_sizes(const moe_config* cfg, size_t* blob_bytes, size_t* arena_bytes,
+                           size_t* workspace_bytes);
+
+/* Builds a context: allocates the pinned host pool of all L*E routed expert
+ * blobs and fills it through `fill` (called once per (layer, expert) and once
+ * per shared expert), copies the router weights (host [L][E][H] bf16) and the
+ * shared experts into HBM, and starts with an empty (cold) cache.
+ * slot_arena_dev (>= C blobs) and workspace_dev are device memory owned by the
+ * caller; they and both streams must outlive the context.
+ * Errors: MOE_EINVAL (shape), MOE_ECAPACITY (cache_slots), MOE_ENOMEM (pinned
+ * pool, device state, or caller buffers too small), MOE_EHIP.  On error *out is
+ * NULL and nothing is leaked. */
+moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
+                         const uint16_t* router_w_bf16,
+                         void* slot_arena_dev, size_t arena_bytes,
+                         void* workspace_dev, size_t workspace_bytes,
+                         void* compute_stream, void* copy_stream, moe_ctx** out);
+
+/* Cache step for one layer with caller-given expert ids (ids_dev: [n_tokens][k]
+ * int32, each in [0, E)): enqueues the resolve kernel on the compute stream,
+ * waits for its miss list, issues one host-to-device copy per miss on the copy
+ * stream and makes the compute stream wait for them.  slots_dev ([n_tokens][k]
+ * int32, may be NULL) receives the slot holding each id; *n_miss_out (host,
+ * may be NULL) the number of misses.  `step` labels the trace records. */
+moe_status moe_cache_resolve(moe_ctx* ctx, int32_t step, int32_t layer, const int32_t* ids_dev,
+                             int32_t n_tokens, int32_t* slots_dev, int32_t* n_miss_out);
+
+/* One layer for n_tokens tokens, causal: router (K1) -> resolve (K2) -> miss
+ * copies -> FFN (K3, K4).  x_bf16_dev: [n_tokens][H]; y_bf16_dev: [n_tokens][H]
+ * = sum_j w_j * FFN_{id_j}(x) + shared(x).  ids_dev_out ([n_tokens][k] int32,
+ * ranked by logit) and w_dev_out ([n_tokens][k] float) may be NULL. */
+moe_status moe_layer_forward(moe_ctx* ctx, int32_t step, int32_t layer, const void* x_bf16_dev,
+                             int32_t n_tokens, void* y_bf16_dev, int32_t* ids_dev_out,
+                             float* w_dev_out);
+
+/* One decode step through all L layers with the configured lookahead.  Layer
+ * l reads x_bf16_dev + l * x_layer_stride elements (stride 0: the same input
+ * for every layer) and writes y_bf16_dev + l * y_layer_stride.  ids_dev_out
+ * ([L][n_tokens][k]) and w_dev_out may be NULL. */
+moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev, int64_t x_layer_stride,
+                             int32_t n_tokens, void* y_bf16_dev, int64_t y_layer_stride,
+                             int32_t* ids_dev_out, float* w_dev_out);
+
+typedef struct {
+    uint64_t hits, misses, evictions;  /* cache accesses (unique (layer, expert) per step) */
+    uint64_t resolves;                 /* layer steps resolved */
+    uint64_t h2d_bytes, h2d_copies;    /* miss copies issued */
+    uint64_t trace_records, trace_dropped;
+    uint64_t k3_launches, k4_launches; /* with MOE_FLAG_PROFILE: timed launches ... */
+    double k3_ms, k4_ms;               /* ... and their summed durations (HIP events) */
+    double h2d_ms;                     /* with MOE_FLAG_PROFILE: summed busy time of the miss copies */
+} moe_counters;
+
+typedef struct {
+    int32_t step, layer, expert, slot, hit, evicted_key; /* evicted_key = layer*E + expert, -1: none */
+} moe_trace_rec;
+
+/* Synchronises the compute stream, then reports counters and drains up to cap
+ * trace records (in order; the rest stay queued) into buf (host, may be NULL
+ * with cap 0).  Profile timings are harvested and reset on every call. */
+moe_status moe_stats(moe_ctx* ctx, moe_counters* out, moe_trace_rec* buf, size_t cap, size_t* n_out);
+
+/* Host-to-device bandwidth of the copy path: n_copies back-to-back copies of
+ * bytes_per_copy from blob-aligned pool offsets (deterministic pseudo-random
+ * order) on the copy stream into a scratch device buffer; returns GB/s (1e9).
+ * Leaves the cache untouched. */
+moe_status moe_measure_h2d(moe_ctx* ctx, size_t bytes_per_copy, int32_t n_copies, double* gbps_out);
+
+/* Reads back the cache state (host buffers, each may be NULL): slot_of
+ * [L*E], key_of [C], stamp [C].  Synchronises the compute stream. */
+moe_status moe_cache_state(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, int64_t* stamp);
+
+/* Frees everything the context owns (after synchronising both streams).  NULL is a no-op. */
+void moe_destroy(moe_ctx* ctx);
+/* Text of the context's last error; with ctx = NULL, of the last failed moe_init_pool on the
+ * calling thread.  Valid until the next call on the same context / thread. */
+const char* moe_last_error(const moe_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,213 @@
+"""Python binding of libmoe.so: decode-time MoE layers over a router-following
+LRU cache of expert slots on an MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP library
+(see ``include/moe.h`` for the C ABI).  PyTorch provides device memory and
+streams.  Importing this package fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7) as the system one.
+# Import it first so the dynamic loader binds libmoe.so to that runtime: the streams and device
+# pointers torch hands over are only valid inside the runtime that created them.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m moe_expert_offload_amd.build "
+        "or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE = 0, -1, -2, -3, -4, -5
+MOE_FLAG_PROFILE = 1
+_STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
+           -5: "MOE_ESTATE"}
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "n_experts", "top_k", "hidden", "inter", "n_shared", "cache_slots", "max_tokens",
+        "lookahead", "trace_capacity", "fill_threads", "flags")]
+
+
+class MoeCounters(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "trace_records",
+        "trace_dropped", "k3_launches", "k4_launches")] + [("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double),
+                                              ("h2d_ms", ctypes.c_double)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class MoeTraceRec(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("step", "layer", "expert", "slot", "hit", "evicted_key")]
+
+
+FILL_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint8))
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_st = ctypes.c_int
+
+_lib.moe_query_sizes.restype = _st
+_lib.moe_query_sizes.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(ctypes.c_size_t),
+                                 ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+_lib.moe_init_pool.restype = _st
+_lib.moe_init_pool.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, ctypes.c_size_t, _P,
+                               ctypes.c_size_t, _P, _P, ctypes.POINTER(_P)]
+_lib.moe_cache_resolve.restype = _st
+_lib.moe_cache_resolve.argtypes = [_P, _I32, _I32, _P, _I32, _P, ctypes.POINTER(_I32)]
+_lib.moe_layer_forward.restype = _st
+_lib.moe_layer_forward.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P, _P]
+_lib.moe_stack_forward.restype = _st
+_lib.moe_stack_forward.argtypes = [_P, _I32, _P, ctypes.c_int64, _I32, _P, ctypes.c_int64, _P, _P]
+_lib.moe_stats.restype = _st
+_lib.moe_stats.argtypes = [_P, ctypes.POINTER(MoeCounters), _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+_lib.moe_measure_h2d.restype = _st
+_lib.moe_measure_h2d.argtypes = [_P, ctypes.c_size_t, _I32, ctypes.POINTER(ctypes.c_double)]
+_lib.moe_cache_state.restype = _st
+_lib.moe_cache_state.argtypes = [_P, _P, _P, _P]
+_lib.moe_destroy.restype = None
+_lib.moe_destroy.argtypes = [_P]
+_lib.moe_last_error.restype = ctypes.c_char_p
+_lib.moe_last_error.argtypes = [_P]
+
+EXPORTED = ("moe_query_sizes", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
+            "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, msg=""):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+
+
+def lib():
+    return _lib
+
+
+def make_config(n_layers, n_experts, top_k, hidden, inter, n_shared, cache_slots, max_tokens,
+                lookahead=1, trace_capacity=0, fill_threads=0, flags=0) -> MoeConfig:
+    return MoeConfig(n_layers, n_experts, top_k, hidden, inter, n_shared, cache_slots, max_tokens,
+                     lookahead, trace_capacity, fill_threads, flags)
+
+
+def query_sizes(cfg: MoeConfig):
+    b, a, w = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = _lib.moe_query_sizes(ctypes.byref(cfg), ctypes.byref(b), ctypes.byref(a), ctypes.byref(w))
+    if st:
+        raise MoeError(st, "moe_query_sizes")
+    return b.value, a.value, w.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class OffloadMoE:
+    """One context: pinned expert pool, slot arena and workspace (torch device tensors), streams.
+
+    fill: (function pointer int, user pointer int) of a C callback, or a Python callable
+    fill(layer, expert, numpy_uint8_view) (slow; serialised by the GIL).
+    router_w: host numpy uint16 array [L][E][H] (bf16 bits).
+    """
+
+    def __init__(self, cfg: MoeConfig, fill, router_w, device=None, compute_stream=None, copy_stream=None):
+        import numpy as np
+        import torch
+
+        self.cfg = cfg
+        self.torch = torch
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+        self.blob_bytes, arena_bytes, ws_bytes = query_sizes(cfg)
+        self.arena = torch.empty(arena_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.compute_stream = compute_stream or torch.cuda.Stream(device=self.device)
+        self.copy_stream = copy_stream or torch.cuda.Stream(device=self.device)
+        rw = np.ascontiguousarray(router_w, dtype=np.uint16)
+        assert rw.shape == (cfg.n_layers, cfg.n_experts, cfg.hidden)
+        self._keep = [rw]
+        if callable(fill):
+            n = self.blob_bytes
+
+            def _cb(user, layer, expert, dst):
+                buf = np.ctypeslib.as_array(dst, shape=(n,))
+                fill(layer, expert, buf)
+
+            cb = FILL_FN(_cb)
+            self._keep.append(cb)
+            fptr, uptr = ctypes.cast(cb, ctypes.c_void_p).value, None
+        else:
+            fptr, uptr = fill
+        ctx = ctypes.c_void_p()
+        torch.cuda.synchronize(self.device)
+        st = _lib.moe_init_pool(ctypes.byref(cfg), fptr, uptr, rw.ctypes.data, _ptr(self.arena), arena_bytes,
+                                _ptr(self.workspace), ws_bytes, ctypes.c_void_p(self.compute_stream.cuda_stream),
+                                ctypes.c_void_p(self.copy_stream.cuda_stream), ctypes.byref(ctx))
+        if st:
+            raise MoeError(st, "moe_init_pool: " + _lib.moe_last_error(None).decode())
+        self.ctx = ctx
+
+    def _check(self, st, what):
+        if st:
+            raise MoeError(st, f"{what}: {_lib.moe_last_error(self.ctx).decode()}")
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            _lib.moe_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- calls (device tensors; all work is ordered on the compute stream) --
+    def cache_resolve(self, step, layer, ids, slots=None):
+        n = ctypes.c_int32()
+        self._check(_lib.moe_cache_resolve(self.ctx, step, layer, _ptr(ids), ids.shape[0], _ptr(slots),
+                                           ctypes.byref(n)), "moe_cache_resolve")
+        return n.value
+
+    def layer_forward(self, step, layer, x, y, ids=None, w=None):
+        self._check(_lib.moe_layer_forward(self.ctx, step, layer, _ptr(x), x.shape[0], _ptr(y), _ptr(ids), _ptr(w)),
+                    "moe_layer_forward")
+
+    def stack_forward(self, step, x, x_layer_stride, n_tokens, y, y_layer_stride, ids=None, w=None):
+        self._check(_lib.moe_stack_forward(self.ctx, step, _ptr(x), x_layer_stride, n_tokens, _ptr(y),
+                                           y_layer_stride, _ptr(ids), _ptr(w)), "moe_stack_forward")
+
+    def stats(self, trace_cap=0):
+        import numpy as np
+        c = MoeCounters()
+        buf = (MoeTraceRec * max(trace_cap, 1))()
+        n = ctypes.c_size_t()
+        self._check(_lib.moe_stats(self.ctx, ctypes.byref(c), ctypes.cast(buf, ctypes.c_void_p) if trace_cap else None,
+                                   trace_cap, ctypes.byref(n)), "moe_stats")
+        dt = np.dtype([(f, np.int32) for f in ("step", "layer", "expert", "slot", "hit", "evicted_key")])
+        recs = np.frombuffer(bytes(buf), dtype=dt, count=n.value).copy() if trace_cap else np.empty(0, dt)
+        return c.as_dict(), recs
+
+    def measure_h2d(self, bytes_per_copy, n_copies):
+        g = ctypes.c_double()
+        self._check(_lib.moe_measure_h2d(self.ctx, bytes_per_copy, n_copies, ctypes.byref(g)), "moe_measure_h2d")
+        return g.value
+
+    def cache_state(self):
+        import numpy as np
+        cfg = self.cfg
+        slot_of = np.empty(cfg.n_layers * cfg.n_experts, np.int32)
+        key_of = np.empty(cfg.cache_slots, np.int32)
+        stamp = np.empty(cfg.cache_slots, np.int64)
+        self._check(_lib.moe_cache_state(self.ctx, slot_of.ctypes.data, key_of.ctypes.data, stamp.ctypes.data),
+                    "moe_cache_state")
+        return slot_of, key_of, stamp

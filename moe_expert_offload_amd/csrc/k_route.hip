@@ -1,0 +1,317 @@
+// K1 router logits + top-k + softmax, K2 cache resolve, for gfx950 (wave64).
+//
+// Router (pirouter.ai "FreeToken x RTX 5090" page, mechanism section: the
+// router picks the experts each token uses, and the cache follows it).  The
+// pages fix neither the logit precision nor the selection rule; this library
+// computes each logit in FP32 with one fixed summation order (element i ->
+// lane (i/8) mod 64, each lane adds its products in increasing i, then an
+// xor-butterfly over 64 lanes), selects the k largest logits with ties going
+// to the lower expert index, and normalises the k selected logits with a
+// softmax.  Products of two bf16 values are exact in FP32, so an FMA and a
+// multiply-add agree and only the additions round.
+//
+// Resolve (ai-hardware-zukan.com FreeToken vs Ollama page, section on how
+// misses are made up for: the cache unit is the (layer, expert) pair and the
+// least recently used entry is replaced; gaming-st.com DeepSeek page: one
+// global LRU over all layers).  The requested set of a step is the ascending
+// unique expert ids of its tokens; hits are refreshed first (ascending id),
+// then every miss (ascending id) takes the next victim: empty slots by
+// ascending index, then the least recently used.  The GPU keeps the victim
+// order explicitly as an array of all C slots sorted by (last use, index) with
+// empty slots first, so each step is one O(C) stable compaction.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------- K1 --
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ float fold8(uint4 wv, uint4 xv, float p) {
+    p = fmaf(bf16lo(wv.x), bf16lo(xv.x), p);
+    p = fmaf(bf16hi(wv.x), bf16hi(xv.x), p);
+    p = fmaf(bf16lo(wv.y), bf16lo(xv.y), p);
+    p = fmaf(bf16hi(wv.y), bf16hi(xv.y), p);
+    p = fmaf(bf16lo(wv.z), bf16lo(xv.z), p);
+    p = fmaf(bf16hi(wv.z), bf16hi(xv.z), p);
+    p = fmaf(bf16lo(wv.w), bf16lo(xv.w), p);
+    p = fmaf(bf16hi(wv.w), bf16hi(xv.w), p);
+    return p;
+}
+
+// order-preserving 64-bit key: larger logit first, then lower expert index
+__device__ __forceinline__ uint64_t topk_key(float z, int e) {
+    uint32_t u = __float_as_uint(z + 0.0f);  // -0 -> +0
+    uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, d);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+constexpr int K1_WAVES = 4;
+constexpr int K1_MAXC = 16;  // candidates per lane: E <= 1024
+
+__global__ __launch_bounds__(K1_WAVES * 64) void k1_router(K1Args a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = blockIdx.x * K1_WAVES + wave;
+    const int b = blockIdx.y;
+    const uint16_t* x = a.x + (size_t)b * a.H;
+    if (e < a.E) {
+        const uint16_t* W = a.W + (size_t)e * a.H;
+        float p = 0.0f;
+        const int ng = a.H >> 3;
+        for (int g = lane; g < ng; g += 64) {
+            uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
+            uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)g * 8);
+            p = fold8(wv, xv, p);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+        if (lane == 0) a.z[(size_t)b * a.E + e] = p;
+    }
+    // the last workgroup to finish this token selects its experts
+    __shared__ int is_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned t = atomicAdd(&a.counter[b], 1u);
+        is_last = (t == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!is_last || wave != 0) return;
+    __threadfence();
+    const float* z = a.z + (size_t)b * a.E;
+    uint64_t key[K1_MAXC];
+#pragma unroll
+    for (int c = 0; c < K1_MAXC; ++c) {
+        int ee = lane + 64 * c;
+        key[c] = ee < a.E ? topk_key(z[ee], ee) : 0ull;
+    }
+    int my_id = 0;
+    for (int j = 0; j < a.k; ++j) {
+        uint64_t best = 0;
+        int bc = -1;
+#pragma unroll
+        for (int c = 0; c < K1_MAXC; ++c)
+            if (key[c] > best) { best = key[c]; bc = c; }
+        uint64_t wbest = wave_max_u64(best);
+        if (bc >= 0 && best == wbest) {
+#pragma unroll
+            for (int c = 0; c < K1_MAXC; ++c)
+                if (c == bc) key[c] = 0;
+        }
+        int id = (int)(0xFFFFFFFFu - (uint32_t)(wbest & 0xFFFFFFFFu));
+        if (lane == j) my_id = id;
+    }
+    // softmax over the k selected logits (FP32); lane j holds rank j
+    float zj = lane < a.k ? z[my_id] : 0.0f;
+    float z0 = __shfl(zj, 0);
+    float ej = lane < a.k ? expf(zj - z0) : 0.0f;
+    float den = 0.0f;
+    for (int j = 0; j < a.k; ++j) den += __shfl(ej, j);
+    if (lane < a.k) {
+        float wj = ej / den;
+        size_t o = (size_t)b * a.k + lane;
+        a.ids[o] = my_id;
+        a.w[o] = wj;
+        if (a.ids_out) a.ids_out[o] = my_id;
+        if (a.w_out) a.w_out[o] = wj;
+    }
+    if (lane == 0) a.counter[b] = 0u;
+}
+
+int launch_k1(const K1Args& a, void* stream) {
+    dim3 grid((a.E + K1_WAVES - 1) / K1_WAVES, a.B);
+    hipLaunchKernelGGL(k1_router, grid, dim3(K1_WAVES * 64), 0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------- K2 --
+
+constexpr int K2_THREADS = 1024;
+constexpr int K2_MAXE = 1024;
+constexpr int K2_MAXC = 16384;
+constexpr int K2_CPT = K2_MAXC / K2_THREADS;  // order entries per thread
+
+// exclusive prefix count of a 0/1 flag over the 1024 threads, in thread order
+__device__ __forceinline__ int block_rank(bool flag, int* s_wave, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t m = __ballot(flag);
+    int r = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < K2_THREADS / 64; ++w) {
+        int c = s_wave[w];
+        before += (w < wave) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return before + r;
+}
+
+// exclusive prefix sum of a small count over the 1024 threads, in thread order
+__device__ __forceinline__ int block_scan(int v, int* s_wave, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < K2_THREADS / 64; ++w) {
+        int c = s_wave[w];
+        before += (w < wave) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t* order_in,
+                                                         int32_t* order_out) {
+    __shared__ int32_t s_req[K2_MAXE];     // requested flag, then final slot per expert
+    __shared__ int32_t s_miss_e[K2_MAXE];  // misses by rank
+    __shared__ int32_t s_victim[K2_MAXE];  // victims by rank
+    __shared__ uint32_t s_hitbits[K2_MAXC / 32];
+    __shared__ int s_wave[K2_THREADS / 64];
+    __shared__ int s_evict, s_invalid;
+    const int tid = threadIdx.x;
+    const int E = a.E, C = a.C, l = a.layer;
+
+    for (int e = tid; e < E; e += K2_THREADS) s_req[e] = 0;
+    for (int i = tid; i < (C + 31) / 32; i += K2_THREADS) s_hitbits[i] = 0u;
+    if (tid == 0) { s_evict = 0; s_invalid = 0; }
+    __syncthreads();
+    for (int i = tid; i < a.n_ids; i += K2_THREADS) {
+        const int id = a.ids[i];
+        if ((unsigned)id < (unsigned)E) s_req[id] = 1;
+        else atomicAdd(&s_invalid, 1);
+    }
+    __syncthreads();
+
+    // classify the requested experts (thread e <-> expert e; E <= 1024)
+    const int e = tid;
+    const bool req = e < E && s_req[e] != 0;
+    const int v = req ? a.c.slot_of[l * E + e] : -1;
+    const bool hit = req && v >= 0;
+    const bool miss = req && v < 0;
+    int nh, nm;
+    const int hr = block_rank(hit, s_wave, nh);
+    const int mr = block_rank(miss, s_wave, nm);
+    const int64_t clock0 = *a.c.clock;
+    if (hit) atomicOr(&s_hitbits[v >> 5], 1u << (v & 31));
+    if (miss) s_miss_e[mr] = e;
+    __syncthreads();
+
+    // stable compaction of the victim order: non-hit slots keep their order;
+    // the first nm of them are this step's victims
+    int ent[K2_CPT];
+    int kept = 0;
+    const int p0 = tid * K2_CPT;
+#pragma unroll
+    for (int c = 0; c < K2_CPT; ++c) {
+        int p = p0 + c;
+        ent[c] = -1;
+        if (p < C) {
+            int sl = order_in[p];
+            bool is_hit = (s_hitbits[sl >> 5] >> (sl & 31)) & 1u;
+            ent[c] = is_hit ? -1 : sl;
+            kept += is_hit ? 0 : 1;
+        }
+    }
+    int nkept;
+    int kr = block_scan(kept, s_wave, nkept);
+#pragma unroll
+    for (int c = 0; c < K2_CPT; ++c) {
+        if (ent[c] < 0) continue;
+        if (kr < nm) s_victim[kr] = ent[c];
+        else order_out[kr - nm] = ent[c];
+        ++kr;
+    }
+    __syncthreads();
+
+    const int64_t trace_base = (int64_t)a.c.trace_head[0];
+    if (hit) {
+        a.c.stamp[v] = clock0 + hr;
+        order_out[C - nh - nm + hr] = v;
+        s_req[e] = v;
+        int64_t ti = trace_base + hr;
+        if (ti < a.c.trace_cap) {
+            TraceRec t = {a.step, l, e, v, 1, -1};
+            a.c.trace[ti] = t;
+        }
+    }
+    if (tid < nm) {
+        const int me = s_miss_e[tid];
+        const int vv = s_victim[tid];
+        const int old = a.c.key_of[vv];
+        if (old >= 0) {
+            a.c.slot_of[old] = -1;
+            atomicAdd(&s_evict, 1);
+        }
+        a.c.key_of[vv] = l * E + me;
+        a.c.slot_of[l * E + me] = vv;
+        a.c.stamp[vv] = clock0 + nh + tid;
+        order_out[C - nm + tid] = vv;
+        s_req[me] = vv;
+        int64_t ti = trace_base + nh + tid;
+        if (ti < a.c.trace_cap) {
+            TraceRec t = {a.step, l, me, vv, 0, old};
+            a.c.trace[ti] = t;
+        }
+        a.ml->e[tid].expert = me;
+        a.ml->e[tid].slot = vv;
+        __threadfence_system();
+    }
+    __syncthreads();
+    for (int i = tid; i < a.n_ids; i += K2_THREADS) {
+        const int id = a.ids[i];
+        int sl = (unsigned)id < (unsigned)E ? s_req[id] : -1;
+        a.slots[i] = sl;
+        if (a.slots_out) a.slots_out[i] = sl;
+    }
+    if (tid == 0) {
+        const int n = nh + nm;
+        *a.c.clock = clock0 + n;
+        a.c.counters[0] += (uint64_t)nh;
+        a.c.counters[1] += (uint64_t)nm;
+        a.c.counters[2] += (uint64_t)s_evict;
+        a.c.counters[3] += 1ull;
+        int64_t fit = a.c.trace_cap - trace_base;
+        fit = fit < 0 ? 0 : (fit > n ? n : fit);
+        a.c.trace_head[0] = (uint64_t)(trace_base + fit);
+        a.c.trace_head[1] += (uint64_t)(n - fit);
+        a.ml->n_miss = nm;
+        a.ml->n_unique = n;
+        a.ml->n_evict = s_evict;
+        a.ml->n_invalid = s_invalid;
+        __threadfence_system();
+        __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void* stream) {
+    hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, (hipStream_t)stream, a, order_in,
+                       order_out);
+    return (int)hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,696 @@
+// Host orchestrator and C ABI (include/moe.h).
+//
+// Owns the pinned host pool of every routed expert (pirouter.ai "FreeToken x
+// RTX 5090" page, section on how 65 GB runs on a 32 GB GPU: experts live in
+// pinned, DMA-readable host RAM), the resident router weights and shared
+// experts, the device cache state and the host-mapped miss lists.  Per layer
+// step it launches the router (K1) and the resolve kernel (K2) on the compute
+// stream, spins on the miss list K2 publishes in host-mapped memory, issues
+// one hipMemcpyAsync per miss on the copy stream (misses stream over PCIe),
+// and makes the compute stream wait for those copies before the FFN kernels
+// (K3, K4).  With lookahead 1 the next layer's K1/K2 and copies are issued
+// before the current layer's FFN, so its misses load while the current layer
+// computes (ai.holude.com preflight page, section on long prompts: the next
+// layer's experts load over PCIe while the GPU computes the current one).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include <immintrin.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+struct ProfSlot {
+    hipEvent_t ev[3];
+};
+
+struct moe_ctx {
+    moe_config cfg{};
+    Layout lay{};
+    int device = 0;
+    int nE = 0;                 // k + n_shared
+    hipStream_t cs = nullptr, ps = nullptr;
+    uint8_t* pool = nullptr;    // pinned host, [L*E][blob]
+    size_t pool_bytes = 0;
+    uint8_t* arena = nullptr;   // caller device memory, [C][blob]
+    uint8_t* shared_dev = nullptr;
+    uint16_t* router_dev = nullptr;
+    uint8_t* state_dev = nullptr;  // cache state block
+    CacheDev cd{};
+    int32_t* order[2] = {nullptr, nullptr};
+    int parity = 0;             // which order buffer is current
+    // workspace carve
+    float* z = nullptr;
+    int32_t* ids[2] = {nullptr, nullptr};
+    float* w[2] = {nullptr, nullptr};
+    int32_t* slots[2] = {nullptr, nullptr};
+    uint16_t* a[2] = {nullptr, nullptr};
+    uint32_t* k1cnt = nullptr;
+    // host-mapped miss lists
+    uint8_t* ml_mem = nullptr;
+    size_t ml_stride = 0;
+    int max_unique = 0;
+    int64_t seq = 0;
+    hipEvent_t copy_ev[2] = {nullptr, nullptr};
+    // host counters
+    uint64_t h2d_bytes = 0, h2d_copies = 0;
+    uint64_t k3_launches = 0, k4_launches = 0;
+    double k3_ms = 0, k4_ms = 0;
+    std::vector<ProfSlot> prof_used, prof_free;
+    std::vector<ProfSlot> copy_used;  // ev[0], ev[1] bracket one layer's miss copies
+    double h2d_ms = 0;
+    double spin_timeout_s = 60.0;
+    bool failed = false;
+    std::string err;
+};
+
+namespace {
+
+// message of the last failed moe_init_pool on this thread (its context no longer exists)
+thread_local std::string g_init_err;
+
+moe_status set_err(moe_ctx* c, moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (c) {
+        c->err = buf;
+        if (st == MOE_EHIP) c->failed = true;
+    }
+    return st;
+}
+
+#define HIPCHK(ctx, call)                                                                    \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return set_err((ctx), MOE_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+#define LAUNCHCHK(ctx, expr)                                                                            \
+    do {                                                                                                \
+        int e_ = (expr);                                                                                \
+        if (e_ != 0)                                                                                    \
+            return set_err((ctx), MOE_EHIP, "%s failed: %s", #expr, hipGetErrorString((hipError_t)e_)); \
+    } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status check_cfg(const moe_config* c) {
+    if (!c) return MOE_EINVAL;
+    if (c->n_layers < 1 || c->n_experts < 1 || c->n_experts > 1024 || c->top_k < 1 ||
+        c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
+        c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
+        c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 1 ||
+        c->cache_slots > 16384 || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0)
+        return MOE_EINVAL;
+    // the down kernel stages every selected expert's intermediate vector in LDS
+    if ((size_t)(c->top_k + c->n_shared) * (c->inter / 32) * 80 > 60 * 1024) return MOE_EINVAL;
+    const int64_t per_step = std::min<int64_t>((int64_t)c->max_tokens * c->top_k, c->n_experts);
+    if ((int64_t)c->cache_slots < 2 * per_step) return MOE_ECAPACITY;
+    return MOE_OK;
+}
+
+struct WsPlan {
+    size_t z, ids, w, slots, a, cnt, total;
+};
+
+WsPlan plan_workspace(const moe_config& c) {
+    WsPlan p{};
+    const size_t B = (size_t)c.max_tokens, k = (size_t)c.top_k, E = (size_t)c.n_experts;
+    const size_t nE = k + (size_t)c.n_shared;
+    size_t off = 0;
+    p.z = off;     off = align_up(off + B * E * 4, 256);
+    p.ids = off;   off = align_up(off + 2 * B * k * 4, 256);
+    p.w = off;     off = align_up(off + 2 * B * k * 4, 256);
+    p.slots = off; off = align_up(off + 2 * B * k * 4, 256);
+    p.a = off;     off = align_up(off + 2 * B * nE * (size_t)c.inter * 2, 256);
+    p.cnt = off;   off = align_up(off + B * 4, 256);
+    p.total = off;
+    return p;
+}
+
+// logical blob -> kernel layout (see moe_internal.h)
+void repack(const Layout& L, const uint8_t* src, uint8_t* dst) {
+    const size_t HI = (size_t)L.H * L.I;
+    const uint8_t* gc = src;
+    const uint8_t* gs = gc + HI / 2;
+    const uint8_t* uc = gs + HI / 32;
+    const uint8_t* us = uc + HI / 2;
+    const uint8_t* dc = us + HI / 32;
+    const uint8_t* ds = dc + HI / 2;
+    const int NB = L.NB, S = L.S3, NBI = L.NBI;
+    for (int tile = 0; tile < L.I / 16; ++tile) {
+        uint8_t* tb = dst + (size_t)tile * 16 * NB * 34;
+        uint8_t* tsc = tb + (size_t)16 * NB * 32;
+        for (int s = 0; s < S; ++s) {
+            const int nb = seg_len(NB, S, s), b0 = seg_begin(NB, S, s);
+            for (int t = 0; t < nb; ++t) {
+                for (int r = 0; r < 16; ++r) {
+                    const size_t row = (size_t)tile * 16 + r;
+                    const int blk = b0 + t;
+                    const size_t c = (size_t)((t * S + s) * 16 + r);
+                    memcpy(tb + c * 32, gc + row * (L.H / 2) + (size_t)blk * 16, 16);
+                    memcpy(tb + c * 32 + 16, uc + row * (L.H / 2) + (size_t)blk * 16, 16);
+                    tsc[c * 2] = gs[row * NB + blk];
+                    tsc[c * 2 + 1] = us[row * NB + blk];
+                }
+            }
+        }
+    }
+    uint8_t* dcd = dst + L.d_codes_off;
+    uint8_t* dsd = dst + L.d_scales_off;
+    for (int t8 = 0; t8 < L.H / 8; ++t8)
+        for (int ib = 0; ib < NBI; ++ib)
+            for (int r = 0; r < 8; ++r) {
+                const size_t h = (size_t)t8 * 8 + r;
+                const size_t cell = ((size_t)t8 * NBI + ib) * 8 + r;
+                memcpy(dcd + cell * 16, dc + h * (L.I / 2) + (size_t)ib * 16, 16);
+                dsd[cell] = ds[h * NBI + ib];
+            }
+}
+
+MissList* miss_list(moe_ctx* c, int parity) {
+    return reinterpret_cast<MissList*>(c->ml_mem + (size_t)parity * c->ml_stride);
+}
+
+void free_all(moe_ctx* c) {
+    if (!c) return;
+    if (c->cs) (void)hipStreamSynchronize(c->cs);
+    if (c->ps) (void)hipStreamSynchronize(c->ps);
+    for (auto& p : c->prof_used) for (auto e : p.ev) (void)hipEventDestroy(e);
+    for (auto& p : c->prof_free) for (auto e : p.ev) (void)hipEventDestroy(e);
+    for (auto& p : c->copy_used) for (auto e : p.ev) (void)hipEventDestroy(e);
+    for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
+    if (c->pool) (void)hipHostFree(c->pool);
+    if (c->ml_mem) (void)hipHostFree(c->ml_mem);
+    if (c->shared_dev) (void)hipFree(c->shared_dev);
+    if (c->router_dev) (void)hipFree(c->router_dev);
+    if (c->state_dev) (void)hipFree(c->state_dev);
+    delete c;
+}
+
+// ---------------------------------------------------------- one layer step --
+
+moe_status launch_route(moe_ctx* c, int layer, const void* x, int B, int par, int32_t* ids_out,
+                        float* w_out) {
+    K1Args a{};
+    a.W = c->router_dev + (size_t)layer * c->cfg.n_experts * c->cfg.hidden;
+    a.x = (const uint16_t*)x;
+    a.z = c->z;
+    a.ids = c->ids[par];
+    a.w = c->w[par];
+    a.ids_out = ids_out;
+    a.w_out = w_out;
+    a.counter = c->k1cnt;
+    a.E = c->cfg.n_experts;
+    a.H = c->cfg.hidden;
+    a.k = c->cfg.top_k;
+    a.B = B;
+    LAUNCHCHK(c, launch_k1(a, c->cs));
+    return MOE_OK;
+}
+
+moe_status launch_resolve(moe_ctx* c, int step, int layer, const int32_t* ids, int n_ids, int par,
+                          int32_t* slots_out) {
+    K2Args a{};
+    a.c = c->cd;
+    a.ids = ids;
+    a.slots = c->slots[par];
+    a.slots_out = slots_out;
+    a.ml = miss_list(c, par);
+    a.seq = ++c->seq;
+    a.n_ids = n_ids;
+    a.layer = layer;
+    a.step = step;
+    a.E = c->cfg.n_experts;
+    a.C = c->cfg.cache_slots;
+    const int p = c->parity;
+    LAUNCHCHK(c, launch_k2(a, c->order[p], c->order[p ^ 1], c->cs));
+    c->parity = p ^ 1;
+    return MOE_OK;
+}
+
+moe_status get_prof(moe_ctx* c, ProfSlot& p);
+
+// Waits for the miss list of resolve `seq` and issues its copies; records
+// copy_ev[par] when there are misses.  n_miss_out gets the count.
+moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss_out) {
+    MissList* ml = miss_list(c, par);
+    auto t0 = std::chrono::steady_clock::now();
+    uint64_t spins = 0;
+    while (__atomic_load_n(&ml->seq, __ATOMIC_ACQUIRE) != seq) {
+        _mm_pause();
+        if ((++spins & 0xFFFF) == 0) {
+            hipError_t q = hipStreamQuery(c->cs);
+            if (q != hipSuccess && q != hipErrorNotReady)
+                return set_err(c, MOE_EHIP, "compute stream failed while waiting for a miss list: %s",
+                               hipGetErrorString(q));
+            double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+            if (dt > c->spin_timeout_s)
+                return set_err(c, MOE_EHIP, "timed out waiting for the miss list of layer %d", layer);
+        }
+    }
+    const int nm = ml->n_miss;
+    if (ml->n_invalid) return set_err(c, MOE_EINVAL, "%d expert ids outside [0, E)", ml->n_invalid);
+    const size_t blob = c->lay.blob_bytes;
+    const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0 && nm > 0;
+    ProfSlot cp{};
+    if (prof) {
+        moe_status st = get_prof(c, cp);
+        if (st) return st;
+        HIPCHK(c, hipEventRecord(cp.ev[0], c->ps));
+    }
+    for (int i = 0; i < nm; ++i) {
+        const MissEntry m = ml->e[i];
+        const uint8_t* src = c->pool + ((size_t)layer * c->cfg.n_experts + m.expert) * blob;
+        uint8_t* dst = c->arena + (size_t)m.slot * blob;
+        HIPCHK(c, hipMemcpyAsync(dst, src, blob, hipMemcpyHostToDevice, c->ps));
+    }
+    if (prof) {
+        HIPCHK(c, hipEventRecord(cp.ev[1], c->ps));
+        c->copy_used.push_back(cp);
+    }
+    if (nm > 0) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
+    c->h2d_bytes += (uint64_t)nm * blob;
+    c->h2d_copies += (uint64_t)nm;
+    if (n_miss_out) *n_miss_out = nm;
+    return MOE_OK;
+}
+
+moe_status get_prof(moe_ctx* c, ProfSlot& p) {
+    if (!c->prof_free.empty()) {
+        p = c->prof_free.back();
+        c->prof_free.pop_back();
+        return MOE_OK;
+    }
+    for (auto& e : p.ev) HIPCHK(c, hipEventCreate(&e));
+    return MOE_OK;
+}
+
+moe_status launch_ffn(moe_ctx* c, int layer, const void* x, int B, int par, void* y, int n_miss) {
+    if (n_miss > 0) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
+    const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0;
+    ProfSlot ps{};
+    if (prof) {
+        moe_status st = get_prof(c, ps);
+        if (st) return st;
+        HIPCHK(c, hipEventRecord(ps.ev[0], c->cs));
+    }
+    K3Args a3{};
+    a3.arena = c->arena;
+    a3.shared = c->shared_dev;
+    a3.slots = c->slots[par];
+    a3.x = (const uint16_t*)x;
+    a3.a = c->a[par];
+    a3.blob_bytes = c->lay.blob_bytes;
+    a3.k = c->cfg.top_k;
+    a3.n_shared = c->cfg.n_shared;
+    a3.nE = c->nE;
+    a3.layer = layer;
+    a3.NB = c->lay.NB;
+    a3.S3 = c->lay.S3;
+    a3.I = c->cfg.inter;
+    LAUNCHCHK(c, launch_k3(a3, c->lay, B, c->cs));
+    if (prof) HIPCHK(c, hipEventRecord(ps.ev[1], c->cs));
+    K4Args a4{};
+    a4.arena = c->arena;
+    a4.shared = c->shared_dev;
+    a4.slots = c->slots[par];
+    a4.w = c->w[par];
+    a4.a = c->a[par];
+    a4.y = (uint16_t*)y;
+    a4.blob_bytes = c->lay.blob_bytes;
+    a4.d_codes_off = c->lay.d_codes_off;
+    a4.d_scales_off = c->lay.d_scales_off;
+    a4.k = c->cfg.top_k;
+    a4.n_shared = c->cfg.n_shared;
+    a4.nE = c->nE;
+    a4.layer = layer;
+    a4.NBI = c->lay.NBI;
+    a4.I = c->cfg.inter;
+    a4.H = c->cfg.hidden;
+    LAUNCHCHK(c, launch_k4(a4, c->lay, B, c->cs));
+    if (prof) {
+        HIPCHK(c, hipEventRecord(ps.ev[2], c->cs));
+        c->prof_used.push_back(ps);
+    }
+    return MOE_OK;
+}
+
+moe_status check_call(moe_ctx* c, int n_tokens) {
+    if (!c) return MOE_EINVAL;
+    if (c->failed) return MOE_ESTATE;
+    if (n_tokens < 1 || n_tokens > c->cfg.max_tokens)
+        return set_err(c, MOE_EINVAL, "n_tokens %d outside [1, %d]", n_tokens, c->cfg.max_tokens);
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI ==
+
+extern "C" {
+
+moe_status moe_query_sizes(const moe_config* cfg, size_t* blob_bytes, size_t* arena_bytes,
+                           size_t* workspace_bytes) {
+    moe_status st = check_cfg(cfg);
+    if (st) return st;
+    Layout L = make_layout(cfg->hidden, cfg->inter);
+    if (blob_bytes) *blob_bytes = L.blob_bytes;
+    if (arena_bytes) *arena_bytes = L.blob_bytes * (size_t)cfg->cache_slots;
+    if (workspace_bytes) *workspace_bytes = plan_workspace(*cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
+                         const uint16_t* router_w_bf16, void* slot_arena_dev, size_t arena_bytes,
+                         void* workspace_dev, size_t workspace_bytes, void* compute_stream,
+                         void* copy_stream, moe_ctx** out) {
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    moe_status st = check_cfg(cfg);
+    if (st) return st;
+    if (!fill || !router_w_bf16 || !slot_arena_dev || !workspace_dev) return MOE_EINVAL;
+    moe_ctx* c = new (std::nothrow) moe_ctx();
+    if (!c) return MOE_ENOMEM;
+    c->cfg = *cfg;
+    c->lay = make_layout(cfg->hidden, cfg->inter);
+    c->nE = cfg->top_k + cfg->n_shared;
+    c->cs = (hipStream_t)compute_stream;
+    c->ps = (hipStream_t)copy_stream;
+    const Layout& L = c->lay;
+    const int Lyr = cfg->n_layers, E = cfg->n_experts, C = cfg->cache_slots;
+    g_init_err.clear();
+    const char* where = "argument check";
+    auto bail = [&](moe_status s) {
+        hipError_t he = hipGetLastError();
+        g_init_err = std::string("moe_init_pool failed at ") + where + ": " + hipGetErrorString(he);
+        free_all(c);
+        return s;
+    };
+    if (arena_bytes < L.blob_bytes * (size_t)C) return bail(MOE_ENOMEM);
+    WsPlan wp = plan_workspace(*cfg);
+    if (workspace_bytes < wp.total) return bail(MOE_ENOMEM);
+    where = "device query";
+    if (hipGetDevice(&c->device) != hipSuccess) return bail(MOE_EHIP);
+    c->arena = (uint8_t*)slot_arena_dev;
+
+    // workspace carve
+    uint8_t* ws = (uint8_t*)workspace_dev;
+    const size_t Bk = (size_t)cfg->max_tokens * cfg->top_k;
+    c->z = (float*)(ws + wp.z);
+    for (int p = 0; p < 2; ++p) {
+        c->ids[p] = (int32_t*)(ws + wp.ids) + p * Bk;
+        c->w[p] = (float*)(ws + wp.w) + p * Bk;
+        c->slots[p] = (int32_t*)(ws + wp.slots) + p * Bk;
+        c->a[p] = (uint16_t*)(ws + wp.a) + (size_t)p * cfg->max_tokens * c->nE * cfg->inter;
+    }
+    c->k1cnt = (uint32_t*)(ws + wp.cnt);
+    where = "workspace clear";
+    if (hipMemsetAsync(c->k1cnt, 0, (size_t)cfg->max_tokens * 4, c->cs) != hipSuccess) return bail(MOE_EHIP);
+
+    // device cache state
+    const size_t n_sl = (size_t)Lyr * E;
+    const size_t trace_cap = (size_t)cfg->trace_capacity;
+    size_t off = 0, o_slot = off;
+    off = align_up(off + n_sl * 4, 256);
+    size_t o_key = off; off = align_up(off + (size_t)C * 4, 256);
+    size_t o_stamp = off; off = align_up(off + (size_t)C * 8, 256);
+    size_t o_clock = off; off = align_up(off + 8, 256);
+    size_t o_cnt = off; off = align_up(off + 4 * 8, 256);
+    size_t o_th = off; off = align_up(off + 2 * 8, 256);
+    size_t o_ord = off; off = align_up(off + 2 * (size_t)C * 4, 256);
+    size_t o_tr = off; off = align_up(off + std::max<size_t>(trace_cap, 1) * sizeof(TraceRec), 256);
+    where = "cache state allocation";
+    if (hipMalloc(&c->state_dev, off) != hipSuccess) return bail(MOE_ENOMEM);
+    c->cd.slot_of = (int32_t*)(c->state_dev + o_slot);
+    c->cd.key_of = (int32_t*)(c->state_dev + o_key);
+    c->cd.stamp = (int64_t*)(c->state_dev + o_stamp);
+    c->cd.clock = (int64_t*)(c->state_dev + o_clock);
+    c->cd.counters = (uint64_t*)(c->state_dev + o_cnt);
+    c->cd.trace_head = (uint64_t*)(c->state_dev + o_th);
+    c->cd.trace = (TraceRec*)(c->state_dev + o_tr);
+    c->cd.trace_cap = (int64_t)trace_cap;
+    c->order[0] = (int32_t*)(c->state_dev + o_ord);
+    c->order[1] = c->order[0] + C;
+    {
+        std::vector<uint8_t> h(o_tr, 0);
+        memset(h.data() + o_slot, 0xFF, n_sl * 4);
+        memset(h.data() + o_key, 0xFF, (size_t)C * 4);
+        memset(h.data() + o_stamp, 0xFF, (size_t)C * 8);
+        int32_t* ord = (int32_t*)(h.data() + o_ord);
+        for (int v = 0; v < C; ++v) ord[v] = v;  // cold start: all empty, ascending index
+        if (hipMemcpy(c->state_dev, h.data(), o_tr, hipMemcpyHostToDevice) != hipSuccess) return bail(MOE_EHIP);
+    }
+
+    // host-mapped miss lists (two, alternating by layer parity)
+    where = "miss list allocation";
+    c->max_unique = (int)std::min<int64_t>((int64_t)cfg->max_tokens * cfg->top_k, E);
+    c->ml_stride = align_up(sizeof(MissList) + sizeof(MissEntry) * (size_t)c->max_unique, 256);
+    if (hipHostMalloc((void**)&c->ml_mem, 2 * c->ml_stride, hipHostMallocMapped | hipHostMallocCoherent) !=
+        hipSuccess)
+        return bail(MOE_ENOMEM);
+    memset(c->ml_mem, 0, 2 * c->ml_stride);
+    for (int p = 0; p < 2; ++p) miss_list(c, p)->seq = -1;
+    for (auto& e : c->copy_ev)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
+
+    // router weights -> HBM
+    where = "router upload";
+    const size_t rbytes = (size_t)Lyr * E * cfg->hidden * 2;
+    if (hipMalloc(&c->router_dev, rbytes) != hipSuccess) return bail(MOE_ENOMEM);
+    if (hipMemcpy(c->router_dev, router_w_bf16, rbytes, hipMemcpyHostToDevice) != hipSuccess) return bail(MOE_EHIP);
+
+    // pinned pool, filled in parallel
+    where = "pinned pool allocation";
+    c->pool_bytes = n_sl * L.blob_bytes;
+    if (hipHostMalloc((void**)&c->pool, c->pool_bytes, hipHostMallocDefault) != hipSuccess) {
+        c->pool = nullptr;
+        return bail(MOE_ENOMEM);
+    }
+    int nth = cfg->fill_threads > 0 ? cfg->fill_threads : (int)std::thread::hardware_concurrency();
+    nth = std::max(1, std::min<int>(nth, (int)std::min<size_t>(n_sl, 64)));
+    std::atomic<size_t> next{0};
+    auto worker = [&]() {
+        std::vector<uint8_t> tmp(L.blob_bytes);
+        for (;;) {
+            size_t i = next.fetch_add(1);
+            if (i >= n_sl) break;
+            fill(user, (int32_t)(i / E), (int32_t)(i % E), tmp.data());
+            repack(L, tmp.data(), c->pool + i * L.blob_bytes);
+        }
+    };
+    std::vector<std::thread> th;
+    for (int t = 0; t < nth; ++t) th.emplace_back(worker);
+    for (auto& t : th) t.join();
+
+    // shared experts -> HBM
+    where = "shared expert upload";
+    if (cfg->n_shared > 0) {
+        const size_t sb = (size_t)Lyr * cfg->n_shared * L.blob_bytes;
+        if (hipMalloc(&c->shared_dev, sb) != hipSuccess) return bail(MOE_ENOMEM);
+        std::vector<uint8_t> tmp(L.blob_bytes), packed(L.blob_bytes);
+        for (int l = 0; l < Lyr; ++l)
+            for (int s = 0; s < cfg->n_shared; ++s) {
+                fill(user, l, -1 - s, tmp.data());
+                repack(L, tmp.data(), packed.data());
+                if (hipMemcpy(c->shared_dev + ((size_t)l * cfg->n_shared + s) * L.blob_bytes, packed.data(),
+                              L.blob_bytes, hipMemcpyHostToDevice) != hipSuccess)
+                    return bail(MOE_EHIP);
+            }
+    }
+    if (hipStreamSynchronize(c->cs) != hipSuccess) return bail(MOE_EHIP);
+    *out = c;
+    return MOE_OK;
+}
+
+moe_status moe_cache_resolve(moe_ctx* c, int32_t step, int32_t layer, const int32_t* ids_dev,
+                             int32_t n_tokens, int32_t* slots_dev, int32_t* n_miss_out) {
+    moe_status st = check_call(c, n_tokens);
+    if (st) return st;
+    if (layer < 0 || layer >= c->cfg.n_layers || !ids_dev) return set_err(c, MOE_EINVAL, "bad layer or ids");
+    st = launch_resolve(c, step, layer, ids_dev, n_tokens * c->cfg.top_k, 0, slots_dev);
+    if (st) return st;
+    int nm = 0;
+    st = stage_misses(c, layer, 0, c->seq, &nm);
+    if (st) return st;
+    if (nm > 0) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[0], 0));
+    if (n_miss_out) *n_miss_out = nm;
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward(moe_ctx* c, int32_t step, int32_t layer, const void* x, int32_t n_tokens,
+                             void* y, int32_t* ids_out, float* w_out) {
+    moe_status st = check_call(c, n_tokens);
+    if (st) return st;
+    if (layer < 0 || layer >= c->cfg.n_layers || !x || !y) return set_err(c, MOE_EINVAL, "bad layer or buffers");
+    if ((st = launch_route(c, layer, x, n_tokens, 0, ids_out, w_out))) return st;
+    if ((st = launch_resolve(c, step, layer, c->ids[0], n_tokens * c->cfg.top_k, 0, nullptr))) return st;
+    int nm = 0;
+    if ((st = stage_misses(c, layer, 0, c->seq, &nm))) return st;
+    return launch_ffn(c, layer, x, n_tokens, 0, y, nm);
+}
+
+moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs, int32_t n_tokens,
+                             void* y, int64_t ys, int32_t* ids_out, float* w_out) {
+    moe_status st = check_call(c, n_tokens);
+    if (st) return st;
+    if (!x || !y) return set_err(c, MOE_EINVAL, "null buffers");
+    const int L = c->cfg.n_layers;
+    const size_t kB = (size_t)n_tokens * c->cfg.top_k;
+    auto xl = [&](int l) { return (const uint16_t*)x + (size_t)l * xs; };
+    auto yl = [&](int l) { return (uint16_t*)y + (size_t)l * ys; };
+    auto idl = [&](int l) { return ids_out ? ids_out + (size_t)l * kB : nullptr; };
+    auto wl = [&](int l) { return w_out ? w_out + (size_t)l * kB : nullptr; };
+    if (c->cfg.lookahead == 0) {
+        for (int l = 0; l < L; ++l) {
+            if ((st = launch_route(c, l, xl(l), n_tokens, 0, idl(l), wl(l)))) return st;
+            if ((st = launch_resolve(c, step, l, c->ids[0], (int)kB, 0, nullptr))) return st;
+            int nm = 0;
+            if ((st = stage_misses(c, l, 0, c->seq, &nm))) return st;
+            if ((st = launch_ffn(c, l, xl(l), n_tokens, 0, yl(l), nm))) return st;
+        }
+        return MOE_OK;
+    }
+    // lookahead 1: K1/K2 of layer l+1 and its copies are issued before layer l's FFN
+    int64_t seq_of[2] = {0, 0};
+    if ((st = launch_route(c, 0, xl(0), n_tokens, 0, idl(0), wl(0)))) return st;
+    if ((st = launch_resolve(c, step, 0, c->ids[0], (int)kB, 0, nullptr))) return st;
+    seq_of[0] = c->seq;
+    for (int l = 0; l < L; ++l) {
+        const int par = l & 1;
+        int nm = 0;
+        if ((st = stage_misses(c, l, par, seq_of[par], &nm))) return st;
+        if (l + 1 < L) {
+            const int np = par ^ 1;
+            if ((st = launch_route(c, l + 1, xl(l + 1), n_tokens, np, idl(l + 1), wl(l + 1)))) return st;
+            if ((st = launch_resolve(c, step, l + 1, c->ids[np], (int)kB, np, nullptr))) return st;
+            seq_of[np] = c->seq;
+        }
+        if ((st = launch_ffn(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t cap, size_t* n_out) {
+    if (!c) return MOE_EINVAL;
+    if (c->failed) return MOE_ESTATE;
+    HIPCHK(c, hipStreamSynchronize(c->cs));
+    HIPCHK(c, hipStreamSynchronize(c->ps));
+    uint64_t cnt[4], th[2];
+    HIPCHK(c, hipMemcpy(cnt, c->cd.counters, sizeof cnt, hipMemcpyDeviceToHost));
+    HIPCHK(c, hipMemcpy(th, c->cd.trace_head, sizeof th, hipMemcpyDeviceToHost));
+    size_t n = (size_t)th[0];
+    size_t take = std::min(n, buf ? cap : 0);
+    if (take) HIPCHK(c, hipMemcpy(buf, c->cd.trace, take * sizeof(moe_trace_rec), hipMemcpyDeviceToHost));
+    uint64_t dropped = th[1] + (n - take);
+    static_assert(sizeof(moe_trace_rec) == sizeof(TraceRec), "trace record layout");
+    // drain: restart the trace at 0, keep the dropped count
+    uint64_t zero2[2] = {0, dropped};
+    HIPCHK(c, hipMemcpy(c->cd.trace_head, zero2, sizeof zero2, hipMemcpyHostToDevice));
+    for (auto& p : c->prof_used) {
+        float a = 0, b = 0;
+        HIPCHK(c, hipEventElapsedTime(&a, p.ev[0], p.ev[1]));
+        HIPCHK(c, hipEventElapsedTime(&b, p.ev[1], p.ev[2]));
+        c->k3_ms += a;
+        c->k4_ms += b;
+        c->k3_launches++;
+        c->k4_launches++;
+        c->prof_free.push_back(p);
+    }
+    c->prof_used.clear();
+    for (auto& p : c->copy_used) {
+        float a = 0;
+        HIPCHK(c, hipEventElapsedTime(&a, p.ev[0], p.ev[1]));
+        c->h2d_ms += a;
+        c->prof_free.push_back(p);
+    }
+    c->copy_used.clear();
+    if (out) {
+        out->hits = cnt[0];
+        out->misses = cnt[1];
+        out->evictions = cnt[2];
+        out->resolves = cnt[3];
+        out->h2d_bytes = c->h2d_bytes;
+        out->h2d_copies = c->h2d_copies;
+        out->trace_records = take;
+        out->trace_dropped = dropped;
+        out->k3_launches = c->k3_launches;
+        out->k4_launches = c->k4_launches;
+        out->k3_ms = c->k3_ms;
+        out->k4_ms = c->k4_ms;
+        out->h2d_ms = c->h2d_ms;
+    }
+    c->k3_launches = c->k4_launches = 0;
+    c->k3_ms = c->k4_ms = c->h2d_ms = 0;
+    if (n_out) *n_out = take;
+    return MOE_OK;
+}
+
+moe_status moe_measure_h2d(moe_ctx* c, size_t bytes, int32_t n_copies, double* gbps) {
+    if (!c || !gbps || bytes == 0 || n_copies < 1) return MOE_EINVAL;
+    if (c->failed) return MOE_ESTATE;
+    const size_t blob = c->lay.blob_bytes;
+    const size_t n_blobs = c->pool_bytes / blob;
+    if (bytes > c->pool_bytes) return set_err(c, MOE_EINVAL, "copy larger than the pool");
+    const size_t span = (bytes + blob - 1) / blob;  // blobs covered by one copy
+    uint8_t* scratch = nullptr;
+    HIPCHK(c, hipMalloc(&scratch, 2 * bytes));
+    hipEvent_t e0, e1;
+    HIPCHK(c, hipEventCreate(&e0));
+    HIPCHK(c, hipEventCreate(&e1));
+    HIPCHK(c, hipStreamSynchronize(c->ps));
+    uint64_t r = 0x9E3779B97F4A7C15ull;
+    auto next_off = [&]() {
+        r ^= r << 13; r ^= r >> 7; r ^= r << 17;
+        size_t i = (size_t)(r % (n_blobs > span ? n_blobs - span + 1 : 1));
+        return i * blob;
+    };
+    // warm-up copy, then the timed ones
+    HIPCHK(c, hipMemcpyAsync(scratch, c->pool + next_off(), bytes, hipMemcpyHostToDevice, c->ps));
+    HIPCHK(c, hipEventRecord(e0, c->ps));
+    for (int i = 0; i < n_copies; ++i)
+        HIPCHK(c, hipMemcpyAsync(scratch + (size_t)(i & 1) * bytes, c->pool + next_off(), bytes,
+                                 hipMemcpyHostToDevice, c->ps));
+    HIPCHK(c, hipEventRecord(e1, c->ps));
+    HIPCHK(c, hipEventSynchronize(e1));
+    float ms = 0;
+    HIPCHK(c, hipEventElapsedTime(&ms, e0, e1));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    HIPCHK(c, hipFree(scratch));
+    *gbps = (double)bytes * n_copies / (ms * 1e-3) / 1e9;
+    return MOE_OK;
+}
+
+moe_status moe_cache_state(moe_ctx* c, int32_t* slot_of, int32_t* key_of, int64_t* stamp) {
+    if (!c) return MOE_EINVAL;
+    if (c->failed) return MOE_ESTATE;
+    HIPCHK(c, hipStreamSynchronize(c->cs));
+    const size_t n_sl = (size_t)c->cfg.n_layers * c->cfg.n_experts, C = (size_t)c->cfg.cache_slots;
+    if (slot_of) HIPCHK(c, hipMemcpy(slot_of, c->cd.slot_of, n_sl * 4, hipMemcpyDeviceToHost));
+    if (key_of) HIPCHK(c, hipMemcpy(key_of, c->cd.key_of, C * 4, hipMemcpyDeviceToHost));
+    if (stamp) HIPCHK(c, hipMemcpy(stamp, c->cd.stamp, C * 8, hipMemcpyDeviceToHost));
+    return MOE_OK;
+}
+
+void moe_destroy(moe_ctx* c) { free_all(c); }
+
+const char* moe_last_error(const moe_ctx* c) { return c ? c->err.c_str() : g_init_err.c_str(); }
+
+}  // extern "C"

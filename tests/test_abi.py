@@ -1,0 +1,71 @@
+"""The C ABI library loads and exports every entry point include/moe.h declares; host-side
+argument checks (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ("moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stats"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import moe_expert_offload_amd as M
+    for n in declared():
+        assert hasattr(M.lib(), n), n
+        assert n in M.EXPORTED
+
+
+def _cfg(**kw):
+    import moe_expert_offload_amd as M
+    base = dict(n_layers=2, n_experts=16, top_k=2, hidden=256, inter=512, n_shared=0, cache_slots=8,
+                max_tokens=1)
+    base.update(kw)
+    return M.make_config(**base)
+
+
+def test_query_sizes_and_blob_size():
+    import moe_expert_offload_amd as M
+    b, a, w = M.query_sizes(_cfg())
+    assert b == 3 * 256 * 512 * 17 // 32
+    assert a == 8 * b and w > 0
+    b, _, _ = M.query_sizes(_cfg(hidden=2880, inter=2880, n_experts=128, top_k=4, cache_slots=1862))
+    assert b == 13_219_200
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=100), -1), (dict(inter=48), -1), (dict(top_k=17), -1), (dict(top_k=20, n_experts=16), -1),
+    (dict(n_experts=2000), -1), (dict(n_shared=2), -1), (dict(max_tokens=0), -1),
+    (dict(cache_slots=3), -4), (dict(max_tokens=4, cache_slots=15), -4), (dict(cache_slots=20000), -1),
+])
+def test_config_rejected(kw, status):
+    import moe_expert_offload_amd as M
+    with pytest.raises(M.MoeError) as ei:
+        M.query_sizes(_cfg(**kw))
+    assert ei.value.status == status
+
+
+def test_null_context_calls_fail_cleanly():
+    import moe_expert_offload_amd as M
+    L = M.lib()
+    assert L.moe_layer_forward(None, 0, 0, None, 1, None, None, None) == M.MOE_EINVAL
+    assert L.moe_stack_forward(None, 0, None, 0, 1, None, 0, None, None) == M.MOE_EINVAL
+    assert L.moe_cache_resolve(None, 0, 0, None, 1, None, None) == M.MOE_EINVAL
+    assert L.moe_stats(None, None, None, 0, None) == M.MOE_EINVAL
+    out = ctypes.c_void_p(1)
+    assert L.moe_init_pool(ctypes.byref(_cfg()), None, None, None, None, 0, None, 0, None, None,
+                           ctypes.byref(out)) == M.MOE_EINVAL
+    assert out.value is None
+    L.moe_destroy(None)

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bit-exact: expert ids, cache trace records, slots and final cache state.
+Tolerance: routing weights |diff| <= 1e-5; layer outputs per (step, layer, token) vector
+relative L2 <= 5e-3 and max|diff| <= 1e-2 * max|ref| (bf16 activations, FP32 accumulation).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import close_enough, make_moe, run_stack, trace_tuples
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref_outputs(wl, X, ref, points):
+    out = {}
+    for (t, l, b) in points:
+        out[(t, l, b)] = oracle.moe_output(wl, l, X[t, b], ref["ids"][t, l, b], ref["w"][t, l, b])
+    return out
+
+
+def _check_run(wl, X, ids, w, y, recs, m, points, ref=None):
+    ref = ref or oracle.decode_trace(wl, synth.router_weights(wl), X)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["w"])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    slot_of, key_of, stamp = m.cache_state()
+    r_slot, r_key, r_stamp = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    np.testing.assert_array_equal(stamp, r_stamp)
+    worst = 0.0
+    for (t, l, b), r in _ref_outputs(wl, X, ref, points).items():
+        rel, mx, ok = close_enough(y[t, l, b], r)
+        worst = max(worst, rel)
+        assert ok, (t, l, b, rel, mx)
+    return ref, worst
+
+
+def test_toy_decode_all_outputs():
+    wl = synth.WORKLOADS["toy"]
+    X = synth.decode_inputs(wl)
+    m, _ = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    cnt, recs = m.stats(trace_cap=1 << 20)
+    T = X.shape[0]
+    points = [(t, l, 0) for t in range(T) for l in range(wl.n_layers)]
+    ref, worst = _check_run(wl, X, ids, w, y, recs, m, points)
+    c = ref["counters"]
+    assert (cnt["hits"], cnt["misses"], cnt["evictions"]) == (c["hits"], c["misses"], c["evictions"])
+    assert cnt["h2d_bytes"] == c["misses"] * wl.blob_bytes
+    print("toy worst rel-L2", worst)
+    m.close()
+
+
+def test_lookahead_and_causal_are_bitwise_equal():
+    wl = synth.WORKLOADS["toy"]
+    X = synth.decode_inputs(wl)[:24]
+    m1, _ = make_moe(wl, lookahead=1)
+    _, _, y1 = run_stack(m1, wl, X)
+    m1.close()
+    m0, _ = make_moe(wl, lookahead=0)
+    _, _, y0 = run_stack(m0, wl, X)
+    m0.close()
+    np.testing.assert_array_equal(y0.view(np.uint32), y1.view(np.uint32))
+
+
+def test_layer_forward_matches_stack():
+    import torch
+    wl = synth.WORKLOADS["toy"]
+    X = synth.decode_inputs(wl)[:8]
+    m, _ = make_moe(wl, lookahead=1)
+    _, _, ys = run_stack(m, wl, X)
+    m.close()
+    m, _ = make_moe(wl, lookahead=0)
+    dev = m.device
+    xd = torch.from_numpy(X.view(np.int16)).to(dev)
+    y = torch.empty((X.shape[0], wl.n_layers, 1, wl.hidden), dtype=torch.int16, device=dev)
+    with torch.cuda.stream(m.compute_stream):
+        for t in range(X.shape[0]):
+            for l in range(wl.n_layers):
+                m.layer_forward(t, l, xd[t], y[t, l])
+    m.compute_stream.synchronize()
+    from gpu_helpers import bf16_to_f32
+    np.testing.assert_array_equal(bf16_to_f32(y).view(np.uint32), ys.view(np.uint32))
+    m.close()
+
+
+# several tiles, ragged segment tails (H = 2880 -> 90 blocks over 16 segments) and a shared expert
+SMALL = [
+    synth.Workload("ragged_2880", 3, 8, 2, 0, 2880, 2880, 6, 12, 1, 0.9, seed=11),
+    synth.Workload("shared_k8", 3, 32, 8, 1, 2048, 512, 20, 16, 1, 0.9, seed=12),
+    synth.Workload("odd_blocks", 2, 24, 3, 1, 800, 96, 8, 16, 1, 0.85, seed=13),
+    synth.Workload("wide_4096", 2, 16, 6, 0, 4096, 2048, 14, 10, 1, 0.85, seed=14),
+    synth.Workload("e512_k10", 2, 512, 10, 1, 3072, 768, 24, 10, 1, 0.9, seed=15),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes_all_outputs(wl):
+    X = synth.decode_inputs(wl)
+    m, _ = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    _, recs = m.stats(trace_cap=1 << 20)
+    points = [(t, l, 0) for t in range(X.shape[0]) for l in range(wl.n_layers)]
+    _, worst = _check_run(wl, X, ids, w, y, recs, m, points)
+    print(wl.name, "worst rel-L2", worst)
+    m.close()
+
+
+def test_zero_input_edge_case():
+    wl = synth.WORKLOADS["toy"]
+    X = np.zeros((3, 1, wl.hidden), np.uint16)
+    m, _ = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    assert np.all(ids == np.arange(wl.top_k))
+    np.testing.assert_allclose(w, 1.0 / wl.top_k, atol=1e-7)
+    assert np.all(y == 0)
+    m.close()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_cache_resolve_random_batches(seed):
+    """moe_cache_resolve with caller ids (several tokens, duplicates) against the oracle LRU."""
+    import torch
+    rng = np.random.default_rng(seed)
+    wl = synth.Workload("resolve", 3, 16, 3, 0, 256, 64, 24, 1, 4, 0.9, seed=seed)
+    m, _ = make_moe(wl, max_tokens=4)
+    cache = oracle.Cache(wl.n_layers, wl.n_experts, wl.cache_slots)
+    recs_ref = []
+    for s in range(60):
+        l = int(rng.integers(0, wl.n_layers))
+        B = int(rng.integers(1, 5))
+        ids = rng.integers(0, wl.n_experts, size=(B, wl.top_k)).astype(np.int32)
+        idd = torch.from_numpy(ids).to(m.device)
+        sl = torch.empty_like(idd)
+        with torch.cuda.stream(m.compute_stream):
+            nm = m.cache_resolve(s, l, idd, sl)
+        m.compute_stream.synchronize()
+        slots_ref, r = cache.step(s, l, ids)
+        recs_ref.append(r)
+        assert nm == int((r["hit"] == 0).sum())
+        np.testing.assert_array_equal(sl.cpu().numpy().ravel(), slots_ref)
+    _, recs = m.stats(trace_cap=1 << 16)
+    assert trace_tuples(recs) == trace_tuples(np.concatenate(recs_ref))
+    m.close()
+
+
+def test_slot_bytes_equal_pool_blob_after_fill():
+    """After misses land, the FFN of a slot equals the FFN of the pool blob: checked through
+    outputs at a cache size that forces evictions every step (C = 2 * k)."""
+    wl = dataclasses.replace(synth.WORKLOADS["toy"], cache_slots=4)
+    X = synth.decode_inputs(wl)[:16]
+    m, _ = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    _, recs = m.stats(trace_cap=1 << 16)
+    points = [(t, l, 0) for t in range(16) for l in range(wl.n_layers)]
+    ref, _ = _check_run(wl, X, ids, w, y, recs, m, points)
+    assert ref["counters"]["evictions"] > 0
+    m.close()
