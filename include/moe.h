@@ -15,11 +15,12 @@
  *   ai.holude.com preflight page, section on long prompts: the next layer's
  *   experts are loaded over PCIe while the GPU computes the current layer.
  *
- * Per token and layer the library runs: router logits + top-k + softmax over
- * the selected logits (K1), resolution of the selected (layer, expert) pairs
- * to cache slots with a miss list (K2), one host-to-device copy per miss on the
- * copy stream, the selected experts' MXFP4 SwiGLU FFNs (K3: gate/up + SwiGLU;
- * K4: down projection fused with the weighted combine and the shared expert).
+ * Per token and layer the library runs: router logits (K1), top-k + softmax
+ * over the selected logits and resolution of the selected (layer, expert)
+ * pairs to cache slots with a miss list (K2), one host-to-device copy per miss
+ * on the copy stream, then the expert FFN: the selected experts' MXFP4
+ * gate/up + SwiGLU (K3), and the down projection fused with the weighted
+ * combine and the shared expert (K4).
  *
  * Conventions
  *  - Every call returns moe_status; nothing throws or aborts across the ABI.
@@ -62,8 +63,7 @@ typedef enum {
 } moe_status;
 
 enum {
-    MOE_FLAG_PROFILE = 1,  /* time every K3 and K4 launch and every layer's miss copies with HIP
-                              events (read via moe_stats) */
+    MOE_FLAG_PROFILE = 1,  /* time every K3 and K4 launch with HIP events (read via moe_stats) */
 };
 
 typedef struct {
@@ -118,8 +118,8 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
 moe_status moe_cache_resolve(moe_ctx* ctx, int32_t step, int32_t layer, const int32_t* ids_dev,
                              int32_t n_tokens, int32_t* slots_dev, int32_t* n_miss_out);
 
-/* One layer for n_tokens tokens, causal: router (K1) -> resolve (K2) -> miss
- * copies -> FFN (K3, K4).  x_bf16_dev: [n_tokens][H]; y_bf16_dev: [n_tokens][H]
+/* One layer for n_tokens tokens, causal: router (K1) -> top-k + resolve (K2)
+ * -> miss copies -> expert FFN (K3, K4).  x_bf16_dev: [n_tokens][H]; y_bf16_dev: [n_tokens][H]
  * = sum_j w_j * FFN_{id_j}(x) + shared(x).  ids_dev_out ([n_tokens][k] int32,
  * ranked by logit) and w_dev_out ([n_tokens][k] float) may be NULL. */
 moe_status moe_layer_forward(moe_ctx* ctx, int32_t step, int32_t layer, const void* x_bf16_dev,
@@ -134,14 +134,20 @@ moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev,
                              int32_t n_tokens, void* y_bf16_dev, int64_t y_layer_stride,
                              int32_t* ids_dev_out, float* w_dev_out);
 
+/* Expert FFN of one layer with caller-resolved slots (e.g. from moe_cache_resolve):
+ * y = sum_j w_j * FFN(slot_j)(x) + shared(x), K3 then K4 on the compute stream.
+ * slots_dev [n_tokens][k] int32 must name slots that hold this layer's experts (the
+ * library does not check); w_dev [n_tokens][k] float. */
+moe_status moe_expert_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16_dev, int32_t n_tokens,
+                              const int32_t* slots_dev, const float* w_dev, void* y_bf16_dev);
+
 typedef struct {
     uint64_t hits, misses, evictions;  /* cache accesses (unique (layer, expert) per step) */
     uint64_t resolves;                 /* layer steps resolved */
     uint64_t h2d_bytes, h2d_copies;    /* miss copies issued */
     uint64_t trace_records, trace_dropped;
-    uint64_t k3_launches, k4_launches; /* with MOE_FLAG_PROFILE: timed launches ... */
-    double k3_ms, k4_ms;               /* ... and their summed durations (HIP events) */
-    double h2d_ms;                     /* with MOE_FLAG_PROFILE: summed busy time of the miss copies */
+    uint64_t ffn_launches;             /* with MOE_FLAG_PROFILE: timed layer FFNs (one K3 + one K4) */
+    double k3_ms, k4_ms;               /* ... and the summed durations of K3 and K4 (HIP events) */
 } moe_counters;
 
 typedef struct {

@@ -40,8 +40,7 @@ class MoeConfig(ctypes.Structure):
 class MoeCounters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "trace_records",
-        "trace_dropped", "k3_launches", "k4_launches")] + [("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double),
-                                              ("h2d_ms", ctypes.c_double)]
+        "trace_dropped", "ffn_launches")] + [("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -69,6 +68,8 @@ _lib.moe_layer_forward.restype = _st
 _lib.moe_layer_forward.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P, _P]
 _lib.moe_stack_forward.restype = _st
 _lib.moe_stack_forward.argtypes = [_P, _I32, _P, ctypes.c_int64, _I32, _P, ctypes.c_int64, _P, _P]
+_lib.moe_expert_forward.restype = _st
+_lib.moe_expert_forward.argtypes = [_P, _I32, _P, _I32, _P, _P, _P]
 _lib.moe_stats.restype = _st
 _lib.moe_stats.argtypes = [_P, ctypes.POINTER(MoeCounters), _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
 _lib.moe_measure_h2d.restype = _st
@@ -81,7 +82,7 @@ _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = [_P]
 
 EXPORTED = ("moe_query_sizes", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
-            "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
+            "moe_expert_forward", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -185,6 +186,10 @@ class OffloadMoE:
     def stack_forward(self, step, x, x_layer_stride, n_tokens, y, y_layer_stride, ids=None, w=None):
         self._check(_lib.moe_stack_forward(self.ctx, step, _ptr(x), x_layer_stride, n_tokens, _ptr(y),
                                            y_layer_stride, _ptr(ids), _ptr(w)), "moe_stack_forward")
+
+    def expert_forward(self, layer, x, slots, w, y):
+        self._check(_lib.moe_expert_forward(self.ctx, layer, _ptr(x), x.shape[0], _ptr(slots), _ptr(w), _ptr(y)),
+                    "moe_expert_forward")
 
     def stats(self, trace_cap=0):
         import numpy as np

@@ -1,6 +1,7 @@
-// K3 (gate/up + SwiGLU) and K4 (down + weighted combine + shared expert):
-// the expert FFN of one MoE layer for a few tokens, streaming MXFP4 weights
-// from HBM (the slot arena, and the resident shared experts).
+// The expert FFN of one MoE layer for a few tokens in one launch: gate/up +
+// SwiGLU (phase 1) and down + weighted combine + shared expert (phase 2),
+// streaming MXFP4 weights from HBM (the slot arena and the resident shared
+// experts).
 //
 // The FFN form is not stated on the pages; the reading used here is the
 // SwiGLU expert of the MoE models they discuss: a = silu(W_gate x) * (W_up x),
@@ -21,6 +22,15 @@
 // distinct addresses a wave reads in one instruction fall in distinct banks.
 // Reductions across lanes and waves run in a fixed order, so results are
 // bitwise reproducible from run to run.
+//
+// Two launches per layer: K3 (gate/up + SwiGLU -> intermediate vector `a`)
+// and K4 (down + weighted combine + shared expert).  K4 needs all of `a` (the
+// down projection reduces over all of I for every expert), and handing it
+// over inside one launch (device-coherent stores, a wait for their
+// completion, and an arrival counter) costs several microseconds per
+// workgroup on this chip, more than the kernel boundary.  For a single token
+// the expert slots and routing weights arrive as launch arguments, so neither
+// kernel starts with a dependent load.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -94,69 +104,117 @@ __device__ __forceinline__ int lds_pos(int blk, int n, int S) {
     return (t * S + s) * 5;
 }
 
-__device__ __forceinline__ const uint8_t* expert_blob(const uint8_t* arena, const uint8_t* shared,
-                                                      const int32_t* slots, int b, int j, int k,
-                                                      int layer, int n_shared, size_t blob_bytes) {
-    if (j < k) return arena + (size_t)slots[b * k + j] * blob_bytes;
-    return shared + (size_t)(layer * n_shared + (j - k)) * blob_bytes;
+// slot / weight of the single token's j-th expert from the launch arguments:
+// constant-index reads and a select chain (indexing the by-value argument
+// array with a variable would copy it to private memory)
+__device__ __forceinline__ int karg_slot(const FfnArgs& a, int j) {
+    int v = a.kslot[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) v = (j == i) ? a.kslot[i] : v;
+    return v;
+}
+__device__ __forceinline__ float karg_w(const FfnArgs& a, int j) {
+    float v = a.kw[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) v = (j == i) ? a.kw[i] : v;
+    return v;
 }
 
-// ------------------------------------------------------------------- K3 --
-// grid (I/16 tiles, nE experts, B tokens); W waves; lane (r = lane&15, s = 4w + lane>>4)
-template <int W, int T>
-__global__ __launch_bounds__(W * 64) void k3_gate_up(K3Args a) {
-    constexpr int S = 4 * W;
-    extern __shared__ uint4 smem[];
-    const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+// blob of the token's j-th expert (j >= k: the shared expert)
+__device__ __forceinline__ const uint8_t* expert_blob(const FfnArgs& a, int b, int j) {
+    if (j < a.k) {
+        const int slot = a.karg ? karg_slot(a, j) : a.slots[b * a.k + j];
+        return a.arena + (size_t)slot * a.blob_bytes;
+    }
+    return a.shared + (size_t)(a.layer * a.n_shared + (j - a.k)) * a.blob_bytes;
+}
+
+__device__ __forceinline__ float expert_weight(const FfnArgs& a, int b, int j) {
+    if (j >= a.k) return 1.0f;
+    return a.karg ? karg_w(a, j) : a.w[b * a.k + j];
+}
+
+constexpr int FFN_THREADS = 256;
+
+// Stage nblk 64-byte blocks (32 bf16 values) from global memory into LDS in
+// lds_pos() order: a thread moves whole blocks, four 16-byte loads in flight
+// before its four LDS writes.  Runs before the weight loads are issued: a
+// weight load issued earlier would make these LDS writes wait for it too
+// (loads complete in order per wave), and a wave dedicated to staging
+// measured slower.
+__device__ __forceinline__ void stage_blocks(uint4* smem, const uint4* src, int nblk, int nseg) {
+    for (int blk = threadIdx.x; blk < nblk; blk += FFN_THREADS) {
+        const uint4 v0 = src[blk * 4 + 0];
+        const uint4 v1 = src[blk * 4 + 1];
+        const uint4 v2 = src[blk * 4 + 2];
+        const uint4 v3 = src[blk * 4 + 3];
+        uint4* d = smem + lds_pos(blk, nblk, nseg);
+        d[0] = v0;
+        d[1] = v1;
+        d[2] = v2;
+        d[3] = v3;
+    }
+}
+
+// ---------------------------------------------------------------- phase 1 --
+// one 16-row tile of one expert: compute lane (r = lane&15, s = 4*wave + lane>>4)
+template <int T1>
+__device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int unit, int b) {
+    constexpr int S = 16;
+    const int tiles = a.I / 16;
+    const int j = __builtin_amdgcn_readfirstlane(unit / tiles), tile = unit - j * tiles;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r = lane & 15, s = w * 4 + (lane >> 4);
     const int NB = a.NB;
+    float* red = reinterpret_cast<float*>(smem + NB * 5);
+    const int r = lane & 15, s = w * 4 + (lane >> 4);
     const int nb = seg_len(NB, S, s);
-    const uint8_t* blob =
-        expert_blob(a.arena, a.shared, a.slots, b, j, a.k, a.layer, a.n_shared, a.blob_bytes);
+    const uint8_t* blob = expert_blob(a, b, j);
     const uint8_t* tb = blob + (size_t)tile * 16 * NB * 34;
+    const uint8_t* tub = tb + (size_t)16 * NB * 16;
     const uint8_t* tsc = tb + (size_t)16 * NB * 32;
 
     float g = 0.0f, u = 0.0f;
-    uint4 gc[T], uc[T];
-    uint32_t sc[T];
+    uint4 gc[T1], uc[T1];
+    uint32_t sc[T1];
+    // Steps past this lane's segment re-read its step-0 chunk (a cache hit) and
+    // are dropped by a select, so loads and compute are branch-free and the
+    // compiler can wait for each step's data separately; an empty segment
+    // (NB < 16) reads the tile's first chunk.
+    const int sv = nb > 0 ? s : 0;
     auto load = [&](int t0) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t < nb) {
-                const size_t c = (size_t)(((t0 + t) * S + s) * 16 + r);
-                gc[t] = ldg16(tb + c * 32);
-                uc[t] = ldg16(tb + c * 32 + 16);
-                sc[t] = *reinterpret_cast<const uint16_t*>(tsc + c * 2);
-            }
+        for (int t = 0; t < T1; ++t) {
+            const int tt = (t0 + t < nb) ? t0 + t : 0;
+            const size_t c = (size_t)((tt * S + sv) * 16 + r);
+            gc[t] = ldg16(tb + c * 16);
+            uc[t] = ldg16(tub + c * 16);
+            sc[t] = *reinterpret_cast<const uint16_t*>(tsc + c * 2);
         }
     };
     auto compute = [&](int t0) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t < nb) {
-                const uint4* xb = smem + ((t0 + t) * S + s) * 5;
-                g = fmaf(e8m0(sc[t]), dot32(gc[t], xb), g);
-                u = fmaf(e8m0(sc[t] >> 8), dot32(uc[t], xb), u);
-            }
+        for (int t = 0; t < T1; ++t) {
+            const int tt = (t0 + t < nb) ? t0 + t : 0;
+            const uint4* xb = smem + (tt * S + sv) * 5;
+            const float pg = e8m0(sc[t]) * dot32(gc[t], xb);
+            const float pu = e8m0(sc[t] >> 8) * dot32(uc[t], xb);
+            g += (t0 + t < nb) ? pg : 0.0f;
+            u += (t0 + t < nb) ? pu : 0.0f;
         }
     };
-    load(0);
-    // activations -> LDS while the first weight loads are in flight
-    const uint4* xg = reinterpret_cast<const uint4*>(a.x + (size_t)b * NB * 32);
-    for (int p = tid; p < NB * 4; p += W * 64) smem[lds_pos(p >> 2, NB, S) + (p & 3)] = xg[p];
+    stage_blocks(smem, reinterpret_cast<const uint4*>(a.x + (size_t)b * a.H), NB, S);
     __syncthreads();
+    load(0);
     compute(0);
-    for (int t0 = T; t0 < nb; t0 += T) {
+    for (int t0 = T1; t0 < nb; t0 += T1) {
         load(t0);
         compute(t0);
     }
-    // segments of a row: lanes r, r+16, r+32, r+48 of every wave
+    // segments of a row: lanes r, r+16, r+32, r+48 of every compute wave
     g += __shfl_xor(g, 16);
     g += __shfl_xor(g, 32);
     u += __shfl_xor(u, 16);
     u += __shfl_xor(u, 32);
-    float* red = reinterpret_cast<float*>(smem + NB * 5);
     if (lane < 16) {
         red[(w * 16 + r) * 2] = g;
         red[(w * 16 + r) * 2 + 1] = u;
@@ -165,7 +223,7 @@ __global__ __launch_bounds__(W * 64) void k3_gate_up(K3Args a) {
     if (tid < 16) {
         float gs = 0.0f, us = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) {
+        for (int ww = 0; ww < 4; ++ww) {
             gs += red[(ww * 16 + tid) * 2];
             us += red[(ww * 16 + tid) * 2 + 1];
         }
@@ -174,135 +232,121 @@ __global__ __launch_bounds__(W * 64) void k3_gate_up(K3Args a) {
     }
 }
 
-// ------------------------------------------------------------------- K4 --
-// grid (H/8 tiles, B tokens); W waves; lane (r = lane&7, s = 8w + lane>>3);
-// segments split the combined (expert, I-block) range of the token.
-template <int W, int T>
-__global__ __launch_bounds__(W * 64) void k4_down(K4Args a) {
-    constexpr int S = 8 * W;
-    extern __shared__ uint4 smem[];
-    const int tile = blockIdx.x, b = blockIdx.y;
+// ---------------------------------------------------------------- phase 2 --
+// one 8-row tile of the output: compute lane (r = lane&7, s = 8*wave + lane>>3);
+// the 32 segments split the combined (expert, I-block) range of the token
+template <int T2>
+__device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile, int b) {
+    constexpr int S = 32;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int NBI = a.NBI, nE = a.nE;
+    const int Q = nE * NBI;
+    float* red = reinterpret_cast<float*>(smem + Q * 5);
     const int r = lane & 7, s = w * 8 + (lane >> 3);
-    const int NBI = a.NBI;
-    const int Q = a.nE * NBI;
     const int nq = seg_len(Q, S, s), q0 = seg_begin(Q, S, s);
-
-    float acc = 0.0f;
-    int j = q0 / NBI, ib = q0 - (q0 / NBI) * NBI;
-    uint4 dc[T];
-    uint32_t sc[T];
-    float cw[T];
+    // A segment (at most ceil(nE*NBI/32) <= NBI + 1 blocks, as nE <= 32)
+    // spans at most two experts: j0 from block ib0 for `split` steps, then j0+1
+    // from block 0.  Steps past the segment re-read step 0 and are dropped; an
+    // empty segment (Q < 32) reads block 0 of expert 0.
+    const int qv = nq > 0 ? q0 : 0;
+    const int j0 = qv / NBI, ib0 = qv - (qv / NBI) * NBI;
+    const int split = NBI - ib0;
+    const int j1 = j0 + 1 < nE ? j0 + 1 : j0;
+    const uint8_t* base0 = expert_blob(a, b, j0);
+    const uint8_t* base1 = expert_blob(a, b, j1);
+    const float cw0 = expert_weight(a, b, j0), cw1 = expert_weight(a, b, j1);
+    const int sv = nq > 0 ? s : 0;
+    uint4 dc[T2];
+    uint32_t sc[T2];
     auto load = [&](int t0) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t < nq) {
-                const uint8_t* blob = expert_blob(a.arena, a.shared, a.slots, b, j, a.k, a.layer,
-                                                  a.n_shared, a.blob_bytes);
-                const size_t cell = ((size_t)tile * NBI + ib) * 8 + r;
-                dc[t] = ldg16(blob + a.d_codes_off + cell * 16);
-                sc[t] = blob[a.d_scales_off + cell];
-                cw[t] = j < a.k ? a.w[b * a.k + j] : 1.0f;
-                if (++ib == NBI) {
-                    ib = 0;
-                    ++j;
-                }
-            }
+        for (int t = 0; t < T2; ++t) {
+            const int tt = (t0 + t < nq) ? t0 + t : 0;
+            const bool first = tt < split;
+            const uint8_t* blob = first ? base0 : base1;
+            const size_t cell = ((size_t)tile * NBI + (first ? ib0 + tt : tt - split)) * 8 + r;
+            dc[t] = ldg16(blob + a.d_codes_off + cell * 16);
+            sc[t] = blob[a.d_scales_off + cell];
         }
     };
+    float acc = 0.0f;
     auto compute = [&](int t0) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t < nq) {
-                const uint4* ab = smem + ((t0 + t) * S + s) * 5;
-                acc = fmaf(cw[t] * e8m0(sc[t]), dot32(dc[t], ab), acc);
-            }
+        for (int t = 0; t < T2; ++t) {
+            const int tt = (t0 + t < nq) ? t0 + t : 0;
+            const uint4* ab = smem + (tt * S + sv) * 5;
+            const float pv = (tt < split ? cw0 : cw1) * e8m0(sc[t]) * dot32(dc[t], ab);
+            acc += (t0 + t < nq) ? pv : 0.0f;
         }
     };
-    load(0);
-    // intermediate activations of all experts of this token -> LDS
-    const uint4* ag = reinterpret_cast<const uint4*>(a.a + (size_t)b * a.nE * a.I);
-    for (int p = tid; p < Q * 4; p += W * 64) smem[lds_pos(p >> 2, Q, S) + (p & 3)] = ag[p];
+    stage_blocks(smem, reinterpret_cast<const uint4*>(a.a + (size_t)b * nE * a.I), Q, S);
     __syncthreads();
+    load(0);
     compute(0);
-    for (int t0 = T; t0 < nq; t0 += T) {
+    for (int t0 = T2; t0 < nq; t0 += T2) {
         load(t0);
         compute(t0);
     }
-    // segments of an output row: lanes r + 8*i of every wave
+    // segments of an output row: lanes r + 8*i of every compute wave
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
-    float* red = reinterpret_cast<float*>(smem + Q * 5);
     if (lane < 8) red[w * 8 + r] = acc;
     __syncthreads();
     if (tid < 8) {
         float ys = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) ys += red[ww * 8 + tid];
+        for (int ww = 0; ww < 4; ++ww) ys += red[ww * 8 + tid];
         a.y[(size_t)b * a.H + tile * 8 + tid] = f32_to_bf16(ys);
     }
 }
 
-// ------------------------------------------------------------ launchers --
-
-template <int W>
-static int launch_k3_w(const K3Args& a, const Layout& L, int B, hipStream_t st) {
-    dim3 grid(L.I / 16, a.nE, B);
-    size_t lds = (size_t)L.NB * 80 + (size_t)W * 16 * 2 * 4;
-    if (L.T3 <= 1)
-        hipLaunchKernelGGL((k3_gate_up<W, 1>), grid, dim3(W * 64), lds, st, a);
-    else if (L.T3 <= 2)
-        hipLaunchKernelGGL((k3_gate_up<W, 2>), grid, dim3(W * 64), lds, st, a);
-    else if (L.T3 <= 4)
-        hipLaunchKernelGGL((k3_gate_up<W, 4>), grid, dim3(W * 64), lds, st, a);
-    else if (L.T3 <= 6)
-        hipLaunchKernelGGL((k3_gate_up<W, 6>), grid, dim3(W * 64), lds, st, a);
-    else
-        hipLaunchKernelGGL((k3_gate_up<W, 8>), grid, dim3(W * 64), lds, st, a);
-    return (int)hipGetLastError();
+// K3: grid (nE * I/16 tiles, B); K4: grid (H/8 tiles, B); 256 threads each
+template <int T1>
+__global__ __launch_bounds__(FFN_THREADS) void k3_gate_up(FfnArgs a) {
+    extern __shared__ uint4 smem[];
+    ffn_gate_up<T1>(a, smem, blockIdx.x, blockIdx.y);
 }
 
-int launch_k3(const K3Args& a, const Layout& L, int B, void* stream) {
+template <int T2>
+__global__ __launch_bounds__(FFN_THREADS) void k4_down(FfnArgs a) {
+    extern __shared__ uint4 smem[];
+    ffn_down<T2>(a, smem, blockIdx.x, blockIdx.y);
+}
+
+size_t ffn_lds_bytes(const Layout& L, int nE) {
+    const size_t p1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
+    const size_t p2 = (size_t)nE * L.NBI * 80 + 4 * 8 * 4;
+    return p1 > p2 ? p1 : p2;
+}
+
+int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid) {
     hipStream_t st = (hipStream_t)stream;
-    switch (L.W3) {
-        case 1: return launch_k3_w<1>(a, L, B, st);
-        case 2: return launch_k3_w<2>(a, L, B, st);
-        case 3: return launch_k3_w<3>(a, L, B, st);
-        default: return launch_k3_w<4>(a, L, B, st);
-    }
-}
-
-int k4_waves(int nE, int NBI) {
-    int w = nE * NBI / 32;
-    return w < 1 ? 1 : (w > 4 ? 4 : w);
-}
-
-template <int W>
-static int launch_k4_w(const K4Args& a, const Layout& L, int B, hipStream_t st) {
-    const int Q = a.nE * L.NBI;
-    const int steps = (Q + 8 * W - 1) / (8 * W);
-    dim3 grid(L.H / 8, B);
-    size_t lds = (size_t)Q * 80 + (size_t)W * 8 * 4;
-    if (steps <= 2)
-        hipLaunchKernelGGL((k4_down<W, 2>), grid, dim3(W * 64), lds, st, a);
-    else if (steps <= 4)
-        hipLaunchKernelGGL((k4_down<W, 4>), grid, dim3(W * 64), lds, st, a);
-    else if (steps <= 8)
-        hipLaunchKernelGGL((k4_down<W, 8>), grid, dim3(W * 64), lds, st, a);
+    a.P1 = a.nE * (L.I / 16);
+    a.P2 = L.H / 8;
+    const int T1 = L.T3;
+    const int T2 = (a.nE * L.NBI + 31) / 32;
+    const size_t lds1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
+    const size_t lds2 = (size_t)a.nE * L.NBI * 80 + 4 * 8 * 4;
+    dim3 g1(a.P1, B), g2(a.P2, B), blk(FFN_THREADS);
+    if (T1 <= 2)
+        hipLaunchKernelGGL(k3_gate_up<2>, g1, blk, lds1, st, a);
+    else if (T1 <= 4)
+        hipLaunchKernelGGL(k3_gate_up<4>, g1, blk, lds1, st, a);
+    else if (T1 <= 6)
+        hipLaunchKernelGGL(k3_gate_up<6>, g1, blk, lds1, st, a);
     else
-        hipLaunchKernelGGL((k4_down<W, 12>), grid, dim3(W * 64), lds, st, a);
+        hipLaunchKernelGGL(k3_gate_up<8>, g1, blk, lds1, st, a);
+    if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
+    if (T2 <= 2)
+        hipLaunchKernelGGL(k4_down<2>, g2, blk, lds2, st, a);
+    else if (T2 <= 4)
+        hipLaunchKernelGGL(k4_down<4>, g2, blk, lds2, st, a);
+    else if (T2 <= 8)
+        hipLaunchKernelGGL(k4_down<8>, g2, blk, lds2, st, a);
+    else
+        hipLaunchKernelGGL(k4_down<12>, g2, blk, lds2, st, a);
     return (int)hipGetLastError();
-}
-
-int launch_k4(const K4Args& a, const Layout& L, int B, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    switch (k4_waves(a.nE, L.NBI)) {
-        case 1: return launch_k4_w<1>(a, L, B, st);
-        case 2: return launch_k4_w<2>(a, L, B, st);
-        case 3: return launch_k4_w<3>(a, L, B, st);
-        default: return launch_k4_w<4>(a, L, B, st);
-    }
 }
 
 }  // namespace moe

@@ -1,4 +1,4 @@
-// K1 router logits + top-k + softmax, K2 cache resolve, for gfx950 (wave64).
+// K1 router logits; K2 top-k + softmax + cache resolve; for gfx950 (wave64).
 //
 // Router (pirouter.ai "FreeToken x RTX 5090" page, mechanism section: the
 // router picks the experts each token uses, and the cache follows it).  The
@@ -60,42 +60,38 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-constexpr int K1_WAVES = 4;
-constexpr int K1_MAXC = 16;  // candidates per lane: E <= 1024
-
-__global__ __launch_bounds__(K1_WAVES * 64) void k1_router(K1Args a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * K1_WAVES + wave;
-    const int b = blockIdx.y;
+// one wave per (expert row, token)
+__global__ __launch_bounds__(64) void k1_logits(K1Args a) {
+    const int lane = threadIdx.x;
+    const int e = blockIdx.x, b = blockIdx.y;
     const uint16_t* x = a.x + (size_t)b * a.H;
-    if (e < a.E) {
-        const uint16_t* W = a.W + (size_t)e * a.H;
-        float p = 0.0f;
-        const int ng = a.H >> 3;
-        for (int g = lane; g < ng; g += 64) {
-            uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
-            uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)g * 8);
-            p = fold8(wv, xv, p);
-        }
+    const uint16_t* W = a.W + (size_t)e * a.H;
+    float p = 0.0f;
+    const int ng = a.H >> 3;
+    for (int g = lane; g < ng; g += 64) {
+        uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
+        uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)g * 8);
+        p = fold8(wv, xv, p);
+    }
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
-        if (lane == 0) a.z[(size_t)b * a.E + e] = p;
-    }
-    // the last workgroup to finish this token selects its experts
-    __shared__ int is_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned t = atomicAdd(&a.counter[b], 1u);
-        is_last = (t == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!is_last || wave != 0) return;
-    __threadfence();
+    for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+    if (lane == 0) a.z[(size_t)b * a.E + e] = p;
+}
+
+int launch_k1(const K1Args& a, void* stream) {
+    hipLaunchKernelGGL(k1_logits, dim3(a.E, a.B), dim3(64), 0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+constexpr int K2_MAXCAND = 16;  // top-k candidates per lane: E <= 1024
+
+// top-k of one token's logits by one wave; ties go to the lower expert index
+__device__ void wave_topk(const K2Args& a, int b) {
+    const int lane = threadIdx.x & 63;
     const float* z = a.z + (size_t)b * a.E;
-    uint64_t key[K1_MAXC];
+    uint64_t key[K2_MAXCAND];
 #pragma unroll
-    for (int c = 0; c < K1_MAXC; ++c) {
+    for (int c = 0; c < K2_MAXCAND; ++c) {
         int ee = lane + 64 * c;
         key[c] = ee < a.E ? topk_key(z[ee], ee) : 0ull;
     }
@@ -104,12 +100,15 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_router(K1Args a) {
         uint64_t best = 0;
         int bc = -1;
 #pragma unroll
-        for (int c = 0; c < K1_MAXC; ++c)
-            if (key[c] > best) { best = key[c]; bc = c; }
+        for (int c = 0; c < K2_MAXCAND; ++c)
+            if (key[c] > best) {
+                best = key[c];
+                bc = c;
+            }
         uint64_t wbest = wave_max_u64(best);
         if (bc >= 0 && best == wbest) {
 #pragma unroll
-            for (int c = 0; c < K1_MAXC; ++c)
+            for (int c = 0; c < K2_MAXCAND; ++c)
                 if (c == bc) key[c] = 0;
         }
         int id = (int)(0xFFFFFFFFu - (uint32_t)(wbest & 0xFFFFFFFFu));
@@ -129,13 +128,6 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k1_router(K1Args a) {
         if (a.ids_out) a.ids_out[o] = my_id;
         if (a.w_out) a.w_out[o] = wj;
     }
-    if (lane == 0) a.counter[b] = 0u;
-}
-
-int launch_k1(const K1Args& a, void* stream) {
-    dim3 grid((a.E + K1_WAVES - 1) / K1_WAVES, a.B);
-    hipLaunchKernelGGL(k1_router, grid, dim3(K1_WAVES * 64), 0, (hipStream_t)stream, a);
-    return (int)hipGetLastError();
 }
 
 // ------------------------------------------------------------------- K2 --
@@ -195,6 +187,12 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     __shared__ int s_evict, s_invalid;
     const int tid = threadIdx.x;
     const int E = a.E, C = a.C, l = a.layer;
+
+    // routing: top-k + softmax of every token (one wave per token)
+    if (a.z) {
+        for (int b = tid >> 6; b < a.B; b += K2_THREADS / 64) wave_topk(a, b);
+        __syncthreads();
+    }
 
     for (int e = tid; e < E; e += K2_THREADS) s_req[e] = 0;
     for (int i = tid; i < (C + 31) / 32; i += K2_THREADS) s_hitbits[i] = 0u;
@@ -287,6 +285,14 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         int sl = (unsigned)id < (unsigned)E ? s_req[id] : -1;
         a.slots[i] = sl;
         if (a.slots_out) a.slots_out[i] = sl;
+    }
+    // token 0's slots and weights ride along with the miss list (the host
+    // passes them to the FFN launch as arguments); written by wave 0, which
+    // also publishes the list below
+    if (tid < a.k && tid < 16) {
+        const int id = a.ids[tid];
+        a.ml->slot0[tid] = (unsigned)id < (unsigned)E ? s_req[id] : -1;
+        a.ml->w0[tid] = a.z ? a.w[tid] : 0.0f;
     }
     if (tid == 0) {
         const int n = nh + nm;

@@ -7,8 +7,8 @@
 // step it launches the router (K1) and the resolve kernel (K2) on the compute
 // stream, spins on the miss list K2 publishes in host-mapped memory, issues
 // one hipMemcpyAsync per miss on the copy stream (misses stream over PCIe),
-// and makes the compute stream wait for those copies before the FFN kernels
-// (K3, K4).  With lookahead 1 the next layer's K1/K2 and copies are issued
+// and makes the compute stream wait for those copies before the expert-FFN
+// kernel.  With lookahead 1 the next layer's K1/K2 and copies are issued
 // before the current layer's FFN, so its misses load while the current layer
 // computes (ai.holude.com preflight page, section on long prompts: the next
 // layer's experts load over PCIe while the GPU computes the current one).
@@ -56,21 +56,22 @@ struct moe_ctx {
     int32_t* ids[2] = {nullptr, nullptr};
     float* w[2] = {nullptr, nullptr};
     int32_t* slots[2] = {nullptr, nullptr};
-    uint16_t* a[2] = {nullptr, nullptr};
-    uint32_t* k1cnt = nullptr;
+    uint16_t* a[3] = {nullptr, nullptr, nullptr};  // [2] serves moe_expert_forward
     // host-mapped miss lists
     uint8_t* ml_mem = nullptr;
     size_t ml_stride = 0;
     int max_unique = 0;
     int64_t seq = 0;
     hipEvent_t copy_ev[2] = {nullptr, nullptr};
+    // token 0's slots and weights of the last miss list read per parity
+    int32_t tok0_slot[2][16] = {};
+    float tok0_w[2][16] = {};
+    bool tok0_valid[2] = {false, false};
     // host counters
     uint64_t h2d_bytes = 0, h2d_copies = 0;
-    uint64_t k3_launches = 0, k4_launches = 0;
+    uint64_t ffn_launches = 0;
     double k3_ms = 0, k4_ms = 0;
     std::vector<ProfSlot> prof_used, prof_free;
-    std::vector<ProfSlot> copy_used;  // ev[0], ev[1] bracket one layer's miss copies
-    double h2d_ms = 0;
     double spin_timeout_s = 60.0;
     bool failed = false;
     std::string err;
@@ -126,7 +127,7 @@ moe_status check_cfg(const moe_config* c) {
 }
 
 struct WsPlan {
-    size_t z, ids, w, slots, a, cnt, total;
+    size_t z, ids, w, slots, a, total;
 };
 
 WsPlan plan_workspace(const moe_config& c) {
@@ -138,8 +139,7 @@ WsPlan plan_workspace(const moe_config& c) {
     p.ids = off;   off = align_up(off + 2 * B * k * 4, 256);
     p.w = off;     off = align_up(off + 2 * B * k * 4, 256);
     p.slots = off; off = align_up(off + 2 * B * k * 4, 256);
-    p.a = off;     off = align_up(off + 2 * B * nE * (size_t)c.inter * 2, 256);
-    p.cnt = off;   off = align_up(off + B * 4, 256);
+    p.a = off;     off = align_up(off + 3 * B * nE * (size_t)c.inter * 2, 256);
     p.total = off;
     return p;
 }
@@ -164,8 +164,8 @@ void repack(const Layout& L, const uint8_t* src, uint8_t* dst) {
                     const size_t row = (size_t)tile * 16 + r;
                     const int blk = b0 + t;
                     const size_t c = (size_t)((t * S + s) * 16 + r);
-                    memcpy(tb + c * 32, gc + row * (L.H / 2) + (size_t)blk * 16, 16);
-                    memcpy(tb + c * 32 + 16, uc + row * (L.H / 2) + (size_t)blk * 16, 16);
+                    memcpy(tb + c * 16, gc + row * (L.H / 2) + (size_t)blk * 16, 16);
+                    memcpy(tb + (size_t)16 * NB * 16 + c * 16, uc + row * (L.H / 2) + (size_t)blk * 16, 16);
                     tsc[c * 2] = gs[row * NB + blk];
                     tsc[c * 2 + 1] = us[row * NB + blk];
                 }
@@ -194,7 +194,6 @@ void free_all(moe_ctx* c) {
     if (c->ps) (void)hipStreamSynchronize(c->ps);
     for (auto& p : c->prof_used) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto& p : c->prof_free) for (auto e : p.ev) (void)hipEventDestroy(e);
-    for (auto& p : c->copy_used) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
     if (c->pool) (void)hipHostFree(c->pool);
     if (c->ml_mem) (void)hipHostFree(c->ml_mem);
@@ -206,50 +205,50 @@ void free_all(moe_ctx* c) {
 
 // ---------------------------------------------------------- one layer step --
 
-moe_status launch_route(moe_ctx* c, int layer, const void* x, int B, int par, int32_t* ids_out,
-                        float* w_out) {
+moe_status launch_route(moe_ctx* c, int layer, const void* x, int B) {
     K1Args a{};
     a.W = c->router_dev + (size_t)layer * c->cfg.n_experts * c->cfg.hidden;
     a.x = (const uint16_t*)x;
     a.z = c->z;
-    a.ids = c->ids[par];
-    a.w = c->w[par];
-    a.ids_out = ids_out;
-    a.w_out = w_out;
-    a.counter = c->k1cnt;
     a.E = c->cfg.n_experts;
     a.H = c->cfg.hidden;
-    a.k = c->cfg.top_k;
     a.B = B;
     LAUNCHCHK(c, launch_k1(a, c->cs));
     return MOE_OK;
 }
 
-moe_status launch_resolve(moe_ctx* c, int step, int layer, const int32_t* ids, int n_ids, int par,
-                          int32_t* slots_out) {
+// K2 for one layer step.  routed: top-k of the logits K1 left in z for B
+// tokens, then resolve; otherwise resolve the caller's ids (n_ids of them).
+moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const int32_t* ids, int B,
+                          int par, int32_t* slots_out, int32_t* ids_out, float* w_out) {
     K2Args a{};
     a.c = c->cd;
-    a.ids = ids;
+    a.z = routed ? c->z : nullptr;
+    a.ids = routed ? c->ids[par] : const_cast<int32_t*>(ids);
+    a.w = c->w[par];
+    a.ids_out = ids_out;
+    a.w_out = w_out;
     a.slots = c->slots[par];
     a.slots_out = slots_out;
     a.ml = miss_list(c, par);
     a.seq = ++c->seq;
-    a.n_ids = n_ids;
+    a.n_ids = B * c->cfg.top_k;
     a.layer = layer;
     a.step = step;
     a.E = c->cfg.n_experts;
     a.C = c->cfg.cache_slots;
+    a.k = c->cfg.top_k;
+    a.B = B;
     const int p = c->parity;
     LAUNCHCHK(c, launch_k2(a, c->order[p], c->order[p ^ 1], c->cs));
     c->parity = p ^ 1;
     return MOE_OK;
 }
 
-moe_status get_prof(moe_ctx* c, ProfSlot& p);
-
 // Waits for the miss list of resolve `seq` and issues its copies; records
 // copy_ev[par] when there are misses.  n_miss_out gets the count.
 moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss_out) {
+    c->tok0_valid[par] = false;
     MissList* ml = miss_list(c, par);
     auto t0 = std::chrono::steady_clock::now();
     uint64_t spins = 0;
@@ -267,23 +266,17 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     }
     const int nm = ml->n_miss;
     if (ml->n_invalid) return set_err(c, MOE_EINVAL, "%d expert ids outside [0, E)", ml->n_invalid);
-    const size_t blob = c->lay.blob_bytes;
-    const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0 && nm > 0;
-    ProfSlot cp{};
-    if (prof) {
-        moe_status st = get_prof(c, cp);
-        if (st) return st;
-        HIPCHK(c, hipEventRecord(cp.ev[0], c->ps));
+    for (int j = 0; j < c->cfg.top_k; ++j) {
+        c->tok0_slot[par][j] = ml->slot0[j];
+        c->tok0_w[par][j] = ml->w0[j];
     }
+    c->tok0_valid[par] = true;
+    const size_t blob = c->lay.blob_bytes;
     for (int i = 0; i < nm; ++i) {
         const MissEntry m = ml->e[i];
         const uint8_t* src = c->pool + ((size_t)layer * c->cfg.n_experts + m.expert) * blob;
         uint8_t* dst = c->arena + (size_t)m.slot * blob;
         HIPCHK(c, hipMemcpyAsync(dst, src, blob, hipMemcpyHostToDevice, c->ps));
-    }
-    if (prof) {
-        HIPCHK(c, hipEventRecord(cp.ev[1], c->ps));
-        c->copy_used.push_back(cp);
     }
     if (nm > 0) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
     c->h2d_bytes += (uint64_t)nm * blob;
@@ -302,7 +295,8 @@ moe_status get_prof(moe_ctx* c, ProfSlot& p) {
     return MOE_OK;
 }
 
-moe_status launch_ffn(moe_ctx* c, int layer, const void* x, int B, int par, void* y, int n_miss) {
+moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par, void* y, int n_miss,
+                            const int32_t* slots_dev = nullptr, const float* w_dev = nullptr) {
     if (n_miss > 0) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
     const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0;
     ProfSlot ps{};
@@ -311,40 +305,32 @@ moe_status launch_ffn(moe_ctx* c, int layer, const void* x, int B, int par, void
         if (st) return st;
         HIPCHK(c, hipEventRecord(ps.ev[0], c->cs));
     }
-    K3Args a3{};
-    a3.arena = c->arena;
-    a3.shared = c->shared_dev;
-    a3.slots = c->slots[par];
-    a3.x = (const uint16_t*)x;
-    a3.a = c->a[par];
-    a3.blob_bytes = c->lay.blob_bytes;
-    a3.k = c->cfg.top_k;
-    a3.n_shared = c->cfg.n_shared;
-    a3.nE = c->nE;
-    a3.layer = layer;
-    a3.NB = c->lay.NB;
-    a3.S3 = c->lay.S3;
-    a3.I = c->cfg.inter;
-    LAUNCHCHK(c, launch_k3(a3, c->lay, B, c->cs));
-    if (prof) HIPCHK(c, hipEventRecord(ps.ev[1], c->cs));
-    K4Args a4{};
-    a4.arena = c->arena;
-    a4.shared = c->shared_dev;
-    a4.slots = c->slots[par];
-    a4.w = c->w[par];
-    a4.a = c->a[par];
-    a4.y = (uint16_t*)y;
-    a4.blob_bytes = c->lay.blob_bytes;
-    a4.d_codes_off = c->lay.d_codes_off;
-    a4.d_scales_off = c->lay.d_scales_off;
-    a4.k = c->cfg.top_k;
-    a4.n_shared = c->cfg.n_shared;
-    a4.nE = c->nE;
-    a4.layer = layer;
-    a4.NBI = c->lay.NBI;
-    a4.I = c->cfg.inter;
-    a4.H = c->cfg.hidden;
-    LAUNCHCHK(c, launch_k4(a4, c->lay, B, c->cs));
+    FfnArgs f{};
+    f.arena = c->arena;
+    f.shared = c->shared_dev;
+    f.slots = slots_dev ? slots_dev : c->slots[par];
+    f.w = w_dev ? w_dev : c->w[par];
+    f.x = (const uint16_t*)x;
+    f.a = c->a[par];
+    f.y = (uint16_t*)y;
+    f.blob_bytes = c->lay.blob_bytes;
+    f.d_codes_off = c->lay.d_codes_off;
+    f.d_scales_off = c->lay.d_scales_off;
+    f.k = c->cfg.top_k;
+    f.n_shared = c->cfg.n_shared;
+    f.nE = c->nE;
+    f.layer = layer;
+    f.NB = c->lay.NB;
+    f.NBI = c->lay.NBI;
+    f.I = c->cfg.inter;
+    f.H = c->cfg.hidden;
+    f.karg = (B == 1 && !slots_dev && par < 2 && c->tok0_valid[par]) ? 1 : 0;
+    if (f.karg)
+        for (int j = 0; j < c->cfg.top_k; ++j) {
+            f.kslot[j] = c->tok0_slot[par][j];
+            f.kw[j] = c->tok0_w[par][j];
+        }
+    LAUNCHCHK(c, launch_ffn(f, c->lay, B, c->cs, prof ? ps.ev[1] : nullptr));
     if (prof) {
         HIPCHK(c, hipEventRecord(ps.ev[2], c->cs));
         c->prof_used.push_back(ps);
@@ -418,11 +404,8 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
         c->ids[p] = (int32_t*)(ws + wp.ids) + p * Bk;
         c->w[p] = (float*)(ws + wp.w) + p * Bk;
         c->slots[p] = (int32_t*)(ws + wp.slots) + p * Bk;
-        c->a[p] = (uint16_t*)(ws + wp.a) + (size_t)p * cfg->max_tokens * c->nE * cfg->inter;
     }
-    c->k1cnt = (uint32_t*)(ws + wp.cnt);
-    where = "workspace clear";
-    if (hipMemsetAsync(c->k1cnt, 0, (size_t)cfg->max_tokens * 4, c->cs) != hipSuccess) return bail(MOE_EHIP);
+    for (int p = 0; p < 3; ++p) c->a[p] = (uint16_t*)(ws + wp.a) + (size_t)p * cfg->max_tokens * c->nE * cfg->inter;
 
     // device cache state
     const size_t n_sl = (size_t)Lyr * E;
@@ -524,7 +507,7 @@ moe_status moe_cache_resolve(moe_ctx* c, int32_t step, int32_t layer, const int3
     moe_status st = check_call(c, n_tokens);
     if (st) return st;
     if (layer < 0 || layer >= c->cfg.n_layers || !ids_dev) return set_err(c, MOE_EINVAL, "bad layer or ids");
-    st = launch_resolve(c, step, layer, ids_dev, n_tokens * c->cfg.top_k, 0, slots_dev);
+    st = launch_resolve(c, step, layer, false, ids_dev, n_tokens, 0, slots_dev, nullptr, nullptr);
     if (st) return st;
     int nm = 0;
     st = stage_misses(c, layer, 0, c->seq, &nm);
@@ -539,11 +522,11 @@ moe_status moe_layer_forward(moe_ctx* c, int32_t step, int32_t layer, const void
     moe_status st = check_call(c, n_tokens);
     if (st) return st;
     if (layer < 0 || layer >= c->cfg.n_layers || !x || !y) return set_err(c, MOE_EINVAL, "bad layer or buffers");
-    if ((st = launch_route(c, layer, x, n_tokens, 0, ids_out, w_out))) return st;
-    if ((st = launch_resolve(c, step, layer, c->ids[0], n_tokens * c->cfg.top_k, 0, nullptr))) return st;
+    if ((st = launch_route(c, layer, x, n_tokens))) return st;
+    if ((st = launch_resolve(c, step, layer, true, nullptr, n_tokens, 0, nullptr, ids_out, w_out))) return st;
     int nm = 0;
     if ((st = stage_misses(c, layer, 0, c->seq, &nm))) return st;
-    return launch_ffn(c, layer, x, n_tokens, 0, y, nm);
+    return launch_ffn_layer(c, layer, x, n_tokens, 0, y, nm);
 }
 
 moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs, int32_t n_tokens,
@@ -559,18 +542,18 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     auto wl = [&](int l) { return w_out ? w_out + (size_t)l * kB : nullptr; };
     if (c->cfg.lookahead == 0) {
         for (int l = 0; l < L; ++l) {
-            if ((st = launch_route(c, l, xl(l), n_tokens, 0, idl(l), wl(l)))) return st;
-            if ((st = launch_resolve(c, step, l, c->ids[0], (int)kB, 0, nullptr))) return st;
+            if ((st = launch_route(c, l, xl(l), n_tokens))) return st;
+            if ((st = launch_resolve(c, step, l, true, nullptr, n_tokens, 0, nullptr, idl(l), wl(l)))) return st;
             int nm = 0;
             if ((st = stage_misses(c, l, 0, c->seq, &nm))) return st;
-            if ((st = launch_ffn(c, l, xl(l), n_tokens, 0, yl(l), nm))) return st;
+            if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, 0, yl(l), nm))) return st;
         }
         return MOE_OK;
     }
     // lookahead 1: K1/K2 of layer l+1 and its copies are issued before layer l's FFN
     int64_t seq_of[2] = {0, 0};
-    if ((st = launch_route(c, 0, xl(0), n_tokens, 0, idl(0), wl(0)))) return st;
-    if ((st = launch_resolve(c, step, 0, c->ids[0], (int)kB, 0, nullptr))) return st;
+    if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
+    if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
     seq_of[0] = c->seq;
     for (int l = 0; l < L; ++l) {
         const int par = l & 1;
@@ -578,13 +561,23 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
         if ((st = stage_misses(c, l, par, seq_of[par], &nm))) return st;
         if (l + 1 < L) {
             const int np = par ^ 1;
-            if ((st = launch_route(c, l + 1, xl(l + 1), n_tokens, np, idl(l + 1), wl(l + 1)))) return st;
-            if ((st = launch_resolve(c, step, l + 1, c->ids[np], (int)kB, np, nullptr))) return st;
+            if ((st = launch_route(c, l + 1, xl(l + 1), n_tokens))) return st;
+            if ((st = launch_resolve(c, step, l + 1, true, nullptr, n_tokens, np, nullptr, idl(l + 1), wl(l + 1))))
+                return st;
             seq_of[np] = c->seq;
         }
-        if ((st = launch_ffn(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
+        if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
     }
     return MOE_OK;
+}
+
+moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t n_tokens,
+                              const int32_t* slots_dev, const float* w_dev, void* y) {
+    moe_status st = check_call(c, n_tokens);
+    if (st) return st;
+    if (layer < 0 || layer >= c->cfg.n_layers || !x || !y || !slots_dev || !w_dev)
+        return set_err(c, MOE_EINVAL, "bad layer or buffers");
+    return launch_ffn_layer(c, layer, x, n_tokens, 2, y, 0, slots_dev, w_dev);
 }
 
 moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t cap, size_t* n_out) {
@@ -609,18 +602,10 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         HIPCHK(c, hipEventElapsedTime(&b, p.ev[1], p.ev[2]));
         c->k3_ms += a;
         c->k4_ms += b;
-        c->k3_launches++;
-        c->k4_launches++;
+        c->ffn_launches++;
         c->prof_free.push_back(p);
     }
     c->prof_used.clear();
-    for (auto& p : c->copy_used) {
-        float a = 0;
-        HIPCHK(c, hipEventElapsedTime(&a, p.ev[0], p.ev[1]));
-        c->h2d_ms += a;
-        c->prof_free.push_back(p);
-    }
-    c->copy_used.clear();
     if (out) {
         out->hits = cnt[0];
         out->misses = cnt[1];
@@ -630,14 +615,12 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         out->h2d_copies = c->h2d_copies;
         out->trace_records = take;
         out->trace_dropped = dropped;
-        out->k3_launches = c->k3_launches;
-        out->k4_launches = c->k4_launches;
+        out->ffn_launches = c->ffn_launches;
         out->k3_ms = c->k3_ms;
         out->k4_ms = c->k4_ms;
-        out->h2d_ms = c->h2d_ms;
     }
-    c->k3_launches = c->k4_launches = 0;
-    c->k3_ms = c->k4_ms = c->h2d_ms = 0;
+    c->ffn_launches = 0;
+    c->k3_ms = c->k4_ms = 0;
     if (n_out) *n_out = take;
     return MOE_OK;
 }

@@ -3,18 +3,20 @@
 // Kernel blob layout (what the pinned pool and the HBM slots hold; same size
 // as the logical blob, 3*H*I*17/32 bytes, a permutation of its bytes):
 //
-//  GU section (gate and up, read by K3), I/16 tiles of 16 rows each.  K3 gives
-//  each 16-row tile to one workgroup of W3 waves; a wave is 16 rows x 4
-//  segments, so a row's NB = H/32 blocks are split into S3 = 4*W3 contiguous
-//  segments (segment s: nb(s) = NB/S3 + (s < NB%S3) blocks starting at
-//  b0(s) = s*(NB/S3) + min(s, NB%S3)).  Lane (r, s) reads block b0(s)+t at
+//  GU section (gate and up, read by the gate/up phase of the FFN kernel), I/16
+//  tiles of 16 rows each.  One workgroup of 4 waves takes a 16-row tile; a wave
+//  is 16 rows x 4 segments, so a row's NB = H/32 blocks are split into S3 = 16
+//  contiguous segments (segment s: nb(s) = NB/16 + (s < NB%16) blocks starting
+//  at b0(s) = s*(NB/16) + min(s, NB%16)).  Lane (r, s) reads block b0(s)+t at
 //  step t.  Chunk c = (t*S3 + s)*16 + r enumerates the tile's (row, block)
 //  pairs densely in that order:
-//     tile + c*32         : gate codes of (row, block) [16 B], up codes [16 B]
-//     tile + 16*NB*32 + c*2: gate scale byte, up scale byte
-//  so the 64 lanes of a wave read 2 KB of contiguous codes per step.
+//     tile + c*16          : gate codes of (row, block) [16 B]
+//     tile + 16*NB*16 + c*16: up codes of (row, block) [16 B]
+//     tile + 16*NB*32 + c*2 : gate scale byte, up scale byte
+//  so the 64 lanes of a wave read 1 KB of contiguous gate codes and 1 KB of
+//  contiguous up codes per step.
 //
-//  D section (down, read by K4): codes [H/8][NB_I][8][16 B] (row tile of 8
+//  D section (down, read by the down phase of the FFN kernel): codes [H/8][NB_I][8][16 B] (row tile of 8
 //  output rows, block along the reduction dim I, row in tile), then scales
 //  [H/8][NB_I][8].  The 8 rows of a (tile, block) are one 128-byte line.
 #pragma once
@@ -25,7 +27,7 @@ namespace moe {
 
 struct Layout {
     int H, I, NB, NBI;     // blocks of 32 along H (gate/up rows) and along I (down rows)
-    int W3, S3, T3;        // K3: waves per workgroup, segments per row, max steps per lane
+    int S3, T3;            // gate/up phase: segments per row (16), max steps per lane
     size_t gu_bytes;       // size of the GU section
     size_t d_codes_off;    // offset of the D codes (== gu_bytes)
     size_t d_scales_off;   // offset of the D scales
@@ -35,11 +37,7 @@ struct Layout {
 inline Layout make_layout(int H, int I) {
     Layout L;
     L.H = H; L.I = I; L.NB = H / 32; L.NBI = I / 32;
-    int w = L.NB / 16;                     // aim at >= 4 blocks per segment, at most 4 waves
-    if (w < 1) w = 1;
-    if (w > 4) w = 4;
-    L.W3 = w;
-    L.S3 = 4 * w;
+    L.S3 = 16;
     L.T3 = (L.NB + L.S3 - 1) / L.S3;
     L.gu_bytes = (size_t)I * (size_t)H * 34 / 32;
     L.d_codes_off = L.gu_bytes;
@@ -60,6 +58,8 @@ struct MissList {
     volatile int64_t seq;      // written last (system-scope release) by the resolve kernel
     int32_t n_miss, n_unique;
     int32_t n_evict, n_invalid;  // n_invalid: ids outside [0, E) (ignored)
+    int32_t slot0[16];         // slots of token 0's k experts (ranked)
+    float w0[16];              // routing weights of token 0 (when the step was routed)
     MissEntry e[1];            // [n_miss], sized at allocation: min(max_tokens*k, E)
 };
 
@@ -84,50 +84,45 @@ struct K1Args {
     const uint16_t* W;      // [E][H] router of this layer
     const uint16_t* x;      // [B][H]
     float* z;               // [B][E]
-    int32_t* ids;           // [B][k]
-    float* w;               // [B][k]
-    int32_t* ids_out;       // optional copies for the caller
-    float* w_out;
-    uint32_t* counter;      // [B] arrival counters (zero between launches)
-    int E, H, k, B;
+    int E, H, B;
 };
 
 struct K2Args {
     CacheDev c;
-    const int32_t* ids;     // [n_ids]
+    const float* z;         // [B][E] logits, or NULL when the ids are given
+    int32_t* ids;           // [n_ids]: written from z (top-k), else read
+    float* w;               // [B][k] routing weights (written when z != NULL)
+    int32_t* ids_out;       // optional copies for the caller
+    float* w_out;
     int32_t* slots;         // [n_ids] slot per id
     int32_t* slots_out;     // optional second copy
     MissList* ml;           // host-mapped
     int64_t seq;
-    int n_ids, layer, step, E, C;
+    int n_ids, layer, step, E, C, k, B;
 };
 
-struct K3Args {
+// one MoE layer's expert FFN for B tokens: gate/up + SwiGLU (K3) and
+// down + weighted combine + shared expert (K4)
+struct FfnArgs {
     const uint8_t* arena;   // slot arena
     const uint8_t* shared;  // [L][n_shared] blobs (kernel layout) in HBM
     const int32_t* slots;   // [B][k]
-    const uint16_t* x;      // [B][H]
-    uint16_t* a;            // [B][nE][I] bf16
-    size_t blob_bytes;
-    int k, n_shared, nE, layer, NB, S3, I;
-};
-
-struct K4Args {
-    const uint8_t* arena;
-    const uint8_t* shared;
-    const int32_t* slots;   // [B][k]
     const float* w;         // [B][k]
-    const uint16_t* a;      // [B][nE][I]
+    const uint16_t* x;      // [B][H]
+    uint16_t* a;            // [B][nE][I] bf16 (K3 -> K4)
     uint16_t* y;            // [B][H] bf16
     size_t blob_bytes, d_codes_off, d_scales_off;
-    int k, n_shared, nE, layer, NBI, I, H;
+    int k, n_shared, nE, layer, NB, NBI, I, H;
+    int P1, P2;             // K3 and K4 workgroups per token
+    int karg;               // 1: slots and weights of the single token come in kslot/kw
+    int32_t kslot[16];
+    float kw[16];
 };
 
 // launchers (defined next to their kernels)
-int k4_waves(int nE, int NBI);
 int launch_k1(const K1Args& a, void* stream);
 int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void* stream);
-int launch_k3(const K3Args& a, const Layout& L, int B, void* stream);
-int launch_k4(const K4Args& a, const Layout& L, int B, void* stream);
+int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid);
+size_t ffn_lds_bytes(const Layout& L, int nE);
 
 }  // namespace moe

@@ -162,3 +162,26 @@ def test_slot_bytes_equal_pool_blob_after_fill():
     ref, _ = _check_run(wl, X, ids, w, y, recs, m, points)
     assert ref["counters"]["evictions"] > 0
     m.close()
+
+
+def test_expert_forward_with_resolved_slots_matches_stack():
+    """moe_expert_forward on slots from the cache state reproduces the stack's output bitwise."""
+    import torch
+    wl = synth.WORKLOADS["toy"]
+    X = synth.decode_inputs(wl)[:6]
+    m, _ = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    slot_of, _, _ = m.cache_state()
+    t = X.shape[0] - 1
+    dev = m.device
+    xd = torch.from_numpy(X[t].view(np.int16)).to(dev)
+    for l in range(wl.n_layers):
+        slots = torch.from_numpy(slot_of[l * wl.n_experts + ids[t, l]].astype(np.int32)).to(dev)
+        wd = torch.from_numpy(w[t, l].astype(np.float32)).to(dev)
+        yo = torch.empty((1, wl.hidden), dtype=torch.int16, device=dev)
+        with torch.cuda.stream(m.compute_stream):
+            m.expert_forward(l, xd, slots, wd, yo)
+        m.compute_stream.synchronize()
+        from gpu_helpers import bf16_to_f32
+        np.testing.assert_array_equal(bf16_to_f32(yo)[0].view(np.uint32), y[t, l, 0].view(np.uint32))
+    m.close()
