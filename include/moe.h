@@ -64,6 +64,7 @@ typedef enum {
 
 enum {
     MOE_FLAG_PROFILE = 1,  /* time every K3 and K4 launch with HIP events (read via moe_stats) */
+    MOE_FLAG_PER_TOKEN_FFN = 2,  /* B > 1: run the per-token GEMV kernels instead of the grouped MFMA path */
 };
 
 typedef struct {

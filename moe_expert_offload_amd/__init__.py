@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE = 0, -1, -2, -3, -4, -5
 MOE_FLAG_PROFILE = 1
+MOE_FLAG_PER_TOKEN_FFN = 2
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
            -5: "MOE_ESTATE"}
 

@@ -33,13 +33,10 @@
 // kernel starts with a dependent load.
 #include <hip/hip_runtime.h>
 
+#include "ffn_device.h"
 #include "moe_internal.h"
 
 namespace moe {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 
 // 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) dotted with
 // 8 bf16 activations (4 dwords, element 2i in the low half of dword i)
@@ -63,29 +60,6 @@ __device__ __forceinline__ float dot32(uint4 c, const uint4* xb) {
     s = dot8(c.z, xb[2], s);
     s = dot8(c.w, xb[3], s);
     return s;
-}
-
-// E8M0 -> float: 2^(E-127); E = 0 is 2^-127 (a denormal), E = 255 is NaN
-__device__ __forceinline__ float e8m0(uint32_t e) {
-    e &= 0xFFu;
-    float f = __uint_as_float(e << 23);
-    f = e == 0u ? __uint_as_float(0x00400000u) : f;
-    return e == 255u ? __uint_as_float(0x7FC00000u) : f;
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// streaming 16-byte load (weights are read once per layer step)
-__device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
-    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // LDS position (in uint4 units, 5 per 64-byte block) of block `blk` of a row
@@ -227,7 +201,7 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
             gs += red[(ww * 16 + tid) * 2];
             us += red[(ww * 16 + tid) * 2 + 1];
         }
-        const float act = gs / (1.0f + __expf(-gs)) * us;
+        const float act = swiglu(gs, us);
         a.a[((size_t)b * a.nE + j) * a.I + tile * 16 + tid] = f32_to_bf16(act);
     }
 }

@@ -1,0 +1,510 @@
+// Grouped expert FFN for a batch of tokens (B > 1): multi-request decode and
+// prefill chunks.
+//
+// With several tokens per step, tokens that chose the same expert share its
+// weights, so the layer is a set of small dense contractions, one per distinct
+// expert: [n_e x H] x [H x 2I] -> SwiGLU -> [n_e x I] x [I x H], then the
+// routing-weighted sum over each token's experts plus the shared expert.  The
+// pages overlap expert loading with a prefill chunk's compute
+// (ai.holude.com preflight page, section on prefill and agent workloads) and
+// show per-request speed falling as concurrent requests share the cache
+// (pirouter.ai "FreeToken x RTX 5090" page, section on the expert path); the
+// grouping itself is not described there and is this library's design.
+//
+// Four launches per layer step:
+//  k2g_group   one workgroup: groups the B*k (token, rank) rows by slot
+//              (distinct experts of the step), appends the shared expert as a
+//              group of all B tokens, and cuts groups into chunks of at most
+//              gm rows (the work unit);
+//  k5_gate_up  per (chunk, 64 intermediate rows): gate and up projections of
+//              the chunk's tokens on the matrix cores, SwiGLU, a (bf16);
+//  k5_down     per (chunk, 64 output rows): down projection, unweighted
+//              expert outputs (fp32) per row;
+//  k5_combine  per (token, 1024 outputs): routing-weighted sum over the
+//              token's experts in rank order, plus the shared expert, bf16.
+//
+// Matrix-core mapping (v_mfma_f32_16x16x32_bf16, wave64): operand A is 16
+// weight rows x 32 reduction elements, operand B is 32 reduction elements x
+// 16 tokens, so a wave's output tile is 16 weight rows x 16 tokens.  Lane l
+// (r = l % 16, q = l / 16) holds weight row r and token r of the tile and the
+// reduction elements 8q..8q+7 of each MFMA.  The reduction order inside an
+// MFMA is free as long as both operands agree, so a k-iteration covers four
+// whole MX blocks of 32 elements: lane group q takes one block, loaded as a
+// single 16-byte chunk of codes plus its scale byte, and MFMA step s (0..3)
+// consumes elements 8s..8s+7 of every lane group's block.  Weights are
+// dequantised with the gfx950 scaled convert (v_cvt_scalef32_pk_bf16_fp4), the
+// E8M0 block scale folded in (a power of two, so the bf16 value is exact);
+// bf16 x bf16 products are exact in the FP32 accumulator.  Both matrices are
+// read in the same repacked blob layout as the single-token kernels, each
+// wave read a contiguous 1 KB (gate/up) or eight whole 128-byte lines (down).
+// Token activations are staged in LDS per k-iteration (double-buffered), one
+// copy shared by the workgroup's four waves.
+//
+// blockIdx -> work mapping is XCD-aware: consecutive workgroups go to
+// different XCDs, so the linear index is remapped so that each XCD gets a
+// contiguous range of (chunk, N tile) units, i.e. the N tiles of one chunk
+// (same tokens, L2-resident activations) run on one XCD.
+#include <hip/hip_runtime.h>
+
+#include "ffn_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int KG_THREADS = 1024;
+constexpr int KG_MAXC = 16384;   // cache slots
+constexpr int KG_MAXG = 1024;    // routed groups (distinct experts <= E <= 1024)
+constexpr int K5_THREADS = 256;
+
+int grouped_gm(int B) { return B <= 16 ? 16 : 64; }
+
+int grouped_max_groups(int B, int k, int E, int n_shared) {
+    const long bk = (long)B * k;
+    return (int)(bk < E ? bk : E) + n_shared;
+}
+
+// sum over groups of ceil(rows / gm) < groups + all rows / gm
+int grouped_max_chunks(int B, int k, int E, int n_shared, int gm) {
+    return grouped_max_groups(B, k, E, n_shared) + (int)(((long)B * (k + n_shared)) / gm);
+}
+
+// ------------------------------------------------------------ k2g_group --
+
+// exclusive prefix sum over the 1024 threads, in thread order
+__device__ __forceinline__ int kg_scan(int v, int* s_wave, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < KG_THREADS / 64; ++w) {
+        int c = s_wave[w];
+        before += (w < wave) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
+    __shared__ uint32_t s_bits[KG_MAXC / 32];
+    __shared__ int32_t s_pre[KG_MAXC / 32];
+    __shared__ int32_t s_cnt[KG_MAXG];
+    __shared__ int32_t s_off[KG_MAXG];
+    __shared__ int32_t s_cur[KG_MAXG];
+    __shared__ int s_wave[KG_THREADS / 64];
+    __shared__ int s_invalid;
+    const int tid = threadIdx.x;
+    const int n = a.B * a.k, nw = (a.C + 31) / 32;
+    for (int i = tid; i < nw; i += KG_THREADS) s_bits[i] = 0u;
+    for (int i = tid; i < KG_MAXG; i += KG_THREADS) {
+        s_cnt[i] = 0;
+        s_cur[i] = 0;
+    }
+    if (tid == 0) s_invalid = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += KG_THREADS) {
+        const int sl = a.slots[i];
+        if ((unsigned)sl < (unsigned)a.C) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
+        else atomicAdd(&s_invalid, 1);
+    }
+    __syncthreads();
+    // nw <= 512: one bitmap word per thread; rank of a slot = present slots below it
+    const int pc = tid < nw ? __popc(s_bits[tid]) : 0;
+    int n_rg;
+    const int pre = kg_scan(pc, s_wave, n_rg);
+    if (tid < nw) s_pre[tid] = pre;
+    const int max_rg = a.p.max_groups - a.n_shared;
+    if (s_invalid != 0 || n_rg > max_rg || n_rg > KG_MAXG) {
+        // slots outside [0, C) or more distinct slots than experts: empty plan,
+        // flagged; the combine then writes NaN outputs
+        if (tid == 0) {
+            a.p.hdr[0] = 0;
+            a.p.hdr[1] = 0;
+            a.p.hdr[2] = 0;
+            a.p.hdr[3] = s_invalid != 0 ? s_invalid : -1;
+        }
+        return;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += KG_THREADS) {
+        const int sl = a.slots[i];
+        const int g = s_pre[sl >> 5] + __popc(s_bits[sl >> 5] & ((1u << (sl & 31)) - 1u));
+        atomicAdd(&s_cnt[g], 1);
+    }
+    if (tid < nw) {
+        uint32_t bits = s_bits[tid];
+        int g = s_pre[tid];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            a.p.g_slot[g++] = tid * 32 + b;
+            bits &= bits - 1u;
+        }
+    }
+    __syncthreads();
+    const int cnt = tid < n_rg ? s_cnt[tid] : 0;
+    int rows;
+    const int off = kg_scan(cnt, s_wave, rows);
+    const int nch = (cnt + a.gm - 1) / a.gm;
+    int n_rch;
+    const int cbase = kg_scan(nch, s_wave, n_rch);
+    if (tid < n_rg) {
+        s_off[tid] = off;
+        a.p.g_off[tid] = off;
+        a.p.g_cnt[tid] = cnt;
+        for (int c = 0; c < nch; ++c) {
+            a.p.chunks[2 * (cbase + c)] = tid;
+            a.p.chunks[2 * (cbase + c) + 1] = c * a.gm;
+        }
+    }
+    // shared expert s: group n_rg + s, rows n + s*B + b (token b), in token order
+    const int sh_nch = (a.B + a.gm - 1) / a.gm;
+    for (int i = tid; i < a.n_shared * sh_nch; i += KG_THREADS) {
+        const int s = i / sh_nch, c = i - s * sh_nch;
+        a.p.chunks[2 * (n_rch + i)] = n_rg + s;
+        a.p.chunks[2 * (n_rch + i) + 1] = c * a.gm;
+    }
+    if (tid < a.n_shared) {
+        a.p.g_slot[n_rg + tid] = -1 - tid;
+        a.p.g_off[n_rg + tid] = n + tid * a.B;
+        a.p.g_cnt[n_rg + tid] = a.B;
+    }
+    for (int i = tid; i < a.n_shared * a.B; i += KG_THREADS) a.p.perm[n + i] = n + i;
+    __syncthreads();
+    // rows of a group in any order: every output element depends on its own
+    // token only, so the order inside a group does not change any result
+    for (int i = tid; i < n; i += KG_THREADS) {
+        const int sl = a.slots[i];
+        const int g = s_pre[sl >> 5] + __popc(s_bits[sl >> 5] & ((1u << (sl & 31)) - 1u));
+        a.p.perm[s_off[g] + atomicAdd(&s_cur[g], 1)] = i;
+    }
+    if (tid == 0) {
+        a.p.hdr[0] = n_rg + a.n_shared;
+        a.p.hdr[1] = n_rch + a.n_shared * sh_nch;
+        a.p.hdr[2] = n_rg;
+        a.p.hdr[3] = 0;
+    }
+}
+
+// ------------------------------------------------------ matrix-core FFN --
+
+__device__ __forceinline__ const uint8_t* group_blob(const GemmArgs& a, int g_slot) {
+    return g_slot >= 0 ? a.arena + (size_t)g_slot * a.blob_bytes
+                       : a.shared + (size_t)(a.layer * a.n_shared + (-1 - g_slot)) * a.blob_bytes;
+}
+
+__device__ __forceinline__ int row_token(const GemmArgs& a, int row) {
+    const int n = a.B * a.k;
+    return row < n ? row / a.k : (row - n) % a.B;
+}
+
+// block index of position p of the gate/up section's (step, segment) order
+__device__ __forceinline__ int gu_block(int p, int NB) { return seg_begin(NB, 16, p & 15) + (p >> 4); }
+
+// 8 E2M1 codes (one dword) times the block scale -> 8 bf16 MFMA operand values
+__device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+    const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                       __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+    const u32x4_t u = {v.x, v.y, v.z, v.w};
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ uint32_t word(uint4 v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Work unit of this workgroup: (chunk ci, N tile nt), XCD-aware.  Returns false
+// when the unit is past the step's chunks (the grid is sized for the maximum).
+struct Unit {
+    int ci, nt, g, nrow, base, g_slot;
+};
+
+__device__ __forceinline__ bool get_unit(const GemmArgs& a, int nt_per_chunk, Unit& u) {
+    const int G = gridDim.x;
+    const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    u.ci = logical / nt_per_chunk;
+    u.nt = logical - u.ci * nt_per_chunk;
+    if (u.ci >= a.p.hdr[1]) return false;
+    u.g = a.p.chunks[2 * u.ci];
+    const int start = a.p.chunks[2 * u.ci + 1];
+    const int cnt = a.p.g_cnt[u.g];
+    u.nrow = min(a.gm, cnt - start);
+    u.base = a.p.g_off[u.g] + start;
+    u.g_slot = a.p.g_slot[u.g];
+    return true;
+}
+
+// Activation staging: the chunk's GM token rows x 4 blocks (64 bytes each) per
+// k-iteration, NTT 16-byte pieces per thread.  Piece v = tid + 256*i is
+// (token t = v/16, lane group q = (v/4)%4, step s = v%4).  LDS: [token][q] in
+// 80-byte cells (5 x 16 B), so the 16 tokens a wave reads at once are spread
+// over the banks.
+template <int NTT>
+struct Stager {
+    const uint16_t* src[NTT];   // row base of the piece's token, or a dummy in-bounds row
+    bool ok[NTT];
+    int dst[NTT];               // LDS cell index (uint4 units)
+    int q[NTT], s[NTT];
+};
+
+template <int NTT>
+__device__ __forceinline__ void stager_init(Stager<NTT>& st, const int* s_row, const uint16_t* src,
+                                            int row_len, const GemmArgs& a, bool rows_are_tokens) {
+#pragma unroll
+    for (int i = 0; i < NTT; ++i) {
+        const int v = threadIdx.x + K5_THREADS * i;
+        const int t = v >> 4;
+        const int row = s_row[t];
+        st.ok[i] = row >= 0;
+        const int rr = row >= 0 ? (rows_are_tokens ? row_token(a, row) : row) : 0;
+        st.src[i] = src + (size_t)rr * row_len;
+        st.q[i] = (v >> 2) & 3;
+        st.s[i] = v & 3;
+        st.dst[i] = (t * 4 + st.q[i]) * 5 + st.s[i];
+    }
+}
+
+// ---------------------------------------------------------- k5_gate_up --
+template <int NTT>
+__global__ __launch_bounds__(K5_THREADS) void k5_gate_up(GemmArgs a) {
+    constexpr int GM = 16 * NTT;
+    __shared__ uint4 xs[2][GM * 4 * 5];
+    __shared__ int s_row[GM];
+    const int nt_per_chunk = (a.I / 16 + 3) / 4;
+    Unit u;
+    if (!get_unit(a, nt_per_chunk, u)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < GM) s_row[tid] = tid < u.nrow ? a.p.perm[u.base + tid] : -1;
+    const int ntt = (u.nrow + 15) >> 4;
+    const int NB = a.NB;
+    const int tile = u.nt * 4 + w;            // 16 intermediate rows
+    const bool tile_ok = tile < (a.I >> 4);
+    const uint8_t* tb = group_blob(a, u.g_slot) + (size_t)(tile_ok ? tile : 0) * 16 * NB * 34;
+    const uint8_t* tub = tb + (size_t)16 * NB * 16;
+    const uint8_t* tsc = tb + (size_t)16 * NB * 32;
+    const int r = lane & 15, q = lane >> 4;
+    __syncthreads();
+    Stager<NTT> st;
+    stager_init<NTT>(st, s_row, a.x, a.H, a, true);
+
+    f32x4_t accg[NTT], accu[NTT];
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+        accg[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        accu[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int nit = (NB + 3) >> 2;
+    // loads of iteration it: activation pieces and this lane's weight chunk;
+    // out-of-range positions read an in-bounds address and are zeroed later
+    uint4 xv[NTT];
+    uint4 gc, uc;
+    uint32_t sc;
+    auto issue = [&](int it) {
+#pragma unroll
+        for (int i = 0; i < NTT; ++i) {
+            const int p = 4 * it + st.q[i];
+            const int blk = gu_block(p < NB ? p : NB - 1, NB);
+            xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + blk * 32 + st.s[i] * 8);
+        }
+        const int p = 4 * it + q;
+        const size_t c = (size_t)(p < NB ? p : NB - 1) * 16 + r;
+        gc = ldg16(tb + c * 16);
+        uc = ldg16(tub + c * 16);
+        sc = *reinterpret_cast<const uint16_t*>(tsc + c * 2);
+    };
+    issue(0);
+    for (int it = 0; it < nit; ++it) {
+        uint4* xb = xs[it & 1];
+#pragma unroll
+        for (int i = 0; i < NTT; ++i) {
+            const bool ok = st.ok[i] && (4 * it + st.q[i]) < NB;
+            xb[st.dst[i]] = ok ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const bool pv = tile_ok && (4 * it + q) < NB;
+        const float sg = pv ? e8m0(sc) : 0.0f, su = pv ? e8m0(sc >> 8) : 0.0f;
+        const uint4 gcw = gc, ucw = uc;
+        __syncthreads();
+        if (it + 1 < nit) issue(it + 1);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8_t wg = dq8(word(gcw, s4), sg);
+            const bf16x8_t wu = dq8(word(ucw, s4), su);
+#pragma unroll
+            for (int m = 0; m < NTT; ++m) {
+                if (m < ntt) {
+                    const bf16x8_t xo = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
+                    accg[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg, xo, accg[m], 0, 0, 0);
+                    accu[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu, xo, accu[m], 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (!tile_ok) return;
+    // lane holds intermediate rows tile*16 + 4q + 0..3 of token r of each tile
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+        if (m < ntt) {
+            const int row = s_row[m * 16 + r];
+            if (row >= 0) {
+                uint32_t lo = (uint32_t)f32_to_bf16(swiglu(accg[m][0], accu[m][0])) |
+                              ((uint32_t)f32_to_bf16(swiglu(accg[m][1], accu[m][1])) << 16);
+                uint32_t hi = (uint32_t)f32_to_bf16(swiglu(accg[m][2], accu[m][2])) |
+                              ((uint32_t)f32_to_bf16(swiglu(accg[m][3], accu[m][3])) << 16);
+                *reinterpret_cast<uint2*>(a.a + (size_t)row * a.I + tile * 16 + 4 * q) = make_uint2(lo, hi);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- k5_down --
+template <int NTT>
+__global__ __launch_bounds__(K5_THREADS) void k5_down(GemmArgs a) {
+    constexpr int GM = 16 * NTT;
+    __shared__ uint4 xs[2][GM * 4 * 5];
+    __shared__ int s_row[GM];
+    const int nt_per_chunk = (a.H / 16 + 3) / 4;
+    Unit u;
+    if (!get_unit(a, nt_per_chunk, u)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < GM) s_row[tid] = tid < u.nrow ? a.p.perm[u.base + tid] : -1;
+    const int ntt = (u.nrow + 15) >> 4;
+    const int NBI = a.NBI;
+    const int tile = u.nt * 4 + w;            // 16 output rows = two 8-row tiles of the D section
+    const bool tile_ok = tile < (a.H >> 4);
+    const int r = lane & 15, q = lane >> 4;
+    const int t8 = 2 * (tile_ok ? tile : 0) + (r >> 3), rr = r & 7;
+    const uint8_t* blob = group_blob(a, u.g_slot);
+    const uint8_t* dcod = blob + a.d_codes_off + ((size_t)t8 * NBI * 8 + rr) * 16;
+    const uint8_t* dsc = blob + a.d_scales_off + (size_t)t8 * NBI * 8 + rr;
+    __syncthreads();
+    Stager<NTT> st;
+    stager_init<NTT>(st, s_row, a.a, a.I, a, false);
+
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nit = (NBI + 3) >> 2;
+    uint4 xv[NTT];
+    uint4 dc;
+    uint32_t sc;
+    auto issue = [&](int it) {
+#pragma unroll
+        for (int i = 0; i < NTT; ++i) {
+            const int p = 4 * it + st.q[i];
+            const int ib = p < NBI ? p : NBI - 1;
+            xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + ib * 32 + st.s[i] * 8);
+        }
+        const int p = 4 * it + q;
+        const int ib = p < NBI ? p : NBI - 1;
+        dc = ldg16(dcod + (size_t)ib * 8 * 16);
+        sc = dsc[(size_t)ib * 8];
+    };
+    issue(0);
+    for (int it = 0; it < nit; ++it) {
+        uint4* xb = xs[it & 1];
+#pragma unroll
+        for (int i = 0; i < NTT; ++i) {
+            const bool ok = st.ok[i] && (4 * it + st.q[i]) < NBI;
+            xb[st.dst[i]] = ok ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const bool pv = tile_ok && (4 * it + q) < NBI;
+        const float sd = pv ? e8m0(sc) : 0.0f;
+        const uint4 dcw = dc;
+        __syncthreads();
+        if (it + 1 < nit) issue(it + 1);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8_t wd = dq8(word(dcw, s4), sd);
+#pragma unroll
+            for (int m = 0; m < NTT; ++m) {
+                if (m < ntt) {
+                    const bf16x8_t ao = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd, ao, acc[m], 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (!tile_ok) return;
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+        if (m < ntt) {
+            const int row = s_row[m * 16 + r];
+            if (row >= 0)
+                *reinterpret_cast<float4*>(a.yp + (size_t)row * a.H + tile * 16 + 4 * q) =
+                    make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------- k5_combine --
+// grid (ceil(H / 1024), B), 256 threads, 4 outputs per thread
+__global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* hdr) {
+    const int b = blockIdx.y;
+    const int h = 4 * (blockIdx.x * 256 + threadIdx.x);
+    if (h >= c.H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (hdr[3] != 0) {
+        acc = make_float4(__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
+                          __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u));
+    } else {
+        for (int j = 0; j < c.k; ++j) {
+            const int row = b * c.k + j;
+            const float wj = c.w[row];
+            const float4 v = *reinterpret_cast<const float4*>(c.yp + (size_t)row * c.H + h);
+            acc.x += wj * v.x;
+            acc.y += wj * v.y;
+            acc.z += wj * v.z;
+            acc.w += wj * v.w;
+        }
+        for (int s = 0; s < c.n_shared; ++s) {
+            const int row = c.B * c.k + s * c.B + b;
+            const float4 v = *reinterpret_cast<const float4*>(c.yp + (size_t)row * c.H + h);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+    *reinterpret_cast<uint2*>(c.y + (size_t)b * c.H + h) = make_uint2(lo, hi);
+}
+
+static int pad8(long v) { return (int)((v + 7) / 8 * 8); }
+
+int launch_grouped_ffn(GroupArgs& g, GemmArgs& m, CombineArgs& c, void* stream, void* ev_mid) {
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(k2g_group, dim3(1), dim3(KG_THREADS), 0, st, g);
+    const int nt1 = (m.I / 16 + 3) / 4, nt2 = (m.H / 16 + 3) / 4;
+    const dim3 g1(pad8((long)m.p.max_chunks * nt1)), g2(pad8((long)m.p.max_chunks * nt2));
+    if (m.gm == 16)
+        hipLaunchKernelGGL(k5_gate_up<1>, g1, dim3(K5_THREADS), 0, st, m);
+    else
+        hipLaunchKernelGGL(k5_gate_up<4>, g1, dim3(K5_THREADS), 0, st, m);
+    if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
+    if (m.gm == 16)
+        hipLaunchKernelGGL(k5_down<1>, g2, dim3(K5_THREADS), 0, st, m);
+    else
+        hipLaunchKernelGGL(k5_down<4>, g2, dim3(K5_THREADS), 0, st, m);
+    hipLaunchKernelGGL(k5_combine, dim3((c.H + 1023) / 1024, c.B), dim3(256), 0, st, c, m.p.hdr);
+    return (int)hipGetLastError();
+}
+
+}  // namespace moe

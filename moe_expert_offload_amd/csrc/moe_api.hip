@@ -57,6 +57,8 @@ struct moe_ctx {
     float* w[2] = {nullptr, nullptr};
     int32_t* slots[2] = {nullptr, nullptr};
     uint16_t* a[3] = {nullptr, nullptr, nullptr};  // [2] serves moe_expert_forward
+    GroupPlanDev gp{};          // grouped path (max_tokens > 1)
+    float* yp = nullptr;
     // host-mapped miss lists
     uint8_t* ml_mem = nullptr;
     size_t ml_stride = 0;
@@ -127,7 +129,8 @@ moe_status check_cfg(const moe_config* c) {
 }
 
 struct WsPlan {
-    size_t z, ids, w, slots, a, total;
+    size_t z, ids, w, slots, a, grp, yp, total;
+    int max_groups, max_chunks;
 };
 
 WsPlan plan_workspace(const moe_config& c) {
@@ -140,6 +143,19 @@ WsPlan plan_workspace(const moe_config& c) {
     p.w = off;     off = align_up(off + 2 * B * k * 4, 256);
     p.slots = off; off = align_up(off + 2 * B * k * 4, 256);
     p.a = off;     off = align_up(off + 3 * B * nE * (size_t)c.inter * 2, 256);
+    p.grp = p.yp = off;
+    p.max_groups = p.max_chunks = 0;
+    if (B > 1) {
+        // grouped path: plan header, groups, chunks, row permutation, expert outputs
+        // the chunk size depends on the call's token count: take the largest bound
+        p.max_groups = grouped_max_groups((int)B, (int)k, (int)E, c.n_shared);
+        for (int b : {(int)B, std::min((int)B, 16)})
+            p.max_chunks = std::max(p.max_chunks, grouped_max_chunks(b, (int)k, (int)E, c.n_shared, grouped_gm(b)));
+        p.grp = off;
+        off = align_up(off + 4 * 4 + 3 * (size_t)p.max_groups * 4 + 2 * (size_t)p.max_chunks * 4 +
+                           B * nE * 4, 256);
+        p.yp = off;    off = align_up(off + B * nE * (size_t)c.hidden * 4, 256);
+    }
     p.total = off;
     return p;
 }
@@ -305,6 +321,48 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         if (st) return st;
         HIPCHK(c, hipEventRecord(ps.ev[0], c->cs));
     }
+    if (B > 1 && !(c->cfg.flags & MOE_FLAG_PER_TOKEN_FFN)) {
+        GroupArgs g{};
+        g.p = c->gp;
+        g.slots = slots_dev ? slots_dev : c->slots[par];
+        g.B = B;
+        g.k = c->cfg.top_k;
+        g.C = c->cfg.cache_slots;
+        g.n_shared = c->cfg.n_shared;
+        g.gm = grouped_gm(B);
+        g.p.max_groups = grouped_max_groups(B, c->cfg.top_k, c->cfg.n_experts, c->cfg.n_shared);
+        g.p.max_chunks = grouped_max_chunks(B, c->cfg.top_k, c->cfg.n_experts, c->cfg.n_shared, g.gm);
+        GemmArgs m{};
+        m.p = g.p;
+        m.arena = c->arena;
+        m.shared = c->shared_dev;
+        m.x = (const uint16_t*)x;
+        m.a = c->a[par];
+        m.yp = c->yp;
+        m.blob_bytes = c->lay.blob_bytes;
+        m.d_codes_off = c->lay.d_codes_off;
+        m.d_scales_off = c->lay.d_scales_off;
+        m.B = B;
+        m.k = c->cfg.top_k;
+        m.n_shared = c->cfg.n_shared;
+        m.layer = layer;
+        m.H = c->cfg.hidden;
+        m.I = c->cfg.inter;
+        m.NB = c->lay.NB;
+        m.NBI = c->lay.NBI;
+        m.gm = g.gm;
+        CombineArgs cb{};
+        cb.yp = c->yp;
+        cb.w = w_dev ? w_dev : c->w[par];
+        cb.slots = g.slots;
+        cb.y = (uint16_t*)y;
+        cb.B = B;
+        cb.k = c->cfg.top_k;
+        cb.n_shared = c->cfg.n_shared;
+        cb.H = c->cfg.hidden;
+        cb.C = c->cfg.cache_slots;
+        LAUNCHCHK(c, launch_grouped_ffn(g, m, cb, c->cs, prof ? ps.ev[1] : nullptr));
+    } else {
     FfnArgs f{};
     f.arena = c->arena;
     f.shared = c->shared_dev;
@@ -331,6 +389,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
             f.kw[j] = c->tok0_w[par][j];
         }
     LAUNCHCHK(c, launch_ffn(f, c->lay, B, c->cs, prof ? ps.ev[1] : nullptr));
+    }
     if (prof) {
         HIPCHK(c, hipEventRecord(ps.ev[2], c->cs));
         c->prof_used.push_back(ps);
@@ -406,6 +465,18 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
         c->slots[p] = (int32_t*)(ws + wp.slots) + p * Bk;
     }
     for (int p = 0; p < 3; ++p) c->a[p] = (uint16_t*)(ws + wp.a) + (size_t)p * cfg->max_tokens * c->nE * cfg->inter;
+    if (cfg->max_tokens > 1) {
+        int32_t* g = (int32_t*)(ws + wp.grp);
+        c->gp.max_groups = wp.max_groups;
+        c->gp.max_chunks = wp.max_chunks;
+        c->gp.hdr = g;
+        c->gp.g_slot = g + 4;
+        c->gp.g_off = c->gp.g_slot + wp.max_groups;
+        c->gp.g_cnt = c->gp.g_off + wp.max_groups;
+        c->gp.chunks = c->gp.g_cnt + wp.max_groups;
+        c->gp.perm = c->gp.chunks + 2 * (size_t)wp.max_chunks;
+        c->yp = (float*)(ws + wp.yp);
+    }
 
     // device cache state
     const size_t n_sl = (size_t)Lyr * E;

@@ -119,10 +119,56 @@ struct FfnArgs {
     float kw[16];
 };
 
+// ---------------------------------------------------- grouped path (B > 1) --
+// Tokens of one layer step grouped by expert: every (token, rank) assignment
+// is a row id r (r < B*k: token r / k, rank r % k; r = B*k + s*B + b: shared
+// expert s for token b).  A group is one distinct slot (or one shared expert);
+// its rows are listed contiguously in `perm`; a chunk is up to `gm` rows of
+// one group, the unit of work of the grouped FFN kernels.
+struct GroupPlanDev {
+    int32_t* hdr;         // [4]: groups, chunks, routed groups, invalid slots
+    int32_t* g_slot;      // [G]: slot, or -1-s for shared expert s
+    int32_t* g_off;       // [G]: first position of the group in perm
+    int32_t* g_cnt;       // [G]: rows of the group
+    int32_t* chunks;      // [2*NCH]: (group, first row within the group)
+    int32_t* perm;        // [B*nE]: row ids in group order
+    int max_groups, max_chunks;
+};
+
+struct GroupArgs {
+    GroupPlanDev p;
+    const int32_t* slots;   // [B*k]
+    int B, k, C, n_shared, gm;
+};
+
+struct GemmArgs {
+    GroupPlanDev p;
+    const uint8_t* arena;
+    const uint8_t* shared;  // [L][n_shared] blobs
+    const uint16_t* x;      // [B][H] (gate/up input)
+    uint16_t* a;            // [B*nE][I] bf16, rows = row ids
+    float* yp;              // [B*nE][H] fp32, rows = row ids (unweighted expert outputs)
+    size_t blob_bytes, d_codes_off, d_scales_off;
+    int B, k, n_shared, layer, H, I, NB, NBI, gm;
+    int nt;                 // N tiles (of 64 output rows) per chunk
+};
+
+struct CombineArgs {
+    const float* yp;
+    const float* w;         // [B][k]
+    const int32_t* slots;   // [B][k] (a row with an invalid slot is skipped)
+    uint16_t* y;            // [B][H] bf16
+    int B, k, n_shared, H, C;
+};
+
 // launchers (defined next to their kernels)
 int launch_k1(const K1Args& a, void* stream);
 int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void* stream);
 int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid);
 size_t ffn_lds_bytes(const Layout& L, int nE);
+int grouped_max_groups(int B, int k, int E, int n_shared);
+int grouped_max_chunks(int B, int k, int E, int n_shared, int gm);
+int grouped_gm(int B);
+int launch_grouped_ffn(GroupArgs& g, GemmArgs& m, CombineArgs& c, void* stream, void* ev_mid);
 
 }  // namespace moe

@@ -221,3 +221,45 @@ def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=N
     return {"ids": ids, "w": w, "slots": slots,
             "trace": np.concatenate(recs) if recs else np.empty(0, TRACE_DTYPE),
             "counters": cache.counters(), "cache": cache}
+
+
+def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X):
+    """Routing and cache trace of a run whose steps have their own token counts.
+
+    steps_X: list of [B_t][H] bf16-bit arrays; step t feeds X_t to every layer (a prefill
+    chunk is one step whose B_t is the chunk length).  Steps run in order, layers 0..L-1
+    inside a step.  Returns dict with per-step lists ids[t] [L][B_t][k], w[t], slots[t],
+    the trace (structured array), counters and the cache.
+    """
+    L, k = wl.n_layers, wl.top_k
+    Xc = np.concatenate([np.asarray(x, dtype=np.uint16).reshape(-1, wl.hidden) for x in steps_X])
+    layers, toks, shapes = [], [], []
+    base = 0
+    for x in steps_X:
+        B = len(x)
+        ll, bb = np.meshgrid(np.arange(L), np.arange(B), indexing="ij")
+        layers.append(ll.ravel())
+        toks.append(base + bb.ravel())
+        shapes.append(B)
+        base += B
+    ids_all, w_all = route_batch(W_all, Xc, k, np.concatenate(layers), np.concatenate(toks))
+    cache = Cache(L, wl.n_experts, wl.cache_slots)
+    out = {"ids": [], "w": [], "slots": []}
+    recs = []
+    pos = 0
+    for t, B in enumerate(shapes):
+        ids = ids_all[pos:pos + L * B].reshape(L, B, k)
+        w = w_all[pos:pos + L * B].reshape(L, B, k)
+        pos += L * B
+        slots = np.empty_like(ids)
+        for l in range(L):
+            s, r = cache.step(t, l, ids[l])
+            slots[l] = s.reshape(B, k)
+            recs.append(r)
+        out["ids"].append(ids)
+        out["w"].append(w)
+        out["slots"].append(slots)
+    out["trace"] = np.concatenate(recs) if recs else np.empty(0, TRACE_DTYPE)
+    out["counters"] = cache.counters()
+    out["cache"] = cache
+    return out

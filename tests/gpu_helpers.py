@@ -57,3 +57,25 @@ def close_enough(y, ref):
 
 def trace_tuples(recs):
     return [tuple(int(r[f]) for f in ("step", "layer", "expert", "slot", "hit", "evicted_key")) for r in recs]
+
+
+def run_steps(m, wl, steps_X):
+    """moe_stack_forward once per step, step t with its own token count B_t (steps_X: list of
+    [B_t][H] bf16 bits).  Returns per-step lists ids [L][B_t][k], w, y [L][B_t][H] float32."""
+    import torch
+    L, k, H = wl.n_layers, wl.top_k, wl.hidden
+    dev = m.device
+    outs = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(m.compute_stream):
+        for t, x in enumerate(steps_X):
+            B = len(x)
+            xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+            y = torch.empty((L, B, H), dtype=torch.int16, device=dev)
+            ids = torch.empty((L, B, k), dtype=torch.int32, device=dev)
+            w = torch.empty((L, B, k), dtype=torch.float32, device=dev)
+            m.stack_forward(t, xd, 0, B, y, B * H, ids, w)
+            outs.append((ids, w, y))
+    m.compute_stream.synchronize()
+    return ([o[0].cpu().numpy() for o in outs], [o[1].cpu().numpy() for o in outs],
+            [bf16_to_f32(o[2]) for o in outs])
