@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 
 
 def decode_rate(tokens, total_s, ttft_s):
@@ -38,40 +39,132 @@ def per_token_budget_gb(link_gbps, tok_per_s):
     return link_gbps / tok_per_s
 
 
-def ffn_bytes(wl):
-    """Algorithmic HBM bytes of one token-layer expert FFN: K3 reads the selected (and shared)
-    experts' MXFP4 gate/up weights and x and writes the intermediate vector; K4 reads the down
-    weights and the intermediate vector and writes y."""
+def ffn_bytes_split(wl):
+    """Algorithmic HBM bytes of one token-layer expert FFN at batch 1: K3 reads the selected (and
+    shared) experts' MXFP4 gate/up weights and x and writes the intermediate vector; K4 reads
+    the down weights and the intermediate vector and writes y."""
     H, I, nE = wl.hidden, wl.inter, wl.top_k + wl.n_shared
     k3 = nE * (I * H * 34 // 32) + H * 2 + nE * I * 2
     k4 = nE * (H * I * 17 // 32) + nE * I * 2 + H * 2
     return k3, k4
 
 
+def ffn_bytes(wl, B, n_distinct):
+    """Algorithmic HBM bytes of one layer's expert FFN for B tokens: the weights of the distinct
+    selected experts and the shared expert, read once; x read and y written; the bf16
+    intermediate vector of every (token, expert) row written and read back."""
+    H, I, nE = wl.hidden, wl.inter, wl.top_k + wl.n_shared
+    blob = 3 * H * I * 17 // 32
+    return (n_distinct + wl.n_shared) * blob + 2 * B * H * 2 + 2 * B * nE * I * 2
+
+
+def ffn_flops(wl, rows):
+    """Multiply-add flops of `rows` (token, expert) rows through one expert FFN (gate, up, down)."""
+    return 2 * rows * 3 * wl.hidden * wl.inter
+
+
+def time_ffn_pass(m, x, layers, slots, w, y, rounds):
+    """Mean time (us) of one layer's expert FFN: moe_expert_forward for each of `layers` (slots,
+    w, y indexed like `layers`), captured as one HIP graph and replayed `rounds` times between
+    two events on the compute stream."""
+    import torch
+    cs = m.compute_stream
+    L = len(layers)
+    y_eager = torch.empty_like(y)
+    with torch.cuda.stream(cs):
+        for i, l in enumerate(layers):
+            m.expert_forward(l, x, slots[i], w[i], y_eager[i])
+    cs.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        for i, l in enumerate(layers):
+            m.expert_forward(l, x, slots[i], w[i], y[i])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        graph.replay()
+        cs.synchronize()
+        assert torch.equal(y, y_eager), "graph replay differs from the eager FFN"
+        e0.record(cs)
+        for _ in range(rounds):
+            graph.replay()
+        e1.record(cs)
+    cs.synchronize()
+    assert torch.equal(y, y_eager), "graph replay differs from the eager FFN"
+    return e0.elapsed_time(e1) * 1e3 / (rounds * L)
+
+
+def run_prefill(m, wl, dev, rounds):
+    """The prefill chunk: one step of all its tokens through every layer (cold cache), then the
+    last layer's grouped expert FFN on the chunk timed alone (its experts are all resident)."""
+    import numpy as np
+    import torch
+    import synth
+    P = synth.prefill_inputs(wl)
+    n, L, H, k = P.shape[0], wl.n_layers, wl.hidden, wl.top_k
+    xp = torch.from_numpy(P.view(np.int16)).to(dev)
+    yp = torch.empty((L, n, H), dtype=torch.int16, device=dev)
+    ids = torch.empty((L, n, k), dtype=torch.int32, device=dev)
+    w = torch.empty((L, n, k), dtype=torch.float32, device=dev)
+    cs = m.compute_stream
+    c0, _ = m.stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(cs):
+        m.stack_forward(0, xp, 0, n, yp, n * H, ids, w)
+    cs.synchronize()
+    m.copy_stream.synchronize()
+    dt = time.perf_counter() - t0
+    c1, _ = m.stats()
+    slot_of, _, _ = m.cache_state()
+    l = L - 1
+    ids_l = ids[l].cpu().numpy()
+    slots = slot_of[l * wl.n_experts + ids_l].astype(np.int32)
+    assert (slots >= 0).all()
+    sd = torch.from_numpy(slots[None]).to(dev)
+    us = time_ffn_pass(m, xp, [l], sd, w[l:l + 1], yp[l:l + 1], rounds)
+    rows = n * (k + wl.n_shared)
+    fl = ffn_flops(wl, rows)
+    nb = ffn_bytes(wl, n, len(np.unique(slots)))
+    tf = fl / (us * 1e-6) / 1e12
+    gbs = nb / (us * 1e-6) / 1e9
+    h2d = c1["h2d_bytes"] - c0["h2d_bytes"]
+    return {"tokens": n, "wall_s": round(dt, 3), "tok_s": round(n / dt, 1),
+            "h2d_GB": round(h2d / 1e9, 2), "h2d_GBps": round(h2d / dt / 1e9, 2),
+            "ffn_layer_us": round(us, 1),
+            "ffn_mfma": {"achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl},
+            "ffn_hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nb}}
+
+
 def cpu_baseline(wl, W, X, budget_s=20.0):
-    """The oracle as it stands, on the host cores: routing, LRU step and FFN of one decode
-    token through every layer, repeated while the budget lasts (at least one token)."""
+    """The oracle as it stands, on the host cores: routing, LRU step and FFN of every token of
+    one decode step through every layer, repeated while the budget lasts (at least one step)."""
     import numpy as np
 
     import oracle
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     cache = oracle.Cache(wl.n_layers, wl.n_experts, wl.cache_slots)
+    B = X.shape[1]
     t0 = time.perf_counter()
     done = 0
     for t in range(X.shape[0]):
         for l in range(wl.n_layers):
-            z = oracle.router_logits(W[l], X[t, 0])
-            ids, w = oracle.topk_softmax(z, wl.top_k)
-            cache.step(t, l, ids)
-            oracle.moe_output(wl, l, X[t, 0], ids, w)
+            step_ids = []
+            for b in range(B):
+                z = oracle.router_logits(W[l], X[t, b])
+                ids, w = oracle.topk_softmax(z, wl.top_k)
+                step_ids.append(ids)
+                oracle.moe_output(wl, l, X[t, b], ids, w)
+            cache.step(t, l, np.stack(step_ids))
         done += 1
         if time.perf_counter() - t0 > budget_s * 0.5:
             break
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tok/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
+    return {"value": done * B / dt, "unit": "tok/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
             "kind": "oracle",
-            "sample": f"{done} decode token(s) x {wl.n_layers} layers of {wl.name}: FP32 router, "
+            "sample": f"{done} decode step(s) of {B} token(s) x {wl.n_layers} layers of {wl.name}: FP32 router, "
                       f"top-{wl.top_k}, LRU step, FP64 MXFP4 SwiGLU FFN of the selected experts"}
 
 
@@ -106,14 +199,16 @@ def main():
         K = T - W_
     flags = 0
     cfg = M.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.n_shared,
-                        wl.cache_slots, wl.n_requests, args.lookahead, 0, 0, flags)
+                        wl.cache_slots, wl.max_tokens, args.lookahead, 0, 0, flags)
     fptr, FillArgs = synth.fill_callback()
     fa = FillArgs(wl.seed, wl.hidden, wl.inter)
     Wr = synth.router_weights(wl)
     t0 = time.perf_counter()
     m = M.OffloadMoE(cfg, (fptr, ctypes.addressof(fa)), Wr)
     init_s = time.perf_counter() - t0
-    print(f"# pool {wl.pool} x {m.blob_bytes} B = {wl.pool * m.blob_bytes / 1e9:.2f} GB pinned, "
+    c_init, _ = m.stats()
+    pinned_gb = c_init["pool_pinned_bytes"] / 1e9
+    print(f"# pool {wl.pool} x {m.blob_bytes} B = {wl.pool * m.blob_bytes / 1e9:.2f} GB ({pinned_gb:.2f} GB pinned), "
           f"cache {wl.cache_slots} slots, init {init_s:.1f} s", file=sys.stderr, flush=True)
 
     # measured host-to-device bandwidth of the copy path (>= 2 GB of blob-sized copies)
@@ -122,13 +217,19 @@ def main():
     h2d_big = m.measure_h2d(64 << 20, 32)
 
     B, L, H = wl.n_requests, wl.n_layers, wl.hidden
+    cs = m.compute_stream
+    extra = {}
+    prefill = None
+    if wl.prefill_tokens:
+        prefill = run_prefill(m, wl, dev, args.ffn_rounds)
+        extra["prefill"] = prefill
     xd = torch.from_numpy(X.view(np.int16)).to(dev)
     y = torch.empty((L, B, H), dtype=torch.int16, device=dev)
-    cs = m.compute_stream
+    s0 = 1 if wl.prefill_tokens else 0
     torch.cuda.synchronize()
     with torch.cuda.stream(cs):
         for t in range(W_):
-            m.stack_forward(t, xd[t], 0, B, y, B * H)
+            m.stack_forward(s0 + t, xd[t], 0, B, y, B * H)
     cs.synchronize()
     c_warm, _ = m.stats()
     ids = torch.empty((L, B, wl.top_k), dtype=torch.int32, device=dev)
@@ -138,7 +239,7 @@ def main():
     with torch.cuda.stream(cs):
         for t in range(W_, W_ + K):
             last = t == W_ + K - 1
-            m.stack_forward(t, xd[t], 0, B, y, B * H, ids if last else None, wts if last else None)
+            m.stack_forward(s0 + t, xd[t], 0, B, y, B * H, ids if last else None, wts if last else None)
     cs.synchronize()
     m.copy_stream.synchronize()
     torch.cuda.synchronize()
@@ -146,73 +247,59 @@ def main():
     c_all, _ = m.stats()
     # device and host counters are cumulative: take the timed region's share
     c = dict(c_all)
-    for key in ("hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies"):
+    for key in ("hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "h2d_bounced"):
         c[key] = c_all[key] - c_warm[key]
     tok_s = K * B / dt
 
-    # Expert-FFN kernel timing: the last token's experts of every layer are resident; run K3+K4
-    # for layer 0..L-1 back to back, several rounds, between two HIP events on the compute
-    # stream (consecutive launches read different experts, so nothing is served from a cache).
+    # Expert-FFN kernel timing on the last step's experts: one pass over the layers whose
+    # selected experts are all still resident (all of them at batch 1; a 16-request step can
+    # touch more experts than there are slots, evicting its own early layers) is captured in a
+    # HIP graph and replayed between two HIP events on the compute stream.  Every layer's
+    # experts sit in their own slots, so consecutive launches read different weights.
     slot_of, _, _ = m.cache_state()
     ids_h = ids.cpu().numpy()
-    slots_h = np.stack([slot_of[l * wl.n_experts + ids_h[l]] for l in range(L)]).astype(np.int32)
-    assert (slots_h >= 0).all()
-    slots_d = torch.from_numpy(slots_h).to(dev)
-    xt = xd[W_ + K - 1]
-    y_eager = torch.empty_like(y)
-    with torch.cuda.stream(cs):
-        for l in range(L):
-            m.expert_forward(l, xt, slots_d[l], wts[l], y_eager[l])
-    cs.synchronize()
-    # one pass over the L layers captured in a HIP graph, so that launch overhead on the host
-    # does not leave gaps between the kernels; replayed between two events
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cs):
-        for l in range(L):
-            m.expert_forward(l, xt, slots_d[l], wts[l], y[l])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(cs):
-        graph.replay()
-        cs.synchronize()
-        assert torch.equal(y, y_eager), "graph replay differs from the eager FFN"
-        e0.record(cs)
-        for r in range(args.ffn_rounds):
-            graph.replay()
-        e1.record(cs)
-    cs.synchronize()
-    assert torch.equal(y, y_eager), "graph replay differs from the eager FFN"
-    ffn_launches = args.ffn_rounds * L
-    ffn_us = e0.elapsed_time(e1) * 1e3 / ffn_launches
+    slots_all = np.stack([slot_of[l * wl.n_experts + ids_h[l]] for l in range(L)]).astype(np.int32)
+    layers = [l for l in range(L) if (slots_all[l] >= 0).all()]
+    assert layers, "no layer of the last step is fully resident"
+    slots_h = slots_all[layers]
+    ffn_us = time_ffn_pass(m, xd[W_ + K - 1], layers, torch.from_numpy(slots_h).to(dev), wts[layers],
+                           y[layers], args.ffn_rounds)
 
-    k3b, k4b = ffn_bytes(wl)
+    nbytes = [ffn_bytes(wl, B, len(np.unique(slots_h[i]))) for i in range(len(layers))]
+    bytes_layer = sum(nbytes) / len(layers)
     acc = c["hits"] + c["misses"]
-    extra = {}
-    gbs = (k3b + k4b) / (ffn_us * 1e-6) / 1e9
+    gbs = bytes_layer / (ffn_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "expert FFN of one layer: k3_gate_up + k4_down (MXFP4 GEMVs, SwiGLU, weighted combine)",
-            "bytes_per_launch": k3b + k4b, "bytes_k3": k3b, "bytes_k4": k4b,
-            "avg_us": round(ffn_us, 2), "launches": ffn_launches}
+            "kernel": ("expert FFN of one layer: k3_gate_up + k4_down (MXFP4 GEMVs, SwiGLU, weighted combine)"
+                       if B == 1 else
+                       "expert FFN of one layer: k2g_group + k5_gate_up + k5_down + k5_combine (grouped MXFP4 MFMA)"),
+            "bytes_per_launch": round(bytes_layer), "avg_us": round(ffn_us, 2),
+            "launches": args.ffn_rounds * len(layers), "layers_timed": len(layers)}
+    if B == 1:
+        roof["bytes_k3"], roof["bytes_k4"] = ffn_bytes_split(wl)
     # miss bytes over the whole timed region: a lower bound on the copy path's achieved rate
     eff = c["h2d_bytes"] / dt / 1e9
     extra["h2d"] = {"effective_GBps": round(eff, 2), "measured_GBps": round(h2d_meas, 2),
                     "measured_64MB_GBps": round(h2d_big, 2), "frac_of_measured": round(eff / h2d_meas, 4)}
+    extra["pool"] = {"GB": round(wl.pool * m.blob_bytes / 1e9, 2), "pinned_GB": round(pinned_gb, 2),
+                     "bounced_copies": c["h2d_bounced"], "copies": c["h2d_copies"]}
     extra["miss_rate"] = round(c["misses"] / acc, 4) if acc else None
     extra["miss_rate_warmup"] = round(c_warm["misses"] / max(1, c_warm["hits"] + c_warm["misses"]), 4)
-    extra["misses_per_token"] = round(c["misses"] / K, 2)
-    extra["h2d_GB_per_token"] = round(c["h2d_bytes"] / K / 1e9, 4)
-    miss_bytes_tok = c["h2d_bytes"] / K
-    hbm_bytes_tok = L * (k3b + k4b)
-    roof_tok = 1.0 / max(hbm_bytes_tok / (HBM_PEAK_GBS * 1e9), miss_bytes_tok / (h2d_meas * 1e9))
-    extra["decode_roofline_tok_s"] = round(roof_tok, 1)
-    extra["decode_frac_of_roofline"] = round(tok_s / roof_tok, 4)
+    extra["misses_per_step"] = round(c["misses"] / K, 2)
+    extra["h2d_GB_per_step"] = round(c["h2d_bytes"] / K / 1e9, 4)
+    miss_bytes_step = c["h2d_bytes"] / K
+    roof_step = 1.0 / max(L * bytes_layer / (HBM_PEAK_GBS * 1e9), miss_bytes_step / (h2d_meas * 1e9))
+    extra["decode_roofline_tok_s"] = round(roof_step * B, 1)
+    extra["decode_frac_of_roofline"] = round(tok_s / (roof_step * B), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, Wr, X)
     m.close()
     out = {
-        "metric": "decode tok/s per MoE stack at batch 1",
+        "metric": ("decode tok/s per MoE stack at batch 1" if B == 1 else
+                   f"decode tok/s per MoE stack, {B} requests in lock-step (aggregate)"),
         "value": round(tok_s, 2),
         "unit": "tok/s",
         "n_gpus": 1,

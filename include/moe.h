@@ -81,6 +81,9 @@ typedef struct {
     int32_t trace_capacity; /* cache trace records kept on the device (0 = none) */
     int32_t fill_threads;   /* host threads calling the fill callback (0 = all cores) */
     int32_t flags;          /* MOE_FLAG_* */
+    int32_t pinned_mb;      /* at most this many MiB of the pool in pinned memory (0 = as much as the
+                               platform grants); the rest is pageable and its misses go through a
+                               ring of pinned bounce buffers */
 } moe_config;
 
 /* Writes the logical blob of routed expert (layer, expert >= 0) or of shared
@@ -148,6 +151,8 @@ typedef struct {
     uint64_t h2d_bytes, h2d_copies;    /* miss copies issued */
     uint64_t trace_records, trace_dropped;
     uint64_t ffn_launches;             /* with MOE_FLAG_PROFILE: timed layer FFNs (one K3 + one K4) */
+    uint64_t h2d_bounced;              /* misses copied from the pageable part through the bounce ring */
+    uint64_t pool_pinned_bytes;        /* bytes of the pool in pinned memory */
     double k3_ms, k4_ms;               /* ... and the summed durations of K3 and K4 (HIP events) */
 } moe_counters;
 

@@ -35,13 +35,14 @@ _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: 
 class MoeConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "n_experts", "top_k", "hidden", "inter", "n_shared", "cache_slots", "max_tokens",
-        "lookahead", "trace_capacity", "fill_threads", "flags")]
+        "lookahead", "trace_capacity", "fill_threads", "flags", "pinned_mb")]
 
 
 class MoeCounters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "trace_records",
-        "trace_dropped", "ffn_launches")] + [("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double)]
+        "trace_dropped", "ffn_launches", "h2d_bounced", "pool_pinned_bytes")] + [
+        ("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -97,9 +98,9 @@ def lib():
 
 
 def make_config(n_layers, n_experts, top_k, hidden, inter, n_shared, cache_slots, max_tokens,
-                lookahead=1, trace_capacity=0, fill_threads=0, flags=0) -> MoeConfig:
+                lookahead=1, trace_capacity=0, fill_threads=0, flags=0, pinned_mb=0) -> MoeConfig:
     return MoeConfig(n_layers, n_experts, top_k, hidden, inter, n_shared, cache_slots, max_tokens,
-                     lookahead, trace_capacity, fill_threads, flags)
+                     lookahead, trace_capacity, fill_threads, flags, pinned_mb)
 
 
 def query_sizes(cfg: MoeConfig):

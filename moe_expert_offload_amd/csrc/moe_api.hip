@@ -29,6 +29,7 @@
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+#include "stager.h"
 
 using namespace moe;
 
@@ -42,8 +43,14 @@ struct moe_ctx {
     int device = 0;
     int nE = 0;                 // k + n_shared
     hipStream_t cs = nullptr, ps = nullptr;
-    uint8_t* pool = nullptr;    // pinned host, [L*E][blob]
-    size_t pool_bytes = 0;
+    uint8_t* pool = nullptr;    // pinned host, blobs [0, n_pin) of [L*E][blob]
+    size_t pool_bytes = 0;      // whole pool
+    size_t n_pin = 0;           // blobs in pinned memory
+    uint8_t* pool_pg = nullptr; // pageable host, blobs [n_pin, L*E)
+    BounceRing bounce;          // pinned bounce ring for the pageable part
+    const uint8_t* blob_src(size_t i) const {
+        return i < n_pin ? pool + i * lay.blob_bytes : pool_pg + (i - n_pin) * lay.blob_bytes;
+    }
     uint8_t* arena = nullptr;   // caller device memory, [C][blob]
     uint8_t* shared_dev = nullptr;
     uint16_t* router_dev = nullptr;
@@ -70,7 +77,7 @@ struct moe_ctx {
     float tok0_w[2][16] = {};
     bool tok0_valid[2] = {false, false};
     // host counters
-    uint64_t h2d_bytes = 0, h2d_copies = 0;
+    uint64_t h2d_bytes = 0, h2d_copies = 0, h2d_bounced = 0;
     uint64_t ffn_launches = 0;
     double k3_ms = 0, k4_ms = 0;
     std::vector<ProfSlot> prof_used, prof_free;
@@ -119,7 +126,8 @@ moe_status check_cfg(const moe_config* c) {
         c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
         c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 1 ||
-        c->cache_slots > 16384 || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0)
+        c->cache_slots > 16384 || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0 ||
+        c->pinned_mb < 0)
         return MOE_EINVAL;
     // the down kernel stages every selected expert's intermediate vector in LDS
     if ((size_t)(c->top_k + c->n_shared) * (c->inter / 32) * 80 > 60 * 1024) return MOE_EINVAL;
@@ -211,7 +219,9 @@ void free_all(moe_ctx* c) {
     for (auto& p : c->prof_used) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto& p : c->prof_free) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
+    c->bounce.shutdown();
     if (c->pool) (void)hipHostFree(c->pool);
+    free(c->pool_pg);
     if (c->ml_mem) (void)hipHostFree(c->ml_mem);
     if (c->shared_dev) (void)hipFree(c->shared_dev);
     if (c->router_dev) (void)hipFree(c->router_dev);
@@ -290,9 +300,14 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     const size_t blob = c->lay.blob_bytes;
     for (int i = 0; i < nm; ++i) {
         const MissEntry m = ml->e[i];
-        const uint8_t* src = c->pool + ((size_t)layer * c->cfg.n_experts + m.expert) * blob;
+        const size_t idx = (size_t)layer * c->cfg.n_experts + m.expert;
         uint8_t* dst = c->arena + (size_t)m.slot * blob;
-        HIPCHK(c, hipMemcpyAsync(dst, src, blob, hipMemcpyHostToDevice, c->ps));
+        if (idx < c->n_pin) {
+            HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(idx), blob, hipMemcpyHostToDevice, c->ps));
+        } else {
+            HIPCHK(c, c->bounce.copy(dst, c->blob_src(idx), blob));
+            ++c->h2d_bounced;
+        }
     }
     if (nm > 0) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
     c->h2d_bytes += (uint64_t)nm * blob;
@@ -531,11 +546,36 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     if (hipMemcpy(c->router_dev, router_w_bf16, rbytes, hipMemcpyHostToDevice) != hipSuccess) return bail(MOE_EHIP);
 
     // pinned pool, filled in parallel
+    // The pool: as many blobs as the platform lets us pin (capped by pinned_mb), the rest in
+    // pageable memory behind a pinned bounce ring.  A failed pinning request is retried 1/8
+    // smaller.
     where = "pinned pool allocation";
     c->pool_bytes = n_sl * L.blob_bytes;
-    if (hipHostMalloc((void**)&c->pool, c->pool_bytes, hipHostMallocDefault) != hipSuccess) {
+    size_t n_pin = n_sl;
+    if (cfg->pinned_mb > 0) n_pin = std::min(n_sl, ((size_t)cfg->pinned_mb << 20) / L.blob_bytes);
+    for (;;) {
+        if (n_pin == 0) break;
+        if (hipHostMalloc((void**)&c->pool, n_pin * L.blob_bytes, hipHostMallocDefault) == hipSuccess) {
+            if (n_pin == n_sl) break;
+            const hipError_t e = c->bounce.init(L.blob_bytes, 8, std::min(4u, std::max(1u, std::thread::hardware_concurrency())), c->ps);
+            if (e == hipSuccess) break;
+            (void)hipHostFree(c->pool);
+        }
+        (void)hipGetLastError();
         c->pool = nullptr;
-        return bail(MOE_ENOMEM);
+        n_pin = n_pin * 7 / 8;
+    }
+    c->n_pin = n_pin;
+    if (n_pin < n_sl) {
+        if (!c->bounce.ready()) {
+            where = "bounce ring allocation";
+            if (c->bounce.init(L.blob_bytes, 8, std::min(4u, std::max(1u, std::thread::hardware_concurrency())), c->ps) != hipSuccess)
+                return bail(MOE_ENOMEM);
+        }
+        where = "pageable pool allocation";
+        const size_t pg = (n_sl - n_pin) * L.blob_bytes;
+        c->pool_pg = (uint8_t*)aligned_alloc(4096, (pg + 4095) / 4096 * 4096);
+        if (!c->pool_pg) return bail(MOE_ENOMEM);
     }
     int nth = cfg->fill_threads > 0 ? cfg->fill_threads : (int)std::thread::hardware_concurrency();
     nth = std::max(1, std::min<int>(nth, (int)std::min<size_t>(n_sl, 64)));
@@ -546,7 +586,7 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
             size_t i = next.fetch_add(1);
             if (i >= n_sl) break;
             fill(user, (int32_t)(i / E), (int32_t)(i % E), tmp.data());
-            repack(L, tmp.data(), c->pool + i * L.blob_bytes);
+            repack(L, tmp.data(), const_cast<uint8_t*>(c->blob_src(i)));
         }
     };
     std::vector<std::thread> th;
@@ -687,6 +727,8 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         out->trace_records = take;
         out->trace_dropped = dropped;
         out->ffn_launches = c->ffn_launches;
+        out->h2d_bounced = c->h2d_bounced;
+        out->pool_pinned_bytes = (uint64_t)(c->n_pin * c->lay.blob_bytes);
         out->k3_ms = c->k3_ms;
         out->k4_ms = c->k4_ms;
     }
@@ -700,8 +742,9 @@ moe_status moe_measure_h2d(moe_ctx* c, size_t bytes, int32_t n_copies, double* g
     if (!c || !gbps || bytes == 0 || n_copies < 1) return MOE_EINVAL;
     if (c->failed) return MOE_ESTATE;
     const size_t blob = c->lay.blob_bytes;
-    const size_t n_blobs = c->pool_bytes / blob;
-    if (bytes > c->pool_bytes) return set_err(c, MOE_EINVAL, "copy larger than the pool");
+    // the pinned part of the pool only: the copy path of a pinned miss
+    const size_t n_blobs = c->n_pin;
+    if (bytes > n_blobs * blob) return set_err(c, MOE_EINVAL, "copy larger than the pinned part of the pool");
     const size_t span = (bytes + blob - 1) / blob;  // blobs covered by one copy
     uint8_t* scratch = nullptr;
     HIPCHK(c, hipMalloc(&scratch, 2 * bytes));

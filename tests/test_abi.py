@@ -49,6 +49,7 @@ def test_query_sizes_and_blob_size():
     (dict(hidden=100), -1), (dict(inter=48), -1), (dict(top_k=17), -1), (dict(top_k=20, n_experts=16), -1),
     (dict(n_experts=2000), -1), (dict(n_shared=2), -1), (dict(max_tokens=0), -1),
     (dict(cache_slots=3), -4), (dict(max_tokens=4, cache_slots=15), -4), (dict(cache_slots=20000), -1),
+    (dict(pinned_mb=-1), -1),
 ])
 def test_config_rejected(kw, status):
     import moe_expert_offload_amd as M
@@ -69,3 +70,14 @@ def test_null_context_calls_fail_cleanly():
                            ctypes.byref(out)) == M.MOE_EINVAL
     assert out.value is None
     L.moe_destroy(None)
+
+
+def test_grouped_workspace_grows_with_max_tokens():
+    """Batches of tokens need the grouped plan and the per-row expert outputs in the workspace."""
+    import moe_expert_offload_amd as M
+    _, _, w1 = M.query_sizes(_cfg(cache_slots=64))
+    _, _, w16 = M.query_sizes(_cfg(max_tokens=16, cache_slots=64))
+    _, _, w100 = M.query_sizes(_cfg(max_tokens=100, cache_slots=64))
+    rows16 = 16 * 2
+    assert w16 - w1 >= rows16 * 256 * 4   # fp32 expert outputs, one row per (token, expert)
+    assert w100 > w16

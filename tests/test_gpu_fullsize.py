@@ -29,3 +29,36 @@ def test_gptoss_shaped_sampled():
         print("t", t, "l", l, "rel-L2", rel)
         assert ok, (t, l, rel, mx)
     m.close()
+
+
+def test_qwen38_shaped_prefill_and_b16_decode_sampled():
+    """The 48 x 512-expert, top-10 + shared workload at full size (92.4 GB pool, 6144 slots): the
+    2048-token prefill chunk (grouped MFMA path, every layer's experts missing on a cold cache),
+    then 8 lock-step decode steps of 16 requests.  ids, weights and the whole trace are checked
+    for every step; outputs at sampled (step, layer, token) points: prefill tokens on both
+    sides of 64-row chunk boundaries and the last token, decode tokens 0, 7 and 15."""
+    import gc
+    from gpu_helpers import run_steps
+    wl = synth.WORKLOADS["qwen38_flash_next_shaped"]
+    T = 8
+    X = synth.decode_inputs(wl)[:T]
+    steps = [synth.prefill_inputs(wl)] + [X[t] for t in range(T)]
+    m, W = make_moe(wl)
+    ids, w, y = run_steps(m, wl, steps)
+    _, recs = m.stats(trace_cap=1 << 20)
+    m.close()
+    del m
+    gc.collect()
+    ref = oracle.run_trace(wl, W, steps)
+    for t in range(len(steps)):
+        np.testing.assert_array_equal(ids[t], ref["ids"][t])
+        assert np.max(np.abs(w[t] - ref["w"][t])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    L = wl.n_layers
+    points = [(0, 0, 0), (0, L - 1, 63), (0, 7, 64), (0, 30, 1000), (0, L - 1, 2047),
+              (1, 0, 0), (1, L - 1, 15), (T, 20, 7), (T, L - 1, 0)]
+    for (t, l, b) in points:
+        r = oracle.moe_output(wl, l, steps[t][b], ref["ids"][t][l, b], ref["w"][t][l, b])
+        rel, mx, ok = close_enough(y[t][l, b], r)
+        print("t", t, "l", l, "b", b, "rel-L2", rel)
+        assert ok, (t, l, b, rel, mx)

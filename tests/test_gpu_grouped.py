@@ -148,3 +148,16 @@ def test_grouped_expert_forward_rejects_bad_slots_with_nan():
     yf = y.view(torch.bfloat16).float().cpu().numpy()
     assert np.isnan(yf).all()
     m.close()
+
+
+def test_grouped_prefill_with_pageable_pool_part():
+    """A prefill chunk whose misses mostly come from the pageable part of the pool (pinned part
+    capped at 2 MiB), then decode steps; same bar."""
+    wl = GROUPED[1]
+    steps = _steps(wl, wl.prefill_tokens, wl.n_requests, wl.decode_tokens)
+    m, _ = make_moe(wl, max_tokens=wl.prefill_tokens, pinned_mb=2)
+    ids, w, y = run_steps(m, wl, steps)
+    cnt, recs = m.stats(trace_cap=1 << 20)
+    assert cnt["h2d_bounced"] > 0
+    _check(wl, steps, ids, w, y, m, recs)
+    m.close()

@@ -185,3 +185,19 @@ def test_expert_forward_with_resolved_slots_matches_stack():
         from gpu_helpers import bf16_to_f32
         np.testing.assert_array_equal(bf16_to_f32(yo)[0].view(np.uint32), y[t, l, 0].view(np.uint32))
     m.close()
+
+
+def test_pageable_pool_part_through_bounce_ring():
+    """pinned_mb caps the pinned part of the pool at 1 MiB (5 of 32 toy blobs); every other miss
+    is copied through the pinned bounce ring.  Same bar as the fully pinned pool, at a cache
+    size that forces evictions every step."""
+    wl = dataclasses.replace(synth.WORKLOADS["toy"], cache_slots=4)
+    X = synth.decode_inputs(wl)[:24]
+    m, _ = make_moe(wl, pinned_mb=1)
+    ids, w, y = run_stack(m, wl, X)
+    cnt, recs = m.stats(trace_cap=1 << 16)
+    assert cnt["pool_pinned_bytes"] == (1 << 20) // wl.blob_bytes * wl.blob_bytes
+    assert cnt["h2d_bounced"] > 0 and cnt["h2d_bounced"] < cnt["h2d_copies"]
+    points = [(t, l, 0) for t in range(24) for l in range(wl.n_layers)]
+    _check_run(wl, X, ids, w, y, recs, m, points)
+    m.close()
