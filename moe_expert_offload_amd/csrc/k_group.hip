@@ -37,7 +37,7 @@
 // bf16 x bf16 products are exact in the FP32 accumulator.  Both matrices are
 // read in the same repacked blob layout as the single-token kernels, each
 // wave read a contiguous 1 KB (gate/up) or eight whole 128-byte lines (down).
-// Token activations are staged in LDS per k-iteration (double-buffered), one
+// Token activations are staged in LDS per k-iteration (three buffers), one
 // copy shared by the workgroup's four waves.
 //
 // blockIdx -> work mapping is XCD-aware: consecutive workgroups go to
@@ -253,202 +253,309 @@ __device__ __forceinline__ bool get_unit(const GemmArgs& a, int nt_per_chunk, Un
 
 // Activation staging: the chunk's GM token rows x 4 blocks (64 bytes each) per
 // k-iteration, NTT 16-byte pieces per thread.  Piece v = tid + 256*i is
-// (token t = v/16, lane group q = (v/4)%4, step s = v%4).  LDS: [token][q] in
+// (token t = v/16, lane group q = (v/4)%4, step s = v%4): q and s are the same
+// for all of a thread's pieces and t grows by 16 per piece.  LDS: [token][q] in
 // 80-byte cells (5 x 16 B), so the 16 tokens a wave reads at once are spread
 // over the banks.
 template <int NTT>
 struct Stager {
-    const uint16_t* src[NTT];   // row base of the piece's token, or a dummy in-bounds row
-    bool ok[NTT];
-    int dst[NTT];               // LDS cell index (uint4 units)
-    int q[NTT], s[NTT];
+    const uint16_t* src[NTT];   // row base of the piece's token (row 0 for an empty row)
+    uint32_t ok;                // bit i: piece i holds a row of the chunk
+    int q, s, dst0;             // lane group, step, LDS cell of piece 0 (piece i: + 320 i)
 };
 
 template <int NTT>
 __device__ __forceinline__ void stager_init(Stager<NTT>& st, const int* s_row, const uint16_t* src,
                                             int row_len, const GemmArgs& a, bool rows_are_tokens) {
+    const int v = threadIdx.x;
+    st.q = (v >> 2) & 3;
+    st.s = v & 3;
+    st.dst0 = ((v >> 4) * 4 + st.q) * 5 + st.s;
+    st.ok = 0u;
 #pragma unroll
     for (int i = 0; i < NTT; ++i) {
-        const int v = threadIdx.x + K5_THREADS * i;
-        const int t = v >> 4;
-        const int row = s_row[t];
-        st.ok[i] = row >= 0;
+        const int row = s_row[(v >> 4) + 16 * i];
+        st.ok |= row >= 0 ? (1u << i) : 0u;
         const int rr = row >= 0 ? (rows_are_tokens ? row_token(a, row) : row) : 0;
-        st.src[i] = src + (size_t)rr * row_len;
-        st.q[i] = (v >> 2) & 3;
-        st.s[i] = v & 3;
-        st.dst[i] = (t * 4 + st.q[i]) * 5 + st.s[i];
+        st.src[i] = src + (size_t)rr * row_len + st.s * 8;
     }
 }
 
+// Main loops: the loads of k-iteration it (activation pieces and this lane's
+// weight chunk) go into a fragment issued DEPTH (2 or 3) iterations ahead;
+// DEPTH fragments and LDS buffers are used in turn (the loop is unrolled by
+// DEPTH so each has fixed registers).  Iterations past the end read clamped,
+// in-bounds addresses and are masked.  Loads complete in order, so a step
+// waits only for its own fragment while the later ones stay in flight.  Token
+// tiles past the chunk's rows are skipped (a wave-uniform branch).
+
 // ---------------------------------------------------------- k5_gate_up --
-template <int NTT>
-__global__ __launch_bounds__(K5_THREADS) void k5_gate_up(GemmArgs a) {
+// RT 16-row tiles of the intermediate dimension per wave (tiles (nt*4 + w)*RT
+// + j), so one LDS read of an activation operand feeds 2*RT MFMAs.
+template <int NTT, int RT>
+struct GuFrag {
+    uint4 xv[NTT];
+    uint4 gc[RT], uc[RT];
+    uint32_t sc[RT];
+};
+
+template <int NTT, int RT, int DEPTH>
+__global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
     constexpr int GM = 16 * NTT;
-    __shared__ uint4 xs[2][GM * 4 * 5];
+    __shared__ uint4 xs[DEPTH][GM * 4 * 5];
     __shared__ int s_row[GM];
-    const int nt_per_chunk = (a.I / 16 + 3) / 4;
+    const int n_tiles = a.I >> 4;
+    const int nt_per_chunk = (n_tiles + 4 * RT - 1) / (4 * RT);
     Unit u;
     if (!get_unit(a, nt_per_chunk, u)) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid < GM) s_row[tid] = tid < u.nrow ? a.p.perm[u.base + tid] : -1;
-    const int ntt = (u.nrow + 15) >> 4;
+    const int ntt = (u.nrow + 15) >> 4;   // token tiles holding rows of the chunk
     const int NB = a.NB;
-    const int tile = u.nt * 4 + w;            // 16 intermediate rows
-    const bool tile_ok = tile < (a.I >> 4);
-    const uint8_t* tb = group_blob(a, u.g_slot) + (size_t)(tile_ok ? tile : 0) * 16 * NB * 34;
-    const uint8_t* tub = tb + (size_t)16 * NB * 16;
-    const uint8_t* tsc = tb + (size_t)16 * NB * 32;
+    const int tile0 = (u.nt * 4 + w) * RT;
+    const uint8_t* blob = group_blob(a, u.g_slot);
+    const uint8_t* tb[RT];
+    bool tok[RT];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+        tok[j] = tile0 + j < n_tiles;
+        tb[j] = blob + (size_t)(tok[j] ? tile0 + j : 0) * 16 * NB * 34;
+    }
     const int r = lane & 15, q = lane >> 4;
     __syncthreads();
     Stager<NTT> st;
     stager_init<NTT>(st, s_row, a.x, a.H, a, true);
 
-    f32x4_t accg[NTT], accu[NTT];
+    f32x4_t accg[RT][NTT], accu[RT][NTT];
 #pragma unroll
-    for (int m = 0; m < NTT; ++m) {
-        accg[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        accu[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int m = 0; m < NTT; ++m) {
+            accg[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accu[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
     const int nit = (NB + 3) >> 2;
-    // loads of iteration it: activation pieces and this lane's weight chunk;
-    // out-of-range positions read an in-bounds address and are zeroed later
-    uint4 xv[NTT];
-    uint4 gc, uc;
-    uint32_t sc;
-    auto issue = [&](int it) {
-#pragma unroll
-        for (int i = 0; i < NTT; ++i) {
-            const int p = 4 * it + st.q[i];
+    auto issue = [&](int it, GuFrag<NTT, RT>& f) {
+        {
+            const int p = 4 * it + st.q;
             const int blk = gu_block(p < NB ? p : NB - 1, NB);
-            xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + blk * 32 + st.s[i] * 8);
+#pragma unroll
+            for (int i = 0; i < NTT; ++i) f.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + blk * 32);
         }
         const int p = 4 * it + q;
         const size_t c = (size_t)(p < NB ? p : NB - 1) * 16 + r;
-        gc = ldg16(tb + c * 16);
-        uc = ldg16(tub + c * 16);
-        sc = *reinterpret_cast<const uint16_t*>(tsc + c * 2);
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            f.gc[j] = ldg16(tb[j] + c * 16);
+            f.uc[j] = ldg16(tb[j] + (size_t)16 * NB * 16 + c * 16);
+            f.sc[j] = *reinterpret_cast<const uint16_t*>(tb[j] + (size_t)16 * NB * 32 + c * 2);
+        }
     };
-    issue(0);
-    for (int it = 0; it < nit; ++it) {
-        uint4* xb = xs[it & 1];
+    auto step = [&](int it, const GuFrag<NTT, RT>& f, uint4* xb) {
+        const bool pin = (4 * it + st.q) < NB;
 #pragma unroll
         for (int i = 0; i < NTT; ++i) {
-            const bool ok = st.ok[i] && (4 * it + st.q[i]) < NB;
-            xb[st.dst[i]] = ok ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+            const bool ok = pin && ((st.ok >> i) & 1u);
+            xb[st.dst0 + 320 * i] = ok ? f.xv[i] : make_uint4(0u, 0u, 0u, 0u);
         }
-        const bool pv = tile_ok && (4 * it + q) < NB;
-        const float sg = pv ? e8m0(sc) : 0.0f, su = pv ? e8m0(sc >> 8) : 0.0f;
-        const uint4 gcw = gc, ucw = uc;
+        const bool pv = (4 * it + q) < NB;
+        float sg[RT], su[RT];
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            sg[j] = pv && tok[j] ? e8m0(f.sc[j]) : 0.0f;
+            su[j] = pv && tok[j] ? e8m0(f.sc[j] >> 8) : 0.0f;
+        }
         __syncthreads();
-        if (it + 1 < nit) issue(it + 1);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            const bf16x8_t wg = dq8(word(gcw, s4), sg);
-            const bf16x8_t wu = dq8(word(ucw, s4), su);
+            bf16x8_t wg[RT], wu[RT];
+#pragma unroll
+            for (int j = 0; j < RT; ++j) {
+                wg[j] = dq8(word(f.gc[j], s4), sg[j]);
+                wu[j] = dq8(word(f.uc[j], s4), su[j]);
+            }
 #pragma unroll
             for (int m = 0; m < NTT; ++m) {
-                if (m < ntt) {
-                    const bf16x8_t xo = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
-                    accg[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg, xo, accg[m], 0, 0, 0);
-                    accu[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu, xo, accu[m], 0, 0, 0);
+                if (NTT > 1 && m >= ntt) continue;
+                const bf16x8_t xo = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
+#pragma unroll
+                for (int j = 0; j < RT; ++j) {
+                    accg[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[j], xo, accg[j][m], 0, 0, 0);
+                    accu[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu[j], xo, accu[j][m], 0, 0, 0);
                 }
             }
         }
+    };
+    if constexpr (DEPTH == 3) {
+        GuFrag<NTT, RT> fa, fb, fc;
+        issue(0, fa);
+        issue(1, fb);
+        issue(2, fc);
+        for (int it = 0; it < nit; it += 3) {
+            step(it, fa, xs[0]);
+            issue(it + 3, fa);
+            step(it + 1, fb, xs[1]);
+            issue(it + 4, fb);
+            step(it + 2, fc, xs[2]);
+            issue(it + 5, fc);
+        }
+    } else {
+        GuFrag<NTT, RT> fa, fb;
+        issue(0, fa);
+        issue(1, fb);
+        for (int it = 0; it < nit; it += 2) {
+            step(it, fa, xs[0]);
+            issue(it + 2, fa);
+            step(it + 1, fb, xs[1]);
+            issue(it + 3, fb);
+        }
     }
-    if (!tile_ok) return;
-    // lane holds intermediate rows tile*16 + 4q + 0..3 of token r of each tile
+    // lane holds intermediate rows (tile0+j)*16 + 4q + 0..3 of token r of each token tile
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
-        if (m < ntt) {
+        {
             const int row = s_row[m * 16 + r];
             if (row >= 0) {
-                uint32_t lo = (uint32_t)f32_to_bf16(swiglu(accg[m][0], accu[m][0])) |
-                              ((uint32_t)f32_to_bf16(swiglu(accg[m][1], accu[m][1])) << 16);
-                uint32_t hi = (uint32_t)f32_to_bf16(swiglu(accg[m][2], accu[m][2])) |
-                              ((uint32_t)f32_to_bf16(swiglu(accg[m][3], accu[m][3])) << 16);
-                *reinterpret_cast<uint2*>(a.a + (size_t)row * a.I + tile * 16 + 4 * q) = make_uint2(lo, hi);
+#pragma unroll
+                for (int j = 0; j < RT; ++j) {
+                    if (!tok[j]) continue;
+                    const f32x4_t g = accg[j][m], v = accu[j][m];
+                    const uint32_t lo = (uint32_t)f32_to_bf16(swiglu(g[0], v[0])) |
+                                        ((uint32_t)f32_to_bf16(swiglu(g[1], v[1])) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(swiglu(g[2], v[2])) |
+                                        ((uint32_t)f32_to_bf16(swiglu(g[3], v[3])) << 16);
+                    *reinterpret_cast<uint2*>(a.a + (size_t)row * a.I + (tile0 + j) * 16 + 4 * q) =
+                        make_uint2(lo, hi);
+                }
             }
         }
     }
 }
 
 // ------------------------------------------------------------- k5_down --
-template <int NTT>
-__global__ __launch_bounds__(K5_THREADS) void k5_down(GemmArgs a) {
+// RT 16-row tiles of the output per wave (tiles (nt*4 + w)*RT + j); a 16-row
+// tile is two 8-row tiles of the D section.
+template <int NTT, int RT>
+struct DnFrag {
+    uint4 xv[NTT];
+    uint4 dc[RT];
+    uint32_t sc[RT];
+};
+
+template <int NTT, int RT, int DEPTH>
+__global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
     constexpr int GM = 16 * NTT;
-    __shared__ uint4 xs[2][GM * 4 * 5];
+    __shared__ uint4 xs[DEPTH][GM * 4 * 5];
     __shared__ int s_row[GM];
-    const int nt_per_chunk = (a.H / 16 + 3) / 4;
+    const int n_tiles = a.H >> 4;
+    const int nt_per_chunk = (n_tiles + 4 * RT - 1) / (4 * RT);
     Unit u;
     if (!get_unit(a, nt_per_chunk, u)) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid < GM) s_row[tid] = tid < u.nrow ? a.p.perm[u.base + tid] : -1;
-    const int ntt = (u.nrow + 15) >> 4;
+    const int ntt = (u.nrow + 15) >> 4;   // token tiles holding rows of the chunk
     const int NBI = a.NBI;
-    const int tile = u.nt * 4 + w;            // 16 output rows = two 8-row tiles of the D section
-    const bool tile_ok = tile < (a.H >> 4);
+    const int tile0 = (u.nt * 4 + w) * RT;
     const int r = lane & 15, q = lane >> 4;
-    const int t8 = 2 * (tile_ok ? tile : 0) + (r >> 3), rr = r & 7;
     const uint8_t* blob = group_blob(a, u.g_slot);
-    const uint8_t* dcod = blob + a.d_codes_off + ((size_t)t8 * NBI * 8 + rr) * 16;
-    const uint8_t* dsc = blob + a.d_scales_off + (size_t)t8 * NBI * 8 + rr;
+    const uint8_t* dcod[RT];
+    const uint8_t* dsc[RT];
+    bool tok[RT];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+        tok[j] = tile0 + j < n_tiles;
+        const int t8 = 2 * (tok[j] ? tile0 + j : 0) + (r >> 3), rr = r & 7;
+        dcod[j] = blob + a.d_codes_off + ((size_t)t8 * NBI * 8 + rr) * 16;
+        dsc[j] = blob + a.d_scales_off + (size_t)t8 * NBI * 8 + rr;
+    }
     __syncthreads();
     Stager<NTT> st;
     stager_init<NTT>(st, s_row, a.a, a.I, a, false);
 
-    f32x4_t acc[NTT];
+    f32x4_t acc[RT][NTT];
 #pragma unroll
-    for (int m = 0; m < NTT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int m = 0; m < NTT; ++m) acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int nit = (NBI + 3) >> 2;
-    uint4 xv[NTT];
-    uint4 dc;
-    uint32_t sc;
-    auto issue = [&](int it) {
-#pragma unroll
-        for (int i = 0; i < NTT; ++i) {
-            const int p = 4 * it + st.q[i];
+    auto issue = [&](int it, DnFrag<NTT, RT>& f) {
+        {
+            const int p = 4 * it + st.q;
             const int ib = p < NBI ? p : NBI - 1;
-            xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + ib * 32 + st.s[i] * 8);
+#pragma unroll
+            for (int i = 0; i < NTT; ++i) f.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + ib * 32);
         }
         const int p = 4 * it + q;
         const int ib = p < NBI ? p : NBI - 1;
-        dc = ldg16(dcod + (size_t)ib * 8 * 16);
-        sc = dsc[(size_t)ib * 8];
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            f.dc[j] = ldg16(dcod[j] + (size_t)ib * 8 * 16);
+            f.sc[j] = dsc[j][(size_t)ib * 8];
+        }
     };
-    issue(0);
-    for (int it = 0; it < nit; ++it) {
-        uint4* xb = xs[it & 1];
+    auto step = [&](int it, const DnFrag<NTT, RT>& f, uint4* xb) {
+        const bool pin = (4 * it + st.q) < NBI;
 #pragma unroll
         for (int i = 0; i < NTT; ++i) {
-            const bool ok = st.ok[i] && (4 * it + st.q[i]) < NBI;
-            xb[st.dst[i]] = ok ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+            const bool ok = pin && ((st.ok >> i) & 1u);
+            xb[st.dst0 + 320 * i] = ok ? f.xv[i] : make_uint4(0u, 0u, 0u, 0u);
         }
-        const bool pv = tile_ok && (4 * it + q) < NBI;
-        const float sd = pv ? e8m0(sc) : 0.0f;
-        const uint4 dcw = dc;
+        const bool pv = (4 * it + q) < NBI;
+        float sd[RT];
+#pragma unroll
+        for (int j = 0; j < RT; ++j) sd[j] = pv && tok[j] ? e8m0(f.sc[j]) : 0.0f;
         __syncthreads();
-        if (it + 1 < nit) issue(it + 1);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            const bf16x8_t wd = dq8(word(dcw, s4), sd);
+            bf16x8_t wd[RT];
+#pragma unroll
+            for (int j = 0; j < RT; ++j) wd[j] = dq8(word(f.dc[j], s4), sd[j]);
 #pragma unroll
             for (int m = 0; m < NTT; ++m) {
-                if (m < ntt) {
-                    const bf16x8_t ao = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd, ao, acc[m], 0, 0, 0);
-                }
+                if (NTT > 1 && m >= ntt) continue;
+                const bf16x8_t ao = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
+#pragma unroll
+                for (int j = 0; j < RT; ++j)
+                    acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd[j], ao, acc[j][m], 0, 0, 0);
             }
         }
+    };
+    if constexpr (DEPTH == 3) {
+        DnFrag<NTT, RT> fa, fb, fc;
+        issue(0, fa);
+        issue(1, fb);
+        issue(2, fc);
+        for (int it = 0; it < nit; it += 3) {
+            step(it, fa, xs[0]);
+            issue(it + 3, fa);
+            step(it + 1, fb, xs[1]);
+            issue(it + 4, fb);
+            step(it + 2, fc, xs[2]);
+            issue(it + 5, fc);
+        }
+    } else {
+        DnFrag<NTT, RT> fa, fb;
+        issue(0, fa);
+        issue(1, fb);
+        for (int it = 0; it < nit; it += 2) {
+            step(it, fa, xs[0]);
+            issue(it + 2, fa);
+            step(it + 1, fb, xs[1]);
+            issue(it + 3, fb);
+        }
     }
-    if (!tile_ok) return;
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
-        if (m < ntt) {
+        {
             const int row = s_row[m * 16 + r];
-            if (row >= 0)
-                *reinterpret_cast<float4*>(a.yp + (size_t)row * a.H + tile * 16 + 4 * q) =
-                    make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+            if (row >= 0) {
+#pragma unroll
+                for (int j = 0; j < RT; ++j) {
+                    if (!tok[j]) continue;
+                    *reinterpret_cast<float4*>(a.yp + (size_t)row * a.H + (tile0 + j) * 16 + 4 * q) =
+                        make_float4(acc[j][m][0], acc[j][m][1], acc[j][m][2], acc[j][m][3]);
+                }
+            }
         }
     }
 }
@@ -489,20 +596,26 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
 
 static int pad8(long v) { return (int)((v + 7) / 8 * 8); }
 
+// row tiles per wave: gate/up and down of prefill-sized chunks (64 rows) take
+// 2 and 4 tiles; single-token-sized chunks (16 rows) keep one for parallelism
+constexpr int RT_GU_BIG = 2, RT_D_BIG = 4;
+
 int launch_grouped_ffn(GroupArgs& g, GemmArgs& m, CombineArgs& c, void* stream, void* ev_mid) {
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(k2g_group, dim3(1), dim3(KG_THREADS), 0, st, g);
-    const int nt1 = (m.I / 16 + 3) / 4, nt2 = (m.H / 16 + 3) / 4;
+    const bool big = m.gm != 16;
+    const int rt1 = big ? RT_GU_BIG : 1, rt2 = big ? RT_D_BIG : 1;
+    const int nt1 = (m.I / 16 + 4 * rt1 - 1) / (4 * rt1), nt2 = (m.H / 16 + 4 * rt2 - 1) / (4 * rt2);
     const dim3 g1(pad8((long)m.p.max_chunks * nt1)), g2(pad8((long)m.p.max_chunks * nt2));
-    if (m.gm == 16)
-        hipLaunchKernelGGL(k5_gate_up<1>, g1, dim3(K5_THREADS), 0, st, m);
+    if (big)
+        hipLaunchKernelGGL((k5_gate_up<4, RT_GU_BIG, 2>), g1, dim3(K5_THREADS), 0, st, m);
     else
-        hipLaunchKernelGGL(k5_gate_up<4>, g1, dim3(K5_THREADS), 0, st, m);
+        hipLaunchKernelGGL((k5_gate_up<1, 1, 3>), g1, dim3(K5_THREADS), 0, st, m);
     if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
-    if (m.gm == 16)
-        hipLaunchKernelGGL(k5_down<1>, g2, dim3(K5_THREADS), 0, st, m);
+    if (big)
+        hipLaunchKernelGGL((k5_down<4, RT_D_BIG, 2>), g2, dim3(K5_THREADS), 0, st, m);
     else
-        hipLaunchKernelGGL(k5_down<4>, g2, dim3(K5_THREADS), 0, st, m);
+        hipLaunchKernelGGL((k5_down<1, 1, 3>), g2, dim3(K5_THREADS), 0, st, m);
     hipLaunchKernelGGL(k5_combine, dim3((c.H + 1023) / 1024, c.B), dim3(256), 0, st, c, m.p.hdr);
     return (int)hipGetLastError();
 }

@@ -314,9 +314,25 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     }
 }
 
+// top-k + softmax of many tokens, one wave per token, ahead of the resolve
+// kernel (whose single workgroup would otherwise take them 16 at a time)
+__global__ __launch_bounds__(256) void k2_topk(K2Args a) {
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b < a.B) wave_topk(a, b);
+}
+
+constexpr int K2_FUSED_TOPK_MAX = 16;  // up to this many tokens the resolve kernel routes them itself
+
 int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void* stream) {
-    hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, (hipStream_t)stream, a, order_in,
-                       order_out);
+    hipStream_t st = (hipStream_t)stream;
+    if (a.z && a.B > K2_FUSED_TOPK_MAX) {
+        hipLaunchKernelGGL(k2_topk, dim3((a.B + 3) / 4), dim3(256), 0, st, a);
+        K2Args r = a;
+        r.z = nullptr;  // resolve the ids just written
+        hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, st, r, order_in, order_out);
+    } else {
+        hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, st, a, order_in, order_out);
+    }
     return (int)hipGetLastError();
 }
 
