@@ -74,6 +74,13 @@ def lib():
         L.orc_cache_state.argtypes = [_P, _P, _P, _P]
         L.orc_cache_step.restype = ctypes.c_int
         L.orc_cache_step.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P, _P]
+        L.orc_static_new.restype = _P
+        L.orc_static_new.argtypes = [ctypes.c_int] * 4
+        L.orc_static_free.argtypes = [_P]
+        L.orc_static_counters.argtypes = [_P, _P]
+        L.orc_static_state.argtypes = [_P, _P, _P]
+        L.orc_static_step.restype = ctypes.c_int
+        L.orc_static_step.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P, _P]
         _lib = L
     return _lib
 
@@ -192,6 +199,42 @@ class Cache:
         return slot_of, key_of, stamp
 
 
+class StaticCache:
+    """Static per-layer split over C slots: keys [0, C - T) resident for good, T transient
+    slots in rotation for every other access (see oracle.c, static per-layer split)."""
+
+    def __init__(self, L: int, E: int, C: int, T: int):
+        self.L, self.E, self.C, self.T = L, E, C, T
+        self._h = lib().orc_static_new(L, E, C, T)
+        if not self._h:
+            raise ValueError("need 1 <= T <= C")
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib().orc_static_free(self._h)
+            self._h = None
+
+    def step(self, step: int, layer: int, ids):
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+        slots = np.empty(ids.size, dtype=np.int32)
+        rec = np.empty(max(1, min(ids.size, self.E)), dtype=TRACE_DTYPE)
+        n = lib().orc_static_step(self._h, step, layer, _ptr(ids), ids.size, _ptr(slots), _ptr(rec))
+        if n < 0:
+            raise ValueError("step misses more distinct experts than there are transient slots")
+        return slots, rec[:n].copy()
+
+    def counters(self):
+        c = np.empty(3, dtype=np.uint64)
+        lib().orc_static_counters(self._h, _ptr(c))
+        return {"hits": int(c[0]), "misses": int(c[1]), "evictions": int(c[2])}
+
+    def state(self):
+        slot_of = np.empty(self.L * self.E, dtype=np.int32)
+        key_of = np.empty(self.C, dtype=np.int32)
+        lib().orc_static_state(self._h, _ptr(slot_of), _ptr(key_of))
+        return slot_of, key_of
+
+
 # ------------------------------------------------------------ whole runs --
 def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=None):
     """Routing and cache trace of a decode run.
@@ -223,13 +266,14 @@ def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=N
             "counters": cache.counters(), "cache": cache}
 
 
-def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X):
+def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X, static_transient: int = 0):
     """Routing and cache trace of a run whose steps have their own token counts.
 
     steps_X: list of [B_t][H] bf16-bit arrays; step t feeds X_t to every layer (a prefill
     chunk is one step whose B_t is the chunk length).  Steps run in order, layers 0..L-1
     inside a step.  Returns dict with per-step lists ids[t] [L][B_t][k], w[t], slots[t],
-    the trace (structured array), counters and the cache.
+    the trace (structured array), counters and the cache.  static_transient > 0 runs the static
+    per-layer split with that many transient slots instead of the LRU cache.
     """
     L, k = wl.n_layers, wl.top_k
     Xc = np.concatenate([np.asarray(x, dtype=np.uint16).reshape(-1, wl.hidden) for x in steps_X])
@@ -243,7 +287,8 @@ def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X):
         shapes.append(B)
         base += B
     ids_all, w_all = route_batch(W_all, Xc, k, np.concatenate(layers), np.concatenate(toks))
-    cache = Cache(L, wl.n_experts, wl.cache_slots)
+    cache = (StaticCache(L, wl.n_experts, wl.cache_slots, static_transient) if static_transient
+             else Cache(L, wl.n_experts, wl.cache_slots))
     out = {"ids": [], "w": [], "slots": []}
     recs = []
     pos = 0

@@ -254,3 +254,88 @@ int orc_cache_step(orc_cache* c, int step, int layer, const int32_t* ids, int n,
     free(req);
     return nrec;
 }
+
+/* ------------------------------------------------- static per-layer split -- */
+
+/* The comparator the ai-hardware-zukan.com FreeToken vs Ollama page contrasts
+ * with the router-following cache (section on how misses are made up for: a
+ * fixed split of experts between GPU and host misses far more often).  Reading:
+ * of the C GPU slots, R = C - T hold the first R (layer, expert) keys in pool
+ * order for good (every layer before R / E whole, then part of the next), and
+ * T transient slots take every other requested expert, one per access, in
+ * rotation: a transient slot is a streaming buffer, not a cache -- only the
+ * resident keys map to slots, a transient slot remembers its last occupant
+ * (the evicted key of its next use), and every access to a non-resident key
+ * streams it again.  Within a step the unique requested experts are taken
+ * hits first, then misses, each ascending by expert id, as in the LRU cache. */
+typedef struct {
+    int L, E, C, T, R;
+    int64_t tclock;     /* transient slots used so far */
+    int32_t* slot_of;   /* [L*E]: the slot of a resident key, else -1 */
+    int32_t* key_of;    /* [C]: resident key, or a transient slot's last occupant */
+    uint64_t hits, misses, evictions;
+} orc_static;
+
+orc_static* orc_static_new(int L, int E, int C, int T) {
+    if (T < 1 || T > C) return NULL;
+    orc_static* c = (orc_static*)calloc(1, sizeof(orc_static));
+    c->L = L; c->E = E; c->C = C; c->T = T; c->R = C - T;
+    c->slot_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)L * E);
+    c->key_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)C);
+    for (int k = 0; k < L * E; ++k) c->slot_of[k] = k < c->R ? k : -1;
+    for (int s = 0; s < C; ++s) c->key_of[s] = s < c->R && s < L * E ? s : -1;
+    return c;
+}
+
+void orc_static_free(orc_static* c) {
+    if (!c) return;
+    free(c->slot_of); free(c->key_of); free(c);
+}
+
+void orc_static_counters(const orc_static* c, uint64_t* out3) {
+    out3[0] = c->hits; out3[1] = c->misses; out3[2] = c->evictions;
+}
+
+void orc_static_state(const orc_static* c, int32_t* slot_of, int32_t* key_of) {
+    memcpy(slot_of, c->slot_of, sizeof(int32_t) * (size_t)c->L * c->E);
+    memcpy(key_of, c->key_of, sizeof(int32_t) * (size_t)c->C);
+}
+
+/* returns the number of trace records, or -1 when the step requests more
+ * distinct experts than there are transient slots */
+int orc_static_step(orc_static* c, int step, int layer, const int32_t* ids, int n,
+                    int32_t* slots_out, orc_trace_rec* trace) {
+    const int E = c->E;
+    char* req = (char*)calloc((size_t)E, 1);
+    for (int j = 0; j < n; ++j) req[ids[j]] = 1;
+    int nmiss = 0;
+    for (int e = 0; e < E; ++e) nmiss += req[e] && layer * E + e >= c->R;
+    if (nmiss > c->T) { free(req); return -1; }
+    int nrec = 0;
+    for (int e = 0; e < E; ++e) {           /* hits: resident keys, ascending */
+        const int key = layer * E + e;
+        if (!req[e] || key >= c->R) continue;
+        c->hits++;
+        orc_trace_rec r = {step, layer, e, key, 1, -1};
+        trace[nrec++] = r;
+    }
+    int32_t* step_slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    for (int e = 0; e < E; ++e) step_slot[e] = layer * E + e < c->R ? layer * E + e : -1;
+    for (int e = 0; e < E; ++e) {           /* misses, ascending: next transient slot */
+        const int key = layer * E + e;
+        if (!req[e] || key < c->R) continue;
+        const int32_t v = c->R + (int32_t)(c->tclock % c->T);
+        c->tclock++;
+        const int32_t old = c->key_of[v];
+        if (old >= 0) c->evictions++;
+        c->key_of[v] = key;
+        step_slot[e] = v;
+        c->misses++;
+        orc_trace_rec r = {step, layer, e, v, 0, old};
+        trace[nrec++] = r;
+    }
+    for (int j = 0; j < n; ++j) slots_out[j] = step_slot[ids[j]];
+    free(step_slot);
+    free(req);
+    return nrec;
+}
