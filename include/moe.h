@@ -62,6 +62,17 @@ typedef enum {
     MOE_ESTATE = -5,     /* context already failed */
 } moe_status;
 
+/* Cache policy (moe_config.policy).
+ * MOE_POLICY_LRU: one least-recently-used cache over all C slots and all layers, following the
+ *   router (ai-hardware-zukan.com FreeToken vs Ollama page, section on how misses are made up
+ *   for; gaming-st.com DeepSeek page: one global LRU expert cache).
+ * MOE_POLICY_STATIC: the static per-layer split the same page compares it with.  The first
+ *   R = C - T keys (layer * E + expert, pool order: whole layers, then part of one) stay in slots
+ *   0..R-1, filled at init; every access to another key is a miss streamed into the next of the
+ *   T = 2 * min(max_tokens * k, E) transient slots, in rotation (a streaming buffer, not a cache:
+ *   the same key requested again is streamed again). */
+enum { MOE_POLICY_LRU = 0, MOE_POLICY_STATIC = 1 };
+
 enum {
     MOE_FLAG_PROFILE = 1,  /* time every K3 and K4 launch with HIP events (read via moe_stats) */
     MOE_FLAG_PER_TOKEN_FFN = 2,  /* B > 1: run the per-token GEMV kernels instead of the grouped MFMA path */
@@ -84,6 +95,7 @@ typedef struct {
     int32_t pinned_mb;      /* at most this many MiB of the pool in pinned memory (0 = as much as the
                                platform grants); the rest is pageable and its misses go through a
                                ring of pinned bounce buffers */
+    int32_t policy;         /* MOE_POLICY_LRU (default) or MOE_POLICY_STATIC */
 } moe_config;
 
 /* Writes the logical blob of routed expert (layer, expert >= 0) or of shared

@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE = 0, -1, -2, -3, -4, -5
 MOE_FLAG_PROFILE = 1
 MOE_FLAG_PER_TOKEN_FFN = 2
+MOE_POLICY_LRU, MOE_POLICY_STATIC = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
            -5: "MOE_ESTATE"}
 
@@ -35,7 +36,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: 
 class MoeConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "n_experts", "top_k", "hidden", "inter", "n_shared", "cache_slots", "max_tokens",
-        "lookahead", "trace_capacity", "fill_threads", "flags", "pinned_mb")]
+        "lookahead", "trace_capacity", "fill_threads", "flags", "pinned_mb", "policy")]
 
 
 class MoeCounters(ctypes.Structure):
@@ -98,9 +99,9 @@ def lib():
 
 
 def make_config(n_layers, n_experts, top_k, hidden, inter, n_shared, cache_slots, max_tokens,
-                lookahead=1, trace_capacity=0, fill_threads=0, flags=0, pinned_mb=0) -> MoeConfig:
+                lookahead=1, trace_capacity=0, fill_threads=0, flags=0, pinned_mb=0, policy=0) -> MoeConfig:
     return MoeConfig(n_layers, n_experts, top_k, hidden, inter, n_shared, cache_slots, max_tokens,
-                     lookahead, trace_capacity, fill_threads, flags, pinned_mb)
+                     lookahead, trace_capacity, fill_threads, flags, pinned_mb, policy)
 
 
 def query_sizes(cfg: MoeConfig):

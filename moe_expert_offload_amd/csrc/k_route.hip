@@ -208,16 +208,49 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     // classify the requested experts (thread e <-> expert e; E <= 1024)
     const int e = tid;
     const bool req = e < E && s_req[e] != 0;
-    const int v = req ? a.c.slot_of[l * E + e] : -1;
+    const bool stat = a.policy != 0;
+    // static split: resident iff key < R (slot = key); LRU: the slot table
+    const int v = req ? (stat ? (l * E + e < a.R ? l * E + e : -1) : a.c.slot_of[l * E + e]) : -1;
     const bool hit = req && v >= 0;
     const bool miss = req && v < 0;
     int nh, nm;
     const int hr = block_rank(hit, s_wave, nh);
     const int mr = block_rank(miss, s_wave, nm);
     const int64_t clock0 = *a.c.clock;
-    if (hit) atomicOr(&s_hitbits[v >> 5], 1u << (v & 31));
+    if (hit && !stat) atomicOr(&s_hitbits[v >> 5], 1u << (v & 31));
     if (miss) s_miss_e[mr] = e;
     __syncthreads();
+
+    const int64_t trace_base = (int64_t)a.c.trace_head[0];
+    if (stat) {
+        // static split: hits keep their fixed slot; misses stream into the next
+        // transient slots in rotation, whose last occupant is the evicted key
+        if (hit) {
+            s_req[e] = v;
+            const int64_t ti = trace_base + hr;
+            if (ti < a.c.trace_cap) {
+                TraceRec t = {a.step, l, e, v, 1, -1};
+                a.c.trace[ti] = t;
+            }
+        }
+        if (tid < nm) {
+            const int me = s_miss_e[tid];
+            const int vv = a.R + (int)((clock0 + tid) % a.T);
+            const int old = a.c.key_of[vv];
+            if (old >= 0) atomicAdd(&s_evict, 1);
+            a.c.key_of[vv] = l * E + me;
+            s_req[me] = vv;
+            const int64_t ti = trace_base + nh + tid;
+            if (ti < a.c.trace_cap) {
+                TraceRec t = {a.step, l, me, vv, 0, old};
+                a.c.trace[ti] = t;
+            }
+            a.ml->e[tid].expert = me;
+            a.ml->e[tid].slot = vv;
+            __threadfence_system();
+        }
+        __syncthreads();
+    } else {
 
     // stable compaction of the victim order: non-hit slots keep their order;
     // the first nm of them are this step's victims
@@ -246,7 +279,6 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     }
     __syncthreads();
 
-    const int64_t trace_base = (int64_t)a.c.trace_head[0];
     if (hit) {
         a.c.stamp[v] = clock0 + hr;
         order_out[C - nh - nm + hr] = v;
@@ -280,6 +312,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         __threadfence_system();
     }
     __syncthreads();
+    }  // LRU
     for (int i = tid; i < a.n_ids; i += K2_THREADS) {
         const int id = a.ids[i];
         int sl = (unsigned)id < (unsigned)E ? s_req[id] : -1;
@@ -296,7 +329,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     }
     if (tid == 0) {
         const int n = nh + nm;
-        *a.c.clock = clock0 + n;
+        *a.c.clock = clock0 + (stat ? nm : n);  // static: transient slots used so far
         a.c.counters[0] += (uint64_t)nh;
         a.c.counters[1] += (uint64_t)nm;
         a.c.counters[2] += (uint64_t)s_evict;

@@ -70,6 +70,7 @@ struct moe_ctx {
     uint8_t* ml_mem = nullptr;
     size_t ml_stride = 0;
     int max_unique = 0;
+    int static_T = 0;           // static split: transient slots (2 * max distinct experts per step)
     int64_t seq = 0;
     hipEvent_t copy_ev[2] = {nullptr, nullptr};
     // token 0's slots and weights of the last miss list read per parity
@@ -127,7 +128,7 @@ moe_status check_cfg(const moe_config* c) {
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
         c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 1 ||
         c->cache_slots > 16384 || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0 ||
-        c->pinned_mb < 0)
+        c->pinned_mb < 0 || c->policy < 0 || c->policy > 1)
         return MOE_EINVAL;
     // the down kernel stages every selected expert's intermediate vector in LDS
     if ((size_t)(c->top_k + c->n_shared) * (c->inter / 32) * 80 > 60 * 1024) return MOE_EINVAL;
@@ -265,6 +266,9 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
     a.C = c->cfg.cache_slots;
     a.k = c->cfg.top_k;
     a.B = B;
+    a.policy = c->cfg.policy;
+    a.T = c->static_T;
+    a.R = c->cfg.cache_slots - c->static_T;
     const int p = c->parity;
     LAUNCHCHK(c, launch_k2(a, c->order[p], c->order[p ^ 1], c->cs));
     c->parity = p ^ 1;
@@ -524,6 +528,14 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
         memset(h.data() + o_stamp, 0xFF, (size_t)C * 8);
         int32_t* ord = (int32_t*)(h.data() + o_ord);
         for (int v = 0; v < C; ++v) ord[v] = v;  // cold start: all empty, ascending index
+        if (cfg->policy == MOE_POLICY_STATIC) {
+            // static split: keys 0..R-1 resident in slots 0..R-1 (filled below)
+            c->static_T = 2 * (int)std::min<int64_t>((int64_t)cfg->max_tokens * cfg->top_k, E);
+            const int R = (int)std::min<int64_t>(C - c->static_T, n_sl);
+            int32_t* so = (int32_t*)(h.data() + o_slot);
+            int32_t* ko = (int32_t*)(h.data() + o_key);
+            for (int v = 0; v < R; ++v) so[v] = ko[v] = v;
+        }
         if (hipMemcpy(c->state_dev, h.data(), o_tr, hipMemcpyHostToDevice) != hipSuccess) return bail(MOE_EHIP);
     }
 
@@ -592,6 +604,15 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     std::vector<std::thread> th;
     for (int t = 0; t < nth; ++t) th.emplace_back(worker);
     for (auto& t : th) t.join();
+
+    if (cfg->policy == MOE_POLICY_STATIC) {
+        where = "static split resident fill";
+        const size_t R = (size_t)std::min<int64_t>(C - c->static_T, n_sl);
+        for (size_t v = 0; v < R; ++v)
+            if (hipMemcpy(c->arena + v * L.blob_bytes, c->blob_src(v), L.blob_bytes, hipMemcpyHostToDevice) !=
+                hipSuccess)
+                return bail(MOE_EHIP);
+    }
 
     // shared experts -> HBM
     where = "shared expert upload";

@@ -99,6 +99,8 @@ struct K2Args {
     MissList* ml;           // host-mapped
     int64_t seq;
     int n_ids, layer, step, E, C, k, B;
+    int policy;             // 0: LRU; 1: static split (R resident keys, T transient slots)
+    int R, T;
 };
 
 // one MoE layer's expert FFN for B tokens: gate/up + SwiGLU (K3) and

@@ -161,3 +161,41 @@ def test_grouped_prefill_with_pageable_pool_part():
     assert cnt["h2d_bounced"] > 0
     _check(wl, steps, ids, w, y, m, recs)
     m.close()
+
+
+@pytest.mark.parametrize("case", ["decode_b1", "prefill_then_b4"])
+def test_static_split_policy_matches_oracle(case):
+    """MOE_POLICY_STATIC: keys below R = C - T resident from init, every other access streamed
+    into T transient slots in rotation.  ids, trace (hit/miss, slot, evicted key), the resident
+    table and outputs against the oracle's static split."""
+    import moe_expert_offload_amd as M
+    if case == "decode_b1":
+        wl = synth.Workload("static_b1", 3, 16, 2, 0, 256, 512, 20, 24, 1, 0.9, seed=31)
+        steps = _steps(wl, 0, 1, wl.decode_tokens)
+        max_tokens = 1
+    else:
+        wl = GROUPED[0]
+        steps = _steps(wl, wl.prefill_tokens, wl.n_requests, wl.decode_tokens)
+        max_tokens = wl.prefill_tokens
+    T = 2 * min(max_tokens * wl.top_k, wl.n_experts)
+    m, _ = make_moe(wl, max_tokens=max_tokens, policy=M.MOE_POLICY_STATIC)
+    ids, w, y = run_steps(m, wl, steps)
+    cnt, recs = m.stats(trace_cap=1 << 20)
+    ref = oracle.run_trace(wl, synth.router_weights(wl), steps, static_transient=T)
+    for t in range(len(steps)):
+        np.testing.assert_array_equal(ids[t], ref["ids"][t])
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    rc = ref["counters"]
+    assert (cnt["hits"], cnt["misses"], cnt["evictions"]) == (rc["hits"], rc["misses"], rc["evictions"])
+    slot_of, key_of, _ = m.cache_state()
+    r_slot, r_key = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    for t, x in enumerate(steps):
+        for l in range(wl.n_layers):
+            for b in range(len(x)):
+                r = oracle.moe_output(wl, l, x[b], ref["ids"][t][l, b], ref["w"][t][l, b])
+                rel, mx, ok = close_enough(y[t][l, b], r)
+                assert ok, (t, l, b, rel, mx)
+    assert cnt["misses"] > 0 and cnt["hits"] > 0
+    m.close()
