@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--lookahead", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ffn-rounds", type=int, default=20)
+    ap.add_argument("--policy", choices=("lru", "static"), default="lru",
+                    help="cache policy: router-following LRU, or the static per-layer split comparator")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU "
@@ -198,8 +200,9 @@ def main():
     if W_ + K > T:
         K = T - W_
     flags = 0
+    policy = M.MOE_POLICY_STATIC if args.policy == "static" else M.MOE_POLICY_LRU
     cfg = M.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.n_shared,
-                        wl.cache_slots, wl.max_tokens, args.lookahead, 0, 0, flags)
+                        wl.cache_slots, wl.max_tokens, args.lookahead, 0, 0, flags, 0, policy)
     fptr, FillArgs = synth.fill_callback()
     fa = FillArgs(wl.seed, wl.hidden, wl.inter)
     Wr = synth.router_weights(wl)
@@ -234,14 +237,22 @@ def main():
     c_warm, _ = m.stats()
     ids = torch.empty((L, B, wl.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((L, B, wl.top_k), dtype=torch.float32, device=dev)
+    # the timed region, in 5 equal segments (each ends with the streams drained) for the
+    # run-to-run spread; value is the whole region's rate
+    nseg = 5 if K >= 5 else 1
+    bounds = [W_ + (K * i) // nseg for i in range(nseg + 1)]
+    seg_rates = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    with torch.cuda.stream(cs):
-        for t in range(W_, W_ + K):
-            last = t == W_ + K - 1
-            m.stack_forward(s0 + t, xd[t], 0, B, y, B * H, ids if last else None, wts if last else None)
-    cs.synchronize()
-    m.copy_stream.synchronize()
+    for si in range(nseg):
+        ts = time.perf_counter()
+        with torch.cuda.stream(cs):
+            for t in range(bounds[si], bounds[si + 1]):
+                last = t == W_ + K - 1
+                m.stack_forward(s0 + t, xd[t], 0, B, y, B * H, ids if last else None, wts if last else None)
+        cs.synchronize()
+        m.copy_stream.synchronize()
+        seg_rates.append((bounds[si + 1] - bounds[si]) * B / (time.perf_counter() - ts))
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     c_all, _ = m.stats()
@@ -284,6 +295,9 @@ def main():
                     "measured_64MB_GBps": round(h2d_big, 2), "frac_of_measured": round(eff / h2d_meas, 4)}
     extra["pool"] = {"GB": round(wl.pool * m.blob_bytes / 1e9, 2), "pinned_GB": round(pinned_gb, 2),
                      "bounced_copies": c["h2d_bounced"], "copies": c["h2d_copies"]}
+    srt = sorted(seg_rates)
+    extra["segments"] = {"n": nseg, "median_tok_s": round(srt[len(srt) // 2], 2), "min_tok_s": round(srt[0], 2),
+                         "max_tok_s": round(srt[-1], 2)}
     extra["miss_rate"] = round(c["misses"] / acc, 4) if acc else None
     extra["miss_rate_warmup"] = round(c_warm["misses"] / max(1, c_warm["hits"] + c_warm["misses"]), 4)
     extra["misses_per_step"] = round(c["misses"] / K, 2)
@@ -313,7 +327,8 @@ def main():
         "data": "synthetic (seeded MXFP4 experts, N(0,0.02) bf16 router, AR(1) hidden states)",
         "config": {"workload": wl.name, "layers": L, "experts": wl.n_experts, "top_k": wl.top_k,
                    "shared": wl.n_shared, "hidden": H, "inter": wl.inter, "cache_slots": wl.cache_slots,
-                   "pool_GB": round(wl.pool * m.blob_bytes / 1e9, 2), "batch": B, "lookahead": args.lookahead},
+                   "pool_GB": round(wl.pool * m.blob_bytes / 1e9, 2), "batch": B, "lookahead": args.lookahead,
+                   "policy": args.policy},
         "roofline": roof,
         "cpu_baseline": cpu,
         **extra,
