@@ -60,7 +60,11 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-// one wave per (expert row, token)
+// one wave per (expert row, token); a lane's groups g = lane + 64 i are
+// loaded eight at a time (all loads of a batch in flight together), then
+// folded in increasing g
+constexpr int K1_BATCH = 8;
+
 __global__ __launch_bounds__(64) void k1_logits(K1Args a) {
     const int lane = threadIdx.x;
     const int e = blockIdx.x, b = blockIdx.y;
@@ -68,10 +72,18 @@ __global__ __launch_bounds__(64) void k1_logits(K1Args a) {
     const uint16_t* W = a.W + (size_t)e * a.H;
     float p = 0.0f;
     const int ng = a.H >> 3;
-    for (int g = lane; g < ng; g += 64) {
-        uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
-        uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)g * 8);
-        p = fold8(wv, xv, p);
+    for (int g0 = lane; g0 < ng; g0 += 64 * K1_BATCH) {
+        uint4 wv[K1_BATCH], xv[K1_BATCH];
+#pragma unroll
+        for (int i = 0; i < K1_BATCH; ++i) {
+            const int g = g0 + 64 * i;
+            const int gc = g < ng ? g : g0;  // past the row: re-read the first group, unused
+            wv[i] = *reinterpret_cast<const uint4*>(W + (size_t)gc * 8);
+            xv[i] = *reinterpret_cast<const uint4*>(x + (size_t)gc * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < K1_BATCH; ++i)
+            if (g0 + 64 * i < ng) p = fold8(wv[i], xv[i], p);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
@@ -245,9 +257,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
                 TraceRec t = {a.step, l, me, vv, 0, old};
                 a.c.trace[ti] = t;
             }
-            a.ml->e[tid].expert = me;
-            a.ml->e[tid].slot = vv;
-            __threadfence_system();
+            s_victim[tid] = vv;  // this step's miss list: (s_miss_e, s_victim) by rank
         }
         __syncthreads();
     } else {
@@ -307,9 +317,6 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
             TraceRec t = {a.step, l, me, vv, 0, old};
             a.c.trace[ti] = t;
         }
-        a.ml->e[tid].expert = me;
-        a.ml->e[tid].slot = vv;
-        __threadfence_system();
     }
     __syncthreads();
     }  // LRU
@@ -319,31 +326,38 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         a.slots[i] = sl;
         if (a.slots_out) a.slots_out[i] = sl;
     }
-    // token 0's slots and weights ride along with the miss list (the host
-    // passes them to the FFN launch as arguments); written by wave 0, which
-    // also publishes the list below
-    if (tid < a.k && tid < 16) {
-        const int id = a.ids[tid];
-        a.ml->slot0[tid] = (unsigned)id < (unsigned)E ? s_req[id] : -1;
-        a.ml->w0[tid] = a.z ? a.w[tid] : 0.0f;
-    }
-    if (tid == 0) {
+    // The miss list goes to host memory from wave 0 alone (entries, token 0's
+    // slots and weights, which the host passes to the FFN launch as
+    // arguments), so one system-scope fence orders all of it before the
+    // sequence number that publishes it.
+    if (tid < 64) {
+        for (int i = tid; i < nm; i += 64) {
+            a.ml->e[i].expert = s_miss_e[i];
+            a.ml->e[i].slot = s_victim[i];
+        }
+        if (tid < a.k && tid < 16) {
+            const int id = a.ids[tid];
+            a.ml->slot0[tid] = (unsigned)id < (unsigned)E ? s_req[id] : -1;
+            a.ml->w0[tid] = a.z ? a.w[tid] : 0.0f;
+        }
         const int n = nh + nm;
-        *a.c.clock = clock0 + (stat ? nm : n);  // static: transient slots used so far
-        a.c.counters[0] += (uint64_t)nh;
-        a.c.counters[1] += (uint64_t)nm;
-        a.c.counters[2] += (uint64_t)s_evict;
-        a.c.counters[3] += 1ull;
-        int64_t fit = a.c.trace_cap - trace_base;
-        fit = fit < 0 ? 0 : (fit > n ? n : fit);
-        a.c.trace_head[0] = (uint64_t)(trace_base + fit);
-        a.c.trace_head[1] += (uint64_t)(n - fit);
-        a.ml->n_miss = nm;
-        a.ml->n_unique = n;
-        a.ml->n_evict = s_evict;
-        a.ml->n_invalid = s_invalid;
+        if (tid == 0) {
+            *a.c.clock = clock0 + (stat ? nm : n);  // static: transient slots used so far
+            a.c.counters[0] += (uint64_t)nh;
+            a.c.counters[1] += (uint64_t)nm;
+            a.c.counters[2] += (uint64_t)s_evict;
+            a.c.counters[3] += 1ull;
+            int64_t fit = a.c.trace_cap - trace_base;
+            fit = fit < 0 ? 0 : (fit > n ? n : fit);
+            a.c.trace_head[0] = (uint64_t)(trace_base + fit);
+            a.c.trace_head[1] += (uint64_t)(n - fit);
+            a.ml->n_miss = nm;
+            a.ml->n_unique = n;
+            a.ml->n_evict = s_evict;
+            a.ml->n_invalid = s_invalid;
+        }
         __threadfence_system();
-        __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (tid == 0) __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
