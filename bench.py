@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--lookahead", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ffn-rounds", type=int, default=20)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with 3 device copies of 256 MiB (reference dispatches for counter scaling)")
     ap.add_argument("--policy", choices=("lru", "static"), default="lru",
                     help="cache policy: router-following LRU, or the static per-layer split comparator")
     args = ap.parse_args()
@@ -307,6 +309,15 @@ def main():
     extra["decode_roofline_tok_s"] = round(roof_step * B, 1)
     extra["decode_frac_of_roofline"] = round(tok_s / (roof_step * B), 4)
 
+    if args.calib_copy:
+        # plain device copies of known size: under a counter profiler their FETCH_SIZE /
+        # WRITE_SIZE per dispatch give the scale from counter units to bytes
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, Wr, X)
