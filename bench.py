@@ -23,6 +23,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 
+# HBM bytes moved per layer FFN launch (k3_gate_up + k4_down, batch 1) from the FETCH_SIZE and
+# WRITE_SIZE counter runs, scaled by a device copy of known size in the same process
+# (profiles/expert_ffn_gptoss120b_shaped_traffic.md).  Set an entry to None when those kernels change.
+FFN_TRAFFIC_BYTES = {"gptoss120b_shaped": 53.74e6}
+
 
 def decode_rate(tokens, total_s, ttft_s):
     """Completion tokens / (total - time to first token)."""
@@ -283,7 +288,8 @@ def main():
     acc = c["hits"] + c["misses"]
     gbs = bytes_layer / (ffn_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": FFN_TRAFFIC_BYTES.get(wl.name) if B == 1 and args.policy == "lru" else None,
             "kernel": ("expert FFN of one layer: k3_gate_up + k4_down (MXFP4 GEMVs, SwiGLU, weighted combine)"
                        if B == 1 else
                        "expert FFN of one layer: k2g_group + k5_gate_up + k5_down + k5_combine (grouped MXFP4 MFMA)"),

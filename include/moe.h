@@ -110,10 +110,13 @@ typedef struct moe_ctx moe_ctx;
 moe_status moe_query_sizes(const moe_config* cfg, size_t* blob_bytes, size_t* arena_bytes,
                            size_t* workspace_bytes);
 
-/* Builds a context: allocates the pinned host pool of all L*E routed expert
- * blobs and fills it through `fill` (called once per (layer, expert) and once
- * per shared expert), copies the router weights (host [L][E][H] bf16) and the
- * shared experts into HBM, and starts with an empty (cold) cache.
+/* Builds a context: allocates the host pool of all L*E routed expert blobs and
+ * fills it through `fill` (called once per (layer, expert) and once per shared
+ * expert), copies the router weights (host [L][E][H] bf16) and the shared
+ * experts into HBM, and starts with an empty (cold) cache (the static policy
+ * fills its resident slots here).  The pool is pinned (DMA-readable) memory as
+ * far as the platform allows and cfg->pinned_mb permits; the rest is pageable
+ * and its misses are staged through a ring of pinned bounce buffers.
  * slot_arena_dev (>= C blobs) and workspace_dev are device memory owned by the
  * caller; they and both streams must outlive the context.
  * Errors: MOE_EINVAL (shape), MOE_ECAPACITY (cache_slots), MOE_ENOMEM (pinned
@@ -135,9 +138,15 @@ moe_status moe_cache_resolve(moe_ctx* ctx, int32_t step, int32_t layer, const in
                              int32_t n_tokens, int32_t* slots_dev, int32_t* n_miss_out);
 
 /* One layer for n_tokens tokens, causal: router (K1) -> top-k + resolve (K2)
- * -> miss copies -> expert FFN (K3, K4).  x_bf16_dev: [n_tokens][H]; y_bf16_dev: [n_tokens][H]
+ * -> miss copies -> expert FFN.  x_bf16_dev: [n_tokens][H]; y_bf16_dev: [n_tokens][H]
  * = sum_j w_j * FFN_{id_j}(x) + shared(x).  ids_dev_out ([n_tokens][k] int32,
- * ranked by logit) and w_dev_out ([n_tokens][k] float) may be NULL. */
+ * ranked by logit) and w_dev_out ([n_tokens][k] float) may be NULL.
+ * One token: per-token GEMV kernels (K3 gate/up, K4 down + combine).  Several
+ * tokens (a prefill chunk, or decode requests in lock-step; pirouter.ai
+ * "FreeToken x RTX 5090" page, expert-path section): the tokens' rows are
+ * grouped by expert and run on the matrix cores, each expert's weights read
+ * once per step (MOE_FLAG_PER_TOKEN_FFN: the GEMV kernels per token instead,
+ * up to any n_tokens). */
 moe_status moe_layer_forward(moe_ctx* ctx, int32_t step, int32_t layer, const void* x_bf16_dev,
                              int32_t n_tokens, void* y_bf16_dev, int32_t* ids_dev_out,
                              float* w_dev_out);
@@ -151,9 +160,11 @@ moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev,
                              int32_t* ids_dev_out, float* w_dev_out);
 
 /* Expert FFN of one layer with caller-resolved slots (e.g. from moe_cache_resolve):
- * y = sum_j w_j * FFN(slot_j)(x) + shared(x), K3 then K4 on the compute stream.
- * slots_dev [n_tokens][k] int32 must name slots that hold this layer's experts (the
- * library does not check); w_dev [n_tokens][k] float. */
+ * y = sum_j w_j * FFN(slot_j)(x) + shared(x), on the compute stream (the same
+ * kernels as moe_layer_forward for that token count).  slots_dev [n_tokens][k]
+ * int32 must name slots that hold this layer's experts (the library does not
+ * check which expert a slot holds; with several tokens a slot outside [0, C)
+ * makes every output NaN); w_dev [n_tokens][k] float. */
 moe_status moe_expert_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16_dev, int32_t n_tokens,
                               const int32_t* slots_dev, const float* w_dev, void* y_bf16_dev);
 
@@ -162,10 +173,12 @@ typedef struct {
     uint64_t resolves;                 /* layer steps resolved */
     uint64_t h2d_bytes, h2d_copies;    /* miss copies issued */
     uint64_t trace_records, trace_dropped;
-    uint64_t ffn_launches;             /* with MOE_FLAG_PROFILE: timed layer FFNs (one K3 + one K4) */
+    uint64_t ffn_launches;             /* with MOE_FLAG_PROFILE: timed layer FFNs */
     uint64_t h2d_bounced;              /* misses copied from the pageable part through the bounce ring */
     uint64_t pool_pinned_bytes;        /* bytes of the pool in pinned memory */
-    double k3_ms, k4_ms;               /* ... and the summed durations of K3 and K4 (HIP events) */
+    double k3_ms, k4_ms;               /* ... summed durations of the FFN's first part (K3; grouped:
+                                          grouping + gate/up) and second part (K4; grouped: down +
+                                          combine), from HIP events */
 } moe_counters;
 
 typedef struct {
