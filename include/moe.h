@@ -130,8 +130,9 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
 
 /* Cache step for one layer with caller-given expert ids (ids_dev: [n_tokens][k]
  * int32, each in [0, E)): enqueues the resolve kernel on the compute stream,
- * waits for its miss list, issues one host-to-device copy per miss on the copy
- * stream and makes the compute stream wait for them.  slots_dev ([n_tokens][k]
+ * waits for its miss list, issues one host-to-device copy per miss (alternating
+ * between the caller's copy stream and a second, library-owned one) and makes
+ * the compute stream wait for them.  slots_dev ([n_tokens][k]
  * int32, may be NULL) receives the slot holding each id; *n_miss_out (host,
  * may be NULL) the number of misses.  `step` labels the trace records. */
 moe_status moe_cache_resolve(moe_ctx* ctx, int32_t step, int32_t layer, const int32_t* ids_dev,
@@ -191,9 +192,10 @@ typedef struct {
 moe_status moe_stats(moe_ctx* ctx, moe_counters* out, moe_trace_rec* buf, size_t cap, size_t* n_out);
 
 /* Host-to-device bandwidth of the copy path: n_copies back-to-back copies of
- * bytes_per_copy from blob-aligned pool offsets (deterministic pseudo-random
- * order) on the copy stream into a scratch device buffer; returns GB/s (1e9).
- * Leaves the cache untouched. */
+ * bytes_per_copy from blob-aligned offsets of the pinned part of the pool
+ * (deterministic pseudo-random order) into a scratch device buffer, alternating
+ * between the caller's copy stream and the library's second copy stream as the
+ * miss stager does; returns GB/s (1e9).  Leaves the cache untouched. */
 moe_status moe_measure_h2d(moe_ctx* ctx, size_t bytes_per_copy, int32_t n_copies, double* gbps_out);
 
 /* Reads back the cache state (host buffers, each may be NULL): slot_of

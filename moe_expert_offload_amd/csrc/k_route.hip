@@ -97,8 +97,9 @@ int launch_k1(const K1Args& a, void* stream) {
 
 constexpr int K2_MAXCAND = 16;  // top-k candidates per lane: E <= 1024
 
-// top-k of one token's logits by one wave; ties go to the lower expert index
-__device__ void wave_topk(const K2Args& a, int b) {
+// top-k of one token's logits by one wave; ties go to the lower expert index.
+// The ids (and token 0's weights) also go to LDS when s_ids / s_w0 are given.
+__device__ void wave_topk(const K2Args& a, int b, int32_t* s_ids = nullptr, float* s_w0 = nullptr) {
     const int lane = threadIdx.x & 63;
     const float* z = a.z + (size_t)b * a.E;
     uint64_t key[K2_MAXCAND];
@@ -139,6 +140,8 @@ __device__ void wave_topk(const K2Args& a, int b) {
         a.w[o] = wj;
         if (a.ids_out) a.ids_out[o] = my_id;
         if (a.w_out) a.w_out[o] = wj;
+        if (s_ids) s_ids[o] = my_id;
+        if (s_w0 && b == 0) s_w0[lane] = wj;
     }
 }
 
@@ -148,6 +151,7 @@ constexpr int K2_THREADS = 1024;
 constexpr int K2_MAXE = 1024;
 constexpr int K2_MAXC = 16384;
 constexpr int K2_CPT = K2_MAXC / K2_THREADS;  // order entries per thread
+constexpr int K2_IDS_LDS = 1024;              // ids of a step kept in LDS up to this many
 
 // exclusive prefix count of a 0/1 flag over the 1024 threads, in thread order
 __device__ __forceinline__ int block_rank(bool flag, int* s_wave, int& total) {
@@ -197,38 +201,53 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     __shared__ uint32_t s_hitbits[K2_MAXC / 32];
     __shared__ int s_wave[K2_THREADS / 64];
     __shared__ int s_evict, s_invalid;
+    __shared__ int32_t s_ids[K2_IDS_LDS];
+    __shared__ float s_w0[16];
     const int tid = threadIdx.x;
     const int E = a.E, C = a.C, l = a.layer;
+    const bool stat = a.policy != 0;
+    const bool ids_lds = a.n_ids <= K2_IDS_LDS;
 
-    // routing: top-k + softmax of every token (one wave per token)
+    // Loads that do not depend on this step's routing are issued first, so their
+    // latency overlaps the logits loads of the top-k: the slot-table entry of
+    // expert e = tid, this thread's slice of the victim order, the clock.
+    const int e = tid;
+    const int v_pre = (!stat && e < E) ? a.c.slot_of[l * E + e] : -1;
+    int ent[K2_CPT];
+    const int p0 = tid * K2_CPT;
+#pragma unroll
+    for (int c = 0; c < K2_CPT; ++c) ent[c] = (!stat && p0 + c < C) ? order_in[p0 + c] : -1;
+    const int64_t clock0 = *a.c.clock;
+
+    // routing: top-k + softmax of every token (one wave per token); otherwise the
+    // given ids, into LDS when they fit
     if (a.z) {
-        for (int b = tid >> 6; b < a.B; b += K2_THREADS / 64) wave_topk(a, b);
-        __syncthreads();
+        for (int b = tid >> 6; b < a.B; b += K2_THREADS / 64)
+            wave_topk(a, b, ids_lds ? s_ids : nullptr, s_w0);
+    } else if (ids_lds) {
+        for (int i = tid; i < a.n_ids; i += K2_THREADS) s_ids[i] = a.ids[i];
     }
 
-    for (int e = tid; e < E; e += K2_THREADS) s_req[e] = 0;
+    for (int i = tid; i < E; i += K2_THREADS) s_req[i] = 0;
     for (int i = tid; i < (C + 31) / 32; i += K2_THREADS) s_hitbits[i] = 0u;
     if (tid == 0) { s_evict = 0; s_invalid = 0; }
     __syncthreads();
     for (int i = tid; i < a.n_ids; i += K2_THREADS) {
-        const int id = a.ids[i];
+        const int id = ids_lds ? s_ids[i] : a.ids[i];
         if ((unsigned)id < (unsigned)E) s_req[id] = 1;
         else atomicAdd(&s_invalid, 1);
     }
     __syncthreads();
 
     // classify the requested experts (thread e <-> expert e; E <= 1024)
-    const int e = tid;
     const bool req = e < E && s_req[e] != 0;
-    const bool stat = a.policy != 0;
     // static split: resident iff key < R (slot = key); LRU: the slot table
-    const int v = req ? (stat ? (l * E + e < a.R ? l * E + e : -1) : a.c.slot_of[l * E + e]) : -1;
+    const int v = req ? (stat ? (l * E + e < a.R ? l * E + e : -1) : v_pre) : -1;
     const bool hit = req && v >= 0;
     const bool miss = req && v < 0;
     int nh, nm;
     const int hr = block_rank(hit, s_wave, nh);
     const int mr = block_rank(miss, s_wave, nm);
-    const int64_t clock0 = *a.c.clock;
     if (hit && !stat) atomicOr(&s_hitbits[v >> 5], 1u << (v & 31));
     if (miss) s_miss_e[mr] = e;
     __syncthreads();
@@ -264,16 +283,12 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
 
     // stable compaction of the victim order: non-hit slots keep their order;
     // the first nm of them are this step's victims
-    int ent[K2_CPT];
     int kept = 0;
-    const int p0 = tid * K2_CPT;
 #pragma unroll
     for (int c = 0; c < K2_CPT; ++c) {
-        int p = p0 + c;
-        ent[c] = -1;
-        if (p < C) {
-            int sl = order_in[p];
-            bool is_hit = (s_hitbits[sl >> 5] >> (sl & 31)) & 1u;
+        const int sl = ent[c];
+        if (sl >= 0) {
+            const bool is_hit = (s_hitbits[sl >> 5] >> (sl & 31)) & 1u;
             ent[c] = is_hit ? -1 : sl;
             kept += is_hit ? 0 : 1;
         }
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     __syncthreads();
     }  // LRU
     for (int i = tid; i < a.n_ids; i += K2_THREADS) {
-        const int id = a.ids[i];
+        const int id = ids_lds ? s_ids[i] : a.ids[i];
         int sl = (unsigned)id < (unsigned)E ? s_req[id] : -1;
         a.slots[i] = sl;
         if (a.slots_out) a.slots_out[i] = sl;
@@ -336,9 +351,9 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
             a.ml->e[i].slot = s_victim[i];
         }
         if (tid < a.k && tid < 16) {
-            const int id = a.ids[tid];
+            const int id = ids_lds ? s_ids[tid] : a.ids[tid];
             a.ml->slot0[tid] = (unsigned)id < (unsigned)E ? s_req[id] : -1;
-            a.ml->w0[tid] = a.z ? a.w[tid] : 0.0f;
+            a.ml->w0[tid] = a.z ? s_w0[tid] : 0.0f;
         }
         const int n = nh + nm;
         if (tid == 0) {

@@ -72,7 +72,10 @@ struct moe_ctx {
     int max_unique = 0;
     int static_T = 0;           // static split: transient slots (2 * max distinct experts per step)
     int64_t seq = 0;
-    hipEvent_t copy_ev[2] = {nullptr, nullptr};
+    hipEvent_t copy_ev[2] = {nullptr, nullptr};    // per parity, on the caller's copy stream
+    hipStream_t ps2 = nullptr;                      // second copy stream (library-owned)
+    hipEvent_t copy_ev2[2] = {nullptr, nullptr};    // per parity, on ps2
+    bool copy_used[3][2] = {};                      // per parity: copies went to ps / ps2
     // token 0's slots and weights of the last miss list read per parity
     int32_t tok0_slot[2][16] = {};
     float tok0_w[2][16] = {};
@@ -217,9 +220,12 @@ void free_all(moe_ctx* c) {
     if (!c) return;
     if (c->cs) (void)hipStreamSynchronize(c->cs);
     if (c->ps) (void)hipStreamSynchronize(c->ps);
+    if (c->ps2) (void)hipStreamSynchronize(c->ps2);
     for (auto& p : c->prof_used) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto& p : c->prof_free) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
+    for (auto e : c->copy_ev2) if (e) (void)hipEventDestroy(e);
+    if (c->ps2) (void)hipStreamDestroy(c->ps2);
     c->bounce.shutdown();
     if (c->pool) (void)hipHostFree(c->pool);
     free(c->pool_pg);
@@ -302,18 +308,26 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     }
     c->tok0_valid[par] = true;
     const size_t blob = c->lay.blob_bytes;
+    bool used[2] = {false, false};
+    int nd = 0;  // direct copies so far: they alternate between the two copy streams
     for (int i = 0; i < nm; ++i) {
         const MissEntry m = ml->e[i];
         const size_t idx = (size_t)layer * c->cfg.n_experts + m.expert;
         uint8_t* dst = c->arena + (size_t)m.slot * blob;
         if (idx < c->n_pin) {
-            HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(idx), blob, hipMemcpyHostToDevice, c->ps));
+            const int q = nd++ & 1;
+            HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(idx), blob, hipMemcpyHostToDevice, q ? c->ps2 : c->ps));
+            used[q] = true;
         } else {
-            HIPCHK(c, c->bounce.copy(dst, c->blob_src(idx), blob));
+            HIPCHK(c, c->bounce.copy(dst, c->blob_src(idx), blob));  // on the caller's copy stream
             ++c->h2d_bounced;
+            used[0] = true;
         }
     }
-    if (nm > 0) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
+    if (used[0]) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
+    if (used[1]) HIPCHK(c, hipEventRecord(c->copy_ev2[par], c->ps2));
+    c->copy_used[par][0] = used[0];
+    c->copy_used[par][1] = used[1];
     c->h2d_bytes += (uint64_t)nm * blob;
     c->h2d_copies += (uint64_t)nm;
     if (n_miss_out) *n_miss_out = nm;
@@ -332,7 +346,10 @@ moe_status get_prof(moe_ctx* c, ProfSlot& p) {
 
 moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par, void* y, int n_miss,
                             const int32_t* slots_dev = nullptr, const float* w_dev = nullptr) {
-    if (n_miss > 0) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
+    if (n_miss > 0 && par < 2) {
+        if (c->copy_used[par][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
+        if (c->copy_used[par][1]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev2[par], 0));
+    }
     const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0;
     ProfSlot ps{};
     if (prof) {
@@ -550,6 +567,11 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     for (int p = 0; p < 2; ++p) miss_list(c, p)->seq = -1;
     for (auto& e : c->copy_ev)
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
+    // a second copy stream (default priority): blob copies alternate between the two, which
+    // keeps two DMA queues busy and hides the per-copy overhead of small blobs
+    if (hipStreamCreateWithFlags(&c->ps2, hipStreamNonBlocking) != hipSuccess) return bail(MOE_EHIP);
+    for (auto& e : c->copy_ev2)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
 
     // router weights -> HBM
     where = "router upload";
@@ -644,7 +666,10 @@ moe_status moe_cache_resolve(moe_ctx* c, int32_t step, int32_t layer, const int3
     int nm = 0;
     st = stage_misses(c, layer, 0, c->seq, &nm);
     if (st) return st;
-    if (nm > 0) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[0], 0));
+    if (nm > 0) {
+        if (c->copy_used[0][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[0], 0));
+        if (c->copy_used[0][1]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev2[0], 0));
+    }
     if (n_miss_out) *n_miss_out = nm;
     return MOE_OK;
 }
@@ -769,28 +794,28 @@ moe_status moe_measure_h2d(moe_ctx* c, size_t bytes, int32_t n_copies, double* g
     const size_t span = (bytes + blob - 1) / blob;  // blobs covered by one copy
     uint8_t* scratch = nullptr;
     HIPCHK(c, hipMalloc(&scratch, 2 * bytes));
-    hipEvent_t e0, e1;
-    HIPCHK(c, hipEventCreate(&e0));
-    HIPCHK(c, hipEventCreate(&e1));
     HIPCHK(c, hipStreamSynchronize(c->ps));
+    HIPCHK(c, hipStreamSynchronize(c->ps2));
     uint64_t r = 0x9E3779B97F4A7C15ull;
     auto next_off = [&]() {
         r ^= r << 13; r ^= r >> 7; r ^= r << 17;
         size_t i = (size_t)(r % (n_blobs > span ? n_blobs - span + 1 : 1));
         return i * blob;
     };
-    // warm-up copy, then the timed ones
+    // the miss path's copies, alternating between the two copy streams, timed on the host
+    // from issue to both streams drained (one untimed copy on each stream first: a stream's
+    // first copy also sets up its DMA queue)
     HIPCHK(c, hipMemcpyAsync(scratch, c->pool + next_off(), bytes, hipMemcpyHostToDevice, c->ps));
-    HIPCHK(c, hipEventRecord(e0, c->ps));
+    HIPCHK(c, hipMemcpyAsync(scratch + bytes, c->pool + next_off(), bytes, hipMemcpyHostToDevice, c->ps2));
+    HIPCHK(c, hipStreamSynchronize(c->ps));
+    HIPCHK(c, hipStreamSynchronize(c->ps2));
+    const auto t0 = std::chrono::steady_clock::now();
     for (int i = 0; i < n_copies; ++i)
         HIPCHK(c, hipMemcpyAsync(scratch + (size_t)(i & 1) * bytes, c->pool + next_off(), bytes,
-                                 hipMemcpyHostToDevice, c->ps));
-    HIPCHK(c, hipEventRecord(e1, c->ps));
-    HIPCHK(c, hipEventSynchronize(e1));
-    float ms = 0;
-    HIPCHK(c, hipEventElapsedTime(&ms, e0, e1));
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
+                                 hipMemcpyHostToDevice, (i & 1) ? c->ps2 : c->ps));
+    HIPCHK(c, hipStreamSynchronize(c->ps));
+    HIPCHK(c, hipStreamSynchronize(c->ps2));
+    const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     HIPCHK(c, hipFree(scratch));
     *gbps = (double)bytes * n_copies / (ms * 1e-3) / 1e9;
     return MOE_OK;
