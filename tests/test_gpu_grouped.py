@@ -199,3 +199,69 @@ def test_static_split_policy_matches_oracle(case):
                 assert ok, (t, l, b, rel, mx)
     assert cnt["misses"] > 0 and cnt["hits"] > 0
     m.close()
+
+
+def test_grouped_wide_4096_shape():
+    """H = 4096, I = 2048, top-6 (the DeepSeek-shaped expert) through the grouped path."""
+    wl = synth.Workload("wide_4096_grouped", 2, 16, 6, 0, 4096, 2048, 40, 2, 3, 0.85,
+                        prefill_tokens=40, seed=26)
+    steps = _steps(wl, wl.prefill_tokens, wl.n_requests, wl.decode_tokens)
+    m, _ = make_moe(wl, max_tokens=wl.prefill_tokens)
+    ids, w, y = run_steps(m, wl, steps)
+    _, recs = m.stats(trace_cap=1 << 20)
+    _, worst = _check(wl, steps, ids, w, y, m, recs, token_sample=lambda t, B: [0, B // 2, B - 1])
+    print("wide_4096_grouped worst rel-L2", worst)
+    m.close()
+
+
+def test_layer_forward_on_a_batch_matches_the_stack():
+    """moe_layer_forward (causal, one layer per call) and moe_stack_forward (lookahead 1) give
+    bitwise equal outputs for a batch step: the same kernels in the same order per layer."""
+    import torch
+    wl = GROUPED[0]
+    steps = _steps(wl, 0, wl.n_requests, 3)
+    m, _ = make_moe(wl, max_tokens=wl.n_requests)
+    _, _, ys = run_steps(m, wl, steps)
+    m.close()
+    m, _ = make_moe(wl, lookahead=0, max_tokens=wl.n_requests)
+    dev = m.device
+    for t, x in enumerate(steps):
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+        y = torch.empty((wl.n_layers, len(x), wl.hidden), dtype=torch.int16, device=dev)
+        with torch.cuda.stream(m.compute_stream):
+            for l in range(wl.n_layers):
+                m.layer_forward(t, l, xd, y[l])
+        m.compute_stream.synchronize()
+        from gpu_helpers import bf16_to_f32
+        np.testing.assert_array_equal(bf16_to_f32(y).view(np.uint32), ys[t].view(np.uint32))
+    m.close()
+
+
+def test_cache_resolve_then_grouped_expert_forward():
+    """The boundary's two halves on a batch: moe_cache_resolve with oracle ids, then
+    moe_expert_forward on the returned slots, against the oracle's layer output."""
+    import torch
+    wl = GROUPED[1]
+    x = synth.decode_inputs(dataclasses.replace(wl, decode_tokens=1))[0]     # [B][H]
+    W = synth.router_weights(wl)
+    ref = oracle.run_trace(wl, W, [x])
+    m, _ = make_moe(wl, max_tokens=wl.n_requests)
+    dev = m.device
+    l = 1
+    ids = torch.from_numpy(ref["ids"][0][l].astype(np.int32)).to(dev)
+    wts = torch.from_numpy(ref["w"][0][l].astype(np.float32)).to(dev)
+    slots = torch.empty_like(ids)
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    y = torch.empty((len(x), wl.hidden), dtype=torch.int16, device=dev)
+    with torch.cuda.stream(m.compute_stream):
+        nm = m.cache_resolve(0, l, ids, slots)
+        m.expert_forward(l, xd, slots, wts, y)
+    m.compute_stream.synchronize()
+    assert nm == len(np.unique(ref["ids"][0][l]))     # cold cache: every distinct expert misses
+    from gpu_helpers import bf16_to_f32
+    yf = bf16_to_f32(y)
+    for b in range(len(x)):
+        r = oracle.moe_output(wl, l, x[b], ref["ids"][0][l, b], ref["w"][0][l, b])
+        rel, mx, ok = close_enough(yf[b], r)
+        assert ok, (b, rel, mx)
+    m.close()

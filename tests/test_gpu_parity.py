@@ -201,3 +201,35 @@ def test_pageable_pool_part_through_bounce_ring():
     points = [(t, l, 0) for t in range(24) for l in range(wl.n_layers)]
     _check_run(wl, X, ids, w, y, recs, m, points)
     m.close()
+
+
+def test_profile_counters_and_h2d_measurement():
+    """MOE_FLAG_PROFILE times every layer FFN with HIP events; moe_measure_h2d returns a plausible
+    copy-path bandwidth (PCIe: between 1 and 70 GB/s)."""
+    import moe_expert_offload_amd as M
+    wl = synth.WORKLOADS["toy"]
+    X = synth.decode_inputs(wl)[:5]
+    m, _ = make_moe(wl, flags=M.MOE_FLAG_PROFILE)
+    run_stack(m, wl, X)
+    cnt, _ = m.stats()
+    assert cnt["ffn_launches"] == 5 * wl.n_layers
+    assert cnt["k3_ms"] > 0 and cnt["k4_ms"] > 0
+    assert cnt["pool_pinned_bytes"] == wl.pool * wl.blob_bytes and cnt["h2d_bounced"] == 0
+    g = m.measure_h2d(wl.blob_bytes, 16)
+    assert 1.0 < g < 70.0, g
+    m.close()
+
+
+def test_out_of_range_ids_are_rejected():
+    """Ids outside [0, E) given to moe_cache_resolve are counted by the resolve kernel (never
+    used as an index) and the call fails with MOE_EINVAL."""
+    import torch
+    import moe_expert_offload_amd as M
+    wl = synth.WORKLOADS["toy"]
+    m, _ = make_moe(wl, max_tokens=2)
+    ids = torch.tensor([[0, wl.n_experts + 5], [1, 2]], dtype=torch.int32, device=m.device)
+    with pytest.raises(M.MoeError) as ei:
+        with torch.cuda.stream(m.compute_stream):
+            m.cache_resolve(0, 0, ids)
+    assert ei.value.status == M.MOE_EINVAL
+    m.close()
