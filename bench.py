@@ -44,6 +44,21 @@ def per_token_budget_gb(link_gbps, tok_per_s):
     return link_gbps / tok_per_s
 
 
+def pcie_link(dev_index=0):
+    """PCIe link of the GPU from sysfs (speed, width, NUMA node), or None where unreadable."""
+    import torch
+    try:
+        p = torch.cuda.get_device_properties(dev_index)
+        bdf = "%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id, p.pci_device_id)
+        base = "/sys/bus/pci/devices/" + bdf + "/"
+        rd = lambda f: open(base + f).read().strip()
+        return {"bdf": bdf, "speed": rd("current_link_speed"), "width": int(rd("current_link_width")),
+                "max_speed": rd("max_link_speed"), "max_width": int(rd("max_link_width")),
+                "numa_node": int(rd("numa_node"))}
+    except Exception:
+        return None
+
+
 def ffn_bytes_split(wl):
     """Algorithmic HBM bytes of one token-layer expert FFN at batch 1: K3 reads the selected (and
     shared) experts' MXFP4 gate/up weights and x and writes the intermediate vector; K4 reads
@@ -237,10 +252,13 @@ def main():
     y = torch.empty((L, B, H), dtype=torch.int16, device=dev)
     s0 = 1 if wl.prefill_tokens else 0
     torch.cuda.synchronize()
+    tw0 = time.perf_counter()
     with torch.cuda.stream(cs):
         for t in range(W_):
             m.stack_forward(s0 + t, xd[t], 0, B, y, B * H)
     cs.synchronize()
+    m.copy_stream.synchronize()
+    warm_s = time.perf_counter() - tw0
     c_warm, _ = m.stats()
     ids = torch.empty((L, B, wl.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((L, B, wl.top_k), dtype=torch.float32, device=dev)
@@ -300,13 +318,19 @@ def main():
     # miss bytes over the whole timed region: a lower bound on the copy path's achieved rate
     eff = c["h2d_bytes"] / dt / 1e9
     extra["h2d"] = {"effective_GBps": round(eff, 2), "measured_GBps": round(h2d_meas, 2),
-                    "measured_64MB_GBps": round(h2d_big, 2), "frac_of_measured": round(eff / h2d_meas, 4)}
+                    "measured_64MB_GBps": round(h2d_big, 2), "frac_of_measured": round(eff / h2d_meas, 4),
+                    "link": pcie_link(0)}
     extra["pool"] = {"GB": round(wl.pool * m.blob_bytes / 1e9, 2), "pinned_GB": round(pinned_gb, 2),
                      "bounced_copies": c["h2d_bounced"], "copies": c["h2d_copies"]}
     srt = sorted(seg_rates)
     extra["segments"] = {"n": nseg, "median_tok_s": round(srt[len(srt) // 2], 2), "min_tok_s": round(srt[0], 2),
                          "max_tok_s": round(srt[-1], 2)}
+    # cold = every token from the empty cache on (warm-up + timed); steady = the timed region
+    extra["cold_tok_s"] = round((W_ + K) * B / (warm_s + dt), 2)
+    if B > 1:
+        extra["per_request_tok_s"] = round(tok_s / B, 2)
     extra["miss_rate"] = round(c["misses"] / acc, 4) if acc else None
+    extra["miss_rate_cumulative"] = round(c_all["misses"] / max(1, c_all["hits"] + c_all["misses"]), 4)
     extra["miss_rate_warmup"] = round(c_warm["misses"] / max(1, c_warm["hits"] + c_warm["misses"]), 4)
     extra["misses_per_step"] = round(c["misses"] / K, 2)
     extra["h2d_GB_per_step"] = round(c["h2d_bytes"] / K / 1e9, 4)

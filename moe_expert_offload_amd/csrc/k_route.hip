@@ -90,8 +90,79 @@ __global__ __launch_bounds__(64) void k1_logits(K1Args a) {
     if (lane == 0) a.z[(size_t)b * a.E + e] = p;
 }
 
+// Many tokens (a prefill chunk, more than 16): a workgroup of 4 waves takes 16
+// experts x 16 tokens; each wave keeps its 4 experts' router rows in registers
+// (G groups of 8 bf16 per lane: lane l holds groups g = l + 64 i, i < G) and
+// walks the 16 tokens, so each router row is read once per token tile instead
+// of once per token.  Every logit is still lane l's fold over its groups in increasing g,
+// then the xor butterfly: the same bits as k1_logits.
+constexpr int K1T_EXP = 4, K1T_TOK = 16;
+
+template <int G>
+__global__ __launch_bounds__(256) void k1_logits_tiled(K1Args a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e0 = (blockIdx.x * 4 + w) * K1T_EXP;
+    const int b0 = blockIdx.y * K1T_TOK;
+    const int ng = a.H >> 3;
+    uint4 wr[K1T_EXP][G];
+#pragma unroll
+    for (int j = 0; j < K1T_EXP; ++j) {
+        const int e = e0 + j < a.E ? e0 + j : a.E - 1;
+        const uint16_t* W = a.W + (size_t)e * a.H;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int g = lane + 64 * i;
+            wr[j][i] = *reinterpret_cast<const uint4*>(W + (size_t)(g < ng ? g : 0) * 8);
+        }
+    }
+    // the next token's activations are loaded while the current one is folded
+    auto load_x = [&](int b, uint4* xv) {
+        const uint16_t* x = a.x + (size_t)(b < a.B ? b : a.B - 1) * a.H;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int g = lane + 64 * i;
+            xv[i] = *reinterpret_cast<const uint4*>(x + (size_t)(g < ng ? g : 0) * 8);
+        }
+    };
+    auto logits = [&](int b, const uint4* xv) {
+#pragma unroll
+        for (int j = 0; j < K1T_EXP; ++j) {
+            float p = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                if (lane + 64 * i < ng) p = fold8(wr[j][i], xv[i], p);
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+            if (lane == 0 && e0 + j < a.E && b < a.B) a.z[(size_t)b * a.E + e0 + j] = p;
+        }
+    };
+    uint4 xa[G], xb[G];
+    load_x(b0, xa);
+    load_x(b0 + 1, xb);
+    for (int t = 0; t < K1T_TOK; t += 2) {
+        logits(b0 + t, xa);
+        load_x(b0 + t + 2, xa);
+        logits(b0 + t + 1, xb);
+        load_x(b0 + t + 3, xb);
+    }
+}
+
 int launch_k1(const K1Args& a, void* stream) {
-    hipLaunchKernelGGL(k1_logits, dim3(a.E, a.B), dim3(64), 0, (hipStream_t)stream, a);
+    hipStream_t st = (hipStream_t)stream;
+    const int G = (a.H / 8 + 63) / 64;  // groups per lane (H <= 4096: G <= 8)
+    if (a.B > K1T_TOK && G <= 8) {
+        const dim3 grid((a.E + 4 * K1T_EXP - 1) / (4 * K1T_EXP), (a.B + K1T_TOK - 1) / K1T_TOK);
+        if (G <= 2)
+            hipLaunchKernelGGL(k1_logits_tiled<2>, grid, dim3(256), 0, st, a);
+        else if (G <= 4)
+            hipLaunchKernelGGL(k1_logits_tiled<4>, grid, dim3(256), 0, st, a);
+        else if (G <= 6)
+            hipLaunchKernelGGL(k1_logits_tiled<6>, grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL(k1_logits_tiled<8>, grid, dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(k1_logits, dim3(a.E, a.B), dim3(64), 0, st, a);
+    }
     return (int)hipGetLastError();
 }
 
