@@ -116,8 +116,9 @@ constexpr int FFN_THREADS = 256;
 // weight load issued earlier would make these LDS writes wait for it too
 // (loads complete in order per wave), and a wave dedicated to staging
 // measured slower.
-__device__ __forceinline__ void stage_blocks(uint4* smem, const uint4* src, int nblk, int nseg) {
-    for (int blk = threadIdx.x; blk < nblk; blk += FFN_THREADS) {
+__device__ __forceinline__ void stage_blocks(uint4* smem, const uint4* src, int nblk, int nseg,
+                                             int nthreads = FFN_THREADS) {
+    for (int blk = threadIdx.x; blk < nblk; blk += nthreads) {
         const uint4 v0 = src[blk * 4 + 0];
         const uint4 v1 = src[blk * 4 + 1];
         const uint4 v2 = src[blk * 4 + 2];
@@ -207,15 +208,21 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
 }
 
 // ---------------------------------------------------------------- phase 2 --
-// one 8-row tile of the output: compute lane (r = lane&7, s = 8*wave + lane>>3);
-// the 32 segments split the combined (expert, I-block) range of the token
-template <int T2>
-__device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile, int b) {
+// R8 8-row tiles of the output per workgroup, four waves on each (sub-tile
+// sub = wave/4), all sharing one LDS copy of the token's activations.  Compute
+// lane (r = lane&7, s = 8*(wave%4) + lane>>3); the 32 segments split the
+// combined (expert, I-block) range of the token.  A sub-tile past H/8 (odd
+// H/8) reads tile 0 and writes nothing.
+template <int T2, int R8>
+__device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile16, int b) {
     constexpr int S = 32;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wf = tid >> 6, w = wf & 3, sub = wf >> 2;
     const int NBI = a.NBI, nE = a.nE;
     const int Q = nE * NBI;
     float* red = reinterpret_cast<float*>(smem + Q * 5);
+    const int t8 = tile16 * R8 + sub;
+    const bool tok = t8 < (a.H >> 3);
+    const int tile = tok ? t8 : 0;
     const int r = lane & 7, s = w * 8 + (lane >> 3);
     const int nq = seg_len(Q, S, s), q0 = seg_begin(Q, S, s);
     // A segment (at most ceil(nE*NBI/32) <= NBI + 1 blocks, as nE <= 32)
@@ -253,7 +260,7 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
             acc += (t0 + t < nq) ? pv : 0.0f;
         }
     };
-    stage_blocks(smem, reinterpret_cast<const uint4*>(a.a + (size_t)b * nE * a.I), Q, S);
+    stage_blocks(smem, reinterpret_cast<const uint4*>(a.a + (size_t)b * nE * a.I), Q, S, 4 * 64 * R8);
     __syncthreads();
     load(0);
     compute(0);
@@ -265,44 +272,52 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
-    if (lane < 8) red[w * 8 + r] = acc;
+    if (lane < 8) red[(sub * 4 + w) * 8 + r] = acc;
     __syncthreads();
-    if (tid < 8) {
+    if (tid < 8 * R8) {
+        const int sb = tid >> 3, rr = tid & 7;
         float ys = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) ys += red[ww * 8 + tid];
-        a.y[(size_t)b * a.H + tile * 8 + tid] = f32_to_bf16(ys);
+        for (int ww = 0; ww < 4; ++ww) ys += red[(sb * 4 + ww) * 8 + rr];
+        const int tt8 = tile16 * R8 + sb;
+        if (tt8 < (a.H >> 3)) a.y[(size_t)b * a.H + tt8 * 8 + rr] = f32_to_bf16(ys);
     }
 }
 
-// K3: grid (nE * I/16 tiles, B); K4: grid (H/8 tiles, B); 256 threads each
+// K3: grid (nE * I/16 tiles, B), 256 threads; K4: grid (ceil(H/16), B), 512
+// threads (two 8-row sub-tiles, so 2880-wide outputs take 180 workgroups per
+// token: one round on 256 CUs instead of two uneven ones, and the activations
+// are staged into LDS half as often)
 template <int T1>
 __global__ __launch_bounds__(FFN_THREADS) void k3_gate_up(FfnArgs a) {
     extern __shared__ uint4 smem[];
     ffn_gate_up<T1>(a, smem, blockIdx.x, blockIdx.y);
 }
 
+constexpr int K4_SUBTILES = 2;
+constexpr int K4_THREADS = 4 * 64 * K4_SUBTILES;
+
 template <int T2>
-__global__ __launch_bounds__(FFN_THREADS) void k4_down(FfnArgs a) {
+__global__ __launch_bounds__(K4_THREADS) void k4_down(FfnArgs a) {
     extern __shared__ uint4 smem[];
-    ffn_down<T2>(a, smem, blockIdx.x, blockIdx.y);
+    ffn_down<T2, K4_SUBTILES>(a, smem, blockIdx.x, blockIdx.y);
 }
 
 size_t ffn_lds_bytes(const Layout& L, int nE) {
     const size_t p1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
-    const size_t p2 = (size_t)nE * L.NBI * 80 + 4 * 8 * 4;
+    const size_t p2 = (size_t)nE * L.NBI * 80 + 4 * K4_SUBTILES * 8 * 4;
     return p1 > p2 ? p1 : p2;
 }
 
 int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid) {
     hipStream_t st = (hipStream_t)stream;
     a.P1 = a.nE * (L.I / 16);
-    a.P2 = L.H / 8;
+    a.P2 = (L.H / 8 + K4_SUBTILES - 1) / K4_SUBTILES;
     const int T1 = L.T3;
     const int T2 = (a.nE * L.NBI + 31) / 32;
     const size_t lds1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
-    const size_t lds2 = (size_t)a.nE * L.NBI * 80 + 4 * 8 * 4;
-    dim3 g1(a.P1, B), g2(a.P2, B), blk(FFN_THREADS);
+    const size_t lds2 = (size_t)a.nE * L.NBI * 80 + 4 * K4_SUBTILES * 8 * 4;
+    dim3 g1(a.P1, B), g2(a.P2, B), blk(FFN_THREADS), blk2(K4_THREADS);
     if (T1 <= 2)
         hipLaunchKernelGGL(k3_gate_up<2>, g1, blk, lds1, st, a);
     else if (T1 <= 4)
@@ -313,13 +328,13 @@ int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid) {
         hipLaunchKernelGGL(k3_gate_up<8>, g1, blk, lds1, st, a);
     if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
     if (T2 <= 2)
-        hipLaunchKernelGGL(k4_down<2>, g2, blk, lds2, st, a);
+        hipLaunchKernelGGL(k4_down<2>, g2, blk2, lds2, st, a);
     else if (T2 <= 4)
-        hipLaunchKernelGGL(k4_down<4>, g2, blk, lds2, st, a);
+        hipLaunchKernelGGL(k4_down<4>, g2, blk2, lds2, st, a);
     else if (T2 <= 8)
-        hipLaunchKernelGGL(k4_down<8>, g2, blk, lds2, st, a);
+        hipLaunchKernelGGL(k4_down<8>, g2, blk2, lds2, st, a);
     else
-        hipLaunchKernelGGL(k4_down<12>, g2, blk, lds2, st, a);
+        hipLaunchKernelGGL(k4_down<12>, g2, blk2, lds2, st, a);
     return (int)hipGetLastError();
 }
 
