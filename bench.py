@@ -157,7 +157,7 @@ def run_prefill(m, wl, dev, rounds):
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nb}}
 
 
-def cpu_baseline(wl, W, X, budget_s=20.0):
+def cpu_baseline(wl, W, X, C, budget_s=20.0):
     """The oracle as it stands, on the host cores: routing, LRU step and FFN of every token of
     one decode step through every layer, repeated while the budget lasts (at least one step)."""
     import numpy as np
@@ -165,7 +165,7 @@ def cpu_baseline(wl, W, X, budget_s=20.0):
     import oracle
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-    cache = oracle.Cache(wl.n_layers, wl.n_experts, wl.cache_slots)
+    cache = oracle.Cache(wl.n_layers, wl.n_experts, C)
     B = X.shape[1]
     t0 = time.perf_counter()
     done = 0
@@ -201,6 +201,11 @@ def main():
                     help="end with 3 device copies of 256 MiB (reference dispatches for counter scaling)")
     ap.add_argument("--policy", choices=("lru", "static"), default="lru",
                     help="cache policy: router-following LRU, or the static per-layer split comparator")
+    ap.add_argument("--cache-slots", default="config",
+                    help="'config' (the workload's cache fraction), 'auto' (as many slots as free HBM holds, "
+                         "whole pool at most), or a slot count")
+    ap.add_argument("--auto-reserve-gb", type=float, default=4.0,
+                    help="HBM kept free by --cache-slots auto (the KV cache's share in a server)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU "
@@ -223,18 +228,22 @@ def main():
         K = T - W_
     flags = 0
     policy = M.MOE_POLICY_STATIC if args.policy == "static" else M.MOE_POLICY_LRU
+    C = {"config": wl.cache_slots, "auto": 0}.get(args.cache_slots)
+    if C is None:
+        C = int(args.cache_slots)
     cfg = M.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.n_shared,
-                        wl.cache_slots, wl.max_tokens, args.lookahead, 0, 0, flags, 0, policy)
+                        C, wl.max_tokens, args.lookahead, 0, 0, flags, 0, policy)
     fptr, FillArgs = synth.fill_callback()
     fa = FillArgs(wl.seed, wl.hidden, wl.inter)
     Wr = synth.router_weights(wl)
     t0 = time.perf_counter()
-    m = M.OffloadMoE(cfg, (fptr, ctypes.addressof(fa)), Wr)
+    m = M.OffloadMoE(cfg, (fptr, ctypes.addressof(fa)), Wr, auto_reserve_bytes=int(args.auto_reserve_gb * 2**30))
     init_s = time.perf_counter() - t0
+    C = m.cfg.cache_slots
     c_init, _ = m.stats()
     pinned_gb = c_init["pool_pinned_bytes"] / 1e9
     print(f"# pool {wl.pool} x {m.blob_bytes} B = {wl.pool * m.blob_bytes / 1e9:.2f} GB ({pinned_gb:.2f} GB pinned), "
-          f"cache {wl.cache_slots} slots, init {init_s:.1f} s", file=sys.stderr, flush=True)
+          f"cache {C} slots ({args.cache_slots}), init {init_s:.1f} s", file=sys.stderr, flush=True)
 
     # measured host-to-device bandwidth of the copy path (>= 2 GB of blob-sized copies)
     n_cp = max(8, int(2e9 // m.blob_bytes) + 1)
@@ -350,7 +359,7 @@ def main():
         del src, dst
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, Wr, X)
+        cpu = cpu_baseline(wl, Wr, X, C)
     m.close()
     out = {
         "metric": ("decode tok/s per MoE stack at batch 1" if B == 1 else
@@ -367,7 +376,7 @@ def main():
         "dtype": "mxfp4-w/bf16-a/fp32-acc",
         "data": "synthetic (seeded MXFP4 experts, N(0,0.02) bf16 router, AR(1) hidden states)",
         "config": {"workload": wl.name, "layers": L, "experts": wl.n_experts, "top_k": wl.top_k,
-                   "shared": wl.n_shared, "hidden": H, "inter": wl.inter, "cache_slots": wl.cache_slots,
+                   "shared": wl.n_shared, "hidden": H, "inter": wl.inter, "cache_slots": C, "cache_sizing": args.cache_slots,
                    "pool_GB": round(wl.pool * m.blob_bytes / 1e9, 2), "batch": B, "lookahead": args.lookahead,
                    "policy": args.policy},
         "roofline": roof,

@@ -110,6 +110,27 @@ typedef struct moe_ctx moe_ctx;
 moe_status moe_query_sizes(const moe_config* cfg, size_t* blob_bytes, size_t* arena_bytes,
                            size_t* workspace_bytes);
 
+/* Cache auto-sizing: the expert-cache share of device memory is taken from
+ * the memory still free (FreeToken's --moe-cache-auto option, which splits
+ * free VRAM between the KV cache and the expert cache; pirouter.ai page
+ * "FreeToken × RTX 5090——120B MoE が 127 tok/s、その請求書", section on how
+ * 65 GB run on a 32 GB GPU).  Call it after the workspace (and anything else
+ * the caller keeps on the device) is allocated; cfg->cache_slots is ignored
+ * (may be 0 here and in moe_query_sizes, which then reports arena_bytes 0).
+ * *slots_out = the largest C with
+ *     C * blob + the library's own device bytes at C (cache state, router
+ *     weights, shared experts; each rounded to 2 MiB) + reserve_bytes
+ *     <= free_bytes,
+ * capped at n_layers * n_experts (the whole pool) and at 16384 slots.
+ * free_bytes: device bytes free; 0 = ask the runtime (hipMemGetInfo on the
+ * current device).  reserve_bytes: kept free for the caller (KV cache,
+ * activations, allocator slack).  Allocates nothing.
+ * Errors: MOE_EINVAL (shape), MOE_EHIP (memory query failed), MOE_ECAPACITY
+ * (the C that fits is below 2 * min(max_tokens * k, E); *slots_out still holds
+ * it). */
+moe_status moe_auto_cache_slots(const moe_config* cfg, uint64_t free_bytes, uint64_t reserve_bytes,
+                                int32_t* slots_out);
+
 /* Builds a context: allocates the host pool of all L*E routed expert blobs and
  * fills it through `fill` (called once per (layer, expert) and once per shared
  * expert), copies the router weights (host [L][E][H] bf16) and the shared

@@ -62,6 +62,9 @@ _st = ctypes.c_int
 _lib.moe_query_sizes.restype = _st
 _lib.moe_query_sizes.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(ctypes.c_size_t),
                                  ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+_lib.moe_auto_cache_slots.restype = _st
+_lib.moe_auto_cache_slots.argtypes = [ctypes.POINTER(MoeConfig), ctypes.c_uint64, ctypes.c_uint64,
+                                      ctypes.POINTER(_I32)]
 _lib.moe_init_pool.restype = _st
 _lib.moe_init_pool.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, ctypes.c_size_t, _P,
                                ctypes.c_size_t, _P, _P, ctypes.POINTER(_P)]
@@ -84,7 +87,7 @@ _lib.moe_destroy.argtypes = [_P]
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = [_P]
 
-EXPORTED = ("moe_query_sizes", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
+EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
             "moe_expert_forward", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
@@ -112,6 +115,17 @@ def query_sizes(cfg: MoeConfig):
     return b.value, a.value, w.value
 
 
+def auto_cache_slots(cfg: MoeConfig, free_bytes: int = 0, reserve_bytes: int = 0) -> int:
+    """Largest cache_slots that fits the device memory left (moe_auto_cache_slots).
+
+    free_bytes 0 asks the runtime for the current device's free memory."""
+    out = _I32()
+    st = _lib.moe_auto_cache_slots(ctypes.byref(cfg), free_bytes, reserve_bytes, ctypes.byref(out))
+    if st:
+        raise MoeError(st, f"moe_auto_cache_slots (fits {out.value} slots)")
+    return out.value
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -122,18 +136,27 @@ class OffloadMoE:
     fill: (function pointer int, user pointer int) of a C callback, or a Python callable
     fill(layer, expert, numpy_uint8_view) (slow; serialised by the GIL).
     router_w: host numpy uint16 array [L][E][H] (bf16 bits).
+    cfg.cache_slots == 0 sizes the cache from the device memory left once the workspace is
+    allocated (moe_auto_cache_slots), keeping auto_reserve_bytes free; self.cfg holds the result.
     """
 
-    def __init__(self, cfg: MoeConfig, fill, router_w, device=None, compute_stream=None, copy_stream=None):
+    def __init__(self, cfg: MoeConfig, fill, router_w, device=None, compute_stream=None, copy_stream=None,
+                 auto_reserve_bytes=2 << 30):
         import numpy as np
         import torch
 
+        cfg = MoeConfig.from_buffer_copy(cfg)
         self.cfg = cfg
         self.torch = torch
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else device)
         self.blob_bytes, arena_bytes, ws_bytes = query_sizes(cfg)
-        self.arena = torch.empty(arena_bytes, dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        if cfg.cache_slots == 0:
+            with torch.cuda.device(self.device):
+                torch.cuda.synchronize()
+                cfg.cache_slots = auto_cache_slots(cfg, 0, auto_reserve_bytes)
+            arena_bytes = cfg.cache_slots * self.blob_bytes
+        self.arena = torch.empty(arena_bytes, dtype=torch.uint8, device=self.device)
         self.compute_stream = compute_stream or torch.cuda.Stream(device=self.device)
         self.copy_stream = copy_stream or torch.cuda.Stream(device=self.device)
         rw = np.ascontiguousarray(router_w, dtype=np.uint16)

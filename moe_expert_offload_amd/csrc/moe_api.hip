@@ -124,20 +124,62 @@ moe_status set_err(moe_ctx* c, moe_status st, const char* fmt, ...) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-moe_status check_cfg(const moe_config* c) {
+constexpr int MAX_CACHE_SLOTS = 16384;  // the resolve and grouping kernels' slot capacity
+
+// distinct experts one layer step can request; the cache needs twice that (one layer in flight
+// while the next one's victims are chosen)
+int64_t min_cache_slots(const moe_config* c) {
+    return 2 * std::min<int64_t>((int64_t)c->max_tokens * c->top_k, c->n_experts);
+}
+
+// shape checks; cache_slots == 0 passes only when allow_auto (size queries before auto sizing)
+moe_status check_cfg(const moe_config* c, bool allow_auto = false) {
     if (!c) return MOE_EINVAL;
     if (c->n_layers < 1 || c->n_experts < 1 || c->n_experts > 1024 || c->top_k < 1 ||
         c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
-        c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 1 ||
-        c->cache_slots > 16384 || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0 ||
+        c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 0 ||
+        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0 ||
         c->pinned_mb < 0 || c->policy < 0 || c->policy > 1)
         return MOE_EINVAL;
     // the down kernel stages every selected expert's intermediate vector in LDS
     if ((size_t)(c->top_k + c->n_shared) * (c->inter / 32) * 80 > 60 * 1024) return MOE_EINVAL;
-    const int64_t per_step = std::min<int64_t>((int64_t)c->max_tokens * c->top_k, c->n_experts);
-    if ((int64_t)c->cache_slots < 2 * per_step) return MOE_ECAPACITY;
+    if (c->cache_slots == 0 && allow_auto) return MOE_OK;
+    if ((int64_t)c->cache_slots < min_cache_slots(c)) return MOE_ECAPACITY;
     return MOE_OK;
+}
+
+// device memory the library allocates itself: the cache state block (slot table, reverse map,
+// stamps, clock, counters, trace head, double-buffered victim order, trace ring), the router
+// weights and the shared experts
+struct StatePlan {
+    size_t slot, key, stamp, clock, cnt, th, ord, tr, total;
+};
+
+StatePlan plan_state(const moe_config& c, int C) {
+    StatePlan p{};
+    const size_t n_sl = (size_t)c.n_layers * c.n_experts;
+    size_t off = 0;
+    p.slot = off;  off = align_up(off + n_sl * 4, 256);
+    p.key = off;   off = align_up(off + (size_t)C * 4, 256);
+    p.stamp = off; off = align_up(off + (size_t)C * 8, 256);
+    p.clock = off; off = align_up(off + 8, 256);
+    p.cnt = off;   off = align_up(off + 4 * 8, 256);
+    p.th = off;    off = align_up(off + 2 * 8, 256);
+    p.ord = off;   off = align_up(off + 2 * (size_t)C * 4, 256);
+    p.tr = off;    off = align_up(off + std::max<size_t>((size_t)c.trace_capacity, 1) * sizeof(TraceRec), 256);
+    p.total = off;
+    return p;
+}
+
+// the library's own device allocations at C slots, each rounded up to the allocator's 2 MiB
+// granularity
+size_t library_device_bytes(const moe_config& c, const Layout& L, int C) {
+    const size_t g = (size_t)2 << 20;
+    size_t b = align_up(plan_state(c, C).total, g);
+    b += align_up((size_t)c.n_layers * c.n_experts * c.hidden * 2, g);
+    if (c.n_shared > 0) b += align_up((size_t)c.n_layers * c.n_shared * L.blob_bytes, g);
+    return b;
 }
 
 struct WsPlan {
@@ -449,12 +491,46 @@ extern "C" {
 
 moe_status moe_query_sizes(const moe_config* cfg, size_t* blob_bytes, size_t* arena_bytes,
                            size_t* workspace_bytes) {
-    moe_status st = check_cfg(cfg);
+    moe_status st = check_cfg(cfg, true);
     if (st) return st;
     Layout L = make_layout(cfg->hidden, cfg->inter);
     if (blob_bytes) *blob_bytes = L.blob_bytes;
     if (arena_bytes) *arena_bytes = L.blob_bytes * (size_t)cfg->cache_slots;
     if (workspace_bytes) *workspace_bytes = plan_workspace(*cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_auto_cache_slots(const moe_config* cfg, uint64_t free_bytes, uint64_t reserve_bytes,
+                                int32_t* slots_out) {
+    if (!slots_out) return MOE_EINVAL;
+    *slots_out = 0;
+    moe_status st = check_cfg(cfg, true);
+    if (st) return st;
+    if (free_bytes == 0) {
+        size_t fr = 0, tot = 0;
+        if (hipMemGetInfo(&fr, &tot) != hipSuccess) {
+            (void)hipGetLastError();
+            return MOE_EHIP;
+        }
+        free_bytes = fr;
+    }
+    const Layout L = make_layout(cfg->hidden, cfg->inter);
+    const int64_t cap = std::min<int64_t>((int64_t)cfg->n_layers * cfg->n_experts, MAX_CACHE_SLOTS);
+    auto fits = [&](int64_t C) {
+        const uint64_t need = (uint64_t)C * L.blob_bytes + library_device_bytes(*cfg, L, (int)C) + reserve_bytes;
+        return need <= free_bytes;
+    };
+    // the need grows with C (blob + 20 B of state per slot), so the largest fitting C is found by
+    // bisection over [0, cap]
+    int64_t lo = 0, hi = cap;
+    if (!fits(0)) lo = -1;
+    else
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (fits(mid)) lo = mid; else hi = mid - 1;
+        }
+    *slots_out = (int32_t)std::max<int64_t>(lo, 0);
+    if (lo < min_cache_slots(cfg)) return MOE_ECAPACITY;
     return MOE_OK;
 }
 
@@ -516,44 +592,35 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
 
     // device cache state
     const size_t n_sl = (size_t)Lyr * E;
-    const size_t trace_cap = (size_t)cfg->trace_capacity;
-    size_t off = 0, o_slot = off;
-    off = align_up(off + n_sl * 4, 256);
-    size_t o_key = off; off = align_up(off + (size_t)C * 4, 256);
-    size_t o_stamp = off; off = align_up(off + (size_t)C * 8, 256);
-    size_t o_clock = off; off = align_up(off + 8, 256);
-    size_t o_cnt = off; off = align_up(off + 4 * 8, 256);
-    size_t o_th = off; off = align_up(off + 2 * 8, 256);
-    size_t o_ord = off; off = align_up(off + 2 * (size_t)C * 4, 256);
-    size_t o_tr = off; off = align_up(off + std::max<size_t>(trace_cap, 1) * sizeof(TraceRec), 256);
+    const StatePlan sp = plan_state(*cfg, C);
     where = "cache state allocation";
-    if (hipMalloc(&c->state_dev, off) != hipSuccess) return bail(MOE_ENOMEM);
-    c->cd.slot_of = (int32_t*)(c->state_dev + o_slot);
-    c->cd.key_of = (int32_t*)(c->state_dev + o_key);
-    c->cd.stamp = (int64_t*)(c->state_dev + o_stamp);
-    c->cd.clock = (int64_t*)(c->state_dev + o_clock);
-    c->cd.counters = (uint64_t*)(c->state_dev + o_cnt);
-    c->cd.trace_head = (uint64_t*)(c->state_dev + o_th);
-    c->cd.trace = (TraceRec*)(c->state_dev + o_tr);
-    c->cd.trace_cap = (int64_t)trace_cap;
-    c->order[0] = (int32_t*)(c->state_dev + o_ord);
+    if (hipMalloc(&c->state_dev, sp.total) != hipSuccess) return bail(MOE_ENOMEM);
+    c->cd.slot_of = (int32_t*)(c->state_dev + sp.slot);
+    c->cd.key_of = (int32_t*)(c->state_dev + sp.key);
+    c->cd.stamp = (int64_t*)(c->state_dev + sp.stamp);
+    c->cd.clock = (int64_t*)(c->state_dev + sp.clock);
+    c->cd.counters = (uint64_t*)(c->state_dev + sp.cnt);
+    c->cd.trace_head = (uint64_t*)(c->state_dev + sp.th);
+    c->cd.trace = (TraceRec*)(c->state_dev + sp.tr);
+    c->cd.trace_cap = (int64_t)cfg->trace_capacity;
+    c->order[0] = (int32_t*)(c->state_dev + sp.ord);
     c->order[1] = c->order[0] + C;
     {
-        std::vector<uint8_t> h(o_tr, 0);
-        memset(h.data() + o_slot, 0xFF, n_sl * 4);
-        memset(h.data() + o_key, 0xFF, (size_t)C * 4);
-        memset(h.data() + o_stamp, 0xFF, (size_t)C * 8);
-        int32_t* ord = (int32_t*)(h.data() + o_ord);
+        std::vector<uint8_t> h(sp.tr, 0);
+        memset(h.data() + sp.slot, 0xFF, n_sl * 4);
+        memset(h.data() + sp.key, 0xFF, (size_t)C * 4);
+        memset(h.data() + sp.stamp, 0xFF, (size_t)C * 8);
+        int32_t* ord = (int32_t*)(h.data() + sp.ord);
         for (int v = 0; v < C; ++v) ord[v] = v;  // cold start: all empty, ascending index
         if (cfg->policy == MOE_POLICY_STATIC) {
             // static split: keys 0..R-1 resident in slots 0..R-1 (filled below)
             c->static_T = 2 * (int)std::min<int64_t>((int64_t)cfg->max_tokens * cfg->top_k, E);
             const int R = (int)std::min<int64_t>(C - c->static_T, n_sl);
-            int32_t* so = (int32_t*)(h.data() + o_slot);
-            int32_t* ko = (int32_t*)(h.data() + o_key);
+            int32_t* so = (int32_t*)(h.data() + sp.slot);
+            int32_t* ko = (int32_t*)(h.data() + sp.key);
             for (int v = 0; v < R; ++v) so[v] = ko[v] = v;
         }
-        if (hipMemcpy(c->state_dev, h.data(), o_tr, hipMemcpyHostToDevice) != hipSuccess) return bail(MOE_EHIP);
+        if (hipMemcpy(c->state_dev, h.data(), sp.tr, hipMemcpyHostToDevice) != hipSuccess) return bail(MOE_EHIP);
     }
 
     // host-mapped miss lists (two, alternating by layer parity)

@@ -16,7 +16,7 @@ def make_moe(wl, lookahead=1, trace_capacity=1 << 20, flags=0, max_tokens=None, 
              policy=0):
     import moe_expert_offload_amd as M
     cfg = M.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.n_shared,
-                        cache_slots or wl.cache_slots, max_tokens or wl.max_tokens, lookahead,
+                        wl.cache_slots if cache_slots is None else cache_slots, max_tokens or wl.max_tokens, lookahead,
                         trace_capacity, 0, flags, pinned_mb, policy)
     fptr, FillArgs = synth.fill_callback()
     args = FillArgs(wl.seed, wl.hidden, wl.inter)

@@ -81,3 +81,59 @@ def test_grouped_workspace_grows_with_max_tokens():
     rows16 = 16 * 2
     assert w16 - w1 >= rows16 * 256 * 4   # fp32 expert outputs, one row per (token, expert)
     assert w100 > w16
+
+
+# --- cache auto-sizing (host arithmetic only: free bytes are given, so no device query) ---
+
+GPTOSS = dict(n_layers=36, n_experts=128, top_k=4, hidden=2880, inter=2880, n_shared=0, cache_slots=0,
+              max_tokens=1)
+
+
+def test_query_sizes_accepts_auto_cache_slots():
+    import moe_expert_offload_amd as M
+    b, a, w = M.query_sizes(_cfg(cache_slots=0))
+    b8, a8, w8 = M.query_sizes(_cfg(cache_slots=8))
+    assert (b, a, w) == (b8, 0, w8)  # the workspace does not depend on C
+
+
+def test_auto_cache_slots_caps_at_the_pool_and_kernel_limit():
+    import moe_expert_offload_amd as M
+    assert M.auto_cache_slots(_cfg(cache_slots=0), free_bytes=1 << 40) == 2 * 16
+    # gpt-oss-120b shape: the 60.9 GB pool fits in 288 GB of HBM whole
+    assert M.auto_cache_slots(_cfg(**GPTOSS), free_bytes=288 * 10**9) == 36 * 128
+    # 48 x 512 keys exceed the 16384 slots the resolve kernel addresses
+    q38 = dict(n_layers=48, n_experts=512, top_k=10, hidden=3072, inter=768, n_shared=1, cache_slots=0,
+               max_tokens=2048)
+    assert M.auto_cache_slots(_cfg(**q38), free_bytes=288 * 10**9) == 16384
+
+
+def test_auto_cache_slots_is_the_largest_that_fits():
+    import moe_expert_offload_amd as M
+    cfg = _cfg(**GPTOSS)
+    blob = M.query_sizes(cfg)[0]
+    router = 36 * 128 * 2880 * 2
+    reserve = 3 * 10**9
+    prev = 0
+    for free in range(25 * 10**9, 40 * 10**9, 997_000_001):
+        C = M.auto_cache_slots(cfg, free_bytes=free, reserve_bytes=reserve)
+        assert C * blob + router + reserve <= free            # what it returns fits
+        assert (C + 1) * blob + router + reserve > free - (8 << 20)  # one more would not (state < 8 MiB)
+        assert C >= prev
+        prev = C
+    # the pages' card: 24.6 GB of a 32 GB RTX 5090 held 40.4 % of the 4608 experts (1862 slots);
+    # with that arena budget plus the library's own bytes, the same count comes out
+    C = M.auto_cache_slots(cfg, free_bytes=1862 * blob + router + (6 << 20))
+    assert C == 1862
+
+
+def test_auto_cache_slots_reports_capacity_shortfall():
+    import moe_expert_offload_amd as M
+    cfg = _cfg(**dict(GPTOSS, max_tokens=16))  # needs 2 * min(16 * 4, 128) = 128 slots
+    blob = M.query_sizes(cfg)[0]
+    with pytest.raises(M.MoeError) as ei:
+        M.auto_cache_slots(cfg, free_bytes=100 * blob)
+    assert ei.value.status == -4 and "fits" in str(ei.value)
+    assert M.auto_cache_slots(cfg, free_bytes=140 * blob) >= 128
+    with pytest.raises(M.MoeError) as ei:
+        M.auto_cache_slots(cfg, free_bytes=1000)
+    assert ei.value.status == -4
