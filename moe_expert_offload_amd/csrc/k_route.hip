@@ -49,6 +49,12 @@ __device__ __forceinline__ uint64_t topk_key(float z, int e) {
     return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// the logit back from its key (exact; -0 comes back as +0)
+__device__ __forceinline__ float topk_key_logit(uint64_t key) {
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
@@ -180,6 +186,7 @@ __device__ void wave_topk(const K2Args& a, int b, int32_t* s_ids = nullptr, floa
         key[c] = ee < a.E ? topk_key(z[ee], ee) : 0ull;
     }
     int my_id = 0;
+    uint64_t my_key = 0;
     for (int j = 0; j < a.k; ++j) {
         uint64_t best = 0;
         int bc = -1;
@@ -196,10 +203,13 @@ __device__ void wave_topk(const K2Args& a, int b, int32_t* s_ids = nullptr, floa
                 if (c == bc) key[c] = 0;
         }
         int id = (int)(0xFFFFFFFFu - (uint32_t)(wbest & 0xFFFFFFFFu));
-        if (lane == j) my_id = id;
+        if (lane == j) {
+            my_id = id;
+            my_key = wbest;
+        }
     }
     // softmax over the k selected logits (FP32); lane j holds rank j
-    float zj = lane < a.k ? z[my_id] : 0.0f;
+    float zj = lane < a.k ? topk_key_logit(my_key) : 0.0f;
     float z0 = __shfl(zj, 0);
     float ej = lane < a.k ? expf(zj - z0) : 0.0f;
     float den = 0.0f;
@@ -281,7 +291,8 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
 
     // Loads that do not depend on this step's routing are issued first, so their
     // latency overlaps the logits loads of the top-k: the slot-table entry of
-    // expert e = tid, this thread's slice of the victim order, the clock.
+    // expert e = tid, this thread's slice of the victim order, the clock and the
+    // trace head.
     const int e = tid;
     const int v_pre = (!stat && e < E) ? a.c.slot_of[l * E + e] : -1;
     int ent[K2_CPT];
@@ -289,6 +300,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
 #pragma unroll
     for (int c = 0; c < K2_CPT; ++c) ent[c] = (!stat && p0 + c < C) ? order_in[p0 + c] : -1;
     const int64_t clock0 = *a.c.clock;
+    const int64_t trace_base = (int64_t)a.c.trace_head[0];
 
     // routing: top-k + softmax of every token (one wave per token); otherwise the
     // given ids, into LDS when they fit
@@ -323,99 +335,44 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     if (miss) s_miss_e[mr] = e;
     __syncthreads();
 
-    const int64_t trace_base = (int64_t)a.c.trace_head[0];
+    // victims, by miss rank
     if (stat) {
-        // static split: hits keep their fixed slot; misses stream into the next
-        // transient slots in rotation, whose last occupant is the evicted key
-        if (hit) {
-            s_req[e] = v;
-            const int64_t ti = trace_base + hr;
-            if (ti < a.c.trace_cap) {
-                TraceRec t = {a.step, l, e, v, 1, -1};
-                a.c.trace[ti] = t;
-            }
-        }
-        if (tid < nm) {
-            const int me = s_miss_e[tid];
-            const int vv = a.R + (int)((clock0 + tid) % a.T);
-            const int old = a.c.key_of[vv];
-            if (old >= 0) atomicAdd(&s_evict, 1);
-            a.c.key_of[vv] = l * E + me;
-            s_req[me] = vv;
-            const int64_t ti = trace_base + nh + tid;
-            if (ti < a.c.trace_cap) {
-                TraceRec t = {a.step, l, me, vv, 0, old};
-                a.c.trace[ti] = t;
-            }
-            s_victim[tid] = vv;  // this step's miss list: (s_miss_e, s_victim) by rank
-        }
-        __syncthreads();
+        // static split: misses stream into the next transient slots in rotation
+        if (tid < nm) s_victim[tid] = a.R + (int)((clock0 + tid) % a.T);
     } else {
-
-    // stable compaction of the victim order: non-hit slots keep their order;
-    // the first nm of them are this step's victims
-    int kept = 0;
+        // stable compaction of the victim order: non-hit slots keep their order;
+        // the first nm of them are this step's victims
+        int kept = 0;
 #pragma unroll
-    for (int c = 0; c < K2_CPT; ++c) {
-        const int sl = ent[c];
-        if (sl >= 0) {
-            const bool is_hit = (s_hitbits[sl >> 5] >> (sl & 31)) & 1u;
-            ent[c] = is_hit ? -1 : sl;
-            kept += is_hit ? 0 : 1;
+        for (int c = 0; c < K2_CPT; ++c) {
+            const int sl = ent[c];
+            if (sl >= 0) {
+                const bool is_hit = (s_hitbits[sl >> 5] >> (sl & 31)) & 1u;
+                ent[c] = is_hit ? -1 : sl;
+                kept += is_hit ? 0 : 1;
+            }
         }
-    }
-    int nkept;
-    int kr = block_scan(kept, s_wave, nkept);
+        int nkept;
+        int kr = block_scan(kept, s_wave, nkept);
 #pragma unroll
-    for (int c = 0; c < K2_CPT; ++c) {
-        if (ent[c] < 0) continue;
-        if (kr < nm) s_victim[kr] = ent[c];
-        else order_out[kr - nm] = ent[c];
-        ++kr;
-    }
-    __syncthreads();
-
-    if (hit) {
-        a.c.stamp[v] = clock0 + hr;
-        order_out[C - nh - nm + hr] = v;
-        s_req[e] = v;
-        int64_t ti = trace_base + hr;
-        if (ti < a.c.trace_cap) {
-            TraceRec t = {a.step, l, e, v, 1, -1};
-            a.c.trace[ti] = t;
-        }
-    }
-    if (tid < nm) {
-        const int me = s_miss_e[tid];
-        const int vv = s_victim[tid];
-        const int old = a.c.key_of[vv];
-        if (old >= 0) {
-            a.c.slot_of[old] = -1;
-            atomicAdd(&s_evict, 1);
-        }
-        a.c.key_of[vv] = l * E + me;
-        a.c.slot_of[l * E + me] = vv;
-        a.c.stamp[vv] = clock0 + nh + tid;
-        order_out[C - nm + tid] = vv;
-        s_req[me] = vv;
-        int64_t ti = trace_base + nh + tid;
-        if (ti < a.c.trace_cap) {
-            TraceRec t = {a.step, l, me, vv, 0, old};
-            a.c.trace[ti] = t;
+        for (int c = 0; c < K2_CPT; ++c) {
+            if (ent[c] < 0) continue;
+            if (kr < nm) s_victim[kr] = ent[c];
+            else order_out[kr - nm] = ent[c];
+            ++kr;
         }
     }
     __syncthreads();
-    }  // LRU
-    for (int i = tid; i < a.n_ids; i += K2_THREADS) {
-        const int id = ids_lds ? s_ids[i] : a.ids[i];
-        int sl = (unsigned)id < (unsigned)E ? s_req[id] : -1;
-        a.slots[i] = sl;
-        if (a.slots_out) a.slots_out[i] = sl;
-    }
-    // The miss list goes to host memory from wave 0 alone (entries, token 0's
-    // slots and weights, which the host passes to the FFN launch as
-    // arguments), so one system-scope fence orders all of it before the
-    // sequence number that publishes it.
+    // final slot of every requested expert
+    if (hit) s_req[e] = v;
+    if (tid < nm) s_req[s_miss_e[tid]] = s_victim[tid];
+    __syncthreads();
+
+    // The miss list goes to host memory as soon as it is known, from wave 0
+    // alone (entries, token 0's slots and weights, which the host passes to the
+    // FFN launch as arguments), so one system-scope fence orders all of it
+    // before the sequence number that publishes it.  The cache bookkeeping
+    // below runs while the host issues the copies.
     if (tid < 64) {
         for (int i = tid; i < nm; i += 64) {
             a.ml->e[i].expert = s_miss_e[i];
@@ -426,25 +383,308 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
             a.ml->slot0[tid] = (unsigned)id < (unsigned)E ? s_req[id] : -1;
             a.ml->w0[tid] = a.z ? s_w0[tid] : 0.0f;
         }
-        const int n = nh + nm;
         if (tid == 0) {
-            *a.c.clock = clock0 + (stat ? nm : n);  // static: transient slots used so far
-            a.c.counters[0] += (uint64_t)nh;
-            a.c.counters[1] += (uint64_t)nm;
-            a.c.counters[2] += (uint64_t)s_evict;
-            a.c.counters[3] += 1ull;
-            int64_t fit = a.c.trace_cap - trace_base;
-            fit = fit < 0 ? 0 : (fit > n ? n : fit);
-            a.c.trace_head[0] = (uint64_t)(trace_base + fit);
-            a.c.trace_head[1] += (uint64_t)(n - fit);
             a.ml->n_miss = nm;
-            a.ml->n_unique = n;
-            a.ml->n_evict = s_evict;
+            a.ml->n_unique = nh + nm;
             a.ml->n_invalid = s_invalid;
         }
         __threadfence_system();
         if (tid == 0) __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+
+    // bookkeeping: stamps, slot table, reverse map, recency order, trace
+    if (hit) {
+        if (!stat) {
+            a.c.stamp[v] = clock0 + hr;
+            order_out[C - nh - nm + hr] = v;
+        }
+        const int64_t ti = trace_base + hr;
+        if (ti < a.c.trace_cap) {
+            TraceRec t = {a.step, l, e, v, 1, -1};
+            a.c.trace[ti] = t;
+        }
+    }
+    if (tid < nm) {
+        const int me = s_miss_e[tid];
+        const int vv = s_victim[tid];
+        const int old = a.c.key_of[vv];  // the static split's transient slots keep their last occupant
+        if (old >= 0) {
+            if (!stat) a.c.slot_of[old] = -1;
+            atomicAdd(&s_evict, 1);
+        }
+        a.c.key_of[vv] = l * E + me;
+        if (!stat) {
+            a.c.slot_of[l * E + me] = vv;
+            a.c.stamp[vv] = clock0 + nh + tid;
+            order_out[C - nm + tid] = vv;
+        }
+        const int64_t ti = trace_base + nh + tid;
+        if (ti < a.c.trace_cap) {
+            TraceRec t = {a.step, l, me, vv, 0, old};
+            a.c.trace[ti] = t;
+        }
+    }
+    for (int i = tid; i < a.n_ids; i += K2_THREADS) {
+        const int id = ids_lds ? s_ids[i] : a.ids[i];
+        int sl = (unsigned)id < (unsigned)E ? s_req[id] : -1;
+        a.slots[i] = sl;
+        if (a.slots_out) a.slots_out[i] = sl;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int n = nh + nm;
+        *a.c.clock = clock0 + (stat ? nm : n);  // static: transient slots used so far
+        a.c.counters[0] += (uint64_t)nh;
+        a.c.counters[1] += (uint64_t)nm;
+        a.c.counters[2] += (uint64_t)s_evict;
+        a.c.counters[3] += 1ull;
+        int64_t fit = a.c.trace_cap - trace_base;
+        fit = fit < 0 ? 0 : (fit > n ? n : fit);
+        a.c.trace_head[0] = (uint64_t)(trace_base + fit);
+        a.c.trace_head[1] += (uint64_t)(n - fit);
+        a.ml->n_evict = s_evict;  // informational; written after the release
+    }
+}
+
+// ------------------------------------------------------------ K2, one token --
+// Decode (one routed token, LRU policy).  Wave 0 routes and resolves the token
+// with wave-level operations and publishes the miss list before any block
+// barrier; the other waves hold their slice of the LRU order in registers and,
+// after two barriers, compact it.  The k selected experts are distinct, so at
+// most k order entries are hit slots and the nm victims (the first nm non-hit
+// entries) are among the first k entries of the order.
+
+// lane permutations inside a row of 16 lanes (DPP)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+    const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+    return o > v ? o : v;
+}
+
+// maximum over the wave, in every lane
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+    v = max_dpp_u64<0xB1>(v);   // quad_perm(1,0,3,2): lane ^ 1
+    v = max_dpp_u64<0x4E>(v);   // quad_perm(2,3,0,1): lane ^ 2
+    v = max_dpp_u64<0x141>(v);  // row_half_mirror: the other quad of each 8
+    v = max_dpp_u64<0x140>(v);  // row_mirror: the other 8 of each 16
+#pragma unroll
+    for (int d = 16; d <= 32; d <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, d);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int lane_i32(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ __forceinline__ float lane_f32(float v, int j) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
+constexpr int K2T_WAVES = 16;
+
+// NC: logit candidates per lane (E <= 64 NC); NI: order entries per lane (C <= 16 * 64 NI)
+template <int NC, int NI>
+__global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const int32_t* order_in,
+                                                                 int32_t* order_out) {
+    __shared__ int32_t s_slot[64 * NC];          // this layer's slot-table entries
+    __shared__ uint32_t s_hbits[K2_MAXC / 32];   // hit slots
+    __shared__ int32_t s_vict[16], s_vkey[16];   // victims and their occupants, by miss rank
+    __shared__ int s_cnt[K2T_WAVES];
+    __shared__ uint64_t s_vmask;                 // order positions (< k) taken as victims
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int E = a.E, C = a.C, l = a.layer, k = a.k;
+
+    // every wave: its slice of the LRU order
+    int ent[NI];
+    const int pw = wv * 64 * NI + lane;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ent[i] = pw + 64 * i < C ? order_in[pw + 64 * i] : -1;
+
+    if (wv == 0) {
+        // loads that do not depend on the routing first
+        float zc[NC];
+        int so[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = lane + 64 * c;
+            zc[c] = e < E ? a.z[e] : 0.0f;
+            so[c] = e < E ? a.c.slot_of[l * E + e] : -1;
+        }
+        const int oj = lane < k ? order_in[lane] : -1;
+        const int64_t clock0 = *a.c.clock;
+        const int64_t trace_base = (int64_t)a.c.trace_head[0];
+        for (int i = lane; i < (C + 31) / 32; i += 64) s_hbits[i] = 0u;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (lane + 64 * c < E) s_slot[lane + 64 * c] = so[c];
+        const int okey = oj >= 0 ? a.c.key_of[oj] : -1;
+
+        // top-k on (logit desc, expert asc); lane j < k ends with rank j
+        uint64_t key[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = lane + 64 * c;
+            key[c] = e < E ? topk_key(zc[c], e) : 0ull;
+        }
+        int my_id = 0;
+        uint64_t my_key = 0;
+        for (int j = 0; j < k; ++j) {
+            uint64_t best = 0;
+            int bc = -1;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (key[c] > best) {
+                    best = key[c];
+                    bc = c;
+                }
+            const uint64_t wbest = wave_max_u64_dpp(best);
+            if (bc >= 0 && best == wbest) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    if (c == bc) key[c] = 0;
+            }
+            if (lane == j) {
+                my_id = (int)(0xFFFFFFFFu - (uint32_t)(wbest & 0xFFFFFFFFu));
+                my_key = wbest;
+            }
+        }
+        // softmax over the k selected logits, summed in rank order
+        const bool sel = lane < k;
+        const float zj = sel ? topk_key_logit(my_key) : 0.0f;
+        const float z0 = lane_f32(zj, 0);
+        const float ej = sel ? expf(zj - z0) : 0.0f;
+        float den = 0.0f;
+        for (int j = 0; j < k; ++j) den += lane_f32(ej, j);
+        const float wj = ej / den;
+
+        // hits and misses; ranks by ascending expert id within each
+        __builtin_amdgcn_wave_barrier();
+        const int vj = sel ? s_slot[my_id] : -1;
+        const bool hit = sel && vj >= 0, miss = sel && vj < 0;
+        const uint64_t hm = __ballot(hit), mm = __ballot(miss);
+        const int nh = __popcll(hm), nm = __popcll(mm);
+        int hr = 0, mr = 0;
+        bool ohit = false;  // order entry oj is a hit slot
+        for (int i = 0; i < k; ++i) {
+            const bool lower = lane_i32(my_id, i) < my_id;
+            hr += (((hm >> i) & 1ull) && lower) ? 1 : 0;
+            mr += (((mm >> i) & 1ull) && lower) ? 1 : 0;
+            ohit |= ((hm >> i) & 1ull) && lane_i32(vj, i) == oj;
+        }
+        if (hit) atomicOr(&s_hbits[vj >> 5], 1u << (vj & 31));
+        // victims: the first nm order entries that are not hit slots
+        const bool keep = lane < k && !ohit;
+        const int kr = __popcll(__ballot(keep) & ((1ull << lane) - 1ull));
+        const bool victim = keep && kr < nm;
+        const uint64_t vmask = __ballot(victim);
+        if (victim) {
+            s_vict[kr] = oj;
+            s_vkey[kr] = okey;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int slot = hit ? vj : (miss ? s_vict[mr] : -1);
+        const int old = miss ? s_vkey[mr] : -1;
+
+        // publish the miss list: one system-scope fence, then the sequence number
+        if (miss) {
+            a.ml->e[mr].expert = my_id;
+            a.ml->e[mr].slot = slot;
+        }
+        if (sel) {
+            a.ml->slot0[lane] = slot;
+            a.ml->w0[lane] = wj;
+        }
+        if (lane == 0) {
+            a.ml->n_miss = nm;
+            a.ml->n_unique = nh + nm;
+            a.ml->n_invalid = 0;
+        }
+        __threadfence_system();
+        if (lane == 0) __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+
+        // bookkeeping
+        const int n_evict = __popcll(__ballot(miss && old >= 0));
+        if (sel) {
+            a.ids[lane] = my_id;
+            a.w[lane] = wj;
+            if (a.ids_out) a.ids_out[lane] = my_id;
+            if (a.w_out) a.w_out[lane] = wj;
+            a.slots[lane] = slot;
+            if (a.slots_out) a.slots_out[lane] = slot;
+            const int rank = hit ? hr : nh + mr;
+            a.c.stamp[slot] = clock0 + rank;
+            order_out[C - nh - nm + rank] = slot;  // hits by hit rank, then misses by miss rank
+            const int64_t ti = trace_base + rank;
+            if (ti < a.c.trace_cap) {
+                TraceRec t = {a.step, l, my_id, slot, hit ? 1 : 0, hit ? -1 : old};
+                a.c.trace[ti] = t;
+            }
+        }
+        if (miss) {
+            if (old >= 0) a.c.slot_of[old] = -1;
+            a.c.key_of[slot] = l * E + my_id;
+            a.c.slot_of[l * E + my_id] = slot;
+        }
+        if (lane == 0) {
+            const int n = nh + nm;
+            *a.c.clock = clock0 + n;
+            a.c.counters[0] += (uint64_t)nh;
+            a.c.counters[1] += (uint64_t)nm;
+            a.c.counters[2] += (uint64_t)n_evict;
+            a.c.counters[3] += 1ull;
+            int64_t fit = a.c.trace_cap - trace_base;
+            fit = fit < 0 ? 0 : (fit > n ? n : fit);
+            a.c.trace_head[0] = (uint64_t)(trace_base + fit);
+            a.c.trace_head[1] += (uint64_t)(n - fit);
+            a.ml->n_evict = n_evict;
+            s_vmask = vmask;
+        }
+    }
+    __syncthreads();
+
+    // order compaction: entries that are neither hit slots nor victims keep their order
+    const uint64_t vm = s_vmask;
+    uint64_t km[NI];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int p = pw + 64 * i, sl = ent[i], slc = sl < 0 ? 0 : sl;
+        const bool hbit = (s_hbits[slc >> 5] >> (slc & 31)) & 1u;
+        const bool rm = sl < 0 || hbit || (p < 64 && ((vm >> p) & 1ull));
+        km[i] = __ballot(!rm);
+        cnt += __popcll(km[i]);
+    }
+    if (lane == 0) s_cnt[wv] = cnt;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wv; ++w) base += s_cnt[w];
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        if ((km[i] >> lane) & 1ull) order_out[base + __popcll(km[i] & below)] = ent[i];
+        base += __popcll(km[i]);
+    }
+}
+
+template <int NC>
+void launch_k2_tok(const K2Args& a, const int32_t* order_in, int32_t* order_out, hipStream_t st) {
+    const dim3 g(1), b(K2T_WAVES * 64);
+    const int per_wave = (a.C + K2T_WAVES - 1) / K2T_WAVES;
+    if (per_wave <= 64 * 2)
+        hipLaunchKernelGGL((k2_resolve_tok<NC, 2>), g, b, 0, st, a, order_in, order_out);
+    else if (per_wave <= 64 * 4)
+        hipLaunchKernelGGL((k2_resolve_tok<NC, 4>), g, b, 0, st, a, order_in, order_out);
+    else if (per_wave <= 64 * 8)
+        hipLaunchKernelGGL((k2_resolve_tok<NC, 8>), g, b, 0, st, a, order_in, order_out);
+    else
+        hipLaunchKernelGGL((k2_resolve_tok<NC, 16>), g, b, 0, st, a, order_in, order_out);
 }
 
 // top-k + softmax of many tokens, one wave per token, ahead of the resolve
@@ -463,6 +703,16 @@ int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void
         K2Args r = a;
         r.z = nullptr;  // resolve the ids just written
         hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, st, r, order_in, order_out);
+    } else if (a.z && a.B == 1 && a.n_ids == a.k && a.policy == 0) {
+        // one routed token: the wave-level resolve
+        if (a.E <= 128)
+            launch_k2_tok<2>(a, order_in, order_out, st);
+        else if (a.E <= 256)
+            launch_k2_tok<4>(a, order_in, order_out, st);
+        else if (a.E <= 512)
+            launch_k2_tok<8>(a, order_in, order_out, st);
+        else
+            launch_k2_tok<16>(a, order_in, order_out, st);
     } else {
         hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, st, a, order_in, order_out);
     }

@@ -57,7 +57,7 @@ struct MissEntry {
 struct MissList {
     volatile int64_t seq;      // written last (system-scope release) by the resolve kernel
     int32_t n_miss, n_unique;
-    int32_t n_evict, n_invalid;  // n_invalid: ids outside [0, E) (ignored)
+    int32_t n_evict, n_invalid;  // n_evict: informational, written after seq; n_invalid: ids outside [0, E)
     int32_t slot0[16];         // slots of token 0's k experts (ranked)
     float w0[16];              // routing weights of token 0 (when the step was routed)
     MissEntry e[1];            // [n_miss], sized at allocation: min(max_tokens*k, E)
