@@ -249,6 +249,8 @@ def main():
     n_cp = max(8, int(2e9 // m.blob_bytes) + 1)
     h2d_meas = m.measure_h2d(m.blob_bytes, n_cp)
     h2d_big = m.measure_h2d(64 << 20, 32)
+    # backend calibration: B_P (blob copies) vs B_H (host expert kernel on this process's cores)
+    calib = m.calibrate_backend(min(16, len(os.sched_getaffinity(0))), host_seconds=2.0)
 
     B, L, H = wl.n_requests, wl.n_layers, wl.hidden
     cs = m.compute_stream
@@ -380,6 +382,7 @@ def main():
                    "pool_GB": round(wl.pool * m.blob_bytes / 1e9, 2), "batch": B, "lookahead": args.lookahead,
                    "policy": args.policy},
         "roofline": roof,
+        "backend_calibration": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in calib.items()},
         "cpu_baseline": cpu,
         **extra,
     }

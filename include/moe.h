@@ -223,6 +223,63 @@ moe_status moe_measure_h2d(moe_ctx* ctx, size_t bytes_per_copy, int32_t n_copies
  * [L*E], key_of [C], stamp [C].  Synchronises the compute stream. */
 moe_status moe_cache_state(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, int64_t* stamp);
 
+/* ---- backend calibration and the hybrid split ----
+ * FreeToken's hybrid backend splits a step's m missing experts between PCIe
+ * transfers and host-side computation so that both finish together; its auto
+ * mode keeps the offload backend unless a stored bandwidth profile shows the
+ * host expert kernel more than twice as fast as the PCIe transfers
+ * (ai-hardware-zukan.com page, section on the hybrid mode; pirouter.ai page,
+ * backend table).  B_P and B_H are measured with the real transfer path and
+ * the real host kernel for the weight format. */
+enum {
+    MOE_BACKEND_OFFLOAD = 0, /* every miss crosses PCIe into a GPU slot (what moe_*_forward run) */
+    MOE_BACKEND_HYBRID = 1,  /* part of the misses computed by the host kernel */
+};
+
+typedef struct {
+    double pcie_gbps;      /* B_P: blob-sized copies from the pinned pool, GB/s */
+    double host_gbps;      /* B_H: blob bytes per second through the host expert kernel */
+    double ratio;          /* B_H / B_P */
+    double threshold;      /* the ratio above which hybrid is recommended */
+    int32_t host_threads;  /* threads the host kernel ran with */
+    int32_t backend;       /* MOE_BACKEND_HYBRID iff ratio > threshold, else MOE_BACKEND_OFFLOAD */
+    char host_isa[16];     /* instruction set of the host kernel: "avx512" or "scalar" */
+} moe_bw_profile;
+
+/* Measures B_P (moe_measure_h2d on >= 2 GB of blob-sized copies) and B_H (the
+ * host expert kernel on host_threads threads for about host_seconds, over 64
+ * blobs spread across the pool) and recommends a backend with the given
+ * threshold (the pages' default is 2.0).  Leaves the cache untouched.
+ * Errors: MOE_EINVAL (arguments), MOE_ESTATE, MOE_EHIP. */
+moe_status moe_calibrate_backend(moe_ctx* ctx, int32_t host_threads, double host_seconds, double threshold,
+                                 moe_bw_profile* out);
+
+/* The auto rule: MOE_BACKEND_HYBRID when host_gbps > threshold * pcie_gbps
+ * (and pcie_gbps > 0), else MOE_BACKEND_OFFLOAD.  Pure function. */
+int32_t moe_select_backend(double pcie_gbps, double host_gbps, double threshold);
+
+/* Transfers q of n_miss missing experts in the hybrid split (the rest go to the
+ * host kernel): with the host's bandwidth left over during the DMA taken as
+ * B_H - B_P, equal finishing times q / B_P = (n_miss - q) / (B_H - B_P) give
+ * q = n_miss * B_P / B_H, rounded to nearest (halves up); all n_miss when
+ * B_H <= B_P.  Pure function; 0 for n_miss <= 0. */
+int32_t moe_hybrid_split(int32_t n_miss, double pcie_gbps, double host_gbps);
+
+/* The host expert kernel: y[H] (FP32, host) = sum_j w[j] * FFN_j(x) over n
+ * experts given as blobs in the pool's layout (host memory; moe_pack_blob
+ * converts a logical blob), x[H] bf16 (host).  SwiGLU as on the GPU: FP32
+ * accumulation, the intermediate vector rounded to bf16.  Experts are shared
+ * out over `threads` host threads.  This is the kernel the calibration times
+ * for B_H.  Needs no GPU.  Errors: MOE_EINVAL. */
+moe_status moe_host_expert_ffn(const moe_config* cfg, const uint8_t* const* blobs, const float* w, int32_t n,
+                               const uint16_t* x, float* y, int32_t threads);
+
+/* Converts one logical expert blob (gate codes, gate scales, up codes, up
+ * scales, down codes, down scales; 3 * H * I * 17/32 bytes) into the pool's
+ * layout (same size, a permutation of the bytes; packed != logical).  Needs no
+ * GPU.  Errors: MOE_EINVAL. */
+moe_status moe_pack_blob(const moe_config* cfg, const uint8_t* logical, uint8_t* packed);
+
 /* Frees everything the context owns (after synchronising both streams).  NULL is a no-op. */
 void moe_destroy(moe_ctx* ctx);
 /* Text of the context's last error; with ctx = NULL, of the last failed moe_init_pool on the

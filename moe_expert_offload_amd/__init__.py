@@ -66,6 +66,16 @@ _lib.moe_auto_cache_slots.restype = _st
 _lib.moe_auto_cache_slots.argtypes = [ctypes.POINTER(MoeConfig), ctypes.c_uint64, ctypes.c_uint64,
                                       ctypes.POINTER(_I32)]
 _lib.moe_init_pool.restype = _st
+_lib.moe_pack_blob.restype = _st
+_lib.moe_pack_blob.argtypes = [ctypes.POINTER(MoeConfig), _P, _P]
+_lib.moe_host_expert_ffn.restype = _st
+_lib.moe_host_expert_ffn.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _I32, _P, _P, _I32]
+_lib.moe_hybrid_split.restype = _I32
+_lib.moe_hybrid_split.argtypes = [_I32, ctypes.c_double, ctypes.c_double]
+_lib.moe_select_backend.restype = _I32
+_lib.moe_select_backend.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
+_lib.moe_calibrate_backend.restype = _st
+_lib.moe_calibrate_backend.argtypes = [_P, _I32, ctypes.c_double, ctypes.c_double, ctypes.c_void_p]
 _lib.moe_init_pool.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, ctypes.c_size_t, _P,
                                ctypes.c_size_t, _P, _P, ctypes.POINTER(_P)]
 _lib.moe_cache_resolve.restype = _st
@@ -87,7 +97,8 @@ _lib.moe_destroy.argtypes = [_P]
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = [_P]
 
-EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
+EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_hybrid_split",
+            "moe_select_backend", "moe_calibrate_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
             "moe_expert_forward", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
@@ -124,6 +135,51 @@ def auto_cache_slots(cfg: MoeConfig, free_bytes: int = 0, reserve_bytes: int = 0
     if st:
         raise MoeError(st, f"moe_auto_cache_slots (fits {out.value} slots)")
     return out.value
+
+
+MOE_BACKEND_OFFLOAD, MOE_BACKEND_HYBRID = 0, 1
+
+
+class MoeBwProfile(ctypes.Structure):
+    _fields_ = [("pcie_gbps", ctypes.c_double), ("host_gbps", ctypes.c_double), ("ratio", ctypes.c_double),
+                ("threshold", ctypes.c_double), ("host_threads", _I32), ("backend", _I32),
+                ("host_isa", ctypes.c_char * 16)]
+
+
+def pack_blob(cfg: MoeConfig, logical):
+    """Logical expert blob (numpy uint8) -> the pool's layout (moe_pack_blob)."""
+    import numpy as np
+    src = np.ascontiguousarray(logical, dtype=np.uint8)
+    dst = np.empty_like(src)
+    st = _lib.moe_pack_blob(ctypes.byref(cfg), src.ctypes.data, dst.ctypes.data)
+    if st:
+        raise MoeError(st, "moe_pack_blob")
+    return dst
+
+
+def host_expert_ffn(cfg: MoeConfig, packed_blobs, w, x, threads=1):
+    """Host expert kernel (moe_host_expert_ffn): float32 [H] = sum_j w[j] * FFN_j(x)."""
+    import numpy as np
+    blobs = [np.ascontiguousarray(b, dtype=np.uint8) for b in packed_blobs]
+    ptrs = (ctypes.c_void_p * max(len(blobs), 1))(*[b.ctypes.data for b in blobs])
+    wv = np.ascontiguousarray(w, dtype=np.float32)
+    xv = np.ascontiguousarray(x, dtype=np.uint16)
+    y = np.empty(cfg.hidden, dtype=np.float32)
+    st = _lib.moe_host_expert_ffn(ctypes.byref(cfg), ptrs, wv.ctypes.data, len(blobs), xv.ctypes.data,
+                                  y.ctypes.data, threads)
+    if st:
+        raise MoeError(st, "moe_host_expert_ffn")
+    return y
+
+
+def select_backend(pcie_gbps: float, host_gbps: float, threshold: float = 2.0) -> str:
+    """The auto rule (moe_select_backend): "hybrid" or "offload"."""
+    return "hybrid" if _lib.moe_select_backend(pcie_gbps, host_gbps, threshold) == MOE_BACKEND_HYBRID else "offload"
+
+
+def hybrid_split(n_miss: int, pcie_gbps: float, host_gbps: float) -> int:
+    """Misses that go over PCIe in the hybrid split (moe_hybrid_split)."""
+    return int(_lib.moe_hybrid_split(n_miss, pcie_gbps, host_gbps))
 
 
 def _ptr(t):
@@ -216,6 +272,14 @@ class OffloadMoE:
     def expert_forward(self, layer, x, slots, w, y):
         self._check(_lib.moe_expert_forward(self.ctx, layer, _ptr(x), x.shape[0], _ptr(slots), _ptr(w), _ptr(y)),
                     "moe_expert_forward")
+
+    def calibrate_backend(self, host_threads, host_seconds=2.0, threshold=2.0):
+        p = MoeBwProfile()
+        self._check(_lib.moe_calibrate_backend(self.ctx, host_threads, host_seconds, threshold, ctypes.byref(p)),
+                    "moe_calibrate_backend")
+        return {"pcie_GBps": p.pcie_gbps, "host_GBps": p.host_gbps, "ratio": p.ratio, "threshold": p.threshold,
+                "host_threads": p.host_threads, "host_isa": p.host_isa.decode(),
+                "backend": "hybrid" if p.backend == MOE_BACKEND_HYBRID else "offload"}
 
     def stats(self, trace_cap=0):
         import numpy as np

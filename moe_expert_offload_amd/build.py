@@ -25,8 +25,18 @@ FLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", "g++")
+# host-only C++ (no device code); vector paths are selected at run time per function
+CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"),
+            "-I", os.path.join(HERE, "csrc")]
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def host_sources():
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:
@@ -37,6 +47,13 @@ def build(verbose: bool = False) -> str:
         o = os.path.join(HERE, "_build", os.path.basename(s) + ".o")
         cmd = [HIPCC, *FLAGS, "-c", s, "-o", o]
         cmd.remove("-shared")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        objs.append(o)
+    for s in host_sources():
+        o = os.path.join(HERE, "_build", os.path.basename(s) + ".o")
+        cmd = [CXX, *CXXFLAGS, "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)

@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -29,6 +30,7 @@
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+#include "host_ffn.h"
 #include "stager.h"
 
 using namespace moe;
@@ -885,6 +887,68 @@ moe_status moe_measure_h2d(moe_ctx* c, size_t bytes, int32_t n_copies, double* g
     const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     HIPCHK(c, hipFree(scratch));
     *gbps = (double)bytes * n_copies / (ms * 1e-3) / 1e9;
+    return MOE_OK;
+}
+
+moe_status moe_pack_blob(const moe_config* cfg, const uint8_t* logical, uint8_t* packed) {
+    moe_status st = check_cfg(cfg, true);
+    if (st) return st;
+    if (!logical || !packed || logical == packed) return MOE_EINVAL;
+    repack(make_layout(cfg->hidden, cfg->inter), logical, packed);
+    return MOE_OK;
+}
+
+moe_status moe_host_expert_ffn(const moe_config* cfg, const uint8_t* const* blobs, const float* w, int32_t n,
+                               const uint16_t* x, float* y, int32_t threads) {
+    moe_status st = check_cfg(cfg, true);
+    if (st) return st;
+    if (n < 0 || (n > 0 && (!blobs || !w)) || !x || !y || threads < 1) return MOE_EINVAL;
+    for (int j = 0; j < n; ++j)
+        if (!blobs[j]) return MOE_EINVAL;
+    host_expert_ffn(make_layout(cfg->hidden, cfg->inter), blobs, w, n, x, y, threads);
+    return MOE_OK;
+}
+
+int32_t moe_hybrid_split(int32_t n_miss, double pcie_gbps, double host_gbps) {
+    if (n_miss <= 0) return 0;
+    if (!(host_gbps > pcie_gbps) || !(pcie_gbps > 0.0)) return n_miss;  // no host bandwidth left over
+    const double q = (double)n_miss * pcie_gbps / host_gbps;
+    const int32_t r = (int32_t)std::floor(q + 0.5);
+    return std::min(std::max(r, (int32_t)0), n_miss);
+}
+
+int32_t moe_select_backend(double pcie_gbps, double host_gbps, double threshold) {
+    return (pcie_gbps > 0.0 && host_gbps > threshold * pcie_gbps) ? MOE_BACKEND_HYBRID : MOE_BACKEND_OFFLOAD;
+}
+
+moe_status moe_calibrate_backend(moe_ctx* c, int32_t host_threads, double host_seconds, double threshold,
+                                 moe_bw_profile* out) {
+    if (!c || !out || host_threads < 1 || !(host_seconds > 0.0) || !(threshold > 0.0)) return MOE_EINVAL;
+    if (c->failed) return MOE_ESTATE;
+    memset(out, 0, sizeof *out);
+    const size_t blob = c->lay.blob_bytes;
+    // PCIe side: blob-sized copies from random offsets of the pinned pool (>= 2 GB)
+    double bp = 0.0;
+    const int n_cp = (int)std::max<size_t>(8, (size_t)(2e9 / (double)blob) + 1);
+    moe_status st = moe_measure_h2d(c, blob, n_cp, &bp);
+    if (st) return st;
+    // host side: the host expert kernel over blobs spread across the pool
+    const size_t n_sl = (size_t)c->cfg.n_layers * c->cfg.n_experts;
+    const int nb = (int)std::min<size_t>(n_sl, 64);
+    std::vector<const uint8_t*> blobs(nb);
+    uint64_t r = 0xD1B54A32D192ED03ull;
+    for (int i = 0; i < nb; ++i) {
+        r ^= r << 13; r ^= r >> 7; r ^= r << 17;
+        blobs[i] = c->blob_src((size_t)(r % n_sl));
+    }
+    const double bh = host_expert_rate(c->lay, blobs.data(), nb, host_threads, host_seconds) / 1e9;
+    out->pcie_gbps = bp;
+    out->host_gbps = bh;
+    out->ratio = bp > 0.0 ? bh / bp : 0.0;
+    out->threshold = threshold;
+    out->host_threads = host_threads;
+    out->backend = moe_select_backend(bp, bh, threshold);
+    snprintf(out->host_isa, sizeof out->host_isa, "%s", host_ffn_isa());
     return MOE_OK;
 }
 

@@ -23,6 +23,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if !defined(__HIPCC__) && !defined(__host__)
+#define __host__
+#define __device__
+#endif
+
 namespace moe {
 
 struct Layout {
