@@ -74,6 +74,11 @@ def lib():
         L.orc_cache_state.argtypes = [_P, _P, _P, _P]
         L.orc_cache_step.restype = ctypes.c_int
         L.orc_cache_step.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P, _P]
+        L.orc_cache_step_split.restype = ctypes.c_int
+        L.orc_cache_step_split.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, ctypes.c_double,
+                                           ctypes.c_double, _P, _P]
+        L.orc_cache_host.restype = ctypes.c_uint64
+        L.orc_cache_host.argtypes = [_P]
         L.orc_static_new.restype = _P
         L.orc_static_new.argtypes = [ctypes.c_int] * 4
         L.orc_static_free.argtypes = [_P]
@@ -177,11 +182,16 @@ class Cache:
             lib().orc_cache_free(self._h)
             self._h = None
 
-    def step(self, step: int, layer: int, ids):
+    def step(self, step: int, layer: int, ids, split=None):
+        """split = (pcie_GBps, host_GBps): a hybrid step (oracle.c, the hybrid split)."""
         ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
         slots = np.empty(ids.size, dtype=np.int32)
         rec = np.empty(max(1, min(ids.size, self.E)), dtype=TRACE_DTYPE)
-        n = lib().orc_cache_step(self._h, step, layer, _ptr(ids), ids.size, _ptr(slots), _ptr(rec))
+        if split is None:
+            n = lib().orc_cache_step(self._h, step, layer, _ptr(ids), ids.size, _ptr(slots), _ptr(rec))
+        else:
+            n = lib().orc_cache_step_split(self._h, step, layer, _ptr(ids), ids.size, float(split[0]),
+                                           float(split[1]), _ptr(slots), _ptr(rec))
         if n < 0:
             raise ValueError("step requests more distinct experts than the cache has slots")
         return slots, rec[:n].copy()
@@ -189,7 +199,8 @@ class Cache:
     def counters(self):
         c = np.empty(3, dtype=np.uint64)
         lib().orc_cache_counters(self._h, _ptr(c))
-        return {"hits": int(c[0]), "misses": int(c[1]), "evictions": int(c[2])}
+        return {"hits": int(c[0]), "misses": int(c[1]), "evictions": int(c[2]),
+                "host": int(lib().orc_cache_host(self._h))}
 
     def state(self):
         slot_of = np.empty(self.L * self.E, dtype=np.int32)
@@ -236,14 +247,15 @@ class StaticCache:
 
 
 # ------------------------------------------------------------ whole runs --
-def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=None):
+def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=None, split=None):
     """Routing and cache trace of a decode run.
 
     X: [T][B][H] bf16 bits (B lock-step requests); every layer of step t sees
     X[t] (the hidden state of a request is fed unchanged to every layer).
     Steps run in order t = 0..T-1, layers 0..L-1 inside a step.
     Returns dict with ids [T][L][B][k], w [T][L][B][k], slots [T][L][B][k],
-    trace (structured array), counters.
+    trace (structured array), counters.  split = (pcie_GBps, host_GBps) runs the hybrid
+    backend's cache steps (misses beyond the transferred share take no slot).
     """
     T, B, H = X.shape
     L, k = wl.n_layers, wl.top_k
@@ -258,7 +270,7 @@ def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=N
     recs = []
     for t in steps:
         for l in range(L):
-            s, r = cache.step(t, l, ids[t, l])
+            s, r = cache.step(t, l, ids[t, l], split)
             slots[t, l] = s.reshape(B, k)
             recs.append(r)
     return {"ids": ids, "w": w, "slots": slots,

@@ -177,6 +177,7 @@ typedef struct {
     int64_t* stamp;
     int64_t clock;
     uint64_t hits, misses, evictions;
+    uint64_t host;   /* misses left to the host in hybrid steps */
 } orc_cache;
 
 typedef struct {
@@ -202,6 +203,8 @@ void orc_cache_free(orc_cache* c) {
 void orc_cache_counters(const orc_cache* c, uint64_t* out3) {
     out3[0] = c->hits; out3[1] = c->misses; out3[2] = c->evictions;
 }
+
+uint64_t orc_cache_host(const orc_cache* c) { return c->host; }
 
 void orc_cache_state(const orc_cache* c, int32_t* slot_of, int32_t* key_of, int64_t* stamp) {
     if (slot_of) memcpy(slot_of, c->slot_of, sizeof(int32_t) * (size_t)c->L * c->E);
@@ -247,6 +250,76 @@ int orc_cache_step(orc_cache* c, int step, int layer, const int32_t* ids, int n,
         c->slot_of[layer * E + e] = v;
         c->stamp[v] = c->clock++;
         c->misses++;
+        orc_trace_rec r = {step, layer, e, v, 0, old};
+        trace[nrec++] = r;
+    }
+    for (int j = 0; j < n; ++j) slots_out[j] = c->slot_of[layer * E + ids[j]];
+    free(req);
+    return nrec;
+}
+
+/* The hybrid split (ai-hardware-zukan.com FreeToken vs Ollama page, section on
+ * the hybrid mode): of a step's m missing experts, q go over PCIe and m - q are
+ * computed by the host so that both finish together.  With PCIe bandwidth B_P,
+ * host expert bandwidth B_H and the host bandwidth left during the DMA taken
+ * as B_H - B_P, q / B_P = (m - q) / (B_H - B_P) gives q = m B_P / B_H; with
+ * B_H <= B_P nothing is left for the host and q = m.  Reading: q is rounded to
+ * the nearest integer (halves up).  */
+static int orc_split_q(int m, double pcie, double host) {
+    if (m <= 0) return 0;
+    if (!(host > pcie) || !(pcie > 0.0)) return m;
+    int q = (int)floor((double)m * pcie / host + 0.5);
+    return q < 0 ? 0 : (q > m ? m : q);
+}
+
+/* One hybrid step: as orc_cache_step, except that only the first q misses
+ * (ascending expert id) are transferred into cache slots; the other m - q are
+ * computed from host memory, take no slot and leave the cache as it was (no
+ * victim, no stamp); their records carry slot -1 and evicted key -1, and
+ * their slots_out entries are -1.  Reading: the transferred misses are the
+ * lowest expert ids, the order in which misses are taken. */
+int orc_cache_step_split(orc_cache* c, int step, int layer, const int32_t* ids, int n, double pcie,
+                         double host, int32_t* slots_out, orc_trace_rec* trace) {
+    const int E = c->E;
+    char* req = (char*)calloc((size_t)E, 1);
+    for (int j = 0; j < n; ++j) req[ids[j]] = 1;
+    int nreq = 0, m = 0;
+    for (int e = 0; e < E; ++e) {
+        nreq += req[e];
+        if (req[e] && c->slot_of[layer * E + e] < 0) ++m;
+    }
+    if (nreq > c->C) { free(req); return -1; }
+    const int q = orc_split_q(m, pcie, host);
+    int nrec = 0;
+    for (int e = 0; e < E; ++e) {           /* hits, ascending */
+        if (!req[e]) continue;
+        int32_t v = c->slot_of[layer * E + e];
+        if (v < 0) continue;
+        c->stamp[v] = c->clock++;
+        c->hits++;
+        orc_trace_rec r = {step, layer, e, v, 1, -1};
+        trace[nrec++] = r;
+    }
+    int mi = 0;
+    for (int e = 0; e < E; ++e) {           /* misses, ascending: q transferred, then host */
+        if (!req[e] || c->slot_of[layer * E + e] >= 0) continue;
+        c->misses++;
+        if (mi++ >= q) {
+            c->host++;
+            orc_trace_rec r = {step, layer, e, -1, 0, -1};
+            trace[nrec++] = r;
+            continue;
+        }
+        int32_t v = -1;
+        for (int s2 = 0; s2 < c->C; ++s2) if (c->key_of[s2] < 0) { v = s2; break; }
+        if (v < 0) {
+            for (int s2 = 0; s2 < c->C; ++s2) if (v < 0 || c->stamp[s2] < c->stamp[v]) v = s2;
+        }
+        int32_t old = c->key_of[v];
+        if (old >= 0) { c->slot_of[old] = -1; c->evictions++; }
+        c->key_of[v] = layer * E + e;
+        c->slot_of[layer * E + e] = v;
+        c->stamp[v] = c->clock++;
         orc_trace_rec r = {step, layer, e, v, 0, old};
         trace[nrec++] = r;
     }

@@ -2,13 +2,15 @@
 and a free-slot set, independent of the oracle's stamp-based implementation."""
 
 
-def simulate(L, E, C, steps):
-    """steps: list of (layer, ids).  Returns (records, slots per step, counters)."""
+def simulate(L, E, C, steps, transferred=None):
+    """steps: list of (layer, ids).  Returns (records, slots per step, counters).
+    transferred(m) -> q: a hybrid step, in which only the first q of the m misses (ascending
+    expert id) enter the cache; the others take no slot (slot -1) and change nothing."""
     recency = []          # keys, least recently used first
     where = {}            # key -> slot
     free = list(range(C))
     recs, slots_all = [], []
-    hits = misses = evictions = 0
+    hits = misses = evictions = host = 0
     for s, (layer, ids) in enumerate(steps):
         R = sorted(set(int(e) for e in ids))
         if len(R) > C:
@@ -21,8 +23,14 @@ def simulate(L, E, C, steps):
             recency.append(key)
             hits += 1
             recs.append((s, layer, e, where[key], 1, -1))
-        for e in miss_e:
+        q = len(miss_e) if transferred is None else transferred(len(miss_e))
+        for i, e in enumerate(miss_e):
             key = layer * E + e
+            if i >= q:
+                misses += 1
+                host += 1
+                recs.append((s, layer, e, -1, 0, -1))
+                continue
             if free:
                 v = min(free)
                 free.remove(v)
@@ -35,5 +43,6 @@ def simulate(L, E, C, steps):
             recency.append(key)
             misses += 1
             recs.append((s, layer, e, v, 0, old))
-        slots_all.append([where[layer * E + int(e)] for e in ids])
-    return recs, slots_all, {"hits": hits, "misses": misses, "evictions": evictions}, recency, where
+        slots_all.append([where.get(layer * E + int(e), -1) for e in ids])
+    return (recs, slots_all, {"hits": hits, "misses": misses, "evictions": evictions, "host": host}, recency,
+            where)
