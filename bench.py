@@ -204,6 +204,9 @@ def main():
     ap.add_argument("--cache-slots", default="config",
                     help="'config' (the workload's cache fraction), 'auto' (as many slots as free HBM holds, "
                          "whole pool at most), or a slot count")
+    ap.add_argument("--backend", choices=("offload", "hybrid", "auto"), default="offload",
+                    help="offload: every miss over PCIe; hybrid: the calibrated split between PCIe and host "
+                         "workers; auto: hybrid when the calibration says the host is more than twice as fast")
     ap.add_argument("--auto-reserve-gb", type=float, default=4.0,
                     help="HBM kept free by --cache-slots auto (the KV cache's share in a server)")
     args = ap.parse_args()
@@ -249,8 +252,13 @@ def main():
     n_cp = max(8, int(2e9 // m.blob_bytes) + 1)
     h2d_meas = m.measure_h2d(m.blob_bytes, n_cp)
     h2d_big = m.measure_h2d(64 << 20, 32)
-    # backend calibration: B_P (blob copies) vs B_H (host expert kernel on this process's cores)
-    calib = m.calibrate_backend(min(16, len(os.sched_getaffinity(0))), host_seconds=2.0)
+    # backend calibration: B_P (blob copies) vs B_H (the host expert kernel on the cores the host
+    # workers would use: all of this process's cores but the one driving the GPU)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))) - 1)
+    calib = m.calibrate_backend(workers, host_seconds=2.0)
+    backend = args.backend if args.backend != "auto" else calib["backend"]
+    if backend == "hybrid":
+        m.set_backend("hybrid", calib["pcie_GBps"], calib["host_GBps"], workers)
 
     B, L, H = wl.n_requests, wl.n_layers, wl.hidden
     cs = m.compute_stream
@@ -294,7 +302,8 @@ def main():
     c_all, _ = m.stats()
     # device and host counters are cumulative: take the timed region's share
     c = dict(c_all)
-    for key in ("hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "h2d_bounced"):
+    for key in ("hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "h2d_bounced", "host_experts",
+                "host_tasks"):
         c[key] = c_all[key] - c_warm[key]
     tok_s = K * B / dt
 
@@ -307,8 +316,15 @@ def main():
     ids_h = ids.cpu().numpy()
     slots_all = np.stack([slot_of[l * wl.n_experts + ids_h[l]] for l in range(L)]).astype(np.int32)
     layers = [l for l in range(L) if (slots_all[l] >= 0).all()]
-    assert layers, "no layer of the last step is fully resident"
-    slots_h = slots_all[layers]
+    if layers:
+        slots_h = slots_all[layers]
+    else:
+        # hybrid steps can leave no layer fully in slots: time the same kernels on distinct
+        # slots per layer (the kernels' time does not depend on the weights' values)
+        layers = list(range(L))
+        kk = slots_all.shape[-1]
+        slots_h = ((np.arange(L)[:, None, None] * kk + np.arange(kk)[None, None, :]) % wl.cache_slots
+                   ).astype(np.int32).repeat(B, axis=1)
     ffn_us = time_ffn_pass(m, xd[W_ + K - 1], layers, torch.from_numpy(slots_h).to(dev), wts[layers],
                            y[layers], args.ffn_rounds)
 
@@ -346,7 +362,15 @@ def main():
     extra["misses_per_step"] = round(c["misses"] / K, 2)
     extra["h2d_GB_per_step"] = round(c["h2d_bytes"] / K / 1e9, 4)
     miss_bytes_step = c["h2d_bytes"] / K
-    roof_step = 1.0 / max(L * bytes_layer / (HBM_PEAK_GBS * 1e9), miss_bytes_step / (h2d_meas * 1e9))
+    host_bytes_step = c["host_experts"] * m.blob_bytes / K
+    roof_step = 1.0 / max(L * bytes_layer / (HBM_PEAK_GBS * 1e9), miss_bytes_step / (h2d_meas * 1e9),
+                          host_bytes_step / (calib["host_GBps"] * 1e9))
+    if backend == "hybrid":
+        extra["host"] = {"workers": workers, "experts_per_step": round(c["host_experts"] / K, 2),
+                         "GB_per_step": round(host_bytes_step / 1e9, 4),
+                         "effective_GBps": round(c["host_experts"] * m.blob_bytes / dt / 1e9, 2),
+                         "calibrated_GBps": round(calib["host_GBps"], 2),
+                         "tasks_per_step": round(c["host_tasks"] / K, 2)}
     extra["decode_roofline_tok_s"] = round(roof_step * B, 1)
     extra["decode_frac_of_roofline"] = round(tok_s / (roof_step * B), 4)
 
@@ -380,7 +404,7 @@ def main():
         "config": {"workload": wl.name, "layers": L, "experts": wl.n_experts, "top_k": wl.top_k,
                    "shared": wl.n_shared, "hidden": H, "inter": wl.inter, "cache_slots": C, "cache_sizing": args.cache_slots,
                    "pool_GB": round(wl.pool * m.blob_bytes / 1e9, 2), "batch": B, "lookahead": args.lookahead,
-                   "policy": args.policy},
+                   "policy": args.policy, "backend": backend},
         "roofline": roof,
         "backend_calibration": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in calib.items()},
         "cpu_baseline": cpu,

@@ -201,6 +201,8 @@ typedef struct {
     double k3_ms, k4_ms;               /* ... summed durations of the FFN's first part (K3; grouped:
                                           grouping + gate/up) and second part (K4; grouped: down +
                                           combine), from HIP events */
+    uint64_t host_experts;             /* hybrid backend: misses computed by the host (included in misses) */
+    uint64_t host_tasks;               /* hybrid backend: layer steps with a host share */
 } moe_counters;
 
 typedef struct {
@@ -253,6 +255,23 @@ typedef struct {
  * Errors: MOE_EINVAL (arguments), MOE_ESTATE, MOE_EHIP. */
 moe_status moe_calibrate_backend(moe_ctx* ctx, int32_t host_threads, double host_seconds, double threshold,
                                  moe_bw_profile* out);
+
+/* Selects the backend of the context's later one-token steps.
+ * MOE_BACKEND_OFFLOAD (default): every miss is transferred.
+ * MOE_BACKEND_HYBRID: in a routed one-token step (moe_stack_forward or
+ *   moe_layer_forward with n_tokens 1) the resolve kernel transfers only the
+ *   first q = moe_hybrid_split(m, pcie_gbps, host_gbps) of the step's m misses
+ *   (ascending expert id) into cache slots; the other m - q take no slot,
+ *   leave the cache unchanged (their trace records carry slot -1) and are
+ *   computed by host_threads persistent host workers (the host expert kernel,
+ *   each expert split over all workers), reading the pool; the down kernel adds
+ *   their weighted sum before rounding.  The token's hidden states are copied
+ *   to the host once per call.  Batches and moe_cache_resolve stay offload.
+ *   The workers spin between tasks and sleep after 20 ms idle.
+ * Needs the LRU policy.  Synchronises the compute stream.
+ * Errors: MOE_EINVAL (backend, bandwidths <= 0, threads outside 1..256,
+ * static policy), MOE_ENOMEM, MOE_ESTATE, MOE_EHIP. */
+moe_status moe_set_backend(moe_ctx* ctx, int32_t backend, double pcie_gbps, double host_gbps, int32_t host_threads);
 
 /* The auto rule: MOE_BACKEND_HYBRID when host_gbps > threshold * pcie_gbps
  * (and pcie_gbps > 0), else MOE_BACKEND_OFFLOAD.  Pure function. */

@@ -43,7 +43,8 @@ class MoeCounters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "trace_records",
         "trace_dropped", "ffn_launches", "h2d_bounced", "pool_pinned_bytes")] + [
-        ("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double)]
+        ("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double),
+        ("host_experts", ctypes.c_uint64), ("host_tasks", ctypes.c_uint64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -72,6 +73,8 @@ _lib.moe_host_expert_ffn.restype = _st
 _lib.moe_host_expert_ffn.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _I32, _P, _P, _I32]
 _lib.moe_hybrid_split.restype = _I32
 _lib.moe_hybrid_split.argtypes = [_I32, ctypes.c_double, ctypes.c_double]
+_lib.moe_set_backend.restype = _st
+_lib.moe_set_backend.argtypes = [_P, _I32, ctypes.c_double, ctypes.c_double, _I32]
 _lib.moe_select_backend.restype = _I32
 _lib.moe_select_backend.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
 _lib.moe_calibrate_backend.restype = _st
@@ -98,7 +101,7 @@ _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = [_P]
 
 EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_hybrid_split",
-            "moe_select_backend", "moe_calibrate_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
+            "moe_select_backend", "moe_calibrate_backend", "moe_set_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
             "moe_expert_forward", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
@@ -272,6 +275,11 @@ class OffloadMoE:
     def expert_forward(self, layer, x, slots, w, y):
         self._check(_lib.moe_expert_forward(self.ctx, layer, _ptr(x), x.shape[0], _ptr(slots), _ptr(w), _ptr(y)),
                     "moe_expert_forward")
+
+    def set_backend(self, backend, pcie_gbps=0.0, host_gbps=0.0, host_threads=1):
+        """backend "offload" or "hybrid" (moe_set_backend)."""
+        b = {"offload": MOE_BACKEND_OFFLOAD, "hybrid": MOE_BACKEND_HYBRID}[backend]
+        self._check(_lib.moe_set_backend(self.ctx, b, pcie_gbps, host_gbps, host_threads), "moe_set_backend")
 
     def calibrate_backend(self, host_threads, host_seconds=2.0, threshold=2.0):
         p = MoeBwProfile()

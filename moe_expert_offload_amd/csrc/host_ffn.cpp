@@ -25,6 +25,20 @@
 #include "moe_internal.h"
 
 namespace moe {
+
+// per-call buffers: x and a split into even / odd elements of each 32-block
+struct Work {
+    std::vector<float> xe, xo, ae, ao, g, u;
+    void size(const Layout& L) {
+        xe.assign((size_t)L.NB * 16, 0.0f);
+        xo.assign((size_t)L.NB * 16, 0.0f);
+        ae.assign((size_t)L.NBI * 16, 0.0f);
+        ao.assign((size_t)L.NBI * 16, 0.0f);
+        g.assign(L.I, 0.0f);
+        u.assign(L.I, 0.0f);
+    }
+};
+
 namespace {
 
 const float kE2M1[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
@@ -58,19 +72,6 @@ inline float round_bf16(float f) {
 
 inline float silu_mul(float g, float u) { return g / (1.0f + std::exp(-g)) * u; }
 
-// per-call buffers: x and a split into even / odd elements of each 32-block
-struct Work {
-    std::vector<float> xe, xo, ae, ao, g, u;
-    void size(const Layout& L) {
-        xe.assign((size_t)L.NB * 16, 0.0f);
-        xo.assign((size_t)L.NB * 16, 0.0f);
-        ae.assign((size_t)L.NBI * 16, 0.0f);
-        ao.assign((size_t)L.NBI * 16, 0.0f);
-        g.assign(L.I, 0.0f);
-        u.assign(L.I, 0.0f);
-    }
-};
-
 void split_even_odd(const float* v, int n_blocks, float* ev, float* od) {
     for (int b = 0; b < n_blocks; ++b)
         for (int i = 0; i < 16; ++i) {
@@ -89,10 +90,10 @@ float dot_block_scalar(const uint8_t* codes, const float* ev, const float* od) {
     return s;
 }
 
-void gate_up_scalar(const Layout& L, const uint8_t* blob, Work& wk) {
+void gate_up_scalar(const Layout& L, const uint8_t* blob, Work& wk, int t_begin, int t_end) {
     int b0[16];
     for (int s = 0; s < 16; ++s) b0[s] = seg_begin(L.NB, 16, s);
-    for (int tile = 0; tile < L.I / 16; ++tile) {
+    for (int tile = t_begin; tile < t_end; ++tile) {
         const uint8_t* tb = blob + (size_t)tile * 16 * L.NB * 34;
         const uint8_t* ub = tb + (size_t)16 * L.NB * 16;
         const uint8_t* sc = tb + (size_t)16 * L.NB * 32;
@@ -112,10 +113,11 @@ void gate_up_scalar(const Layout& L, const uint8_t* blob, Work& wk) {
     }
 }
 
-void down_scalar(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y) {
+void down_scalar(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y, int t_begin,
+                 int t_end) {
     const uint8_t* dc = blob + L.d_codes_off;
     const uint8_t* ds = blob + L.d_scales_off;
-    for (int t8 = 0; t8 < L.H / 8; ++t8) {
+    for (int t8 = t_begin; t8 < t_end; ++t8) {
         float acc[8] = {};
         for (int ib = 0; ib < L.NBI; ++ib)
             for (int r = 0; r < 8; ++r) {
@@ -136,11 +138,11 @@ MOE_AVX512 inline __m512 dot_block_v(const uint8_t* codes, __m512 lut, __m512 ev
     return _mm512_fmadd_ps(hi, od, _mm512_mul_ps(lo, ev));
 }
 
-MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, Work& wk) {
+MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, Work& wk, int t_begin, int t_end) {
     const __m512 lut = _mm512_loadu_ps(kE2M1);
     int b0[16];
     for (int s = 0; s < 16; ++s) b0[s] = seg_begin(L.NB, 16, s);
-    for (int tile = 0; tile < L.I / 16; ++tile) {
+    for (int tile = t_begin; tile < t_end; ++tile) {
         const uint8_t* tb = blob + (size_t)tile * 16 * L.NB * 34;
         const uint8_t* sc = tb + (size_t)16 * L.NB * 32;
         // gate rows from the gate codes, then up rows from the parallel up codes
@@ -165,11 +167,12 @@ MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, Work& wk) {
     }
 }
 
-MOE_AVX512 void down_avx512(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y) {
+MOE_AVX512 void down_avx512(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y,
+                            int t_begin, int t_end) {
     const __m512 lut = _mm512_loadu_ps(kE2M1);
     const uint8_t* dc = blob + L.d_codes_off;
     const uint8_t* ds = blob + L.d_scales_off;
-    for (int t8 = 0; t8 < L.H / 8; ++t8) {
+    for (int t8 = t_begin; t8 < t_end; ++t8) {
         __m512 acc[8];
         for (int r = 0; r < 8; ++r) acc[r] = _mm512_setzero_ps();
         for (int ib = 0; ib < L.NBI; ++ib) {
@@ -192,15 +195,31 @@ bool have_avx512() {
     return ok && !(force && force[0] == '1');
 }
 
+void gate_up_rows(const Layout& L, const uint8_t* blob, Work& wk, int t_begin, int t_end, bool vec) {
+    if (vec) gate_up_avx512(L, blob, wk, t_begin, t_end);
+    else gate_up_scalar(L, blob, wk, t_begin, t_end);
+}
+
+void down_rows(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y, int t_begin, int t_end,
+               bool vec) {
+    if (vec) down_avx512(L, blob, wk, w, y, t_begin, t_end);
+    else down_scalar(L, blob, wk, w, y, t_begin, t_end);
+}
+
+// the intermediate vector of 32-blocks [b_begin, b_end): bf16(silu(g) * u), split even / odd
+void activation_blocks(const Work& src, Work& dst, int b_begin, int b_end) {
+    for (int b = b_begin; b < b_end; ++b)
+        for (int i = 0; i < 16; ++i) {
+            dst.ae[b * 16 + i] = round_bf16(silu_mul(src.g[b * 32 + 2 * i], src.u[b * 32 + 2 * i]));
+            dst.ao[b * 16 + i] = round_bf16(silu_mul(src.g[b * 32 + 2 * i + 1], src.u[b * 32 + 2 * i + 1]));
+        }
+}
+
 // one expert for one token: y += w * down(silu(gate x) * (up x))
 void expert_one(const Layout& L, const uint8_t* blob, float w, Work& wk, float* y, bool vec) {
-    if (vec) gate_up_avx512(L, blob, wk);
-    else gate_up_scalar(L, blob, wk);
-    std::vector<float> a(L.I);
-    for (int i = 0; i < L.I; ++i) a[i] = round_bf16(silu_mul(wk.g[i], wk.u[i]));
-    split_even_odd(a.data(), L.NBI, wk.ae.data(), wk.ao.data());
-    if (vec) down_avx512(L, blob, wk, w, y);
-    else down_scalar(L, blob, wk, w, y);
+    gate_up_rows(L, blob, wk, 0, L.I / 16, vec);
+    activation_blocks(wk, wk, 0, L.NBI);
+    down_rows(L, blob, wk, w, y, 0, L.H / 8, vec);
 }
 
 }  // namespace
@@ -229,6 +248,137 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
     for (auto& th : pool) th.join();
     for (int t = 0; t < threads; ++t)
         for (int i = 0; i < L.H; ++i) y[i] += part[t][i];
+}
+
+// ------------------------------------------------------------- worker pool --
+
+HostExpertPool::~HostExpertPool() { stop(); }
+
+bool HostExpertPool::start(int n_workers) {
+    stop();
+    if (n_workers < 1) return false;
+    n_ = n_workers;
+    quit_.store(false);
+    gen_.store(0);
+    done_.store(0);
+    bar_count_.store(0);
+    bar_gen_.store(0);
+    work_.assign(n_, nullptr);
+    for (int t = 0; t < n_; ++t) work_[t] = new Work();
+    shared_ = new Work();
+    try {
+        for (int t = 0; t < n_; ++t) threads_.emplace_back(&HostExpertPool::run, this, t);
+    } catch (...) {
+        stop();
+        return false;
+    }
+    return true;
+}
+
+void HostExpertPool::stop() {
+    if (!threads_.empty()) {
+        quit_.store(true);
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            gen_.fetch_add(1);
+        }
+        cv_.notify_all();
+        for (auto& th : threads_) th.join();
+        threads_.clear();
+    }
+    for (Work* w : work_) delete w;
+    work_.clear();
+    delete shared_;
+    shared_ = nullptr;
+    n_ = 0;
+}
+
+void HostExpertPool::submit(const Layout& L, const uint8_t* const* blobs, const float* w, int n, const uint16_t* x,
+                            float* y) {
+    task_.L = L;
+    task_.n = n < 16 ? n : 16;
+    for (int j = 0; j < task_.n; ++j) {
+        task_.blobs[j] = blobs[j];
+        task_.w[j] = w[j];
+    }
+    task_.x = x;
+    task_.y = y;
+    done_.store(0);
+    {
+        std::lock_guard<std::mutex> lk(mu_);
+        gen_.fetch_add(1, std::memory_order_release);
+    }
+    cv_.notify_all();
+}
+
+void HostExpertPool::wait() {
+    while (done_.load(std::memory_order_acquire) < n_) _mm_pause();
+}
+
+// all workers meet (spinning; the generation flips once everyone arrived)
+void HostExpertPool::barrier() {
+    const int g = bar_gen_.load(std::memory_order_acquire);
+    if (bar_count_.fetch_add(1, std::memory_order_acq_rel) == n_ - 1) {
+        bar_count_.store(0, std::memory_order_relaxed);
+        bar_gen_.store(g + 1, std::memory_order_release);
+    } else {
+        while (bar_gen_.load(std::memory_order_acquire) == g) _mm_pause();
+    }
+}
+
+void HostExpertPool::run(int t) {
+    const bool vec = have_avx512();
+    Work& wk = *work_[t];
+    int seen = 0;
+    for (;;) {
+        // spin for the next task for a while (decode steps arrive every few tens of
+        // microseconds), then sleep until one comes
+        const auto t0 = std::chrono::steady_clock::now();
+        int spins = 0;
+        while (gen_.load(std::memory_order_acquire) == seen) {
+            _mm_pause();
+            if ((++spins & 1023) == 0 &&
+                std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(20)) {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return gen_.load(std::memory_order_acquire) != seen; });
+            }
+        }
+        seen = gen_.load(std::memory_order_acquire);
+        if (quit_.load()) return;
+        const Layout& L = task_.L;
+        if ((int)wk.xe.size() != L.NB * 16 || (int)wk.g.size() != L.I) wk.size(L);
+        if (t == 0 && ((int)shared_->g.size() != L.I || (int)shared_->ae.size() != L.NBI * 16)) shared_->size(L);
+        // x split even / odd (every worker its own copy)
+        for (int b = 0; b < L.NB; ++b)
+            for (int i = 0; i < 16; ++i) {
+                wk.xe[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i]);
+                wk.xo[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i + 1]);
+            }
+        // rows of y this worker owns: row tiles [d0, d1) of 8; zero them
+        const int nt8 = L.H / 8, ngu = L.I / 16;
+        const int d0 = (int)((long)nt8 * t / n_), d1 = (int)((long)nt8 * (t + 1) / n_);
+        const int g0 = (int)((long)ngu * t / n_), g1 = (int)((long)ngu * (t + 1) / n_);
+        const int a0 = (int)((long)L.NBI * t / n_), a1 = (int)((long)L.NBI * (t + 1) / n_);
+        std::fill(task_.y + d0 * 8, task_.y + d1 * 8, 0.0f);
+        barrier();  // shared_ sized by worker 0
+        for (int j = 0; j < task_.n; ++j) {
+            // gate/up rows of this worker into the shared g / u
+            gate_up_rows(L, task_.blobs[j], wk, g0, g1, vec);
+            for (int i = g0 * 16; i < g1 * 16; ++i) {
+                shared_->g[i] = wk.g[i];
+                shared_->u[i] = wk.u[i];
+            }
+            barrier();
+            activation_blocks(*shared_, *shared_, a0, a1);
+            barrier();
+            // down rows of this worker: y rows [8 d0, 8 d1), summed over the experts in order
+            std::copy(shared_->ae.begin(), shared_->ae.end(), wk.ae.begin());
+            std::copy(shared_->ao.begin(), shared_->ao.end(), wk.ao.begin());
+            down_rows(L, task_.blobs[j], wk, task_.w[j], task_.y, d0, d1, vec);
+            barrier();  // the next expert overwrites the shared vectors
+        }
+        done_.fetch_add(1, std::memory_order_acq_rel);
+    }
 }
 
 double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int threads, double min_seconds) {

@@ -1,5 +1,11 @@
 // Host-CPU MXFP4 SwiGLU expert kernel (reads blobs in the pool's layout).
 #pragma once
+#include <atomic>
+#include <condition_variable>
+#include <mutex>
+#include <thread>
+#include <vector>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -17,5 +23,46 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
 // bytes of blob processed per second by `threads` threads running the kernel
 // over blobs[0..n) round robin for about min_seconds
 double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int threads, double min_seconds);
+
+struct Work;
+
+// Persistent host workers for the hybrid backend: one task at a time, y[H]
+// (FP32) = sum_j w[j] * FFN_j(x) over up to 16 experts, every expert split over
+// all workers by row tiles (gate/up tiles, then activation blocks, then down
+// row tiles, with a barrier between phases).  Each output row is summed by one
+// worker over the experts in order, so the result does not depend on the
+// worker count.  Workers spin between tasks and sleep after 20 ms idle.
+class HostExpertPool {
+public:
+    ~HostExpertPool();
+    bool start(int n_workers);
+    void stop();
+    bool running() const { return n_ > 0; }
+    int workers() const { return n_; }
+    // x (bf16, host) and y (FP32, host) must stay valid until wait() returns
+    void submit(const Layout& L, const uint8_t* const* blobs, const float* w, int n, const uint16_t* x, float* y);
+    void wait();
+
+private:
+    struct Task {
+        Layout L{};
+        const uint8_t* blobs[16] = {};
+        float w[16] = {};
+        int n = 0;
+        const uint16_t* x = nullptr;
+        float* y = nullptr;
+    };
+    void run(int t);
+    void barrier();
+    int n_ = 0;
+    Task task_;
+    std::vector<std::thread> threads_;
+    std::vector<Work*> work_;
+    Work* shared_ = nullptr;
+    std::atomic<int> gen_{0}, done_{0}, bar_count_{0}, bar_gen_{0};
+    std::atomic<bool> quit_{false};
+    std::mutex mu_;
+    std::condition_variable cv_;
+};
 
 }  // namespace moe

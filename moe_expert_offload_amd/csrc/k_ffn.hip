@@ -224,6 +224,13 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
     const bool tok = t8 < (a.H >> 3);
     const int tile = tok ? t8 : 0;
     const int r = lane & 7, s = w * 8 + (lane >> 3);
+    // host-computed experts' sum for the rows this thread writes, fetched first
+    // (host-mapped memory: a PCIe round trip that overlaps the weight stream)
+    float yhv = 0.0f;
+    if (a.yh && tid < 8 * R8) {
+        const int yr = (tile16 * R8 + (tid >> 3)) * 8 + (tid & 7);
+        if (yr < a.H) yhv = a.yh[(size_t)b * a.H + yr];
+    }
     const int nq = seg_len(Q, S, s), q0 = seg_begin(Q, S, s);
     // A segment (at most ceil(nE*NBI/32) <= NBI + 1 blocks, as nE <= 32)
     // spans at most two experts: j0 from block ib0 for `split` steps, then j0+1
@@ -279,6 +286,7 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
         float ys = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) ys += red[(sb * 4 + ww) * 8 + rr];
+        ys += yhv;
         const int tt8 = tile16 * R8 + sb;
         if (tt8 < (a.H >> 3)) a.y[(size_t)b * a.H + tt8 * 8 + rr] = f32_to_bf16(ys);
     }
@@ -303,6 +311,12 @@ __global__ __launch_bounds__(K4_THREADS) void k4_down(FfnArgs a) {
     ffn_down<T2, K4_SUBTILES>(a, smem, blockIdx.x, blockIdx.y);
 }
 
+// a layer step whose experts all ran on the host: y = bf16(yh)
+__global__ __launch_bounds__(256) void k_host_only_out(const float* yh, uint16_t* y, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = f32_to_bf16(yh[i]);
+}
+
 size_t ffn_lds_bytes(const Layout& L, int nE) {
     const size_t p1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
     const size_t p2 = (size_t)nE * L.NBI * 80 + 4 * K4_SUBTILES * 8 * 4;
@@ -311,6 +325,14 @@ size_t ffn_lds_bytes(const Layout& L, int nE) {
 
 int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid) {
     hipStream_t st = (hipStream_t)stream;
+    if (a.nE == 0) {
+        // no expert on the GPU (hybrid step, no shared expert): the host's sum is the output
+        if (!a.yh) return (int)hipErrorInvalidValue;
+        const int n = B * L.H;
+        if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
+        hipLaunchKernelGGL(k_host_only_out, dim3((n + 255) / 256), dim3(256), 0, st, a.yh, a.y, n);
+        return (int)hipGetLastError();
+    }
     a.P1 = a.nE * (L.I / 16);
     a.P2 = (L.H / 8 + K4_SUBTILES - 1) / K4_SUBTILES;
     const int T1 = L.T3;

@@ -382,9 +382,11 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
             const int id = ids_lds ? s_ids[tid] : a.ids[tid];
             a.ml->slot0[tid] = (unsigned)id < (unsigned)E ? s_req[id] : -1;
             a.ml->w0[tid] = a.z ? s_w0[tid] : 0.0f;
+            a.ml->ids0[tid] = id;
         }
         if (tid == 0) {
             a.ml->n_miss = nm;
+            a.ml->n_xfer = nm;
             a.ml->n_unique = nh + nm;
             a.ml->n_invalid = s_invalid;
         }
@@ -570,6 +572,14 @@ __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const
         const bool hit = sel && vj >= 0, miss = sel && vj < 0;
         const uint64_t hm = __ballot(hit), mm = __ballot(miss);
         const int nh = __popcll(hm), nm = __popcll(mm);
+        // hybrid split: the first q misses (ascending expert id) are transferred,
+        // q = m B_P / B_H to the nearest integer (halves up); all of them when the
+        // host has no bandwidth to spare
+        int q = nm;
+        if (a.hybrid && nm > 0 && a.bh > a.bp && a.bp > 0.0) {
+            q = (int)floor((double)nm * a.bp / a.bh + 0.5);
+            q = q < 0 ? 0 : (q > nm ? nm : q);
+        }
         int hr = 0, mr = 0;
         bool ohit = false;  // order entry oj is a hit slot
         for (int i = 0; i < k; ++i) {
@@ -579,18 +589,19 @@ __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const
             ohit |= ((hm >> i) & 1ull) && lane_i32(vj, i) == oj;
         }
         if (hit) atomicOr(&s_hbits[vj >> 5], 1u << (vj & 31));
-        // victims: the first nm order entries that are not hit slots
+        // victims: the first q order entries that are not hit slots
         const bool keep = lane < k && !ohit;
         const int kr = __popcll(__ballot(keep) & ((1ull << lane) - 1ull));
-        const bool victim = keep && kr < nm;
+        const bool victim = keep && kr < q;
         const uint64_t vmask = __ballot(victim);
         if (victim) {
             s_vict[kr] = oj;
             s_vkey[kr] = okey;
         }
         __builtin_amdgcn_wave_barrier();
-        const int slot = hit ? vj : (miss ? s_vict[mr] : -1);
-        const int old = miss ? s_vkey[mr] : -1;
+        const bool xfer = miss && mr < q;  // the other misses are computed by the host
+        const int slot = hit ? vj : (xfer ? s_vict[mr] : -1);
+        const int old = xfer ? s_vkey[mr] : -1;
 
         // publish the miss list: one system-scope fence, then the sequence number
         if (miss) {
@@ -600,9 +611,11 @@ __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const
         if (sel) {
             a.ml->slot0[lane] = slot;
             a.ml->w0[lane] = wj;
+            a.ml->ids0[lane] = my_id;
         }
         if (lane == 0) {
             a.ml->n_miss = nm;
+            a.ml->n_xfer = q;
             a.ml->n_unique = nh + nm;
             a.ml->n_invalid = 0;
         }
@@ -610,7 +623,7 @@ __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const
         if (lane == 0) __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 
         // bookkeeping
-        const int n_evict = __popcll(__ballot(miss && old >= 0));
+        const int n_evict = __popcll(__ballot(xfer && old >= 0));
         if (sel) {
             a.ids[lane] = my_id;
             a.w[lane] = wj;
@@ -619,26 +632,29 @@ __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const
             a.slots[lane] = slot;
             if (a.slots_out) a.slots_out[lane] = slot;
             const int rank = hit ? hr : nh + mr;
-            a.c.stamp[slot] = clock0 + rank;
-            order_out[C - nh - nm + rank] = slot;  // hits by hit rank, then misses by miss rank
+            if (hit || xfer) {
+                a.c.stamp[slot] = clock0 + rank;
+                order_out[C - nh - q + rank] = slot;  // hits by hit rank, then transfers by miss rank
+            }
             const int64_t ti = trace_base + rank;
             if (ti < a.c.trace_cap) {
-                TraceRec t = {a.step, l, my_id, slot, hit ? 1 : 0, hit ? -1 : old};
+                TraceRec t = {a.step, l, my_id, slot, hit ? 1 : 0, xfer ? old : -1};
                 a.c.trace[ti] = t;
             }
         }
-        if (miss) {
+        if (xfer) {
             if (old >= 0) a.c.slot_of[old] = -1;
             a.c.key_of[slot] = l * E + my_id;
             a.c.slot_of[l * E + my_id] = slot;
         }
         if (lane == 0) {
             const int n = nh + nm;
-            *a.c.clock = clock0 + n;
+            *a.c.clock = clock0 + nh + q;
             a.c.counters[0] += (uint64_t)nh;
             a.c.counters[1] += (uint64_t)nm;
             a.c.counters[2] += (uint64_t)n_evict;
             a.c.counters[3] += 1ull;
+            a.c.counters[4] += (uint64_t)(nm - q);
             int64_t fit = a.c.trace_cap - trace_base;
             fit = fit < 0 ? 0 : (fit > n ? n : fit);
             a.c.trace_head[0] = (uint64_t)(trace_base + fit);

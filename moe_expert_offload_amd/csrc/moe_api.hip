@@ -87,6 +87,20 @@ struct moe_ctx {
     uint64_t ffn_launches = 0;
     double k3_ms = 0, k4_ms = 0;
     std::vector<ProfSlot> prof_used, prof_free;
+    // hybrid backend: part of a one-token step's misses computed by host workers
+    int backend = MOE_BACKEND_OFFLOAD;
+    double hyb_bp = 0.0, hyb_bh = 0.0;   // B_P and B_H of the split
+    HostExpertPool hpool;
+    hipStream_t xs_stream = nullptr;     // device-to-host copies of the hidden states
+    hipEvent_t xs_start = nullptr, xs_done = nullptr;
+    uint16_t* xh = nullptr;              // pinned host copy of the call's hidden states
+    size_t xh_cap = 0;
+    int64_t xh_stride = 0;
+    bool xh_pending = false;
+    bool hyb_call = false;               // the current call runs hybrid steps
+    float* yh = nullptr;                 // host-mapped [2][H]: the host experts' sum per parity
+    bool host_pending[2] = {false, false};
+    uint64_t host_tasks = 0;
     double spin_timeout_s = 60.0;
     bool failed = false;
     std::string err;
@@ -166,7 +180,7 @@ StatePlan plan_state(const moe_config& c, int C) {
     p.key = off;   off = align_up(off + (size_t)C * 4, 256);
     p.stamp = off; off = align_up(off + (size_t)C * 8, 256);
     p.clock = off; off = align_up(off + 8, 256);
-    p.cnt = off;   off = align_up(off + 4 * 8, 256);
+    p.cnt = off;   off = align_up(off + 8 * 8, 256);
     p.th = off;    off = align_up(off + 2 * 8, 256);
     p.ord = off;   off = align_up(off + 2 * (size_t)C * 4, 256);
     p.tr = off;    off = align_up(off + std::max<size_t>((size_t)c.trace_capacity, 1) * sizeof(TraceRec), 256);
@@ -270,6 +284,13 @@ void free_all(moe_ctx* c) {
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev2) if (e) (void)hipEventDestroy(e);
     if (c->ps2) (void)hipStreamDestroy(c->ps2);
+    c->hpool.stop();
+    if (c->xs_stream) (void)hipStreamSynchronize(c->xs_stream);
+    if (c->xs_start) (void)hipEventDestroy(c->xs_start);
+    if (c->xs_done) (void)hipEventDestroy(c->xs_done);
+    if (c->xs_stream) (void)hipStreamDestroy(c->xs_stream);
+    if (c->xh) (void)hipHostFree(c->xh);
+    if (c->yh) (void)hipHostFree(c->yh);
     c->bounce.shutdown();
     if (c->pool) (void)hipHostFree(c->pool);
     free(c->pool_pg);
@@ -319,9 +340,38 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
     a.policy = c->cfg.policy;
     a.T = c->static_T;
     a.R = c->cfg.cache_slots - c->static_T;
+    a.hybrid = (c->hyb_call && routed && B == 1) ? 1 : 0;
+    a.bp = c->hyb_bp;
+    a.bh = c->hyb_bh;
     const int p = c->parity;
     LAUNCHCHK(c, launch_k2(a, c->order[p], c->order[p ^ 1], c->cs));
     c->parity = p ^ 1;
+    return MOE_OK;
+}
+
+// Hybrid steps need the token's hidden states on the host: one device-to-host
+// copy per call of the `layers` vectors at stride xs (elements), ordered after
+// everything already on the compute stream.  Only one-token calls with the LRU
+// policy run hybrid steps.
+moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
+    c->hyb_call = false;
+    if (c->backend != MOE_BACKEND_HYBRID || B != 1 || c->cfg.policy != MOE_POLICY_LRU || xs < 0) return MOE_OK;
+    const size_t bytes = ((size_t)(layers - 1) * (size_t)xs + (size_t)c->cfg.hidden) * 2;
+    if (bytes > c->xh_cap) {
+        if (c->xh) HIPCHK(c, hipHostFree(c->xh));
+        c->xh = nullptr;
+        c->xh_cap = 0;
+        if (hipHostMalloc((void**)&c->xh, bytes, 0) != hipSuccess)
+            return set_err(c, MOE_ENOMEM, "pinned buffer of %zu bytes for the hidden states", bytes);
+        c->xh_cap = bytes;
+    }
+    HIPCHK(c, hipEventRecord(c->xs_start, c->cs));
+    HIPCHK(c, hipStreamWaitEvent(c->xs_stream, c->xs_start, 0));
+    HIPCHK(c, hipMemcpyAsync(c->xh, x, bytes, hipMemcpyDeviceToHost, c->xs_stream));
+    HIPCHK(c, hipEventRecord(c->xs_done, c->xs_stream));
+    c->xh_pending = true;
+    c->xh_stride = xs;
+    c->hyb_call = true;
     return MOE_OK;
 }
 
@@ -345,17 +395,41 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         }
     }
     const int nm = ml->n_miss;
+    const int nx = ml->n_xfer;
     if (ml->n_invalid) return set_err(c, MOE_EINVAL, "%d expert ids outside [0, E)", ml->n_invalid);
     for (int j = 0; j < c->cfg.top_k; ++j) {
         c->tok0_slot[par][j] = ml->slot0[j];
         c->tok0_w[par][j] = ml->w0[j];
     }
     c->tok0_valid[par] = true;
+    if (nx < nm) {
+        // hybrid step: token 0's experts without a slot run on the host workers, in rank order
+        if (!c->hyb_call || !c->hpool.running())
+            return set_err(c, MOE_EINVAL, "host share in a step that is not hybrid");
+        if (c->xh_pending) {
+            HIPCHK(c, hipEventSynchronize(c->xs_done));
+            c->xh_pending = false;
+        }
+        const uint8_t* blobs[16];
+        float w[16];
+        int nh = 0;
+        for (int j = 0; j < c->cfg.top_k; ++j)
+            if (ml->slot0[j] < 0) {
+                blobs[nh] = c->blob_src((size_t)layer * c->cfg.n_experts + ml->ids0[j]);
+                w[nh++] = ml->w0[j];
+            }
+        c->hpool.submit(c->lay, blobs, w, nh, c->xh + (size_t)layer * c->xh_stride, c->yh + (size_t)par * c->cfg.hidden);
+        c->host_pending[par] = true;
+        ++c->host_tasks;
+    }
     const size_t blob = c->lay.blob_bytes;
     bool used[2] = {false, false};
     int nd = 0;  // direct copies so far: they alternate between the two copy streams
+    int ncopy = 0;
     for (int i = 0; i < nm; ++i) {
         const MissEntry m = ml->e[i];
+        if (m.slot < 0) continue;  // computed by the host
+        ++ncopy;
         const size_t idx = (size_t)layer * c->cfg.n_experts + m.expert;
         uint8_t* dst = c->arena + (size_t)m.slot * blob;
         if (idx < c->n_pin) {
@@ -372,9 +446,9 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     if (used[1]) HIPCHK(c, hipEventRecord(c->copy_ev2[par], c->ps2));
     c->copy_used[par][0] = used[0];
     c->copy_used[par][1] = used[1];
-    c->h2d_bytes += (uint64_t)nm * blob;
-    c->h2d_copies += (uint64_t)nm;
-    if (n_miss_out) *n_miss_out = nm;
+    c->h2d_bytes += (uint64_t)ncopy * blob;
+    c->h2d_copies += (uint64_t)ncopy;
+    if (n_miss_out) *n_miss_out = ncopy;
     return MOE_OK;
 }
 
@@ -390,6 +464,13 @@ moe_status get_prof(moe_ctx* c, ProfSlot& p) {
 
 moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par, void* y, int n_miss,
                             const int32_t* slots_dev = nullptr, const float* w_dev = nullptr) {
+    const float* yh = nullptr;
+    if (par < 2 && c->host_pending[par]) {
+        // the host experts of this step: their sum is added by the down kernel
+        c->hpool.wait();
+        c->host_pending[par] = false;
+        yh = c->yh + (size_t)par * c->cfg.hidden;
+    }
     if (n_miss > 0 && par < 2) {
         if (c->copy_used[par][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
         if (c->copy_used[par][1]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev2[par], 0));
@@ -463,11 +544,20 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
     f.I = c->cfg.inter;
     f.H = c->cfg.hidden;
     f.karg = (B == 1 && !slots_dev && par < 2 && c->tok0_valid[par]) ? 1 : 0;
-    if (f.karg)
-        for (int j = 0; j < c->cfg.top_k; ++j) {
-            f.kslot[j] = c->tok0_slot[par][j];
-            f.kw[j] = c->tok0_w[par][j];
-        }
+    if (f.karg) {
+        // the experts in GPU slots, in rank order (hybrid steps leave some to the host)
+        int kk = 0;
+        for (int j = 0; j < c->cfg.top_k; ++j)
+            if (c->tok0_slot[par][j] >= 0) {
+                f.kslot[kk] = c->tok0_slot[par][j];
+                f.kw[kk++] = c->tok0_w[par][j];
+            }
+        f.k = kk;
+        f.nE = kk + c->cfg.n_shared;
+        f.yh = yh;
+    } else if (yh) {
+        return set_err(c, MOE_EINVAL, "host share without the single-token launch path");
+    }
     LAUNCHCHK(c, launch_ffn(f, c->lay, B, c->cs, prof ? ps.ev[1] : nullptr));
     }
     if (prof) {
@@ -748,6 +838,7 @@ moe_status moe_layer_forward(moe_ctx* c, int32_t step, int32_t layer, const void
     moe_status st = check_call(c, n_tokens);
     if (st) return st;
     if (layer < 0 || layer >= c->cfg.n_layers || !x || !y) return set_err(c, MOE_EINVAL, "bad layer or buffers");
+    if ((st = hyb_begin(c, x, 0, 1, n_tokens))) return st;
     if ((st = launch_route(c, layer, x, n_tokens))) return st;
     if ((st = launch_resolve(c, step, layer, true, nullptr, n_tokens, 0, nullptr, ids_out, w_out))) return st;
     int nm = 0;
@@ -766,6 +857,7 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     auto yl = [&](int l) { return (uint16_t*)y + (size_t)l * ys; };
     auto idl = [&](int l) { return ids_out ? ids_out + (size_t)l * kB : nullptr; };
     auto wl = [&](int l) { return w_out ? w_out + (size_t)l * kB : nullptr; };
+    if ((st = hyb_begin(c, x, xs, L, n_tokens))) return st;
     if (c->cfg.lookahead == 0) {
         for (int l = 0; l < L; ++l) {
             if ((st = launch_route(c, l, xl(l), n_tokens))) return st;
@@ -811,7 +903,7 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
     if (c->failed) return MOE_ESTATE;
     HIPCHK(c, hipStreamSynchronize(c->cs));
     HIPCHK(c, hipStreamSynchronize(c->ps));
-    uint64_t cnt[4], th[2];
+    uint64_t cnt[5], th[2];
     HIPCHK(c, hipMemcpy(cnt, c->cd.counters, sizeof cnt, hipMemcpyDeviceToHost));
     HIPCHK(c, hipMemcpy(th, c->cd.trace_head, sizeof th, hipMemcpyDeviceToHost));
     size_t n = (size_t)th[0];
@@ -846,6 +938,8 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         out->pool_pinned_bytes = (uint64_t)(c->n_pin * c->lay.blob_bytes);
         out->k3_ms = c->k3_ms;
         out->k4_ms = c->k4_ms;
+        out->host_experts = cnt[4];
+        out->host_tasks = c->host_tasks;
     }
     c->ffn_launches = 0;
     c->k3_ms = c->k4_ms = 0;
@@ -915,6 +1009,36 @@ int32_t moe_hybrid_split(int32_t n_miss, double pcie_gbps, double host_gbps) {
     const double q = (double)n_miss * pcie_gbps / host_gbps;
     const int32_t r = (int32_t)std::floor(q + 0.5);
     return std::min(std::max(r, (int32_t)0), n_miss);
+}
+
+moe_status moe_set_backend(moe_ctx* c, int32_t backend, double pcie_gbps, double host_gbps, int32_t host_threads) {
+    if (!c) return MOE_EINVAL;
+    if (c->failed) return MOE_ESTATE;
+    HIPCHK(c, hipStreamSynchronize(c->cs));
+    if (backend == MOE_BACKEND_OFFLOAD) {
+        c->hpool.stop();
+        c->backend = MOE_BACKEND_OFFLOAD;
+        return MOE_OK;
+    }
+    if (backend != MOE_BACKEND_HYBRID || !(pcie_gbps > 0.0) || !(host_gbps > 0.0) || host_threads < 1 ||
+        host_threads > 256)
+        return set_err(c, MOE_EINVAL, "backend %d with B_P %g, B_H %g, %d threads", backend, pcie_gbps, host_gbps,
+                       host_threads);
+    if (c->cfg.policy != MOE_POLICY_LRU) return set_err(c, MOE_EINVAL, "the hybrid backend needs the LRU policy");
+    if (!c->yh && hipHostMalloc((void**)&c->yh, 2 * (size_t)c->cfg.hidden * sizeof(float),
+                                hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
+        return set_err(c, MOE_ENOMEM, "host-mapped buffer for the host experts' sums");
+    if (!c->xs_stream) {
+        HIPCHK(c, hipStreamCreateWithFlags(&c->xs_stream, hipStreamNonBlocking));
+        HIPCHK(c, hipEventCreateWithFlags(&c->xs_start, hipEventDisableTiming));
+        HIPCHK(c, hipEventCreateWithFlags(&c->xs_done, hipEventDisableTiming));
+    }
+    if (c->hpool.workers() != host_threads && !c->hpool.start(host_threads))
+        return set_err(c, MOE_ENOMEM, "could not start %d host workers", host_threads);
+    c->backend = MOE_BACKEND_HYBRID;
+    c->hyb_bp = pcie_gbps;
+    c->hyb_bh = host_gbps;
+    return MOE_OK;
 }
 
 int32_t moe_select_backend(double pcie_gbps, double host_gbps, double threshold) {

@@ -63,8 +63,10 @@ struct MissList {
     volatile int64_t seq;      // written last (system-scope release) by the resolve kernel
     int32_t n_miss, n_unique;
     int32_t n_evict, n_invalid;  // n_evict: informational, written after seq; n_invalid: ids outside [0, E)
-    int32_t slot0[16];         // slots of token 0's k experts (ranked)
+    int32_t slot0[16];         // slots of token 0's k experts (ranked); -1: computed by the host
     float w0[16];              // routing weights of token 0 (when the step was routed)
+    int32_t ids0[16];          // token 0's experts (ranked)
+    int32_t n_xfer;            // misses transferred (entries [0, n_xfer)); the rest have slot -1
     MissEntry e[1];            // [n_miss], sized at allocation: min(max_tokens*k, E)
 };
 
@@ -78,7 +80,7 @@ struct CacheDev {
     int32_t* key_of;      // [C]    key (layer*E + expert) or -1
     int64_t* stamp;       // [C]    last use or -1
     int64_t* clock;       // [1]
-    uint64_t* counters;   // [4] hits, misses, evictions, resolves
+    uint64_t* counters;   // [5] hits, misses, evictions, resolves, host-computed misses
     TraceRec* trace;      // [trace_cap]
     uint64_t* trace_head; // [2] records written (monotone), records dropped
     int64_t trace_cap;
@@ -106,6 +108,8 @@ struct K2Args {
     int n_ids, layer, step, E, C, k, B;
     int policy;             // 0: LRU; 1: static split (R resident keys, T transient slots)
     int R, T;
+    int hybrid;             // one-token LRU steps: transfer only q = round(nm * bp / bh) misses
+    double bp, bh;          // PCIe and host expert bandwidths of the hybrid split
 };
 
 // one MoE layer's expert FFN for B tokens: gate/up + SwiGLU (K3) and
@@ -118,6 +122,7 @@ struct FfnArgs {
     const uint16_t* x;      // [B][H]
     uint16_t* a;            // [B][nE][I] bf16 (K3 -> K4)
     uint16_t* y;            // [B][H] bf16
+    const float* yh;        // [B][H] FP32 added before rounding (host-computed experts), or NULL
     size_t blob_bytes, d_codes_off, d_scales_off;
     int k, n_shared, nE, layer, NB, NBI, I, H;
     int P1, P2;             // K3 and K4 workgroups per token

@@ -1,0 +1,124 @@
+"""Hybrid backend on the device: a one-token step transfers q = m B_P / B_H of its m misses and the
+host workers compute the rest.  Against the oracle: ids, cache trace (host misses carry slot -1),
+final cache state and counters bit-exact with the oracle's hybrid steps; outputs within relative
+L2 5e-3 and max|diff| 1e-2 * max|ref| of the plain MoE output (placement does not change it)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import close_enough, make_moe, run_stack, trace_tuples
+
+pytestmark = pytest.mark.gpu
+
+TOY = synth.WORKLOADS["toy"]
+SHARED = synth.Workload("hyb_shared_k8", 3, 32, 8, 1, 2048, 512, 20, 12, 1, 0.8, seed=51)
+WIDE = synth.Workload("hyb_2880", 3, 16, 4, 0, 2880, 2880, 10, 10, 1, 0.7, seed=52)
+
+# (B_P, B_H): every miss on the host (q = round(m / 40) = 0 for m < 20), the pages' calibration
+# (q = 0.59 m), this box's measured ratio (q = 0.19 m), and no spare host bandwidth (offload)
+SPLITS = [(10.0, 400.0), (26.7, 45.5), (56.0, 290.0), (50.0, 50.0)]
+
+
+def _hybrid(wl, split, threads=4, **kw):
+    m, W = make_moe(wl, **kw)
+    m.set_backend("hybrid", split[0], split[1], threads)
+    return m, W
+
+
+def _check(wl, X, W, m, ids, w, y, split):
+    cnt, recs = m.stats(trace_cap=1 << 20)
+    ref = oracle.decode_trace(wl, W, X, split=split)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["w"])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    slot_of, key_of, stamp = m.cache_state()
+    r_slot, r_key, r_stamp = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    np.testing.assert_array_equal(stamp, r_stamp)
+    c = ref["counters"]
+    assert (cnt["hits"], cnt["misses"], cnt["evictions"], cnt["host_experts"]) == \
+        (c["hits"], c["misses"], c["evictions"], c["host"])
+    assert cnt["h2d_copies"] == c["misses"] - c["host"]
+    worst = 0.0
+    T = X.shape[0]
+    for t in range(T):
+        for l in range(wl.n_layers):
+            r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
+            rel, mx, ok = close_enough(y[t, l, 0], r)
+            worst = max(worst, rel)
+            assert ok, (t, l, rel, mx)
+    return c, worst
+
+
+@pytest.mark.parametrize("split", SPLITS, ids=[f"{a}_{b}" for a, b in SPLITS])
+@pytest.mark.parametrize("wl", [TOY, SHARED, WIDE], ids=lambda w: w.name)
+def test_hybrid_decode_matches_oracle(wl, split):
+    X = synth.decode_inputs(wl)[:24]
+    m, W = _hybrid(wl, split)
+    ids, w, y = run_stack(m, wl, X)
+    c, worst = _check(wl, X, W, m, ids, w, y, split)
+    print(wl.name, split, c, "worst rel-L2 %.2e" % worst)
+    if split[1] > split[0]:
+        assert c["host"] > 0
+    m.close()
+
+
+def test_hybrid_is_bitwise_independent_of_workers_and_lookahead():
+    wl = WIDE
+    X = synth.decode_inputs(wl)[:12]
+    outs = []
+    for threads, la in ((1, 1), (7, 1), (4, 0)):
+        m, _ = _hybrid(wl, (26.7, 45.5), threads=threads, lookahead=la)
+        outs.append(run_stack(m, wl, X)[2])
+        m.close()
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
+def test_hybrid_layer_forward_matches_stack_and_pageable_pool():
+    import torch
+    wl = SHARED
+    X = synth.decode_inputs(wl)[:8]
+    m, W = _hybrid(wl, (10.0, 400.0), pinned_mb=1)   # most of the pool pageable
+    _, _, ys = run_stack(m, wl, X)
+    m.close()
+    m, W = _hybrid(wl, (10.0, 400.0), lookahead=0, pinned_mb=1)
+    dev = m.device
+    H = wl.hidden
+    xd = torch.from_numpy(X.view(np.int16)).to(dev)
+    y = torch.empty((X.shape[0], wl.n_layers, 1, H), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(m.compute_stream):
+        for t in range(X.shape[0]):
+            for l in range(wl.n_layers):
+                m.layer_forward(t, l, xd[t], y[t, l])
+    m.compute_stream.synchronize()
+    yl = y.view(torch.bfloat16).float().cpu().numpy()
+    np.testing.assert_array_equal(yl.view(np.uint32), ys.view(np.uint32))
+    cnt, _ = m.stats()
+    assert cnt["host_experts"] > 0 and cnt["host_tasks"] > 0
+    m.close()
+
+
+def test_set_backend_rejects_bad_arguments_and_switches_back():
+    import moe_expert_offload_amd as M
+    m, W = make_moe(TOY)
+    for args in (("hybrid", 0.0, 10.0, 2), ("hybrid", 10.0, -1.0, 2), ("hybrid", 10.0, 20.0, 0)):
+        with pytest.raises(M.MoeError):
+            m.set_backend(*args)
+    X = synth.decode_inputs(TOY)[:6]
+    m.set_backend("hybrid", 10.0, 400.0, 2)
+    run_stack(m, TOY, X[:3])
+    m.set_backend("offload")
+    run_stack(m, TOY, X[3:], step0=3)
+    cnt, recs = m.stats(trace_cap=1 << 16)
+    # the steps after the switch transfer every miss
+    late = [r for r in trace_tuples(recs) if r[0] >= 3 and r[4] == 0]
+    assert late and all(r[3] >= 0 for r in late)
+    m.close()
+    ms, _ = make_moe(TOY, policy=1)
+    with pytest.raises(M.MoeError):
+        ms.set_backend("hybrid", 10.0, 20.0, 2)
+    ms.close()
