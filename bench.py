@@ -303,7 +303,7 @@ def main():
     # device and host counters are cumulative: take the timed region's share
     c = dict(c_all)
     for key in ("hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "h2d_bounced", "host_experts",
-                "host_tasks"):
+                "host_tasks", "host_busy_ms", "host_wait_ms"):
         c[key] = c_all[key] - c_warm[key]
     tok_s = K * B / dt
 
@@ -370,7 +370,9 @@ def main():
                          "GB_per_step": round(host_bytes_step / 1e9, 4),
                          "effective_GBps": round(c["host_experts"] * m.blob_bytes / dt / 1e9, 2),
                          "calibrated_GBps": round(calib["host_GBps"], 2),
-                         "tasks_per_step": round(c["host_tasks"] / K, 2)}
+                         "tasks_per_step": round(c["host_tasks"] / K, 2),
+                         "busy_ms_per_step": round(c["host_busy_ms"] / K, 3),
+                         "wait_ms_per_step": round(c["host_wait_ms"] / K, 3)}
     extra["decode_roofline_tok_s"] = round(roof_step * B, 1)
     extra["decode_frac_of_roofline"] = round(tok_s / (roof_step * B), 4)
 

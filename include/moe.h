@@ -203,6 +203,8 @@ typedef struct {
                                           combine), from HIP events */
     uint64_t host_experts;             /* hybrid backend: misses computed by the host (included in misses) */
     uint64_t host_tasks;               /* hybrid backend: layer steps with a host share */
+    double host_busy_ms;               /* ... summed time from a host task's submission to its end */
+    double host_wait_ms;               /* ... time the calling thread waited for host tasks */
 } moe_counters;
 
 typedef struct {

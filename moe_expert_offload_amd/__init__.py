@@ -44,7 +44,8 @@ class MoeCounters(ctypes.Structure):
         "hits", "misses", "evictions", "resolves", "h2d_bytes", "h2d_copies", "trace_records",
         "trace_dropped", "ffn_launches", "h2d_bounced", "pool_pinned_bytes")] + [
         ("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double),
-        ("host_experts", ctypes.c_uint64), ("host_tasks", ctypes.c_uint64)]
+        ("host_experts", ctypes.c_uint64), ("host_tasks", ctypes.c_uint64),
+        ("host_busy_ms", ctypes.c_double), ("host_wait_ms", ctypes.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -250,6 +250,18 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
         for (int i = 0; i < L.H; ++i) y[i] += part[t][i];
 }
 
+// Units of work are handed out dynamically (an atomic counter per phase), so a
+// slow or descheduled worker delays a phase by at most one unit.  Unit sizes
+// aim at about four units per worker and phase, within these bounds.
+constexpr int kGuChunkMax = 4;   // 16-row gate/up tiles per unit
+constexpr int kActChunkMax = 8;  // 32-blocks of the intermediate vector per unit
+constexpr int kDChunkMax = 8;    // 8-row output tiles per unit (all experts, in order)
+
+inline int unit_size(long items, int workers, int max_chunk) {
+    const long c = items / (4L * workers);
+    return (int)std::max<long>(1, std::min<long>(max_chunk, c));
+}
+
 // ------------------------------------------------------------- worker pool --
 
 HostExpertPool::~HostExpertPool() { stop(); }
@@ -261,11 +273,9 @@ bool HostExpertPool::start(int n_workers) {
     quit_.store(false);
     gen_.store(0);
     done_.store(0);
-    bar_count_.store(0);
-    bar_gen_.store(0);
     work_.assign(n_, nullptr);
     for (int t = 0; t < n_; ++t) work_[t] = new Work();
-    shared_ = new Work();
+    shared_ = new Work[16];
     try {
         for (int t = 0; t < n_; ++t) threads_.emplace_back(&HostExpertPool::run, this, t);
     } catch (...) {
@@ -288,8 +298,10 @@ void HostExpertPool::stop() {
     }
     for (Work* w : work_) delete w;
     work_.clear();
-    delete shared_;
+    delete[] shared_;
     shared_ = nullptr;
+    delete caller_work_;
+    caller_work_ = nullptr;
     n_ = 0;
 }
 
@@ -300,10 +312,23 @@ void HostExpertPool::submit(const Layout& L, const uint8_t* const* blobs, const 
     for (int j = 0; j < task_.n; ++j) {
         task_.blobs[j] = blobs[j];
         task_.w[j] = w[j];
+        if ((int)shared_[j].g.size() != L.I || (int)shared_[j].ae.size() != L.NBI * 16) shared_[j].size(L);
     }
     task_.x = x;
     task_.y = y;
+    // about four units per participant (workers and the waiting caller) and phase
+    const int np = n_ + 1;
+    task_.gu_chunk = unit_size((long)task_.n * (L.I / 16), np, kGuChunkMax);
+    task_.act_chunk = unit_size((long)task_.n * L.NBI, np, kActChunkMax);
+    task_.d_chunk = unit_size(L.H / 8, np, kDChunkMax);
+    gu_next_.store(0, std::memory_order_relaxed);
+    act_next_.store(0, std::memory_order_relaxed);
+    d_next_.store(0, std::memory_order_relaxed);
+    gu_done_.store(0, std::memory_order_relaxed);
+    act_done_.store(0, std::memory_order_relaxed);
+    d_done_.store(0, std::memory_order_relaxed);
     done_.store(0);
+    t_submit_ = std::chrono::steady_clock::now();
     {
         std::lock_guard<std::mutex> lk(mu_);
         gen_.fetch_add(1, std::memory_order_release);
@@ -312,17 +337,55 @@ void HostExpertPool::submit(const Layout& L, const uint8_t* const* blobs, const 
 }
 
 void HostExpertPool::wait() {
+    // the caller works on the task too, then waits until every worker has left it
+    // (a worker still inside could otherwise take a unit of the next task)
+    if (!caller_work_) caller_work_ = new Work();
+    work(*caller_work_, have_avx512());
     while (done_.load(std::memory_order_acquire) < n_) _mm_pause();
 }
 
-// all workers meet (spinning; the generation flips once everyone arrived)
-void HostExpertPool::barrier() {
-    const int g = bar_gen_.load(std::memory_order_acquire);
-    if (bar_count_.fetch_add(1, std::memory_order_acq_rel) == n_ - 1) {
-        bar_count_.store(0, std::memory_order_relaxed);
-        bar_gen_.store(g + 1, std::memory_order_release);
-    } else {
-        while (bar_gen_.load(std::memory_order_acquire) == g) _mm_pause();
+// one participant's share of the current task: units from the three phases in
+// order; a phase ends when all of its units are done (counted, not a barrier of
+// a fixed set of threads), so the calling thread can join in while it waits
+void HostExpertPool::work(Work& wk, bool vec) {
+    const Layout& L = task_.L;
+    const int n = task_.n;
+    if ((int)wk.xe.size() != L.NB * 16 || (int)wk.g.size() != L.I) wk.size(L);
+    for (int b = 0; b < L.NB; ++b)
+        for (int i = 0; i < 16; ++i) {
+            wk.xe[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i]);
+            wk.xo[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i + 1]);
+        }
+    const int gu_chunk = task_.gu_chunk, act_chunk = task_.act_chunk, d_chunk = task_.d_chunk;
+    const int ngu = L.I / 16, nt8 = L.H / 8;
+    // gate/up: (expert, chunk of tiles) units
+    const int gu_per = (ngu + gu_chunk - 1) / gu_chunk, n_gu = n * gu_per;
+    for (int u; (u = gu_next_.fetch_add(1, std::memory_order_relaxed)) < n_gu;) {
+        const int j = u / gu_per, t0c = (u % gu_per) * gu_chunk;
+        const int t1c = std::min(ngu, t0c + gu_chunk);
+        gate_up_rows(L, task_.blobs[j], wk, t0c, t1c, vec);
+        std::copy(wk.g.begin() + t0c * 16, wk.g.begin() + t1c * 16, shared_[j].g.begin() + t0c * 16);
+        std::copy(wk.u.begin() + t0c * 16, wk.u.begin() + t1c * 16, shared_[j].u.begin() + t0c * 16);
+        gu_done_.fetch_add(1, std::memory_order_release);
+    }
+    while (gu_done_.load(std::memory_order_acquire) < n_gu) _mm_pause();
+    // intermediate vectors: (expert, chunk of 32-blocks) units
+    const int act_per = (L.NBI + act_chunk - 1) / act_chunk, n_act = n * act_per;
+    for (int u; (u = act_next_.fetch_add(1, std::memory_order_relaxed)) < n_act;) {
+        const int j = u / act_per, b0 = (u % act_per) * act_chunk;
+        activation_blocks(shared_[j], shared_[j], b0, std::min(L.NBI, b0 + act_chunk));
+        act_done_.fetch_add(1, std::memory_order_release);
+    }
+    while (act_done_.load(std::memory_order_acquire) < n_act) _mm_pause();
+    // down: chunks of output rows, each summed over the experts in order by one participant
+    const int n_d = (nt8 + d_chunk - 1) / d_chunk;
+    for (int u; (u = d_next_.fetch_add(1, std::memory_order_relaxed)) < n_d;) {
+        const int d0 = u * d_chunk, d1 = std::min(nt8, d0 + d_chunk);
+        std::fill(task_.y + d0 * 8, task_.y + d1 * 8, 0.0f);
+        for (int j = 0; j < n; ++j) down_rows(L, task_.blobs[j], shared_[j], task_.w[j], task_.y, d0, d1, vec);
+        if (d_done_.fetch_add(1, std::memory_order_acq_rel) == n_d - 1)
+            busy_ns_.fetch_add((uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
+                                   std::chrono::steady_clock::now() - t_submit_).count());
     }
 }
 
@@ -345,39 +408,8 @@ void HostExpertPool::run(int t) {
         }
         seen = gen_.load(std::memory_order_acquire);
         if (quit_.load()) return;
-        const Layout& L = task_.L;
-        if ((int)wk.xe.size() != L.NB * 16 || (int)wk.g.size() != L.I) wk.size(L);
-        if (t == 0 && ((int)shared_->g.size() != L.I || (int)shared_->ae.size() != L.NBI * 16)) shared_->size(L);
-        // x split even / odd (every worker its own copy)
-        for (int b = 0; b < L.NB; ++b)
-            for (int i = 0; i < 16; ++i) {
-                wk.xe[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i]);
-                wk.xo[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i + 1]);
-            }
-        // rows of y this worker owns: row tiles [d0, d1) of 8; zero them
-        const int nt8 = L.H / 8, ngu = L.I / 16;
-        const int d0 = (int)((long)nt8 * t / n_), d1 = (int)((long)nt8 * (t + 1) / n_);
-        const int g0 = (int)((long)ngu * t / n_), g1 = (int)((long)ngu * (t + 1) / n_);
-        const int a0 = (int)((long)L.NBI * t / n_), a1 = (int)((long)L.NBI * (t + 1) / n_);
-        std::fill(task_.y + d0 * 8, task_.y + d1 * 8, 0.0f);
-        barrier();  // shared_ sized by worker 0
-        for (int j = 0; j < task_.n; ++j) {
-            // gate/up rows of this worker into the shared g / u
-            gate_up_rows(L, task_.blobs[j], wk, g0, g1, vec);
-            for (int i = g0 * 16; i < g1 * 16; ++i) {
-                shared_->g[i] = wk.g[i];
-                shared_->u[i] = wk.u[i];
-            }
-            barrier();
-            activation_blocks(*shared_, *shared_, a0, a1);
-            barrier();
-            // down rows of this worker: y rows [8 d0, 8 d1), summed over the experts in order
-            std::copy(shared_->ae.begin(), shared_->ae.end(), wk.ae.begin());
-            std::copy(shared_->ao.begin(), shared_->ao.end(), wk.ao.begin());
-            down_rows(L, task_.blobs[j], wk, task_.w[j], task_.y, d0, d1, vec);
-            barrier();  // the next expert overwrites the shared vectors
-        }
-        done_.fetch_add(1, std::memory_order_acq_rel);
+        work(wk, vec);
+        done_.fetch_add(1, std::memory_order_acq_rel);  // this worker has left the task
     }
 }
 

@@ -1,6 +1,7 @@
 // Host-CPU MXFP4 SwiGLU expert kernel (reads blobs in the pool's layout).
 #pragma once
 #include <atomic>
+#include <chrono>
 #include <condition_variable>
 #include <mutex>
 #include <thread>
@@ -27,11 +28,15 @@ double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int
 struct Work;
 
 // Persistent host workers for the hybrid backend: one task at a time, y[H]
-// (FP32) = sum_j w[j] * FFN_j(x) over up to 16 experts, every expert split over
-// all workers by row tiles (gate/up tiles, then activation blocks, then down
-// row tiles, with a barrier between phases).  Each output row is summed by one
-// worker over the experts in order, so the result does not depend on the
-// worker count.  Workers spin between tasks and sleep after 20 ms idle.
+// (FP32) = sum_j w[j] * FFN_j(x) over up to 16 experts.  Three phases over all
+// of the task's experts, each handing out small units through an atomic
+// counter and ending when all of its units are done: (expert, gate/up tiles),
+// (expert, blocks of the intermediate vector), then chunks of output rows,
+// each summed over the experts in order by the participant that takes it.
+// The caller of wait() works on the task as well.  Every value is
+// computed by one worker in a fixed order, so the result does not depend on
+// the worker count or on which worker takes a unit.
+// Workers spin between tasks and sleep after 20 ms idle.
 class HostExpertPool {
 public:
     ~HostExpertPool();
@@ -41,7 +46,9 @@ public:
     int workers() const { return n_; }
     // x (bf16, host) and y (FP32, host) must stay valid until wait() returns
     void submit(const Layout& L, const uint8_t* const* blobs, const float* w, int n, const uint16_t* x, float* y);
-    void wait();
+    void wait();  // helps with the task, then returns once it is complete
+    // nanoseconds from submit to the last worker's finish, summed over tasks
+    uint64_t busy_ns() const { return busy_ns_.load(); }
 
 private:
     struct Task {
@@ -51,15 +58,21 @@ private:
         int n = 0;
         const uint16_t* x = nullptr;
         float* y = nullptr;
+        int gu_chunk = 1, act_chunk = 1, d_chunk = 1;  // unit sizes of the three phases
     };
     void run(int t);
-    void barrier();
+    void work(Work& wk, bool vec);
     int n_ = 0;
     Task task_;
     std::vector<std::thread> threads_;
     std::vector<Work*> work_;
-    Work* shared_ = nullptr;
-    std::atomic<int> gen_{0}, done_{0}, bar_count_{0}, bar_gen_{0};
+    Work* shared_ = nullptr;  // [16]: per expert g, u and the intermediate vector
+    std::atomic<int> gen_{0}, done_{0};
+    std::atomic<int> gu_next_{0}, act_next_{0}, d_next_{0};  // next unit of each phase
+    std::atomic<int> gu_done_{0}, act_done_{0}, d_done_{0};  // units finished per phase
+    Work* caller_work_ = nullptr;                            // buffers of the waiting caller
+    std::atomic<uint64_t> busy_ns_{0};
+    std::chrono::steady_clock::time_point t_submit_{};
     std::atomic<bool> quit_{false};
     std::mutex mu_;
     std::condition_variable cv_;

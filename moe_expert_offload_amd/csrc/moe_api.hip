@@ -101,6 +101,7 @@ struct moe_ctx {
     float* yh = nullptr;                 // host-mapped [2][H]: the host experts' sum per parity
     bool host_pending[2] = {false, false};
     uint64_t host_tasks = 0;
+    double host_wait_ms = 0.0;           // time the calling thread waited for host tasks
     double spin_timeout_s = 60.0;
     bool failed = false;
     std::string err;
@@ -467,7 +468,9 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
     const float* yh = nullptr;
     if (par < 2 && c->host_pending[par]) {
         // the host experts of this step: their sum is added by the down kernel
+        const auto tw = std::chrono::steady_clock::now();
         c->hpool.wait();
+        c->host_wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
         c->host_pending[par] = false;
         yh = c->yh + (size_t)par * c->cfg.hidden;
     }
@@ -940,6 +943,8 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         out->k4_ms = c->k4_ms;
         out->host_experts = cnt[4];
         out->host_tasks = c->host_tasks;
+        out->host_busy_ms = (double)c->hpool.busy_ns() * 1e-6;
+        out->host_wait_ms = c->host_wait_ms;
     }
     c->ffn_launches = 0;
     c->k3_ms = c->k4_ms = 0;
