@@ -62,3 +62,33 @@ def test_qwen38_shaped_prefill_and_b16_decode_sampled():
         rel, mx, ok = close_enough(y[t][l, b], r)
         print("t", t, "l", l, "b", b, "rel-L2", rel)
         assert ok, (t, l, b, rel, mx)
+
+
+def test_gptoss_shaped_hybrid_sampled():
+    """The same workload with the hybrid backend at a split like the one calibrated on these hosts
+    (B_P 56 GB/s, B_H 290 GB/s: about one miss in five transferred) and 15 host workers: ids, the
+    trace (host misses with slot -1) and the final cache state bit-exact with the oracle's hybrid
+    steps; outputs at sampled points against the plain MoE output."""
+    wl = synth.WORKLOADS["gptoss120b_shaped"]
+    T = 32
+    X = synth.decode_inputs(wl)[:T]
+    m, W = make_moe(wl)
+    split = (56.0, 290.0)
+    m.set_backend("hybrid", split[0], split[1], 15)
+    ids, w, y = run_stack(m, wl, X)
+    cnt, recs = m.stats(trace_cap=1 << 20)
+    ref = oracle.decode_trace(wl, W, X, split=split)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["w"])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    slot_of, key_of, _ = m.cache_state()
+    r_slot, r_key, _ = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    assert cnt["host_experts"] == ref["counters"]["host"] > 0
+    for (t, l) in [(0, 0), (2, 35), (9, 17), (T // 2, 3), (T - 1, 0), (T - 1, 35)]:
+        r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
+        rel, mx, ok = close_enough(y[t, l, 0], r)
+        print("hybrid t", t, "l", l, "rel-L2", rel)
+        assert ok, (t, l, rel, mx)
+    m.close()
