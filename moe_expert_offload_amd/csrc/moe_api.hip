@@ -99,7 +99,8 @@ struct moe_ctx {
     bool xh_pending = false;
     bool hyb_call = false;               // the current call runs hybrid steps
     float* yh = nullptr;                 // host-mapped [2][H]: the host experts' sum per parity
-    bool host_pending[2] = {false, false};
+    bool host_has[2] = {false, false};   // this parity's FFN adds yh[parity]
+    int host_running = -1;               // parity of the host task in flight, -1: none
     uint64_t host_tasks = 0;
     double host_wait_ms = 0.0;           // time the calling thread waited for host tasks
     double spin_timeout_s = 60.0;
@@ -419,8 +420,17 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
                 blobs[nh] = c->blob_src((size_t)layer * c->cfg.n_experts + ml->ids0[j]);
                 w[nh++] = ml->w0[j];
             }
+        if (c->host_running >= 0) {
+            // one task at a time: the previous layer's host experts finish first (its sum
+            // stays in its own parity's buffer for that layer's FFN)
+            const auto tw = std::chrono::steady_clock::now();
+            c->hpool.wait();
+            c->host_wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
+            c->host_running = -1;
+        }
         c->hpool.submit(c->lay, blobs, w, nh, c->xh + (size_t)layer * c->xh_stride, c->yh + (size_t)par * c->cfg.hidden);
-        c->host_pending[par] = true;
+        c->host_running = par;
+        c->host_has[par] = true;
         ++c->host_tasks;
     }
     const size_t blob = c->lay.blob_bytes;
@@ -466,12 +476,15 @@ moe_status get_prof(moe_ctx* c, ProfSlot& p) {
 moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par, void* y, int n_miss,
                             const int32_t* slots_dev = nullptr, const float* w_dev = nullptr) {
     const float* yh = nullptr;
-    if (par < 2 && c->host_pending[par]) {
+    if (par < 2 && c->host_has[par]) {
         // the host experts of this step: their sum is added by the down kernel
-        const auto tw = std::chrono::steady_clock::now();
-        c->hpool.wait();
-        c->host_wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
-        c->host_pending[par] = false;
+        if (c->host_running == par) {
+            const auto tw = std::chrono::steady_clock::now();
+            c->hpool.wait();
+            c->host_wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
+            c->host_running = -1;
+        }
+        c->host_has[par] = false;
         yh = c->yh + (size_t)par * c->cfg.hidden;
     }
     if (n_miss > 0 && par < 2) {
@@ -873,6 +886,27 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     }
     // lookahead 1: K1/K2 of layer l+1 and its copies are issued before layer l's FFN
     int64_t seq_of[2] = {0, 0};
+    if (c->hyb_call) {
+        // hybrid steps: layer l+1's miss list is taken (and its host task started) before
+        // layer l's FFN is launched, so the host workers go from one layer's experts to the
+        // next without waiting for the launches in between
+        if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
+        if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
+        int nm_of[2] = {0, 0};
+        if ((st = stage_misses(c, 0, 0, c->seq, &nm_of[0]))) return st;
+        for (int l = 0; l < L; ++l) {
+            const int par = l & 1, np = par ^ 1;
+            if (l + 1 < L) {
+                if ((st = launch_route(c, l + 1, xl(l + 1), n_tokens))) return st;
+                if ((st = launch_resolve(c, step, l + 1, true, nullptr, n_tokens, np, nullptr, idl(l + 1),
+                                         wl(l + 1))))
+                    return st;
+                if ((st = stage_misses(c, l + 1, np, c->seq, &nm_of[np]))) return st;
+            }
+            if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm_of[par]))) return st;
+        }
+        return MOE_OK;
+    }
     if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
     if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
     seq_of[0] = c->seq;
