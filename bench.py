@@ -207,12 +207,14 @@ def main():
     ap.add_argument("--backend", choices=("offload", "hybrid", "auto"), default="offload",
                     help="offload: every miss over PCIe; hybrid: the calibrated split between PCIe and host "
                          "workers; auto: hybrid when the calibration says the host is more than twice as fast")
+    ap.add_argument("--host-workers", type=int, default=0,
+                    help="host worker threads of the hybrid backend (0: this process's cores - 1, at most 15)")
     ap.add_argument("--auto-reserve-gb", type=float, default=4.0,
                     help="HBM kept free by --cache-slots auto (the KV cache's share in a server)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU "
-              "sharding in this build", file=sys.stderr)
+              "sharding", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -254,7 +256,7 @@ def main():
     h2d_big = m.measure_h2d(64 << 20, 32)
     # backend calibration: B_P (blob copies) vs B_H (the host expert kernel on the cores the host
     # workers would use: all of this process's cores but the one driving the GPU)
-    workers = max(1, min(16, len(os.sched_getaffinity(0))) - 1)
+    workers = args.host_workers or max(1, min(16, len(os.sched_getaffinity(0))) - 1)
     calib = m.calibrate_backend(workers, host_seconds=2.0)
     backend = args.backend if args.backend != "auto" else calib["backend"]
     if backend == "hybrid":
