@@ -2,7 +2,8 @@
 // bandwidth calibration runs to measure B_H, the rate at which the host
 // processes experts in this weight format (ai-hardware-zukan.com page, section
 // on the hybrid mode: B_H is the speed of the actual expert kernel, not a raw
-// memory read, and it depends on the weight format).
+// memory read, and it depends on the weight format), and the kernel the hybrid
+// backend's host workers run on their share of the misses.
 //
 // It reads the blob in the pool's layout (the layout the GPU kernels read; see
 // moe_internal.h), in memory order: gate/up tile by tile (16 rows, chunks
@@ -10,6 +11,8 @@
 // 16-byte chunk holds one 32-element block of one row; element 2i is the low
 // nibble of byte i.  Accumulation is FP32; the intermediate vector is rounded
 // to bf16 (round to nearest even) before the down projection, as on the GPU.
+// Activations are kept split into the even and odd elements of each 32-block
+// (16 + 16 floats), the order in which a chunk's low and high nibbles decode.
 #include <algorithm>
 #include <atomic>
 #include <chrono>
@@ -25,19 +28,6 @@
 #include "moe_internal.h"
 
 namespace moe {
-
-// per-call buffers: x and a split into even / odd elements of each 32-block
-struct Work {
-    std::vector<float> xe, xo, ae, ao, g, u;
-    void size(const Layout& L) {
-        xe.assign((size_t)L.NB * 16, 0.0f);
-        xo.assign((size_t)L.NB * 16, 0.0f);
-        ae.assign((size_t)L.NBI * 16, 0.0f);
-        ao.assign((size_t)L.NBI * 16, 0.0f);
-        g.assign(L.I, 0.0f);
-        u.assign(L.I, 0.0f);
-    }
-};
 
 namespace {
 
@@ -72,11 +62,12 @@ inline float round_bf16(float f) {
 
 inline float silu_mul(float g, float u) { return g / (1.0f + std::exp(-g)) * u; }
 
-void split_even_odd(const float* v, int n_blocks, float* ev, float* od) {
-    for (int b = 0; b < n_blocks; ++b)
+// 32-blocks [b0, b1) of a bf16 vector into FP32, split even / odd
+void split_blocks(const uint16_t* x, int b0, int b1, float* ev, float* od) {
+    for (int b = b0; b < b1; ++b)
         for (int i = 0; i < 16; ++i) {
-            ev[b * 16 + i] = v[b * 32 + 2 * i];
-            od[b * 16 + i] = v[b * 32 + 2 * i + 1];
+            ev[b * 16 + i] = bf16_to_f32(x[b * 32 + 2 * i]);
+            od[b * 16 + i] = bf16_to_f32(x[b * 32 + 2 * i + 1]);
         }
 }
 
@@ -90,7 +81,8 @@ float dot_block_scalar(const uint8_t* codes, const float* ev, const float* od) {
     return s;
 }
 
-void gate_up_scalar(const Layout& L, const uint8_t* blob, Work& wk, int t_begin, int t_end) {
+void gate_up_scalar(const Layout& L, const uint8_t* blob, const float* xe, const float* xo, float* g, float* u,
+                    int t_begin, int t_end) {
     int b0[16];
     for (int s = 0; s < 16; ++s) b0[s] = seg_begin(L.NB, 16, s);
     for (int tile = t_begin; tile < t_end; ++tile) {
@@ -102,19 +94,19 @@ void gate_up_scalar(const Layout& L, const uint8_t* blob, Work& wk, int t_begin,
             const int blk = b0[q & 15] + (q >> 4);
             for (int r = 0; r < 16; ++r) {
                 const size_t c = (size_t)q * 16 + r;
-                ag[r] += e8m0(sc[c * 2]) * dot_block_scalar(tb + c * 16, &wk.xe[blk * 16], &wk.xo[blk * 16]);
-                au[r] += e8m0(sc[c * 2 + 1]) * dot_block_scalar(ub + c * 16, &wk.xe[blk * 16], &wk.xo[blk * 16]);
+                ag[r] += e8m0(sc[c * 2]) * dot_block_scalar(tb + c * 16, xe + blk * 16, xo + blk * 16);
+                au[r] += e8m0(sc[c * 2 + 1]) * dot_block_scalar(ub + c * 16, xe + blk * 16, xo + blk * 16);
             }
         }
         for (int r = 0; r < 16; ++r) {
-            wk.g[tile * 16 + r] = ag[r];
-            wk.u[tile * 16 + r] = au[r];
+            g[tile * 16 + r] = ag[r];
+            u[tile * 16 + r] = au[r];
         }
     }
 }
 
-void down_scalar(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y, int t_begin,
-                 int t_end) {
+void down_scalar(const Layout& L, const uint8_t* blob, const float* ae, const float* ao, float w, float* y,
+                 int t_begin, int t_end) {
     const uint8_t* dc = blob + L.d_codes_off;
     const uint8_t* ds = blob + L.d_scales_off;
     for (int t8 = t_begin; t8 < t_end; ++t8) {
@@ -122,7 +114,7 @@ void down_scalar(const Layout& L, const uint8_t* blob, const Work& wk, float w, 
         for (int ib = 0; ib < L.NBI; ++ib)
             for (int r = 0; r < 8; ++r) {
                 const size_t cell = ((size_t)t8 * L.NBI + ib) * 8 + r;
-                acc[r] += e8m0(ds[cell]) * dot_block_scalar(dc + cell * 16, &wk.ae[ib * 16], &wk.ao[ib * 16]);
+                acc[r] += e8m0(ds[cell]) * dot_block_scalar(dc + cell * 16, ae + ib * 16, ao + ib * 16);
             }
         for (int r = 0; r < 8; ++r) y[t8 * 8 + r] += w * acc[r];
     }
@@ -138,7 +130,8 @@ MOE_AVX512 inline __m512 dot_block_v(const uint8_t* codes, __m512 lut, __m512 ev
     return _mm512_fmadd_ps(hi, od, _mm512_mul_ps(lo, ev));
 }
 
-MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, Work& wk, int t_begin, int t_end) {
+MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, const float* xe, const float* xo, float* g,
+                               float* u, int t_begin, int t_end) {
     const __m512 lut = _mm512_loadu_ps(kE2M1);
     int b0[16];
     for (int s = 0; s < 16; ++s) b0[s] = seg_begin(L.NB, 16, s);
@@ -152,8 +145,8 @@ MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, Work& wk, i
             for (int r = 0; r < 16; ++r) acc[r] = _mm512_setzero_ps();
             for (int q = 0; q < L.NB; ++q) {
                 const int blk = b0[q & 15] + (q >> 4);
-                const __m512 ev = _mm512_loadu_ps(&wk.xe[(size_t)blk * 16]);
-                const __m512 od = _mm512_loadu_ps(&wk.xo[(size_t)blk * 16]);
+                const __m512 ev = _mm512_loadu_ps(xe + (size_t)blk * 16);
+                const __m512 od = _mm512_loadu_ps(xo + (size_t)blk * 16);
                 const uint8_t* cq = cb + (size_t)q * 256;
                 const uint8_t* sq = sc + (size_t)q * 32 + part;
 #pragma GCC unroll 16
@@ -161,14 +154,14 @@ MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, Work& wk, i
                     acc[r] = _mm512_fmadd_ps(dot_block_v(cq + r * 16, lut, ev, od), _mm512_set1_ps(e8m0(sq[r * 2])),
                                              acc[r]);
             }
-            float* out = part ? wk.u.data() : wk.g.data();
+            float* out = part ? u : g;
             for (int r = 0; r < 16; ++r) out[tile * 16 + r] = _mm512_reduce_add_ps(acc[r]);
         }
     }
 }
 
-MOE_AVX512 void down_avx512(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y,
-                            int t_begin, int t_end) {
+MOE_AVX512 void down_avx512(const Layout& L, const uint8_t* blob, const float* ae, const float* ao, float w,
+                            float* y, int t_begin, int t_end) {
     const __m512 lut = _mm512_loadu_ps(kE2M1);
     const uint8_t* dc = blob + L.d_codes_off;
     const uint8_t* ds = blob + L.d_scales_off;
@@ -176,8 +169,8 @@ MOE_AVX512 void down_avx512(const Layout& L, const uint8_t* blob, const Work& wk
         __m512 acc[8];
         for (int r = 0; r < 8; ++r) acc[r] = _mm512_setzero_ps();
         for (int ib = 0; ib < L.NBI; ++ib) {
-            const __m512 ev = _mm512_loadu_ps(&wk.ae[(size_t)ib * 16]);
-            const __m512 od = _mm512_loadu_ps(&wk.ao[(size_t)ib * 16]);
+            const __m512 ev = _mm512_loadu_ps(ae + (size_t)ib * 16);
+            const __m512 od = _mm512_loadu_ps(ao + (size_t)ib * 16);
             const size_t cell = ((size_t)t8 * L.NBI + ib) * 8;
 #pragma GCC unroll 8
             for (int r = 0; r < 8; ++r)
@@ -195,31 +188,32 @@ bool have_avx512() {
     return ok && !(force && force[0] == '1');
 }
 
-void gate_up_rows(const Layout& L, const uint8_t* blob, Work& wk, int t_begin, int t_end, bool vec) {
-    if (vec) gate_up_avx512(L, blob, wk, t_begin, t_end);
-    else gate_up_scalar(L, blob, wk, t_begin, t_end);
+void gate_up_rows(const Layout& L, const uint8_t* blob, const TokenBuf& x, ExpertBuf& e, int t_begin, int t_end,
+                  bool vec) {
+    if (vec) gate_up_avx512(L, blob, x.xe.data(), x.xo.data(), e.g.data(), e.u.data(), t_begin, t_end);
+    else gate_up_scalar(L, blob, x.xe.data(), x.xo.data(), e.g.data(), e.u.data(), t_begin, t_end);
 }
 
-void down_rows(const Layout& L, const uint8_t* blob, const Work& wk, float w, float* y, int t_begin, int t_end,
+void down_rows(const Layout& L, const uint8_t* blob, const ExpertBuf& e, float w, float* y, int t_begin, int t_end,
                bool vec) {
-    if (vec) down_avx512(L, blob, wk, w, y, t_begin, t_end);
-    else down_scalar(L, blob, wk, w, y, t_begin, t_end);
+    if (vec) down_avx512(L, blob, e.ae.data(), e.ao.data(), w, y, t_begin, t_end);
+    else down_scalar(L, blob, e.ae.data(), e.ao.data(), w, y, t_begin, t_end);
 }
 
 // the intermediate vector of 32-blocks [b_begin, b_end): bf16(silu(g) * u), split even / odd
-void activation_blocks(const Work& src, Work& dst, int b_begin, int b_end) {
+void activation_blocks(ExpertBuf& e, int b_begin, int b_end) {
     for (int b = b_begin; b < b_end; ++b)
         for (int i = 0; i < 16; ++i) {
-            dst.ae[b * 16 + i] = round_bf16(silu_mul(src.g[b * 32 + 2 * i], src.u[b * 32 + 2 * i]));
-            dst.ao[b * 16 + i] = round_bf16(silu_mul(src.g[b * 32 + 2 * i + 1], src.u[b * 32 + 2 * i + 1]));
+            e.ae[b * 16 + i] = round_bf16(silu_mul(e.g[b * 32 + 2 * i], e.u[b * 32 + 2 * i]));
+            e.ao[b * 16 + i] = round_bf16(silu_mul(e.g[b * 32 + 2 * i + 1], e.u[b * 32 + 2 * i + 1]));
         }
 }
 
 // one expert for one token: y += w * down(silu(gate x) * (up x))
-void expert_one(const Layout& L, const uint8_t* blob, float w, Work& wk, float* y, bool vec) {
-    gate_up_rows(L, blob, wk, 0, L.I / 16, vec);
-    activation_blocks(wk, wk, 0, L.NBI);
-    down_rows(L, blob, wk, w, y, 0, L.H / 8, vec);
+void expert_one(const Layout& L, const uint8_t* blob, float w, const TokenBuf& x, ExpertBuf& e, float* y, bool vec) {
+    gate_up_rows(L, blob, x, e, 0, L.I / 16, vec);
+    activation_blocks(e, 0, L.NBI);
+    down_rows(L, blob, e, w, y, 0, L.H / 8, vec);
 }
 
 }  // namespace
@@ -228,8 +222,9 @@ const char* host_ffn_isa() { return have_avx512() ? "avx512" : "scalar"; }
 
 void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* w, int n, const uint16_t* x,
                      float* y, int threads) {
-    std::vector<float> xf(L.H);
-    for (int i = 0; i < L.H; ++i) xf[i] = bf16_to_f32(x[i]);
+    TokenBuf xb;
+    xb.size(L);
+    split_blocks(x, 0, L.NB, xb.xe.data(), xb.xo.data());
     std::fill(y, y + L.H, 0.0f);
     const bool vec = have_avx512();
     threads = std::max(1, std::min(threads, n));
@@ -237,10 +232,9 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
     // partial, and the partials are added in thread order
     std::vector<std::vector<float>> part(threads, std::vector<float>(L.H, 0.0f));
     auto run = [&](int t) {
-        Work wk;
-        wk.size(L);
-        split_even_odd(xf.data(), L.NB, wk.xe.data(), wk.xo.data());
-        for (int j = t; j < n; j += threads) expert_one(L, blobs[j], w[j], wk, part[t].data(), vec);
+        ExpertBuf eb;
+        eb.size(L);
+        for (int j = t; j < n; j += threads) expert_one(L, blobs[j], w[j], xb, eb, part[t].data(), vec);
     };
     std::vector<std::thread> pool;
     for (int t = 1; t < threads; ++t) pool.emplace_back(run, t);
@@ -252,13 +246,14 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
 
 // Units of work are handed out dynamically (an atomic counter per phase), so a
 // slow or descheduled worker delays a phase by at most one unit.  Unit sizes
-// aim at about four units per worker and phase, within these bounds.
+// aim at about four units per participant and phase, within these bounds.
+constexpr int kXChunkMax = 32;   // 32-blocks of a hidden state per unit
 constexpr int kGuChunkMax = 4;   // 16-row gate/up tiles per unit
 constexpr int kActChunkMax = 8;  // 32-blocks of the intermediate vector per unit
-constexpr int kDChunkMax = 8;    // 8-row output tiles per unit (all experts, in order)
+constexpr int kDChunkMax = 8;    // 8-row output tiles per unit (a token's experts, in order)
 
-inline int unit_size(long items, int workers, int max_chunk) {
-    const long c = items / (4L * workers);
+inline int unit_size(long items, int participants, int max_chunk) {
+    const long c = items / (4L * participants);
     return (int)std::max<long>(1, std::min<long>(max_chunk, c));
 }
 
@@ -273,9 +268,6 @@ bool HostExpertPool::start(int n_workers) {
     quit_.store(false);
     gen_.store(0);
     done_.store(0);
-    work_.assign(n_, nullptr);
-    for (int t = 0; t < n_; ++t) work_[t] = new Work();
-    shared_ = new Work[16];
     try {
         for (int t = 0; t < n_; ++t) threads_.emplace_back(&HostExpertPool::run, this, t);
     } catch (...) {
@@ -296,37 +288,39 @@ void HostExpertPool::stop() {
         for (auto& th : threads_) th.join();
         threads_.clear();
     }
-    for (Work* w : work_) delete w;
-    work_.clear();
-    delete[] shared_;
-    shared_ = nullptr;
-    delete caller_work_;
-    caller_work_ = nullptr;
     n_ = 0;
 }
 
-void HostExpertPool::submit(const Layout& L, const uint8_t* const* blobs, const float* w, int n, const uint16_t* x,
-                            float* y) {
+void HostExpertPool::submit(const Layout& L, int n_tok, const uint16_t* const* x, float* const* y,
+                            const HostEntry* entries, int n) {
     task_.L = L;
-    task_.n = n < 16 ? n : 16;
-    for (int j = 0; j < task_.n; ++j) {
-        task_.blobs[j] = blobs[j];
-        task_.w[j] = w[j];
-        if ((int)shared_[j].g.size() != L.I || (int)shared_[j].ae.size() != L.NBI * 16) shared_[j].size(L);
+    task_.ntok = std::max(0, std::min(n_tok, kHostMaxTokens));
+    n = std::max(0, std::min(n, kHostMaxEntries));
+    for (int b = 0; b < task_.ntok; ++b) {
+        task_.x[b] = x[b];
+        task_.y[b] = y[b];
     }
-    task_.x = x;
-    task_.y = y;
+    // entries grouped by token; a token's entries keep their order
+    int pos = 0;
+    for (int b = 0; b < task_.ntok; ++b) {
+        task_.tok_begin[b] = pos;
+        for (int j = 0; j < n; ++j)
+            if (entries[j].tok == b) task_.e[pos++] = entries[j];
+    }
+    task_.tok_begin[task_.ntok] = pos;
+    task_.n = pos;
+    if ((int)ebuf_.size() < task_.n) ebuf_.resize(task_.n);
+    for (int j = 0; j < task_.n; ++j) ebuf_[j].size(L);
+    if ((int)xbuf_.size() < task_.ntok) xbuf_.resize(task_.ntok);
+    for (int b = 0; b < task_.ntok; ++b) xbuf_[b].size(L);
     // about four units per participant (workers and the waiting caller) and phase
     const int np = n_ + 1;
+    task_.x_chunk = unit_size((long)task_.ntok * L.NB, np, kXChunkMax);
     task_.gu_chunk = unit_size((long)task_.n * (L.I / 16), np, kGuChunkMax);
     task_.act_chunk = unit_size((long)task_.n * L.NBI, np, kActChunkMax);
-    task_.d_chunk = unit_size(L.H / 8, np, kDChunkMax);
-    gu_next_.store(0, std::memory_order_relaxed);
-    act_next_.store(0, std::memory_order_relaxed);
-    d_next_.store(0, std::memory_order_relaxed);
-    gu_done_.store(0, std::memory_order_relaxed);
-    act_done_.store(0, std::memory_order_relaxed);
-    d_done_.store(0, std::memory_order_relaxed);
+    task_.d_chunk = unit_size((long)task_.ntok * (L.H / 8), np, kDChunkMax);
+    for (std::atomic<int>* c : {&x_next_, &gu_next_, &act_next_, &d_next_, &x_done_, &gu_done_, &act_done_, &d_done_})
+        c->store(0, std::memory_order_relaxed);
     done_.store(0);
     t_submit_ = std::chrono::steady_clock::now();
     {
@@ -339,59 +333,60 @@ void HostExpertPool::submit(const Layout& L, const uint8_t* const* blobs, const 
 void HostExpertPool::wait() {
     // the caller works on the task too, then waits until every worker has left it
     // (a worker still inside could otherwise take a unit of the next task)
-    if (!caller_work_) caller_work_ = new Work();
-    work(*caller_work_, have_avx512());
+    work(have_avx512());
     while (done_.load(std::memory_order_acquire) < n_) _mm_pause();
 }
 
-// one participant's share of the current task: units from the three phases in
-// order; a phase ends when all of its units are done (counted, not a barrier of
-// a fixed set of threads), so the calling thread can join in while it waits
-void HostExpertPool::work(Work& wk, bool vec) {
+// one participant's share of the current task: units from the phases in order;
+// a phase ends when all of its units are done (counted, not a barrier of a
+// fixed set of threads), so the calling thread can join in while it waits
+void HostExpertPool::work(bool vec) {
     const Layout& L = task_.L;
-    const int n = task_.n;
-    if ((int)wk.xe.size() != L.NB * 16 || (int)wk.g.size() != L.I) wk.size(L);
-    for (int b = 0; b < L.NB; ++b)
-        for (int i = 0; i < 16; ++i) {
-            wk.xe[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i]);
-            wk.xo[b * 16 + i] = bf16_to_f32(task_.x[b * 32 + 2 * i + 1]);
-        }
-    const int gu_chunk = task_.gu_chunk, act_chunk = task_.act_chunk, d_chunk = task_.d_chunk;
-    const int ngu = L.I / 16, nt8 = L.H / 8;
-    // gate/up: (expert, chunk of tiles) units
-    const int gu_per = (ngu + gu_chunk - 1) / gu_chunk, n_gu = n * gu_per;
+    const int n = task_.n, ntok = task_.ntok;
+    auto finish_phase = [](const std::atomic<int>& done, int total) {
+        while (done.load(std::memory_order_acquire) < total) _mm_pause();
+    };
+    // hidden states to FP32: (token, chunk of 32-blocks) units
+    const int xc = task_.x_chunk, x_per = (L.NB + xc - 1) / xc, n_x = ntok * x_per;
+    for (int u; (u = x_next_.fetch_add(1, std::memory_order_relaxed)) < n_x;) {
+        const int b = u / x_per, b0 = (u % x_per) * xc;
+        split_blocks(task_.x[b], b0, std::min(L.NB, b0 + xc), xbuf_[b].xe.data(), xbuf_[b].xo.data());
+        x_done_.fetch_add(1, std::memory_order_release);
+    }
+    finish_phase(x_done_, n_x);
+    // gate/up: (entry, chunk of tiles) units
+    const int ngu = L.I / 16, gc = task_.gu_chunk, gu_per = (ngu + gc - 1) / gc, n_gu = n * gu_per;
     for (int u; (u = gu_next_.fetch_add(1, std::memory_order_relaxed)) < n_gu;) {
-        const int j = u / gu_per, t0c = (u % gu_per) * gu_chunk;
-        const int t1c = std::min(ngu, t0c + gu_chunk);
-        gate_up_rows(L, task_.blobs[j], wk, t0c, t1c, vec);
-        std::copy(wk.g.begin() + t0c * 16, wk.g.begin() + t1c * 16, shared_[j].g.begin() + t0c * 16);
-        std::copy(wk.u.begin() + t0c * 16, wk.u.begin() + t1c * 16, shared_[j].u.begin() + t0c * 16);
+        const int j = u / gu_per, t0 = (u % gu_per) * gc;
+        gate_up_rows(L, task_.e[j].blob, xbuf_[task_.e[j].tok], ebuf_[j], t0, std::min(ngu, t0 + gc), vec);
         gu_done_.fetch_add(1, std::memory_order_release);
     }
-    while (gu_done_.load(std::memory_order_acquire) < n_gu) _mm_pause();
-    // intermediate vectors: (expert, chunk of 32-blocks) units
-    const int act_per = (L.NBI + act_chunk - 1) / act_chunk, n_act = n * act_per;
+    finish_phase(gu_done_, n_gu);
+    // intermediate vectors: (entry, chunk of 32-blocks) units
+    const int ac = task_.act_chunk, act_per = (L.NBI + ac - 1) / ac, n_act = n * act_per;
     for (int u; (u = act_next_.fetch_add(1, std::memory_order_relaxed)) < n_act;) {
-        const int j = u / act_per, b0 = (u % act_per) * act_chunk;
-        activation_blocks(shared_[j], shared_[j], b0, std::min(L.NBI, b0 + act_chunk));
+        const int j = u / act_per, b0 = (u % act_per) * ac;
+        activation_blocks(ebuf_[j], b0, std::min(L.NBI, b0 + ac));
         act_done_.fetch_add(1, std::memory_order_release);
     }
-    while (act_done_.load(std::memory_order_acquire) < n_act) _mm_pause();
-    // down: chunks of output rows, each summed over the experts in order by one participant
-    const int n_d = (nt8 + d_chunk - 1) / d_chunk;
+    finish_phase(act_done_, n_act);
+    // down: (token, chunk of output rows) units, each summed over the token's
+    // entries in order by the participant that takes it
+    const int nt8 = L.H / 8, dc = task_.d_chunk, d_per = (nt8 + dc - 1) / dc, n_d = ntok * d_per;
     for (int u; (u = d_next_.fetch_add(1, std::memory_order_relaxed)) < n_d;) {
-        const int d0 = u * d_chunk, d1 = std::min(nt8, d0 + d_chunk);
-        std::fill(task_.y + d0 * 8, task_.y + d1 * 8, 0.0f);
-        for (int j = 0; j < n; ++j) down_rows(L, task_.blobs[j], shared_[j], task_.w[j], task_.y, d0, d1, vec);
+        const int b = u / d_per, d0 = (u % d_per) * dc, d1 = std::min(nt8, d0 + dc);
+        float* y = task_.y[b];
+        std::fill(y + d0 * 8, y + d1 * 8, 0.0f);
+        for (int j = task_.tok_begin[b]; j < task_.tok_begin[b + 1]; ++j)
+            down_rows(L, task_.e[j].blob, ebuf_[j], task_.e[j].w, y, d0, d1, vec);
         if (d_done_.fetch_add(1, std::memory_order_acq_rel) == n_d - 1)
             busy_ns_.fetch_add((uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
                                    std::chrono::steady_clock::now() - t_submit_).count());
     }
 }
 
-void HostExpertPool::run(int t) {
+void HostExpertPool::run(int) {
     const bool vec = have_avx512();
-    Work& wk = *work_[t];
     int seen = 0;
     for (;;) {
         // spin for the next task for a while (decode steps arrive every few tens of
@@ -408,7 +403,7 @@ void HostExpertPool::run(int t) {
         }
         seen = gen_.load(std::memory_order_acquire);
         if (quit_.load()) return;
-        work(wk, vec);
+        work(vec);
         done_.fetch_add(1, std::memory_order_acq_rel);  // this worker has left the task
     }
 }
@@ -422,14 +417,15 @@ double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int
     std::atomic<bool> stop{false};
     std::vector<long> done(threads, 0);
     auto run = [&](int t) {
-        Work wk;
-        wk.size(L);
-        std::vector<float> xf(L.H), y(L.H, 0.0f);
-        for (int i = 0; i < L.H; ++i) xf[i] = bf16_to_f32(x[i]);
-        split_even_odd(xf.data(), L.NB, wk.xe.data(), wk.xo.data());
+        TokenBuf xb;
+        xb.size(L);
+        split_blocks(x.data(), 0, L.NB, xb.xe.data(), xb.xo.data());
+        ExpertBuf eb;
+        eb.size(L);
+        std::vector<float> y(L.H, 0.0f);
         while (!stop.load(std::memory_order_relaxed)) {
             const long j = next.fetch_add(1);
-            expert_one(L, blobs[j % n], 1.0f, wk, y.data(), vec);
+            expert_one(L, blobs[j % n], 1.0f, xb, eb, y.data(), vec);
             ++done[t];
         }
     };

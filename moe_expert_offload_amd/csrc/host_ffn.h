@@ -25,18 +25,50 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
 // over blobs[0..n) round robin for about min_seconds
 double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int threads, double min_seconds);
 
-struct Work;
+// one expert's intermediate state for one token: g, u [I] and the
+// intermediate vector split into the even / odd elements of each 32-block
+struct ExpertBuf {
+    std::vector<float> g, u, ae, ao;
+    void size(const Layout& L) {
+        if ((int)g.size() == L.I && (int)ae.size() == L.NBI * 16) return;
+        g.assign(L.I, 0.0f);
+        u.assign(L.I, 0.0f);
+        ae.assign((size_t)L.NBI * 16, 0.0f);
+        ao.assign((size_t)L.NBI * 16, 0.0f);
+    }
+};
 
-// Persistent host workers for the hybrid backend: one task at a time, y[H]
-// (FP32) = sum_j w[j] * FFN_j(x) over up to 16 experts.  Three phases over all
-// of the task's experts, each handing out small units through an atomic
-// counter and ending when all of its units are done: (expert, gate/up tiles),
-// (expert, blocks of the intermediate vector), then chunks of output rows,
-// each summed over the experts in order by the participant that takes it.
-// The caller of wait() works on the task as well.  Every value is
-// computed by one worker in a fixed order, so the result does not depend on
-// the worker count or on which worker takes a unit.
-// Workers spin between tasks and sleep after 20 ms idle.
+// a token's hidden state in FP32, split even / odd per 32-block
+struct TokenBuf {
+    std::vector<float> xe, xo;
+    void size(const Layout& L) {
+        if ((int)xe.size() == L.NB * 16) return;
+        xe.assign((size_t)L.NB * 16, 0.0f);
+        xo.assign((size_t)L.NB * 16, 0.0f);
+    }
+};
+
+constexpr int kHostMaxTokens = 16;    // tokens of one host task
+constexpr int kHostMaxEntries = 256;  // (expert, token) pairs of one host task
+
+// one expert applied to one token of a task, weighted by w
+struct HostEntry {
+    const uint8_t* blob;  // the expert's blob in the pool's layout (host memory)
+    float w;
+    int tok;              // index into the task's tokens
+};
+
+// Persistent host workers for the hybrid backend: one task at a time, for
+// each of up to 16 tokens b, y_b[H] (FP32) = sum over the task's entries of
+// token b, in their order, of w * FFN(x_b).  Four phases, each handing out
+// small units through an atomic counter and ending when all of its units are
+// done: (token, blocks of x) to FP32, (entry, gate/up tiles), (entry, blocks
+// of the intermediate vector), then (token, chunks of output rows), each
+// summed over the token's entries in order by the participant that takes it.
+// The caller of wait() works on the task as well.  Every value is computed by
+// one participant in a fixed order, so the result does not depend on the
+// worker count or on which worker takes a unit.  Workers spin between tasks
+// and sleep after 20 ms idle.
 class HostExpertPool {
 public:
     ~HostExpertPool();
@@ -44,33 +76,35 @@ public:
     void stop();
     bool running() const { return n_ > 0; }
     int workers() const { return n_; }
-    // x (bf16, host) and y (FP32, host) must stay valid until wait() returns
-    void submit(const Layout& L, const uint8_t* const* blobs, const float* w, int n, const uint16_t* x, float* y);
+    // x[b] (bf16 [H], host) and y[b] (FP32 [H], host) for b < n_tok must stay
+    // valid until wait() returns; entries are copied (at most kHostMaxEntries,
+    // tokens below min(n_tok, kHostMaxTokens); others are dropped)
+    void submit(const Layout& L, int n_tok, const uint16_t* const* x, float* const* y, const HostEntry* entries,
+                int n);
     void wait();  // helps with the task, then returns once it is complete
-    // nanoseconds from submit to the last worker's finish, summed over tasks
+    // nanoseconds from submit to the last unit's finish, summed over tasks
     uint64_t busy_ns() const { return busy_ns_.load(); }
 
 private:
     struct Task {
         Layout L{};
-        const uint8_t* blobs[16] = {};
-        float w[16] = {};
-        int n = 0;
-        const uint16_t* x = nullptr;
-        float* y = nullptr;
-        int gu_chunk = 1, act_chunk = 1, d_chunk = 1;  // unit sizes of the three phases
+        HostEntry e[kHostMaxEntries] = {};  // grouped by token
+        int tok_begin[kHostMaxTokens + 1] = {};
+        int n = 0, ntok = 0;
+        const uint16_t* x[kHostMaxTokens] = {};
+        float* y[kHostMaxTokens] = {};
+        int x_chunk = 1, gu_chunk = 1, act_chunk = 1, d_chunk = 1;  // unit sizes of the phases
     };
     void run(int t);
-    void work(Work& wk, bool vec);
+    void work(bool vec);
     int n_ = 0;
     Task task_;
     std::vector<std::thread> threads_;
-    std::vector<Work*> work_;
-    Work* shared_ = nullptr;  // [16]: per expert g, u and the intermediate vector
+    std::vector<ExpertBuf> ebuf_;  // per entry: g, u and the intermediate vector
+    std::vector<TokenBuf> xbuf_;   // per token: x split even / odd
     std::atomic<int> gen_{0}, done_{0};
-    std::atomic<int> gu_next_{0}, act_next_{0}, d_next_{0};  // next unit of each phase
-    std::atomic<int> gu_done_{0}, act_done_{0}, d_done_{0};  // units finished per phase
-    Work* caller_work_ = nullptr;                            // buffers of the waiting caller
+    std::atomic<int> x_next_{0}, gu_next_{0}, act_next_{0}, d_next_{0};  // next unit of each phase
+    std::atomic<int> x_done_{0}, gu_done_{0}, act_done_{0}, d_done_{0};  // units finished per phase
     std::atomic<uint64_t> busy_ns_{0};
     std::chrono::steady_clock::time_point t_submit_{};
     std::atomic<bool> quit_{false};

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
     for (int i = tid; i < n; i += KG_THREADS) {
         const int sl = a.slots[i];
         if ((unsigned)sl < (unsigned)a.C) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
-        else atomicAdd(&s_invalid, 1);
+        else if (!(a.host_rows && sl == -1)) atomicAdd(&s_invalid, 1);  // -1 with host_rows: the host's row
     }
     __syncthreads();
     // nw <= 512: one bitmap word per thread; rank of a slot = present slots below it
@@ -138,6 +138,7 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
     __syncthreads();
     for (int i = tid; i < n; i += KG_THREADS) {
         const int sl = a.slots[i];
+        if (sl < 0) continue;  // a host row
         const int g = s_pre[sl >> 5] + __popc(s_bits[sl >> 5] & ((1u << (sl & 31)) - 1u));
         atomicAdd(&s_cnt[g], 1);
     }
@@ -184,6 +185,7 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
     // token only, so the order inside a group does not change any result
     for (int i = tid; i < n; i += KG_THREADS) {
         const int sl = a.slots[i];
+        if (sl < 0) continue;  // a host row
         const int g = s_pre[sl >> 5] + __popc(s_bits[sl >> 5] & ((1u << (sl & 31)) - 1u));
         a.p.perm[s_off[g] + atomicAdd(&s_cur[g], 1)] = i;
     }
@@ -573,6 +575,7 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
     } else {
         for (int j = 0; j < c.k; ++j) {
             const int row = b * c.k + j;
+            if (c.host_rows && c.slots[row] < 0) continue;  // computed by the host
             const float wj = c.w[row];
             const float4 v = *reinterpret_cast<const float4*>(c.yp + (size_t)row * c.H + h);
             acc.x += wj * v.x;
@@ -583,6 +586,14 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
         for (int s = 0; s < c.n_shared; ++s) {
             const int row = c.B * c.k + s * c.B + b;
             const float4 v = *reinterpret_cast<const float4*>(c.yp + (size_t)row * c.H + h);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        if (c.yh) {
+            // the host-computed experts' weighted sum for this token (host-mapped memory)
+            const float4 v = *reinterpret_cast<const float4*>(c.yh + (size_t)b * c.H + h);
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;

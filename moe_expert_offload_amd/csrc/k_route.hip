@@ -334,6 +334,14 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     if (hit && !stat) atomicOr(&s_hitbits[v >> 5], 1u << (v & 31));
     if (miss) s_miss_e[mr] = e;
     __syncthreads();
+    // hybrid split (LRU, routed batches of at most 16 tokens): the first q misses
+    // (ascending expert id) are transferred, q = m B_P / B_H to the nearest
+    // integer (halves up); the rest are computed by the host and take no slot
+    int q = nm;
+    if (!stat && a.hybrid && nm > 0 && a.bh > a.bp && a.bp > 0.0) {
+        q = (int)floor((double)nm * a.bp / a.bh + 0.5);
+        q = q < 0 ? 0 : (q > nm ? nm : q);
+    }
 
     // victims, by miss rank
     if (stat) {
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         if (tid < nm) s_victim[tid] = a.R + (int)((clock0 + tid) % a.T);
     } else {
         // stable compaction of the victim order: non-hit slots keep their order;
-        // the first nm of them are this step's victims
+        // the first q of them are this step's victims
         int kept = 0;
 #pragma unroll
         for (int c = 0; c < K2_CPT; ++c) {
@@ -357,15 +365,15 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
 #pragma unroll
         for (int c = 0; c < K2_CPT; ++c) {
             if (ent[c] < 0) continue;
-            if (kr < nm) s_victim[kr] = ent[c];
-            else order_out[kr - nm] = ent[c];
+            if (kr < q) s_victim[kr] = ent[c];
+            else order_out[kr - q] = ent[c];
             ++kr;
         }
     }
     __syncthreads();
-    // final slot of every requested expert
+    // final slot of every requested expert (-1: computed by the host)
     if (hit) s_req[e] = v;
-    if (tid < nm) s_req[s_miss_e[tid]] = s_victim[tid];
+    if (tid < nm) s_req[s_miss_e[tid]] = tid < q ? s_victim[tid] : -1;
     __syncthreads();
 
     // The miss list goes to host memory as soon as it is known, from wave 0
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     if (tid < 64) {
         for (int i = tid; i < nm; i += 64) {
             a.ml->e[i].expert = s_miss_e[i];
-            a.ml->e[i].slot = s_victim[i];
+            a.ml->e[i].slot = i < q ? s_victim[i] : -1;
         }
         if (tid < a.k && tid < 16) {
             const int id = ids_lds ? s_ids[tid] : a.ids[tid];
@@ -384,9 +392,16 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
             a.ml->w0[tid] = a.z ? s_w0[tid] : 0.0f;
             a.ml->ids0[tid] = id;
         }
+        if (q < nm) {
+            // every token's experts and weights, for the host's share of a batch
+            for (int i = tid; i < a.n_ids && i < HYB_MAX_IDS; i += 64) {
+                a.ml->ids_all[i] = ids_lds ? s_ids[i] : a.ids[i];
+                a.ml->w_all[i] = a.w[i];
+            }
+        }
         if (tid == 0) {
             a.ml->n_miss = nm;
-            a.ml->n_xfer = nm;
+            a.ml->n_xfer = q;
             a.ml->n_unique = nh + nm;
             a.ml->n_invalid = s_invalid;
         }
@@ -398,7 +413,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     if (hit) {
         if (!stat) {
             a.c.stamp[v] = clock0 + hr;
-            order_out[C - nh - nm + hr] = v;
+            order_out[C - nh - q + hr] = v;
         }
         const int64_t ti = trace_base + hr;
         if (ti < a.c.trace_cap) {
@@ -406,7 +421,15 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
             a.c.trace[ti] = t;
         }
     }
-    if (tid < nm) {
+    if (tid >= q && tid < nm) {
+        // computed by the host: no slot, the cache unchanged
+        const int64_t ti = trace_base + nh + tid;
+        if (ti < a.c.trace_cap) {
+            TraceRec t = {a.step, l, s_miss_e[tid], -1, 0, -1};
+            a.c.trace[ti] = t;
+        }
+    }
+    if (tid < q) {
         const int me = s_miss_e[tid];
         const int vv = s_victim[tid];
         const int old = a.c.key_of[vv];  // the static split's transient slots keep their last occupant
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         if (!stat) {
             a.c.slot_of[l * E + me] = vv;
             a.c.stamp[vv] = clock0 + nh + tid;
-            order_out[C - nm + tid] = vv;
+            order_out[C - q + tid] = vv;
         }
         const int64_t ti = trace_base + nh + tid;
         if (ti < a.c.trace_cap) {
@@ -435,11 +458,12 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     __syncthreads();
     if (tid == 0) {
         const int n = nh + nm;
-        *a.c.clock = clock0 + (stat ? nm : n);  // static: transient slots used so far
+        *a.c.clock = clock0 + (stat ? nm : nh + q);  // static: transient slots used so far
         a.c.counters[0] += (uint64_t)nh;
         a.c.counters[1] += (uint64_t)nm;
         a.c.counters[2] += (uint64_t)s_evict;
         a.c.counters[3] += 1ull;
+        a.c.counters[4] += (uint64_t)(nm - q);
         int64_t fit = a.c.trace_cap - trace_base;
         fit = fit < 0 ? 0 : (fit > n ? n : fit);
         a.c.trace_head[0] = (uint64_t)(trace_base + fit);

@@ -87,7 +87,7 @@ struct moe_ctx {
     uint64_t ffn_launches = 0;
     double k3_ms = 0, k4_ms = 0;
     std::vector<ProfSlot> prof_used, prof_free;
-    // hybrid backend: part of a one-token step's misses computed by host workers
+    // hybrid backend: part of a step's misses (batches of at most 16 tokens) computed by host workers
     int backend = MOE_BACKEND_OFFLOAD;
     double hyb_bp = 0.0, hyb_bh = 0.0;   // B_P and B_H of the split
     HostExpertPool hpool;
@@ -98,7 +98,8 @@ struct moe_ctx {
     int64_t xh_stride = 0;
     bool xh_pending = false;
     bool hyb_call = false;               // the current call runs hybrid steps
-    float* yh = nullptr;                 // host-mapped [2][H]: the host experts' sum per parity
+    int hyb_B = 0;                       // its token count
+    float* yh = nullptr;                 // host-mapped [2][16][H]: the host experts' sums per parity and token
     bool host_has[2] = {false, false};   // this parity's FFN adds yh[parity]
     int host_running = -1;               // parity of the host task in flight, -1: none
     uint64_t host_tasks = 0;
@@ -143,6 +144,7 @@ moe_status set_err(moe_ctx* c, moe_status st, const char* fmt, ...) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int MAX_CACHE_SLOTS = 16384;  // the resolve and grouping kernels' slot capacity
+constexpr int MAX_EXPERTS = 1024;       // experts per layer the resolve kernel handles
 
 // distinct experts one layer step can request; the cache needs twice that (one layer in flight
 // while the next one's victims are chosen)
@@ -153,7 +155,7 @@ int64_t min_cache_slots(const moe_config* c) {
 // shape checks; cache_slots == 0 passes only when allow_auto (size queries before auto sizing)
 moe_status check_cfg(const moe_config* c, bool allow_auto = false) {
     if (!c) return MOE_EINVAL;
-    if (c->n_layers < 1 || c->n_experts < 1 || c->n_experts > 1024 || c->top_k < 1 ||
+    if (c->n_layers < 1 || c->n_experts < 1 || c->n_experts > MAX_EXPERTS || c->top_k < 1 ||
         c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
         c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 0 ||
@@ -342,7 +344,7 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
     a.policy = c->cfg.policy;
     a.T = c->static_T;
     a.R = c->cfg.cache_slots - c->static_T;
-    a.hybrid = (c->hyb_call && routed && B == 1) ? 1 : 0;
+    a.hybrid = (c->hyb_call && routed && B <= kHostMaxTokens) ? 1 : 0;
     a.bp = c->hyb_bp;
     a.bh = c->hyb_bh;
     const int p = c->parity;
@@ -351,14 +353,16 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
     return MOE_OK;
 }
 
-// Hybrid steps need the token's hidden states on the host: one device-to-host
-// copy per call of the `layers` vectors at stride xs (elements), ordered after
-// everything already on the compute stream.  Only one-token calls with the LRU
-// policy run hybrid steps.
+// Hybrid steps need the tokens' hidden states on the host: one device-to-host
+// copy per call of the `layers` [B][H] blocks at stride xs (elements), ordered
+// after everything already on the compute stream.  Calls of at most 16 tokens
+// with the LRU policy run hybrid steps (batches through the grouped FFN path).
 moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
     c->hyb_call = false;
-    if (c->backend != MOE_BACKEND_HYBRID || B != 1 || c->cfg.policy != MOE_POLICY_LRU || xs < 0) return MOE_OK;
-    const size_t bytes = ((size_t)(layers - 1) * (size_t)xs + (size_t)c->cfg.hidden) * 2;
+    if (c->backend != MOE_BACKEND_HYBRID || B > kHostMaxTokens || c->cfg.policy != MOE_POLICY_LRU || xs < 0 ||
+        (B > 1 && (c->cfg.flags & MOE_FLAG_PER_TOKEN_FFN)))
+        return MOE_OK;
+    const size_t bytes = ((size_t)(layers - 1) * (size_t)xs + (size_t)B * c->cfg.hidden) * 2;
     if (bytes > c->xh_cap) {
         if (c->xh) HIPCHK(c, hipHostFree(c->xh));
         c->xh = nullptr;
@@ -374,6 +378,7 @@ moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
     c->xh_pending = true;
     c->xh_stride = xs;
     c->hyb_call = true;
+    c->hyb_B = B;
     return MOE_OK;
 }
 
@@ -405,30 +410,49 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     }
     c->tok0_valid[par] = true;
     if (nx < nm) {
-        // hybrid step: token 0's experts without a slot run on the host workers, in rank order
+        // hybrid step: the experts without a slot run on the host workers, for every
+        // token that selected them, in rank order
         if (!c->hyb_call || !c->hpool.running())
             return set_err(c, MOE_EINVAL, "host share in a step that is not hybrid");
         if (c->xh_pending) {
             HIPCHK(c, hipEventSynchronize(c->xs_done));
             c->xh_pending = false;
         }
-        const uint8_t* blobs[16];
-        float w[16];
+        const int B = c->hyb_B, k = c->cfg.top_k, E = c->cfg.n_experts;
+        HostEntry ent[kHostMaxEntries];
         int nh = 0;
-        for (int j = 0; j < c->cfg.top_k; ++j)
-            if (ml->slot0[j] < 0) {
-                blobs[nh] = c->blob_src((size_t)layer * c->cfg.n_experts + ml->ids0[j]);
-                w[nh++] = ml->w0[j];
+        if (B == 1) {
+            for (int j = 0; j < k; ++j)
+                if (ml->slot0[j] < 0)
+                    ent[nh++] = {c->blob_src((size_t)layer * E + ml->ids0[j]), ml->w0[j], 0};
+        } else {
+            uint64_t host_set[(MAX_EXPERTS + 63) / 64] = {};
+            for (int i = nx; i < nm; ++i) {
+                const int e = ml->e[i].expert;
+                host_set[e >> 6] |= 1ull << (e & 63);
             }
+            for (int i = 0; i < B * k; ++i) {
+                const int e = ml->ids_all[i];
+                if ((unsigned)e < (unsigned)E && ((host_set[e >> 6] >> (e & 63)) & 1ull))
+                    ent[nh++] = {c->blob_src((size_t)layer * E + e), ml->w_all[i], i / k};
+            }
+        }
         if (c->host_running >= 0) {
-            // one task at a time: the previous layer's host experts finish first (its sum
-            // stays in its own parity's buffer for that layer's FFN)
+            // one task at a time: the previous layer's host experts finish first (their sums
+            // stay in their own parity's buffers for that layer's FFN)
             const auto tw = std::chrono::steady_clock::now();
             c->hpool.wait();
             c->host_wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
             c->host_running = -1;
         }
-        c->hpool.submit(c->lay, blobs, w, nh, c->xh + (size_t)layer * c->xh_stride, c->yh + (size_t)par * c->cfg.hidden);
+        const uint16_t* xs[kHostMaxTokens];
+        float* ys[kHostMaxTokens];
+        const size_t H = c->cfg.hidden;
+        for (int b = 0; b < B; ++b) {
+            xs[b] = c->xh + (size_t)layer * c->xh_stride + (size_t)b * H;
+            ys[b] = c->yh + ((size_t)par * kHostMaxTokens + b) * H;
+        }
+        c->hpool.submit(c->lay, B, xs, ys, ent, nh);
         c->host_running = par;
         c->host_has[par] = true;
         ++c->host_tasks;
@@ -485,7 +509,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
             c->host_running = -1;
         }
         c->host_has[par] = false;
-        yh = c->yh + (size_t)par * c->cfg.hidden;
+        yh = c->yh + (size_t)par * kHostMaxTokens * c->cfg.hidden;
     }
     if (n_miss > 0 && par < 2) {
         if (c->copy_used[par][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
@@ -507,6 +531,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         g.C = c->cfg.cache_slots;
         g.n_shared = c->cfg.n_shared;
         g.gm = grouped_gm(B);
+        g.host_rows = yh ? 1 : 0;
         g.p.max_groups = grouped_max_groups(B, c->cfg.top_k, c->cfg.n_experts, c->cfg.n_shared);
         g.p.max_chunks = grouped_max_chunks(B, c->cfg.top_k, c->cfg.n_experts, c->cfg.n_shared, g.gm);
         GemmArgs m{};
@@ -538,6 +563,8 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         cb.n_shared = c->cfg.n_shared;
         cb.H = c->cfg.hidden;
         cb.C = c->cfg.cache_slots;
+        cb.yh = yh;
+        cb.host_rows = yh ? 1 : 0;
         LAUNCHCHK(c, launch_grouped_ffn(g, m, cb, c->cs, prof ? ps.ev[1] : nullptr));
     } else {
     FfnArgs f{};
@@ -1064,7 +1091,7 @@ moe_status moe_set_backend(moe_ctx* c, int32_t backend, double pcie_gbps, double
         return set_err(c, MOE_EINVAL, "backend %d with B_P %g, B_H %g, %d threads", backend, pcie_gbps, host_gbps,
                        host_threads);
     if (c->cfg.policy != MOE_POLICY_LRU) return set_err(c, MOE_EINVAL, "the hybrid backend needs the LRU policy");
-    if (!c->yh && hipHostMalloc((void**)&c->yh, 2 * (size_t)c->cfg.hidden * sizeof(float),
+    if (!c->yh && hipHostMalloc((void**)&c->yh, 2 * (size_t)kHostMaxTokens * c->cfg.hidden * sizeof(float),
                                 hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
         return set_err(c, MOE_ENOMEM, "host-mapped buffer for the host experts' sums");
     if (!c->xs_stream) {

@@ -56,6 +56,8 @@ __host__ __device__ inline int seg_len(int n, int S, int s) { return n / S + (s 
 __host__ __device__ inline int seg_begin(int n, int S, int s) { return s * (n / S) + (s < n % S ? s : n % S); }
 
 // host-mapped miss list written by the resolve kernel for one layer step
+constexpr int HYB_MAX_IDS = 256;  // B * k of a hybrid batch step
+
 struct MissEntry {
     int32_t expert, slot;
 };
@@ -67,6 +69,8 @@ struct MissList {
     float w0[16];              // routing weights of token 0 (when the step was routed)
     int32_t ids0[16];          // token 0's experts (ranked)
     int32_t n_xfer;            // misses transferred (entries [0, n_xfer)); the rest have slot -1
+    int32_t ids_all[256];      // hybrid batches (n_xfer < n_miss, B * k <= 256): every token's
+    float w_all[256];          // experts and weights, [B][k]
     MissEntry e[1];            // [n_miss], sized at allocation: min(max_tokens*k, E)
 };
 
@@ -151,6 +155,7 @@ struct GroupArgs {
     GroupPlanDev p;
     const int32_t* slots;   // [B*k]
     int B, k, C, n_shared, gm;
+    int host_rows;          // 1: slot -1 marks a row computed by the host (left out of the groups)
 };
 
 struct GemmArgs {
@@ -168,9 +173,11 @@ struct GemmArgs {
 struct CombineArgs {
     const float* yp;
     const float* w;         // [B][k]
-    const int32_t* slots;   // [B][k] (a row with an invalid slot is skipped)
+    const int32_t* slots;   // [B][k]
     uint16_t* y;            // [B][H] bf16
+    const float* yh;        // [B][H] FP32 sums of the host-computed rows (host_rows), or NULL
     int B, k, n_shared, H, C;
+    int host_rows;          // 1: rows with slot -1 were computed by the host and are skipped
 };
 
 // launchers (defined next to their kernels)

@@ -1,5 +1,6 @@
-"""Hybrid backend on the device: a one-token step transfers q = m B_P / B_H of its m misses and the
-host workers compute the rest.  Against the oracle: ids, cache trace (host misses carry slot -1),
+"""Hybrid backend on the device: a decode step (one token, or a batch of at most 16 lock-step
+requests) transfers q = m B_P / B_H of its m misses and the host workers compute the rest, for
+every token that selected them.  Against the oracle: ids, cache trace (host misses carry slot -1),
 final cache state and counters bit-exact with the oracle's hybrid steps; outputs within relative
 L2 5e-3 and max|diff| 1e-2 * max|ref| of the plain MoE output (placement does not change it)."""
 import numpy as np
@@ -14,6 +15,10 @@ pytestmark = pytest.mark.gpu
 TOY = synth.WORKLOADS["toy"]
 SHARED = synth.Workload("hyb_shared_k8", 3, 32, 8, 1, 2048, 512, 20, 12, 1, 0.8, seed=51)
 WIDE = synth.Workload("hyb_2880", 3, 16, 4, 0, 2880, 2880, 10, 10, 1, 0.7, seed=52)
+# batches of lock-step requests (the grouped FFN path); capacity C >= 2 min(B k, E)
+BATCH4 = synth.Workload("hyb_b4", 3, 32, 4, 1, 512, 256, 40, 10, 4, 0.8, seed=53)
+BATCH16 = synth.Workload("hyb_b16_k8", 3, 64, 8, 0, 1024, 512, 130, 8, 16, 0.8, seed=54)
+BATCH8W = synth.Workload("hyb_b8_2880", 2, 16, 4, 1, 2880, 2880, 32, 6, 8, 0.7, seed=55)
 
 # (B_P, B_H): every miss on the host (q = round(m / 40) = 0 for m < 20), the pages' calibration
 # (q = 0.59 m), this box's measured ratio (q = 0.19 m), and no spare host bandwidth (offload)
@@ -42,13 +47,14 @@ def _check(wl, X, W, m, ids, w, y, split):
         (c["hits"], c["misses"], c["evictions"], c["host"])
     assert cnt["h2d_copies"] == c["misses"] - c["host"]
     worst = 0.0
-    T = X.shape[0]
+    T, B = X.shape[:2]
     for t in range(T):
         for l in range(wl.n_layers):
-            r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
-            rel, mx, ok = close_enough(y[t, l, 0], r)
-            worst = max(worst, rel)
-            assert ok, (t, l, rel, mx)
+            for b in range(B):
+                r = oracle.moe_output(wl, l, X[t, b], ref["ids"][t, l, b], ref["w"][t, l, b])
+                rel, mx, ok = close_enough(y[t, l, b], r)
+                worst = max(worst, rel)
+                assert ok, (t, l, b, rel, mx)
     return c, worst
 
 
@@ -63,6 +69,44 @@ def test_hybrid_decode_matches_oracle(wl, split):
     if split[1] > split[0]:
         assert c["host"] > 0
     m.close()
+
+
+@pytest.mark.parametrize("split", SPLITS[:3], ids=[f"{a}_{b}" for a, b in SPLITS[:3]])
+@pytest.mark.parametrize("wl", [BATCH4, BATCH16, BATCH8W], ids=lambda w: w.name)
+def test_hybrid_batch_decode_matches_oracle(wl, split):
+    X = synth.decode_inputs(wl)
+    m, W = _hybrid(wl, split)
+    ids, w, y = run_stack(m, wl, X)
+    c, worst = _check(wl, X, W, m, ids, w, y, split)
+    print(wl.name, split, c, "worst rel-L2 %.2e" % worst)
+    assert c["host"] > 0
+    cnt, _ = m.stats()
+    assert cnt["host_tasks"] > 0
+    m.close()
+
+
+def test_hybrid_batch_is_bitwise_independent_of_workers_and_lookahead():
+    wl = BATCH8W
+    X = synth.decode_inputs(wl)[:4]
+    outs = []
+    for threads, la in ((1, 1), (9, 1), (4, 0)):
+        m, _ = _hybrid(wl, (26.7, 45.5), threads=threads, lookahead=la)
+        outs.append(run_stack(m, wl, X)[2])
+        m.close()
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
+def test_hybrid_batches_beyond_16_tokens_and_per_token_ffn_run_offload_steps():
+    import moe_expert_offload_amd as M
+    big = synth.Workload("hyb_b20", 2, 32, 4, 0, 512, 256, 64, 4, 20, 0.8, seed=56)
+    for wl, flags in ((big, 0), (BATCH4, M.MOE_FLAG_PER_TOKEN_FFN)):
+        X = synth.decode_inputs(wl)
+        m, W = _hybrid(wl, (10.0, 400.0), flags=flags)
+        ids, w, y = run_stack(m, wl, X)
+        c, _ = _check(wl, X, W, m, ids, w, y, None)
+        assert c["host"] == 0
+        m.close()
 
 
 def test_hybrid_is_bitwise_independent_of_workers_and_lookahead():
