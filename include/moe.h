@@ -258,18 +258,21 @@ typedef struct {
 moe_status moe_calibrate_backend(moe_ctx* ctx, int32_t host_threads, double host_seconds, double threshold,
                                  moe_bw_profile* out);
 
-/* Selects the backend of the context's later one-token steps.
+/* Selects the backend of the context's later decode steps.
  * MOE_BACKEND_OFFLOAD (default): every miss is transferred.
- * MOE_BACKEND_HYBRID: in a routed one-token step (moe_stack_forward or
- *   moe_layer_forward with n_tokens 1) the resolve kernel transfers only the
- *   first q = moe_hybrid_split(m, pcie_gbps, host_gbps) of the step's m misses
- *   (ascending expert id) into cache slots; the other m - q take no slot,
- *   leave the cache unchanged (their trace records carry slot -1) and are
- *   computed by host_threads persistent host workers (the host expert kernel,
- *   each expert split over all workers), reading the pool; the down kernel adds
- *   their weighted sum before rounding.  The token's hidden states are copied
- *   to the host once per call.  Batches and moe_cache_resolve stay offload.
- *   The workers spin between tasks and sleep after 20 ms idle.
+ * MOE_BACKEND_HYBRID: in a routed step of at most 16 tokens (moe_stack_forward
+ *   or moe_layer_forward) the resolve kernel transfers only the first
+ *   q = moe_hybrid_split(m, pcie_gbps, host_gbps) of the step's m distinct
+ *   missing experts (ascending expert id) into cache slots; the other m - q
+ *   take no slot, leave the cache unchanged (their trace records carry slot
+ *   -1) and are computed by host_threads persistent host workers (the host
+ *   expert kernel, work split over all workers), reading the pool, for every
+ *   token of the step that selected them.  The FFN adds each token's host sum
+ *   before rounding its output.  The tokens' hidden states are copied to the
+ *   host once per call.  Steps of more tokens, steps run with
+ *   MOE_FLAG_PER_TOKEN_FFN and more than one token, and moe_cache_resolve
+ *   transfer every miss.  The workers spin between tasks and sleep after
+ *   20 ms idle.
  * Needs the LRU policy.  Synchronises the compute stream.
  * Errors: MOE_EINVAL (backend, bandwidths <= 0, threads outside 1..256,
  * static policy), MOE_ENOMEM, MOE_ESTATE, MOE_EHIP. */

@@ -247,6 +247,11 @@ class StaticCache:
 
 
 # ------------------------------------------------------------ whole runs --
+# Steps of more tokens than this run every miss through the cache even under the hybrid
+# backend (the host share is a decode-time split; a prefill chunk transfers all of its misses).
+HYBRID_MAX_TOKENS = 16
+
+
 def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=None, split=None):
     """Routing and cache trace of a decode run.
 
@@ -255,9 +260,12 @@ def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=N
     Steps run in order t = 0..T-1, layers 0..L-1 inside a step.
     Returns dict with ids [T][L][B][k], w [T][L][B][k], slots [T][L][B][k],
     trace (structured array), counters.  split = (pcie_GBps, host_GBps) runs the hybrid
-    backend's cache steps (misses beyond the transferred share take no slot).
+    backend's cache steps (misses beyond the transferred share take no slot) when B is at
+    most HYBRID_MAX_TOKENS.
     """
     T, B, H = X.shape
+    if B > HYBRID_MAX_TOKENS:
+        split = None
     L, k = wl.n_layers, wl.top_k
     steps = range(T) if steps is None else steps
     Xf = X.reshape(T * B, H)
@@ -278,15 +286,18 @@ def decode_trace(wl: "synth.Workload", W_all: np.ndarray, X: np.ndarray, steps=N
             "counters": cache.counters(), "cache": cache}
 
 
-def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X, static_transient: int = 0):
+def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X, static_transient: int = 0, split=None):
     """Routing and cache trace of a run whose steps have their own token counts.
 
     steps_X: list of [B_t][H] bf16-bit arrays; step t feeds X_t to every layer (a prefill
     chunk is one step whose B_t is the chunk length).  Steps run in order, layers 0..L-1
     inside a step.  Returns dict with per-step lists ids[t] [L][B_t][k], w[t], slots[t],
     the trace (structured array), counters and the cache.  static_transient > 0 runs the static
-    per-layer split with that many transient slots instead of the LRU cache.
+    per-layer split with that many transient slots instead of the LRU cache.  split =
+    (pcie_GBps, host_GBps) runs the hybrid backend's cache steps for the steps of at most
+    HYBRID_MAX_TOKENS tokens.
     """
+    assert not (split and static_transient), "the hybrid split runs on the LRU cache"
     L, k = wl.n_layers, wl.top_k
     Xc = np.concatenate([np.asarray(x, dtype=np.uint16).reshape(-1, wl.hidden) for x in steps_X])
     layers, toks, shapes = [], [], []
@@ -309,8 +320,9 @@ def run_trace(wl: "synth.Workload", W_all: np.ndarray, steps_X, static_transient
         w = w_all[pos:pos + L * B].reshape(L, B, k)
         pos += L * B
         slots = np.empty_like(ids)
+        sp = split if B <= HYBRID_MAX_TOKENS else None
         for l in range(L):
-            s, r = cache.step(t, l, ids[l])
+            s, r = cache.step(t, l, ids[l], sp) if sp else cache.step(t, l, ids[l])
             slots[l] = s.reshape(B, k)
             recs.append(r)
         out["ids"].append(ids)

@@ -92,3 +92,40 @@ def test_gptoss_shaped_hybrid_sampled():
         print("hybrid t", t, "l", l, "rel-L2", rel)
         assert ok, (t, l, rel, mx)
     m.close()
+
+
+def test_qwen38_shaped_hybrid_prefill_and_b16_decode_sampled():
+    """The 48 x 512-expert workload with the hybrid backend (B_P 56 GB/s, B_H 290 GB/s, 14 host
+    workers): the 2048-token prefill chunk transfers all of its misses, the 16-request decode
+    steps split theirs.  ids, weights, the whole trace (host misses with slot -1) and the final
+    cache state bit-exact with the oracle; outputs at sampled (step, layer, token) points."""
+    import gc
+    from gpu_helpers import run_steps
+    wl = synth.WORKLOADS["qwen38_flash_next_shaped"]
+    T = 6
+    X = synth.decode_inputs(wl)[:T]
+    steps = [synth.prefill_inputs(wl)] + [X[t] for t in range(T)]
+    split = (56.0, 290.0)
+    m, W = make_moe(wl)
+    m.set_backend("hybrid", split[0], split[1], 14)
+    ids, w, y = run_steps(m, wl, steps)
+    cnt, recs = m.stats(trace_cap=1 << 21)
+    slot_of, key_of, _ = m.cache_state()
+    m.close()
+    del m
+    gc.collect()
+    ref = oracle.run_trace(wl, W, steps, split=split)
+    for t in range(len(steps)):
+        np.testing.assert_array_equal(ids[t], ref["ids"][t])
+        assert np.max(np.abs(w[t] - ref["w"][t])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    r_slot, r_key, _ = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    assert cnt["host_experts"] == ref["counters"]["host"] > 0
+    L = wl.n_layers
+    for (t, l, b) in [(0, 5, 2047), (1, 0, 0), (1, L - 1, 15), (3, 20, 7), (T, L - 1, 0), (T, 11, 9)]:
+        r = oracle.moe_output(wl, l, steps[t][b], ref["ids"][t][l, b], ref["w"][t][l, b])
+        rel, mx, ok = close_enough(y[t][l, b], r)
+        print("hybrid t", t, "l", l, "b", b, "rel-L2", rel)
+        assert ok, (t, l, b, rel, mx)
