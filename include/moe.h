@@ -298,6 +298,21 @@ int32_t moe_hybrid_split(int32_t n_miss, double pcie_gbps, double host_gbps);
 moe_status moe_host_expert_ffn(const moe_config* cfg, const uint8_t* const* blobs, const float* w, int32_t n,
                                const uint16_t* x, float* y, int32_t threads);
 
+/* The hybrid backend's host workers on one task, for callers and tests with no
+ * GPU: for every token b < n_tok, y[b][H] (FP32, host) = the sum over the
+ * entries j with tok[j] == b, in their order, of w[j] * FFN_j(x[b]), where
+ * blobs[j] is an expert in the pool's layout (host memory) and x is bf16
+ * [n_tok][H] (host); a token with no entry gets zeros.  The work runs on
+ * `threads` persistent workers plus the calling thread (started and stopped
+ * by the call), split into (token, block), (entry, gate/up tile), (entry,
+ * intermediate block) and (token, output rows) units; every value is summed
+ * by one thread in a fixed order, so y does not depend on `threads`.
+ * n_tok in 1..16, n in 0..256, threads in 1..256.
+ * Errors: MOE_EINVAL (arguments, tok[j] outside [0, n_tok)), MOE_ENOMEM. */
+moe_status moe_host_expert_batch(const moe_config* cfg, int32_t n_tok, const uint16_t* x, float* y,
+                                 const uint8_t* const* blobs, const float* w, const int32_t* tok, int32_t n,
+                                 int32_t threads);
+
 /* Converts one logical expert blob (gate codes, gate scales, up codes, up
  * scales, down codes, down scales; 3 * H * I * 17/32 bytes) into the pool's
  * layout (same size, a permutation of the bytes; packed != logical).  Needs no

@@ -72,6 +72,8 @@ _lib.moe_pack_blob.restype = _st
 _lib.moe_pack_blob.argtypes = [ctypes.POINTER(MoeConfig), _P, _P]
 _lib.moe_host_expert_ffn.restype = _st
 _lib.moe_host_expert_ffn.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _I32, _P, _P, _I32]
+_lib.moe_host_expert_batch.restype = _st
+_lib.moe_host_expert_batch.argtypes = [ctypes.POINTER(MoeConfig), _I32, _P, _P, _P, _P, _P, _I32, _I32]
 _lib.moe_hybrid_split.restype = _I32
 _lib.moe_hybrid_split.argtypes = [_I32, ctypes.c_double, ctypes.c_double]
 _lib.moe_set_backend.restype = _st
@@ -101,7 +103,8 @@ _lib.moe_destroy.argtypes = [_P]
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = [_P]
 
-EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_hybrid_split",
+EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_host_expert_batch",
+            "moe_hybrid_split",
             "moe_select_backend", "moe_calibrate_backend", "moe_set_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
             "moe_expert_forward", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
@@ -173,6 +176,26 @@ def host_expert_ffn(cfg: MoeConfig, packed_blobs, w, x, threads=1):
                                   y.ctypes.data, threads)
     if st:
         raise MoeError(st, "moe_host_expert_ffn")
+    return y
+
+
+def host_expert_batch(cfg: MoeConfig, packed_blobs, w, tok, x, threads=1):
+    """The hybrid backend's host workers on one task (moe_host_expert_batch): x bf16 bits
+    [n_tok][H]; returns float32 [n_tok][H], row b = the sum over the entries j with tok[j] == b,
+    in order, of w[j] * FFN_j(x[b])."""
+    import numpy as np
+    blobs = [np.ascontiguousarray(b, dtype=np.uint8) for b in packed_blobs]
+    ptrs = (ctypes.c_void_p * max(len(blobs), 1))(*[b.ctypes.data for b in blobs])
+    wv = np.ascontiguousarray(w, dtype=np.float32)
+    tv = np.ascontiguousarray(tok, dtype=np.int32)
+    xv = np.ascontiguousarray(x, dtype=np.uint16)
+    if xv.ndim != 2 or xv.shape[1] != cfg.hidden or len(wv) != len(blobs) or len(tv) != len(blobs):
+        raise ValueError("x must be [n_tok][hidden]; w and tok one per blob")
+    y = np.empty(xv.shape, dtype=np.float32)
+    st = _lib.moe_host_expert_batch(ctypes.byref(cfg), xv.shape[0], xv.ctypes.data, y.ctypes.data, ptrs,
+                                    wv.ctypes.data, tv.ctypes.data, len(blobs), threads)
+    if st:
+        raise MoeError(st, "moe_host_expert_batch")
     return y
 
 

@@ -1069,6 +1069,34 @@ moe_status moe_host_expert_ffn(const moe_config* cfg, const uint8_t* const* blob
     return MOE_OK;
 }
 
+moe_status moe_host_expert_batch(const moe_config* cfg, int32_t n_tok, const uint16_t* x, float* y,
+                                 const uint8_t* const* blobs, const float* w, const int32_t* tok, int32_t n,
+                                 int32_t threads) {
+    moe_status st = check_cfg(cfg, true);
+    if (st) return st;
+    if (n_tok < 1 || n_tok > kHostMaxTokens || n < 0 || n > kHostMaxEntries || !x || !y ||
+        (n > 0 && (!blobs || !w || !tok)) || threads < 1 || threads > 256)
+        return MOE_EINVAL;
+    std::vector<HostEntry> ent((size_t)n);
+    for (int j = 0; j < n; ++j) {
+        if (!blobs[j] || tok[j] < 0 || tok[j] >= n_tok) return MOE_EINVAL;
+        ent[j] = {blobs[j], w[j], tok[j]};
+    }
+    const Layout L = make_layout(cfg->hidden, cfg->inter);
+    const uint16_t* xs[kHostMaxTokens];
+    float* ys[kHostMaxTokens];
+    for (int b = 0; b < n_tok; ++b) {
+        xs[b] = x + (size_t)b * L.H;
+        ys[b] = y + (size_t)b * L.H;
+    }
+    HostExpertPool pool;
+    if (!pool.start(threads)) return MOE_ENOMEM;
+    pool.submit(L, n_tok, xs, ys, ent.data(), n);
+    pool.wait();
+    pool.stop();
+    return MOE_OK;
+}
+
 int32_t moe_hybrid_split(int32_t n_miss, double pcie_gbps, double host_gbps) {
     if (n_miss <= 0) return 0;
     if (!(host_gbps > pcie_gbps) || !(pcie_gbps > 0.0)) return n_miss;  // no host bandwidth left over

@@ -116,3 +116,77 @@ def test_hybrid_split_balances_finishing_times():
         q_star = m * bp / bh
         assert abs(q_star / bp - (m - q_star) / (bh - bp)) < 1e-9 * m
         assert abs(q - q_star) <= 0.5 + 1e-9
+
+
+# the hybrid backend's host workers on one task: (expert, token) entries over up to 16 tokens
+BATCH_SHAPES = [(256, 512), (800, 96), (2880, 2880)]
+
+
+def _batch_case(H, I, n_tok, seed):
+    import moe_expert_offload_amd as M
+    cfg = _cfg(H, I)
+    rng = np.random.default_rng(seed)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((n_tok, H)).astype(np.float32))
+    n_exp = 5
+    logical = [synth.blob(seed, 2, e, H, I) for e in range(n_exp)]
+    packed = [M.pack_blob(cfg, b) for b in logical]
+    ent = []   # (expert, weight, token); token 1 selects nothing
+    for b in range(n_tok):
+        if b == 1:
+            continue
+        for e in rng.choice(n_exp, size=int(rng.integers(1, 4)), replace=False):
+            ent.append((int(e), float(rng.uniform(0.05, 1.0)), b))
+    order = rng.permutation(len(ent))            # tokens interleaved in the entry list
+    ent = [ent[i] for i in order]
+    return cfg, x, logical, packed, ent
+
+
+@pytest.mark.parametrize("H,I", BATCH_SHAPES, ids=[f"{h}x{i}" for h, i in BATCH_SHAPES])
+def test_host_batch_matches_oracle_per_token(H, I):
+    import moe_expert_offload_amd as M
+    n_tok = 5
+    cfg, x, logical, packed, ent = _batch_case(H, I, n_tok, H + 7)
+    y = M.host_expert_batch(cfg, [packed[e] for e, _, _ in ent], [w for _, w, _ in ent],
+                            [b for _, _, b in ent], x, threads=3)
+    for b in range(n_tok):
+        ref = np.zeros(H)
+        for e, w, t in ent:
+            if t == b:
+                ref += w * oracle.expert_ffn(logical[e], H, I, x[b])
+        if b == 1:
+            assert not np.any(y[b])
+            continue
+        rel, mx, ok = _close(y[b].astype(np.float64), ref)
+        assert ok, (b, rel, mx)
+
+
+def test_host_batch_is_bitwise_independent_of_threads_and_matches_the_single_token_kernel():
+    import moe_expert_offload_amd as M
+    H, I, n_tok = 800, 96, 16
+    cfg, x, _, packed, ent = _batch_case(H, I, n_tok, 11)
+    args = ([packed[e] for e, _, _ in ent], [w for _, w, _ in ent], [b for _, _, b in ent], x)
+    ys = [M.host_expert_batch(cfg, *args, threads=t) for t in (1, 4, 9)]
+    for y in ys[1:]:
+        np.testing.assert_array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+    # one thread of the single-token kernel adds a token's experts in the same order
+    for b in range(n_tok):
+        mine = [(e, w) for e, w, t in ent if t == b]
+        y1 = M.host_expert_ffn(cfg, [packed[e] for e, _ in mine], [w for _, w in mine], x[b], threads=1)
+        np.testing.assert_array_equal(y1.view(np.uint32), ys[0][b].view(np.uint32))
+
+
+def test_host_batch_rejects_bad_arguments():
+    import moe_expert_offload_amd as M
+    H, I = 256, 512
+    cfg = _cfg(H, I)
+    p = M.pack_blob(cfg, synth.blob(1, 0, 0, H, I))
+    x = np.zeros((2, H), dtype=np.uint16)
+    for blobs, w, tok, xx, th in (([p], [1.0], [2], x, 1),                            # token out of range
+                                  ([p], [1.0], [-1], x, 1),
+                                  ([p], [1.0], [0], np.zeros((17, H), np.uint16), 1),  # more than 16 tokens
+                                  ([p] * 257, [1.0] * 257, [0] * 257, x, 1),           # more than 256 entries
+                                  ([p], [1.0], [0], x, 0)):                            # no worker
+        with pytest.raises(M.MoeError):
+            M.host_expert_batch(cfg, blobs, w, tok, xx, threads=th)
+    y = M.host_expert_batch(cfg, [], [], [], x, threads=2)
+    assert y.shape == (2, H) and not np.any(y)
