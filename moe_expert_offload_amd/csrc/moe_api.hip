@@ -359,6 +359,12 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
 // with the LRU policy run hybrid steps (batches through the grouped FFN path).
 moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
     c->hyb_call = false;
+    // a call that returned early can leave a host task running or a host sum unclaimed
+    if (c->host_running >= 0) {
+        c->hpool.wait();
+        c->host_running = -1;
+    }
+    c->host_has[0] = c->host_has[1] = false;
     if (c->backend != MOE_BACKEND_HYBRID || B > kHostMaxTokens || c->cfg.policy != MOE_POLICY_LRU || xs < 0 ||
         (B > 1 && (c->cfg.flags & MOE_FLAG_PER_TOKEN_FFN)))
         return MOE_OK;
@@ -1109,6 +1115,12 @@ moe_status moe_set_backend(moe_ctx* c, int32_t backend, double pcie_gbps, double
     if (!c) return MOE_EINVAL;
     if (c->failed) return MOE_ESTATE;
     HIPCHK(c, hipStreamSynchronize(c->cs));
+    // a task left running by a call that returned early ends before the pool changes
+    if (c->host_running >= 0) {
+        c->hpool.wait();
+        c->host_running = -1;
+    }
+    c->host_has[0] = c->host_has[1] = false;
     if (backend == MOE_BACKEND_OFFLOAD) {
         c->hpool.stop();
         c->backend = MOE_BACKEND_OFFLOAD;
