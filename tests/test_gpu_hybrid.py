@@ -121,10 +121,11 @@ def test_hybrid_is_bitwise_independent_of_workers_and_lookahead():
         np.testing.assert_array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
-def test_hybrid_layer_forward_matches_stack_and_pageable_pool():
+@pytest.mark.parametrize("wl", [SHARED, BATCH4], ids=lambda w: w.name)
+def test_hybrid_layer_forward_matches_stack_and_pageable_pool(wl):
     import torch
-    wl = SHARED
     X = synth.decode_inputs(wl)[:8]
+    B = X.shape[1]
     m, W = _hybrid(wl, (10.0, 400.0), pinned_mb=1)   # most of the pool pageable
     _, _, ys = run_stack(m, wl, X)
     m.close()
@@ -132,7 +133,7 @@ def test_hybrid_layer_forward_matches_stack_and_pageable_pool():
     dev = m.device
     H = wl.hidden
     xd = torch.from_numpy(X.view(np.int16)).to(dev)
-    y = torch.empty((X.shape[0], wl.n_layers, 1, H), dtype=torch.int16, device=dev)
+    y = torch.empty((X.shape[0], wl.n_layers, B, H), dtype=torch.int16, device=dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(m.compute_stream):
         for t in range(X.shape[0]):
@@ -144,6 +145,47 @@ def test_hybrid_layer_forward_matches_stack_and_pageable_pool():
     cnt, _ = m.stats()
     assert cnt["host_experts"] > 0 and cnt["host_tasks"] > 0
     m.close()
+
+
+@pytest.mark.parametrize("wl", [SHARED, BATCH4], ids=lambda w: w.name)
+def test_hybrid_stack_with_its_own_input_per_layer(wl):
+    """moe_stack_forward with a different hidden state per layer (layer stride B*H): every
+    layer's host share reads its own layer's inputs.  Equal bit for bit to moe_layer_forward
+    calls in the same order, and within tolerance of the plain MoE output."""
+    import torch
+    T, L = 5, wl.n_layers
+    X = synth.decode_inputs(wl)[:T]
+    B, H = X.shape[1], wl.hidden
+    # layer l of step t sees step (t + 3 l) mod T's states: distinct per layer, same shapes
+    XL = np.stack([np.stack([X[(t + 3 * l) % T] for l in range(L)]) for t in range(T)])  # [T][L][B][H]
+    split = (26.7, 45.5)
+    outs, traces = [], []
+    for by_layer in (False, True):
+        m, W = _hybrid(wl, split)
+        dev = m.device
+        xd = torch.from_numpy(np.ascontiguousarray(XL).view(np.int16)).to(dev)
+        y = torch.empty((T, L, B, H), dtype=torch.int16, device=dev)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(m.compute_stream):
+            for t in range(T):
+                if by_layer:
+                    for l in range(L):
+                        m.layer_forward(t, l, xd[t, l], y[t, l])
+                else:
+                    m.stack_forward(t, xd[t], B * H, B, y[t], B * H)
+        m.compute_stream.synchronize()
+        outs.append(y.view(torch.bfloat16).float().cpu().numpy())
+        cnt, recs = m.stats(trace_cap=1 << 16)
+        traces.append(trace_tuples(recs))
+        assert cnt["host_experts"] > 0
+        m.close()
+    np.testing.assert_array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert traces[0] == traces[1]
+    for (t, l, b) in [(0, 0, 0), (T - 1, L - 1, B - 1), (2, L // 2, 0)]:
+        ids, w = oracle.route_batch(W, XL[t, l, b:b + 1], wl.top_k, np.array([l]), np.array([0]))
+        r = oracle.moe_output(wl, l, XL[t, l, b], ids[0], w[0])
+        rel, mx, ok = close_enough(outs[0][t, l, b], r)
+        assert ok, (t, l, b, rel, mx)
 
 
 def test_set_backend_rejects_bad_arguments_and_switches_back():
