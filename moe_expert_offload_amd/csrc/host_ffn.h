@@ -60,10 +60,11 @@ struct HostEntry {
 
 // Persistent host workers for the hybrid backend: one task at a time, for
 // each of up to 16 tokens b, y_b[H] (FP32) = sum over the task's entries of
-// token b, in their order, of w * FFN(x_b).  Four phases, each handing out
+// token b, in their order, of w * FFN(x_b).  Three phases, each handing out
 // small units through an atomic counter and ending when all of its units are
-// done: (token, blocks of x) to FP32, (entry, gate/up tiles), (entry, blocks
-// of the intermediate vector), then (token, chunks of output rows), each
+// done: (token, blocks of x) to FP32; (entry, an even number of gate/up
+// tiles), which also forms the intermediate vector of those rows (two 16-row
+// tiles are one 32-element block); then (token, chunks of output rows), each
 // summed over the token's entries in order by the participant that takes it.
 // The caller of wait() works on the task as well.  Every value is computed by
 // one participant in a fixed order, so the result does not depend on the
@@ -93,7 +94,9 @@ private:
         int n = 0, ntok = 0;
         const uint16_t* x[kHostMaxTokens] = {};
         float* y[kHostMaxTokens] = {};
-        int x_chunk = 1, gu_chunk = 1, act_chunk = 1, d_chunk = 1;  // unit sizes of the phases
+        int x_chunk = 1, gu_chunk = 2, d_chunk = 1;  // unit sizes of the phases
+        int gu_per = 1, d_per = 1;                   // units per entry / per token
+        int gu_step = 1, d_step = 1;                 // unit order: u -> u * step mod count
     };
     void run(int t);
     void work(bool vec);
@@ -102,10 +105,17 @@ private:
     std::vector<std::thread> threads_;
     std::vector<ExpertBuf> ebuf_;  // per entry: g, u and the intermediate vector
     std::vector<TokenBuf> xbuf_;   // per token: x split even / odd
-    std::atomic<int> gen_{0}, done_{0};
-    std::atomic<int> x_next_{0}, gu_next_{0}, act_next_{0}, d_next_{0};  // next unit of each phase
-    std::atomic<int> x_done_{0}, gu_done_{0}, act_done_{0}, d_done_{0};  // units finished per phase
-    std::atomic<uint64_t> busy_ns_{0};
+    // each counter on a cache line of its own: participants on different cores
+    // update them concurrently, and the waiting ones poll the done counters
+    alignas(128) std::atomic<int> gen_{0};
+    alignas(128) std::atomic<int> done_{0};
+    alignas(128) std::atomic<int> x_next_{0};   // next unit of each phase
+    alignas(128) std::atomic<int> gu_next_{0};
+    alignas(128) std::atomic<int> d_next_{0};
+    alignas(128) std::atomic<int> x_done_{0};   // units finished per phase
+    alignas(128) std::atomic<int> gu_done_{0};
+    alignas(128) std::atomic<int> d_done_{0};
+    alignas(128) std::atomic<uint64_t> busy_ns_{0};
     std::chrono::steady_clock::time_point t_submit_{};
     std::atomic<bool> quit_{false};
     std::mutex mu_;
