@@ -79,18 +79,21 @@ __device__ __forceinline__ int lds_pos(int blk, int n, int S) {
 }
 
 // slot / weight of the single token's j-th expert from the launch arguments:
-// constant-index reads and a select chain (indexing the by-value argument
-// array with a variable would copy it to private memory)
+// a select chain over wave-uniform copies of the 16 entries.  Indexing the
+// by-value argument array with a variable, or a select chain on the entries
+// themselves (which the compiler folds into one), becomes a per-lane load
+// from the argument block whose latency precedes the first weight load.
 __device__ __forceinline__ int karg_slot(const FfnArgs& a, int j) {
-    int v = a.kslot[0];
+    int v = __builtin_amdgcn_readfirstlane(a.kslot[0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) v = (j == i) ? a.kslot[i] : v;
+    for (int i = 1; i < 16; ++i) v = (j == i) ? __builtin_amdgcn_readfirstlane(a.kslot[i]) : v;
     return v;
 }
 __device__ __forceinline__ float karg_w(const FfnArgs& a, int j) {
-    float v = a.kw[0];
+    float v = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.kw[0])));
 #pragma unroll
-    for (int i = 1; i < 16; ++i) v = (j == i) ? a.kw[i] : v;
+    for (int i = 1; i < 16; ++i)
+        v = (j == i) ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.kw[i]))) : v;
     return v;
 }
 
@@ -110,15 +113,33 @@ __device__ __forceinline__ float expert_weight(const FfnArgs& a, int b, int j) {
 
 constexpr int FFN_THREADS = 256;
 
-// Stage nblk 64-byte blocks (32 bf16 values) from global memory into LDS in
-// lds_pos() order: a thread moves whole blocks, four 16-byte loads in flight
-// before its four LDS writes.  Runs before the weight loads are issued: a
-// weight load issued earlier would make these LDS writes wait for it too
-// (loads complete in order per wave), and a wave dedicated to staging
-// measured slower.
-__device__ __forceinline__ void stage_blocks(uint4* smem, const uint4* src, int nblk, int nseg,
-                                             int nthreads = FFN_THREADS) {
-    for (int blk = threadIdx.x; blk < nblk; blk += nthreads) {
+// Activations are staged into LDS in lds_pos() order, one 64-byte block (32
+// bf16 values) per thread and step, in two halves around the weight loads:
+// stage_first() loads a thread's first block into registers; the caller then
+// issues its weight loads; stage_commit() writes the block to LDS, which waits
+// for the staging loads alone (loads complete in order per wave), and stages
+// any further blocks (shapes with more blocks than threads).  The activations'
+// latency and the weights' then overlap; a scheduling barrier on each side of
+// the weight loads keeps the compiler from moving the staging loads behind them.
+struct StageRegs {
+    uint4 v0, v1, v2, v3;
+};
+
+__device__ __forceinline__ StageRegs stage_first(const uint4* src, int nblk) {
+    const int bc = (int)threadIdx.x < nblk ? (int)threadIdx.x : 0;
+    return StageRegs{src[bc * 4 + 0], src[bc * 4 + 1], src[bc * 4 + 2], src[bc * 4 + 3]};
+}
+
+__device__ __forceinline__ void stage_commit(const StageRegs& r, uint4* smem, const uint4* src, int nblk, int nseg,
+                                             int nthreads) {
+    if ((int)threadIdx.x < nblk) {
+        uint4* d = smem + lds_pos(threadIdx.x, nblk, nseg);
+        d[0] = r.v0;
+        d[1] = r.v1;
+        d[2] = r.v2;
+        d[3] = r.v3;
+    }
+    for (int blk = threadIdx.x + nthreads; blk < nblk; blk += nthreads) {
         const uint4 v0 = src[blk * 4 + 0];
         const uint4 v1 = src[blk * 4 + 1];
         const uint4 v2 = src[blk * 4 + 2];
@@ -177,9 +198,13 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
             u += (t0 + t < nb) ? pu : 0.0f;
         }
     };
-    stage_blocks(smem, reinterpret_cast<const uint4*>(a.x + (size_t)b * a.H), NB, S);
-    __syncthreads();
+    const uint4* xsrc = reinterpret_cast<const uint4*>(a.x + (size_t)b * a.H);
+    const StageRegs xr = stage_first(xsrc, NB);
+    __builtin_amdgcn_sched_barrier(0);
     load(0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_commit(xr, smem, xsrc, NB, S, FFN_THREADS);
+    __syncthreads();
     compute(0);
     for (int t0 = T1; t0 < nb; t0 += T1) {
         load(t0);
@@ -224,13 +249,6 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
     const bool tok = t8 < (a.H >> 3);
     const int tile = tok ? t8 : 0;
     const int r = lane & 7, s = w * 8 + (lane >> 3);
-    // host-computed experts' sum for the rows this thread writes, fetched first
-    // (host-mapped memory: a PCIe round trip that overlaps the weight stream)
-    float yhv = 0.0f;
-    if (a.yh && tid < 8 * R8) {
-        const int yr = (tile16 * R8 + (tid >> 3)) * 8 + (tid & 7);
-        if (yr < a.H) yhv = a.yh[(size_t)b * a.H + yr];
-    }
     const int nq = seg_len(Q, S, s), q0 = seg_begin(Q, S, s);
     // A segment (at most ceil(nE*NBI/32) <= NBI + 1 blocks, as nE <= 32)
     // spans at most two experts: j0 from block ib0 for `split` steps, then j0+1
@@ -267,9 +285,20 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
             acc += (t0 + t < nq) ? pv : 0.0f;
         }
     };
-    stage_blocks(smem, reinterpret_cast<const uint4*>(a.a + (size_t)b * nE * a.I), Q, S, 4 * 64 * R8);
-    __syncthreads();
+    const uint4* asrc = reinterpret_cast<const uint4*>(a.a + (size_t)b * nE * a.I);
+    const StageRegs ar = stage_first(asrc, Q);
+    __builtin_amdgcn_sched_barrier(0);
     load(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the host-computed experts' sum for the rows this thread writes (host-mapped memory: a PCIe
+    // round trip), issued behind the weights, which it does not hold up, and used at the end
+    float yhv = 0.0f;
+    if (a.yh && tid < 8 * R8) {
+        const int yr = (tile16 * R8 + (tid >> 3)) * 8 + (tid & 7);
+        if (yr < a.H) yhv = a.yh[(size_t)b * a.H + yr];
+    }
+    stage_commit(ar, smem, asrc, Q, S, 4 * 64 * R8);
+    __syncthreads();
     compute(0);
     for (int t0 = T2; t0 < nq; t0 += T2) {
         load(t0);
