@@ -243,13 +243,18 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
     std::fill(y, y + L.H, 0.0f);
     const bool vec = have_avx512();
     threads = std::max(1, std::min(threads, n));
-    // experts are shared out over the threads; each thread sums into its own
-    // partial, and the partials are added in thread order
+    // experts are shared out over the threads; each expert's weighted output is
+    // formed on its own and added to its thread's partial, and the partials are
+    // added in thread order (with one thread: the worker pool's order)
     std::vector<std::vector<float>> part(threads, std::vector<float>(L.H, 0.0f));
     auto run = [&](int t) {
         ExpertBuf eb;
         eb.size(L);
-        for (int j = t; j < n; j += threads) expert_one(L, blobs[j], w[j], xb, eb, part[t].data(), vec);
+        for (int j = t; j < n; j += threads) {
+            std::fill(eb.yp.begin(), eb.yp.end(), 0.0f);
+            expert_one(L, blobs[j], w[j], xb, eb, eb.yp.data(), vec);
+            for (int i = 0; i < L.H; ++i) part[t][i] += eb.yp[i];
+        }
     };
     std::vector<std::thread> pool;
     for (int t = 1; t < threads; ++t) pool.emplace_back(run, t);
@@ -259,11 +264,11 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
         for (int i = 0; i < L.H; ++i) y[i] += part[t][i];
 }
 
-// Units of work are handed out dynamically (an atomic counter per phase), so a
-// slow or descheduled worker delays a phase by at most one unit.  Unit sizes
-// aim at about four units per participant and phase, within these bounds.
+// Units of work are handed out dynamically (atomic counters), so a slow or
+// descheduled worker delays the task by at most one unit.  Unit sizes aim at
+// about four units per participant and kind, within these bounds.
 constexpr int kGuChunkMax = 4;   // 16-row gate/up tiles per unit (even: whole 32-blocks of a)
-constexpr int kDChunkMax = 8;    // 8-row output tiles per unit (a token's experts, in order)
+constexpr int kDChunkMax = 32;   // 8-row output tiles of one entry per unit
 
 inline int unit_size(long items, int participants, int max_chunk) {
     const long c = items / (4L * participants);
@@ -337,17 +342,18 @@ void HostExpertPool::submit(const Layout& L, int n_tok, const uint16_t* const* x
     for (int j = 0; j < task_.n; ++j) ebuf_[j].size(L);
     if ((int)xbuf_.size() < task_.ntok) xbuf_.resize(task_.ntok);
     for (int b = 0; b < task_.ntok; ++b) xbuf_[b].size(L);
-    // about four units per participant (workers and the waiting caller) and phase
+    // about four units per participant (workers and the waiting caller) and kind
     const int np = n_ + 1;
-    task_.x_chunk = L.NB;  // a whole hidden state per unit: converting one takes about a microsecond
     task_.gu_chunk = std::max(2, unit_size((long)task_.n * (L.I / 16), np, kGuChunkMax) & ~1);
-    task_.d_chunk = unit_size((long)task_.ntok * (L.H / 8), np, kDChunkMax);
+    task_.d_chunk = unit_size((long)task_.n * (L.H / 8), np, kDChunkMax);
     task_.gu_per = (L.I / 16 + task_.gu_chunk - 1) / task_.gu_chunk;
     task_.d_per = (L.H / 8 + task_.d_chunk - 1) / task_.d_chunk;
-    task_.gu_step = unit_step(task_.n * task_.gu_per, np);
-    task_.d_step = unit_step(task_.ntok * task_.d_per, np);
-    for (std::atomic<int>* c : {&x_next_, &gu_next_, &d_next_, &x_done_, &gu_done_, &d_done_})
-        c->store(0, std::memory_order_relaxed);
+    task_.gu_step = unit_step(task_.gu_per, np);
+    task_.d_step = unit_step(task_.d_per, np);
+    for (int j = 0; j < task_.n; ++j) gu_left_[j].v.store(task_.gu_per, std::memory_order_relaxed);
+    for (int b = 0; b < task_.ntok; ++b)
+        d_left_[b].v.store((task_.tok_begin[b + 1] - task_.tok_begin[b]) * task_.d_per, std::memory_order_relaxed);
+    for (std::atomic<int>* c : {&x_next_, &x_done_, &main_next_, &tok_done_}) c->store(0, std::memory_order_relaxed);
     done_.store(0);
     t_submit_ = std::chrono::steady_clock::now();
     {
@@ -364,47 +370,79 @@ void HostExpertPool::wait() {
     while (done_.load(std::memory_order_acquire) < n_) _mm_pause();
 }
 
-// one participant's share of the current task: units from the phases in order;
-// a phase ends when all of its units are done (counted, not a barrier of a
-// fixed set of threads), so the calling thread can join in while it waits
+// one participant's share of the current task.  The x units come first (a
+// down unit of any entry may need any token's x); then the main list, where
+// segment s holds the gate/up units of entry s followed by the down units of
+// entry s - 1, so a down unit is taken well after its entry's gate/up units
+// and rarely waits for them.
 void HostExpertPool::work(bool vec) {
     const Layout& L = task_.L;
     const int n = task_.n, ntok = task_.ntok;
-    auto finish_phase = [](const std::atomic<int>& done, int total) {
-        while (done.load(std::memory_order_acquire) < total) _mm_pause();
-    };
-    // hidden states to FP32: (token, chunk of 32-blocks) units
-    const int xc = task_.x_chunk, x_per = (L.NB + xc - 1) / xc, n_x = ntok * x_per;
-    for (int u; (u = x_next_.fetch_add(1, std::memory_order_relaxed)) < n_x;) {
-        const int b = u / x_per, b0 = (u % x_per) * xc;
-        split_blocks(task_.x[b], b0, std::min(L.NB, b0 + xc), xbuf_[b].xe.data(), xbuf_[b].xo.data());
-        x_done_.fetch_add(1, std::memory_order_release);
-    }
-    finish_phase(x_done_, n_x);
-    // gate/up and the intermediate vector of the same rows: (entry, chunk of an
-    // even number of tiles) units (I is a multiple of 32, so I/16 tiles is even)
-    const int ngu = L.I / 16, gc = task_.gu_chunk, gu_per = task_.gu_per, n_gu = n * gu_per;
-    for (int u; (u = gu_next_.fetch_add(1, std::memory_order_relaxed)) < n_gu;) {
-        const int uu = (int)((long)u * task_.gu_step % n_gu);
-        const int j = uu / gu_per, t0 = (uu % gu_per) * gc, t1 = std::min(ngu, t0 + gc);
-        gate_up_rows(L, task_.e[j].blob, xbuf_[task_.e[j].tok], ebuf_[j], t0, t1, vec);
-        activation_blocks(ebuf_[j], t0 / 2, t1 / 2);
-        gu_done_.fetch_add(1, std::memory_order_release);
-    }
-    finish_phase(gu_done_, n_gu);
-    // down: (token, chunk of output rows) units, each summed over the token's
-    // entries in order by the participant that takes it
-    const int nt8 = L.H / 8, dc = task_.d_chunk, d_per = task_.d_per, n_d = ntok * d_per;
-    for (int u; (u = d_next_.fetch_add(1, std::memory_order_relaxed)) < n_d;) {
-        const int uu = (int)((long)u * task_.d_step % n_d);
-        const int b = uu / d_per, d0 = (uu % d_per) * dc, d1 = std::min(nt8, d0 + dc);
-        float* y = task_.y[b];
-        std::fill(y + d0 * 8, y + d1 * 8, 0.0f);
-        for (int j = task_.tok_begin[b]; j < task_.tok_begin[b + 1]; ++j)
-            down_rows(L, task_.e[j].blob, ebuf_[j], task_.e[j].w, y, d0, d1, vec);
-        if (d_done_.fetch_add(1, std::memory_order_acq_rel) == n_d - 1)
+    auto token_done = [&]() {
+        if (tok_done_.fetch_add(1, std::memory_order_acq_rel) == ntok - 1)
             busy_ns_.fetch_add((uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
                                    std::chrono::steady_clock::now() - t_submit_).count());
+    };
+    // hidden states to FP32, one unit per token; a token without entries gets zeros
+    for (int b; (b = x_next_.fetch_add(1, std::memory_order_relaxed)) < ntok;) {
+        split_blocks(task_.x[b], 0, L.NB, xbuf_[b].xe.data(), xbuf_[b].xo.data());
+        if (task_.tok_begin[b + 1] == task_.tok_begin[b]) {
+            std::fill(task_.y[b], task_.y[b] + L.H, 0.0f);
+            token_done();
+        }
+        x_done_.fetch_add(1, std::memory_order_release);
+    }
+    while (x_done_.load(std::memory_order_acquire) < ntok) _mm_pause();
+    const int ngu = L.I / 16, nt8 = L.H / 8;
+    const int gc = task_.gu_chunk, gu_per = task_.gu_per, dc = task_.d_chunk, d_per = task_.d_per;
+    const int seg = gu_per + d_per, n_main = n * seg;
+    for (int u; (u = main_next_.fetch_add(1, std::memory_order_relaxed)) < n_main;) {
+        // unit u of the main list -> (gate/up or down, entry, unit within the entry)
+        bool is_gu;
+        int j, k;
+        if (u < gu_per) {
+            is_gu = true;
+            j = 0;
+            k = u;
+        } else {
+            const int v = u - gu_per, s = 1 + v / seg, off = v - (s - 1) * seg;
+            if (s < n && off < gu_per) {
+                is_gu = true;
+                j = s;
+                k = off;
+            } else {
+                is_gu = false;
+                j = s - 1;
+                k = s < n ? off - gu_per : off;
+            }
+        }
+        const HostEntry& e = task_.e[j];
+        if (is_gu) {
+            const int kk = (int)((long)k * task_.gu_step % gu_per);
+            const int t0 = kk * gc, t1 = std::min(ngu, t0 + gc);
+            gate_up_rows(L, e.blob, xbuf_[e.tok], ebuf_[j], t0, t1, vec);
+            activation_blocks(ebuf_[j], t0 / 2, t1 / 2);
+            gu_left_[j].v.fetch_sub(1, std::memory_order_release);
+            continue;
+        }
+        // down rows of entry j: w * (the expert's output rows) into its own buffer
+        while (gu_left_[j].v.load(std::memory_order_acquire) > 0) _mm_pause();
+        const int kk = (int)((long)k * task_.d_step % d_per);
+        const int d0 = kk * dc, d1 = std::min(nt8, d0 + dc);
+        float* yp = ebuf_[j].yp.data();
+        std::fill(yp + d0 * 8, yp + d1 * 8, 0.0f);
+        down_rows(L, e.blob, ebuf_[j], e.w, yp, d0, d1, vec);
+        if (d_left_[e.tok].v.fetch_sub(1, std::memory_order_acq_rel) == 1) {
+            // the token's last down unit: its output is the sum of its entries, in order
+            const int b = e.tok;
+            float* y = task_.y[b];
+            std::fill(y, y + L.H, 0.0f);
+            for (int jj = task_.tok_begin[b]; jj < task_.tok_begin[b + 1]; ++jj) {
+                const float* p = ebuf_[jj].yp.data();
+                for (int i = 0; i < L.H; ++i) y[i] += p[i];
+            }
+            token_done();
+        }
     }
 }
 

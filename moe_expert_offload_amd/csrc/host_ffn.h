@@ -25,16 +25,18 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
 // over blobs[0..n) round robin for about min_seconds
 double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int threads, double min_seconds);
 
-// one expert's intermediate state for one token: g, u [I] and the
-// intermediate vector split into the even / odd elements of each 32-block
+// one expert's intermediate state for one token: g, u [I], the intermediate
+// vector split into the even / odd elements of each 32-block, and (worker
+// pool) its weighted output w * FFN(x) [H]
 struct ExpertBuf {
-    std::vector<float> g, u, ae, ao;
+    std::vector<float> g, u, ae, ao, yp;
     void size(const Layout& L) {
-        if ((int)g.size() == L.I && (int)ae.size() == L.NBI * 16) return;
+        if ((int)g.size() == L.I && (int)ae.size() == L.NBI * 16 && (int)yp.size() == L.H) return;
         g.assign(L.I, 0.0f);
         u.assign(L.I, 0.0f);
         ae.assign((size_t)L.NBI * 16, 0.0f);
         ao.assign((size_t)L.NBI * 16, 0.0f);
+        yp.assign(L.H, 0.0f);
     }
 };
 
@@ -60,16 +62,18 @@ struct HostEntry {
 
 // Persistent host workers for the hybrid backend: one task at a time, for
 // each of up to 16 tokens b, y_b[H] (FP32) = sum over the task's entries of
-// token b, in their order, of w * FFN(x_b).  Three phases, each handing out
-// small units through an atomic counter and ending when all of its units are
-// done: (token, blocks of x) to FP32; (entry, an even number of gate/up
-// tiles), which also forms the intermediate vector of those rows (two 16-row
-// tiles are one 32-element block); then (token, chunks of output rows), each
-// summed over the token's entries in order by the participant that takes it.
-// The caller of wait() works on the task as well.  Every value is computed by
-// one participant in a fixed order, so the result does not depend on the
-// worker count or on which worker takes a unit.  Workers spin between tasks
-// and sleep after 20 ms idle.
+// token b, in their order, of w * FFN(x_b).  Units are handed out through
+// atomic counters: first one unit per token (x to FP32), then one list that
+// interleaves, entry by entry, (entry, an even number of gate/up tiles) units,
+// which also form the intermediate vector of those rows (two 16-row tiles are
+// one 32-element block), with the (entry, chunk of output rows) down units of
+// the entry before, which write w * (its rows of the expert's output).  A down
+// unit waits only for its own entry's gate/up units; the participant that
+// finishes a token's last down unit sums the token's entries in order.  The
+// caller of wait() works on the task as well.  Every value is computed by one
+// participant in a fixed order, so the result does not depend on the worker
+// count or on which worker takes a unit.  Workers spin between tasks and
+// sleep after 20 ms idle.
 class HostExpertPool {
 public:
     ~HostExpertPool();
@@ -94,9 +98,9 @@ private:
         int n = 0, ntok = 0;
         const uint16_t* x[kHostMaxTokens] = {};
         float* y[kHostMaxTokens] = {};
-        int x_chunk = 1, gu_chunk = 2, d_chunk = 1;  // unit sizes of the phases
-        int gu_per = 1, d_per = 1;                   // units per entry / per token
-        int gu_step = 1, d_step = 1;                 // unit order: u -> u * step mod count
+        int gu_chunk = 2, d_chunk = 1;  // 16-row gate/up tiles and 8-row output tiles per unit
+        int gu_per = 1, d_per = 1;      // gate/up and down units per entry
+        int gu_step = 1, d_step = 1;    // order within an entry: k -> k * step mod count
     };
     void run(int t);
     void work(bool vec);
@@ -105,16 +109,19 @@ private:
     std::vector<std::thread> threads_;
     std::vector<ExpertBuf> ebuf_;  // per entry: g, u and the intermediate vector
     std::vector<TokenBuf> xbuf_;   // per token: x split even / odd
+    struct alignas(128) Counter {
+        std::atomic<int> v{0};
+    };
     // each counter on a cache line of its own: participants on different cores
-    // update them concurrently, and the waiting ones poll the done counters
+    // update them concurrently, and the waiting ones poll them
     alignas(128) std::atomic<int> gen_{0};
     alignas(128) std::atomic<int> done_{0};
-    alignas(128) std::atomic<int> x_next_{0};   // next unit of each phase
-    alignas(128) std::atomic<int> gu_next_{0};
-    alignas(128) std::atomic<int> d_next_{0};
-    alignas(128) std::atomic<int> x_done_{0};   // units finished per phase
-    alignas(128) std::atomic<int> gu_done_{0};
-    alignas(128) std::atomic<int> d_done_{0};
+    alignas(128) std::atomic<int> x_next_{0};     // next x unit
+    alignas(128) std::atomic<int> x_done_{0};     // x units finished
+    alignas(128) std::atomic<int> main_next_{0};  // next gate/up or down unit
+    alignas(128) std::atomic<int> tok_done_{0};   // tokens whose output is complete
+    Counter gu_left_[kHostMaxEntries];            // gate/up units of an entry not yet finished
+    Counter d_left_[kHostMaxTokens];              // down units of a token's entries not yet finished
     alignas(128) std::atomic<uint64_t> busy_ns_{0};
     std::chrono::steady_clock::time_point t_submit_{};
     std::atomic<bool> quit_{false};
