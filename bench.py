@@ -208,7 +208,8 @@ def main():
                     help="offload: every miss over PCIe; hybrid: the calibrated split between PCIe and host "
                          "workers; auto: hybrid when the calibration says the host is more than twice as fast")
     ap.add_argument("--host-workers", type=int, default=0,
-                    help="host worker threads of the hybrid backend (0: this process's cores - 2, at most 14)")
+                    help="host worker threads of the hybrid backend (0: this process's cores - 2, at most 14; "
+                         "4 fewer when part of the pool is pageable)")
     ap.add_argument("--auto-reserve-gb", type=float, default=4.0,
                     help="HBM kept free by --cache-slots auto (the KV cache's share in a server)")
     args = ap.parse_args()
@@ -256,8 +257,12 @@ def main():
     h2d_big = m.measure_h2d(64 << 20, 32)
     # backend calibration: B_P (blob copies) vs B_H (the host expert kernel on the cores the host
     # workers would use: all of this process's cores but two, one for the thread that drives the
-    # GPU and one for the HIP runtime's own threads (measured: 14 workers on 16 cores beat 15)
-    workers = args.host_workers or max(1, min(16, len(os.sched_getaffinity(0))) - 2)
+    # GPU and one for the HIP runtime's own threads (measured: 14 workers on 16 cores beat 15);
+    # a pool with a pageable part also leaves the bounce ring's 4 copy threads their cores
+    # (measured on 16 cores: 10 workers beat 14 there, DeepSeek-shaped 82 -> 90 tok/s)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    pageable = c_init["pool_pinned_bytes"] < wl.pool * m.blob_bytes
+    workers = args.host_workers or max(1, cores - 2 - (min(4, cores // 4) if pageable else 0))
     calib = m.calibrate_backend(workers, host_seconds=2.0)
     backend = args.backend if args.backend != "auto" else calib["backend"]
     if backend == "hybrid":
