@@ -275,10 +275,10 @@ inline int unit_size(long items, int participants, int max_chunk) {
     return (int)std::max<long>(1, std::min<long>(max_chunk, c));
 }
 
-// Units are taken in the order u -> u * step mod n, with step coprime to n
-// (a permutation) and about n / participants, so the units running at the same
-// time read places far apart in the pool rather than adjacent ones (measured
-// 3-4 % faster on the EPYC hosts).
+// An entry's units are taken in the order k -> k * step mod n, with step
+// coprime to n (a permutation) and about n / participants, so the units running
+// at the same time read places far apart in the expert rather than adjacent
+// ones (measured 3-4 % faster on the EPYC hosts).
 inline int unit_step(int n, int participants) {
     if (n <= 1) return 1;
     int s = std::max(1, n / participants);
@@ -370,8 +370,8 @@ void HostExpertPool::wait() {
     while (done_.load(std::memory_order_acquire) < n_) _mm_pause();
 }
 
-// one participant's share of the current task.  The x units come first (a
-// down unit of any entry may need any token's x); then the main list, where
+// one participant's share of the current task.  The x units come first (the
+// gate/up units of any entry may need any token's x); then the main list, where
 // segment s holds the gate/up units of entry s followed by the down units of
 // entry s - 1, so a down unit is taken well after its entry's gate/up units
 // and rarely waits for them.
