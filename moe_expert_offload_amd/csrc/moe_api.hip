@@ -45,6 +45,20 @@ struct moe_ctx {
     int device = 0;
     int nE = 0;                 // k + n_shared
     hipStream_t cs = nullptr, ps = nullptr;
+    // Router and resolve stream (library-owned) of one-token hybrid stack calls: K1/K2 of layer
+    // l+1 run there, so a layer's miss list (the host workers' next task) does not wait behind an
+    // FFN that waits for its copies.  Events order the rest: rs_start (call start on cs) before
+    // the call's first K1; ffn_done[p] (on cs, after the FFN of the last layer of parity p) before
+    // the copies that may overwrite that layer's slots (the copies of layer l+2); k2_done[p]
+    // before an FFN that reads K2's slot and weight buffers (the one-token FFN takes them as
+    // launch arguments instead); rs_end joins rs back into cs.
+    hipStream_t rs = nullptr;
+    hipEvent_t rs_start = nullptr, rs_end = nullptr;
+    hipEvent_t k2_done[2] = {nullptr, nullptr};
+    hipEvent_t ffn_done[2] = {nullptr, nullptr};
+    bool ffn_done_valid[2] = {false, false};
+    hipStream_t ks = nullptr;   // stream K1/K2 launch on: rs inside a route-stream call, else cs
+    bool rs_active = false;     // the current call runs K1/K2 on rs
     uint8_t* pool = nullptr;    // pinned host, blobs [0, n_pin) of [L*E][blob]
     size_t pool_bytes = 0;      // whole pool
     size_t n_pin = 0;           // blobs in pinned memory
@@ -99,7 +113,9 @@ struct moe_ctx {
     bool xh_pending = false;
     bool hyb_call = false;               // the current call runs hybrid steps
     int hyb_B = 0;                       // its token count
-    float* yh = nullptr;                 // host-mapped [2][16][H]: the host experts' sums per parity and token
+    float* yh = nullptr;                 // host-mapped [L][16][H]: the host experts' sums per layer and token
+                                         // (a layer's own rows: its FFN may still be queued when the
+                                         // host task of a later layer is submitted)
     bool host_has[2] = {false, false};   // this parity's FFN adds yh[parity]
     int host_running = -1;               // parity of the host task in flight, -1: none
     uint64_t host_tasks = 0;
@@ -283,6 +299,10 @@ void free_all(moe_ctx* c) {
     if (c->cs) (void)hipStreamSynchronize(c->cs);
     if (c->ps) (void)hipStreamSynchronize(c->ps);
     if (c->ps2) (void)hipStreamSynchronize(c->ps2);
+    if (c->rs) (void)hipStreamSynchronize(c->rs);
+    for (auto e : {c->rs_start, c->rs_end, c->k2_done[0], c->k2_done[1], c->ffn_done[0], c->ffn_done[1]})
+        if (e) (void)hipEventDestroy(e);
+    if (c->rs) (void)hipStreamDestroy(c->rs);
     for (auto& p : c->prof_used) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto& p : c->prof_free) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
@@ -315,7 +335,7 @@ moe_status launch_route(moe_ctx* c, int layer, const void* x, int B) {
     a.E = c->cfg.n_experts;
     a.H = c->cfg.hidden;
     a.B = B;
-    LAUNCHCHK(c, launch_k1(a, c->cs));
+    LAUNCHCHK(c, launch_k1(a, c->ks ? c->ks : c->cs));
     return MOE_OK;
 }
 
@@ -348,7 +368,7 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
     a.bp = c->hyb_bp;
     a.bh = c->hyb_bh;
     const int p = c->parity;
-    LAUNCHCHK(c, launch_k2(a, c->order[p], c->order[p ^ 1], c->cs));
+    LAUNCHCHK(c, launch_k2(a, c->order[p], c->order[p ^ 1], c->ks ? c->ks : c->cs));
     c->parity = p ^ 1;
     return MOE_OK;
 }
@@ -456,7 +476,7 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         const size_t H = c->cfg.hidden;
         for (int b = 0; b < B; ++b) {
             xs[b] = c->xh + (size_t)layer * c->xh_stride + (size_t)b * H;
-            ys[b] = c->yh + ((size_t)par * kHostMaxTokens + b) * H;
+            ys[b] = c->yh + ((size_t)layer * kHostMaxTokens + b) * H;
         }
         c->hpool.submit(c->lay, B, xs, ys, ent, nh);
         c->host_running = par;
@@ -464,6 +484,12 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         ++c->host_tasks;
     }
     const size_t blob = c->lay.blob_bytes;
+    if (c->rs_active && nx > 0 && c->ffn_done_valid[par]) {
+        // this step's victims may hold the slots of the layer two back (same parity), whose FFN
+        // runs on the compute stream while this step was resolved on the route stream
+        HIPCHK(c, hipStreamWaitEvent(c->ps, c->ffn_done[par], 0));
+        HIPCHK(c, hipStreamWaitEvent(c->ps2, c->ffn_done[par], 0));
+    }
     bool used[2] = {false, false};
     int nd = 0;  // direct copies so far: they alternate between the two copy streams
     int ncopy = 0;
@@ -515,12 +541,16 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
             c->host_running = -1;
         }
         c->host_has[par] = false;
-        yh = c->yh + (size_t)par * kHostMaxTokens * c->cfg.hidden;
+        yh = c->yh + (size_t)layer * kHostMaxTokens * c->cfg.hidden;
     }
     if (n_miss > 0 && par < 2) {
         if (c->copy_used[par][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
         if (c->copy_used[par][1]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev2[par], 0));
     }
+    // the single-token kernels take their slots and weights as launch arguments; every other
+    // FFN reads the ones K2 wrote, on the route stream in a route-stream call
+    if (c->rs_active && par < 2 && !(B == 1 && !slots_dev && c->tok0_valid[par]))
+        HIPCHK(c, hipStreamWaitEvent(c->cs, c->k2_done[par], 0));
     const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0;
     ProfSlot ps{};
     if (prof) {
@@ -613,8 +643,40 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         HIPCHK(c, hipEventRecord(ps.ev[2], c->cs));
         c->prof_used.push_back(ps);
     }
+    if (c->rs_active && par < 2) {
+        HIPCHK(c, hipEventRecord(c->ffn_done[par], c->cs));
+        c->ffn_done_valid[par] = true;
+    }
     return MOE_OK;
 }
+
+// A route-stream call runs K1/K2 on the route stream from here to route_stream_end: the stream
+// first waits for everything already on the compute stream (the call's inputs and every earlier
+// FFN, whose slots this call's first victims may hold).
+moe_status route_stream_begin(moe_ctx* c) {
+    HIPCHK(c, hipEventRecord(c->rs_start, c->cs));
+    HIPCHK(c, hipStreamWaitEvent(c->rs, c->rs_start, 0));
+    c->rs_active = true;
+    c->ks = c->rs;
+    c->ffn_done_valid[0] = c->ffn_done_valid[1] = false;
+    return MOE_OK;
+}
+
+// joins the route stream back into the compute stream (the caller's ids and weights outputs, the
+// cache state and the trace are then ordered before anything the caller enqueues next)
+moe_status route_stream_end(moe_ctx* c) {
+    if (!c->rs_active) return MOE_OK;
+    c->rs_active = false;
+    c->ks = nullptr;
+    HIPCHK(c, hipEventRecord(c->rs_end, c->rs));
+    HIPCHK(c, hipStreamWaitEvent(c->cs, c->rs_end, 0));
+    return MOE_OK;
+}
+
+struct RouteStreamGuard {
+    moe_ctx* c;
+    ~RouteStreamGuard() { (void)route_stream_end(c); }
+};
 
 moe_status check_call(moe_ctx* c, int n_tokens) {
     if (!c) return MOE_EINVAL;
@@ -780,6 +842,10 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     if (hipStreamCreateWithFlags(&c->ps2, hipStreamNonBlocking) != hipSuccess) return bail(MOE_EHIP);
     for (auto& e : c->copy_ev2)
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
+    // the route stream of hybrid stack calls (default priority) and its events
+    if (hipStreamCreateWithFlags(&c->rs, hipStreamNonBlocking) != hipSuccess) return bail(MOE_EHIP);
+    for (hipEvent_t* e : {&c->rs_start, &c->rs_end, &c->k2_done[0], &c->k2_done[1], &c->ffn_done[0], &c->ffn_done[1]})
+        if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
 
     // router weights -> HBM
     where = "router upload";
@@ -923,8 +989,16 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
         // hybrid steps: layer l+1's miss list is taken (and its host task started) before
         // layer l's FFN is launched, so the host workers go from one layer's experts to the
         // next without waiting for the launches in between
+        // one token: K1/K2 on the route stream, so a layer's miss list (the host workers' next
+        // task) does not wait behind an FFN that waits for its copies; copies still wait for the
+        // FFN two layers back (their victims may hold its slots).  Batches keep one stream: their
+        // FFN reads K2's slot buffers, and the waits that protects cost more than the overlap
+        // gains (measured)
+        RouteStreamGuard guard{c};
+        if (n_tokens == 1 && (st = route_stream_begin(c))) return st;
         if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
         if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
+        if (c->rs_active) HIPCHK(c, hipEventRecord(c->k2_done[0], c->rs));
         int nm_of[2] = {0, 0};
         if ((st = stage_misses(c, 0, 0, c->seq, &nm_of[0]))) return st;
         for (int l = 0; l < L; ++l) {
@@ -934,11 +1008,12 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
                 if ((st = launch_resolve(c, step, l + 1, true, nullptr, n_tokens, np, nullptr, idl(l + 1),
                                          wl(l + 1))))
                     return st;
+                if (c->rs_active) HIPCHK(c, hipEventRecord(c->k2_done[np], c->rs));
                 if ((st = stage_misses(c, l + 1, np, c->seq, &nm_of[np]))) return st;
             }
             if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm_of[par]))) return st;
         }
-        return MOE_OK;
+        return route_stream_end(c);
     }
     if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
     if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
@@ -1131,7 +1206,8 @@ moe_status moe_set_backend(moe_ctx* c, int32_t backend, double pcie_gbps, double
         return set_err(c, MOE_EINVAL, "backend %d with B_P %g, B_H %g, %d threads", backend, pcie_gbps, host_gbps,
                        host_threads);
     if (c->cfg.policy != MOE_POLICY_LRU) return set_err(c, MOE_EINVAL, "the hybrid backend needs the LRU policy");
-    if (!c->yh && hipHostMalloc((void**)&c->yh, 2 * (size_t)kHostMaxTokens * c->cfg.hidden * sizeof(float),
+    if (!c->yh && hipHostMalloc((void**)&c->yh,
+                                (size_t)c->cfg.n_layers * kHostMaxTokens * c->cfg.hidden * sizeof(float),
                                 hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
         return set_err(c, MOE_ENOMEM, "host-mapped buffer for the host experts' sums");
     if (!c->xs_stream) {
