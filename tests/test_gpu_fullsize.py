@@ -1,7 +1,9 @@
-"""Full-size parity on the gpt-oss-120b-shaped workload (36 x 128 experts, H = I = 2880, top-4,
-1862 of 4608 experts cached, the full 60.9 GB pool in pinned host RAM), in the launch
-configuration the benchmark times (batch 1, lookahead 1).  Routing ids and the cache trace are
-checked bit-exactly for every step run; outputs at sampled (step, layer) points."""
+"""Full-size parity on every workload shape: gpt-oss-120b (36 x 128 experts, H = I = 2880, top-4,
+1862 of 4608 experts cached, the full 60.9 GB pool in pinned host RAM), Qwen3.6-35B-A3B,
+DeepSeek-V4-Flash (a 147 GB pool, partly pageable) and Qwen3.8-Flash-Next (prefill and 16-request
+decode), in the launch configuration the benchmark times (lookahead 1), with the offload and the
+hybrid backends.  Routing ids and the cache trace are checked bit-exactly for every step run;
+outputs at sampled (step, layer[, token]) points."""
 import numpy as np
 import pytest
 
@@ -129,3 +131,60 @@ def test_qwen38_shaped_hybrid_prefill_and_b16_decode_sampled():
         rel, mx, ok = close_enough(y[t][l, b], r)
         print("hybrid t", t, "l", l, "b", b, "rel-L2", rel)
         assert ok, (t, l, b, rel, mx)
+
+
+@pytest.mark.parametrize("name,T,points", [
+    ("qwen36_35b_a3b_shaped", 64, [(0, 0), (1, 39), (7, 20), (40, 3), (63, 0), (63, 39)]),
+    ("dsv4_flash_shaped", 24, [(0, 0), (1, 42), (5, 21), (12, 3), (23, 0), (23, 42)]),
+], ids=["qwen36_35b_a3b_shaped", "dsv4_flash_shaped"])
+def test_other_shapes_sampled(name, T, points):
+    """The Qwen3.6-shaped (40 x 256 experts, top-8 + shared, 17.1 GB pool, 3789 slots) and the
+    DeepSeek-V4-Flash-shaped (43 x 256, top-6, H = 4096, I = 2048, 147 GB pool, 1211 slots; the
+    pool's unpinned part goes through the bounce ring) workloads at full size, in the benchmark's
+    launch configuration (batch 1, lookahead 1): ids, weights and the whole trace bit-exact for
+    every step run, outputs at sampled (step, layer) points."""
+    wl = synth.WORKLOADS[name]
+    X = synth.decode_inputs(wl)[:T]
+    m, W = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    _, recs = m.stats(trace_cap=1 << 20)
+    m.close()
+    ref = oracle.decode_trace(wl, W, X)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["w"])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    assert ref["counters"]["evictions"] > 0
+    for (t, l) in points:
+        r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
+        rel, mx, ok = close_enough(y[t, l, 0], r)
+        print(name, "t", t, "l", l, "rel-L2", rel)
+        assert ok, (t, l, rel, mx)
+
+
+def test_dsv4_shaped_hybrid_sampled():
+    """The DeepSeek-shaped workload with the hybrid backend (B_P 56 GB/s, B_H 240 GB/s, 10 host
+    workers, as the benchmark runs it on a partly pageable pool): the route-stream schedule, the
+    bounce ring and the host workers together.  ids, trace (host misses with slot -1) and final
+    cache state bit-exact with the oracle's hybrid steps; outputs at sampled points."""
+    wl = synth.WORKLOADS["dsv4_flash_shaped"]
+    T = 40   # long enough for the transferred misses to fill the 1211 slots and start evicting
+    X = synth.decode_inputs(wl)[:T]
+    m, W = make_moe(wl)
+    split = (56.0, 240.0)
+    m.set_backend("hybrid", split[0], split[1], 10)
+    ids, w, y = run_stack(m, wl, X)
+    cnt, recs = m.stats(trace_cap=1 << 20)
+    slot_of, key_of, _ = m.cache_state()
+    m.close()
+    ref = oracle.decode_trace(wl, W, X, split=split)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    r_slot, r_key, _ = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    assert cnt["host_experts"] == ref["counters"]["host"] > 0 and ref["counters"]["evictions"] > 0
+    for (t, l) in [(0, 0), (3, 42), (17, 17), (T - 1, 0), (T - 1, 42)]:
+        r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
+        rel, mx, ok = close_enough(y[t, l, 0], r)
+        print("hybrid t", t, "l", l, "rel-L2", rel)
+        assert ok, (t, l, rel, mx)
