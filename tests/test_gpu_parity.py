@@ -123,6 +123,47 @@ def test_zero_input_edge_case():
     m.close()
 
 
+def test_every_expert_selected():
+    """k = E: every step selects all experts of every layer (softmax over all of them, ids in
+    rank order); with C = L E the whole pool fits, so after the first step every access hits."""
+    wl = synth.Workload("k_eq_e", 3, 4, 4, 1, 256, 128, 12, 10, 1, 0.9, seed=71)
+    X = synth.decode_inputs(wl)
+    m, _ = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    cnt, recs = m.stats(trace_cap=1 << 16)
+    points = [(t, l, 0) for t in range(X.shape[0]) for l in range(wl.n_layers)]
+    ref, _ = _check_run(wl, X, ids, w, y, recs, m, points)
+    assert np.all(np.sort(ids, axis=-1) == np.arange(wl.top_k))
+    assert cnt["misses"] == wl.n_layers * wl.n_experts and cnt["evictions"] == 0
+    m.close()
+
+
+def test_exact_logit_ties_take_the_lower_expert():
+    """Router rows duplicated in pairs (expert 2i+1 = expert 2i) make every logit an exact tie
+    with its partner at a non-zero input: both sides pick the lower index first, so ids, trace,
+    weights and outputs match the oracle bit for bit / within tolerance."""
+    import ctypes
+    import moe_expert_offload_amd as M
+    wl = dataclasses.replace(synth.WORKLOADS["toy"], name="toy_ties", decode_tokens=12)
+    W = synth.router_weights(wl).copy()
+    W[:, 1::2, :] = W[:, 0::2, :]
+    X = synth.decode_inputs(wl)
+    cfg = M.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.n_shared, wl.cache_slots,
+                        wl.max_tokens, 1, 1 << 16, 0, 0, 0, 0)
+    fptr, FillArgs = synth.fill_callback()
+    fa = FillArgs(wl.seed, wl.hidden, wl.inter)
+    m = M.OffloadMoE(cfg, (fptr, ctypes.addressof(fa)), W)
+    ids, w, y = run_stack(m, wl, X)
+    _, recs = m.stats(trace_cap=1 << 16)
+    ref = oracle.decode_trace(wl, W, X)
+    points = [(t, l, 0) for t in range(X.shape[0]) for l in range(wl.n_layers)]
+    _check_run(wl, X, ids, w, y, recs, m, points, ref=ref)
+    # each top-2 pick is a tied pair (2i, 2i+1) in that order, with equal weights
+    assert np.all(ids[..., 0] % 2 == 0) and np.all(ids[..., 1] == ids[..., 0] + 1)
+    np.testing.assert_array_equal(w[..., 0], w[..., 1])
+    m.close()
+
+
 @pytest.mark.parametrize("seed", range(3))
 def test_cache_resolve_random_batches(seed):
     """moe_cache_resolve with caller ids (several tokens, duplicates) against the oracle LRU."""
