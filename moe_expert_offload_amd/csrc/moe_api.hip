@@ -418,10 +418,14 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     while (__atomic_load_n(&ml->seq, __ATOMIC_ACQUIRE) != seq) {
         _mm_pause();
         if ((++spins & 0xFFFF) == 0) {
-            hipError_t q = hipStreamQuery(c->cs);
-            if (q != hipSuccess && q != hipErrorNotReady)
-                return set_err(c, MOE_EHIP, "compute stream failed while waiting for a miss list: %s",
-                               hipGetErrorString(q));
+            // the resolve runs on the compute stream, or on the route stream of a route-stream call
+            for (hipStream_t sq : {c->cs, c->ks}) {
+                if (!sq) continue;
+                hipError_t q = hipStreamQuery(sq);
+                if (q != hipSuccess && q != hipErrorNotReady)
+                    return set_err(c, MOE_EHIP, "%s stream failed while waiting for a miss list: %s",
+                                   sq == c->cs ? "compute" : "route", hipGetErrorString(q));
+            }
             double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
             if (dt > c->spin_timeout_s)
                 return set_err(c, MOE_EHIP, "timed out waiting for the miss list of layer %d", layer);

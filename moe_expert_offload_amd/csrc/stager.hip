@@ -54,11 +54,12 @@ void BounceRing::shutdown() {
     for (auto& t : th_) t.join();
     th_.clear();
     n_threads_ = 1;
-    for (size_t i = 0; i < slot_.size(); ++i) {
+    // (a failed init can leave one more slot than events)
+    for (size_t i = 0; i < ev_.size(); ++i) {
         if (busy_[i]) (void)hipEventSynchronize(ev_[i]);
         (void)hipEventDestroy(ev_[i]);
-        (void)hipHostFree(slot_[i]);
     }
+    for (uint8_t* p : slot_) (void)hipHostFree(p);
     slot_.clear();
     ev_.clear();
     busy_.clear();
