@@ -69,6 +69,28 @@ def test_lookahead_and_causal_are_bitwise_equal():
     np.testing.assert_array_equal(y0.view(np.uint32), y1.view(np.uint32))
 
 
+def test_whole_pool_cache_route_stream_matches_causal_and_oracle():
+    """With the whole pool in the cache (C = L E) one-token stack calls resolve on the route stream
+    and the host gates the copies on the FFN two layers back.  Ids, trace and outputs equal the
+    causal schedule's bit for bit and the oracle's within tolerance."""
+    wl = dataclasses.replace(synth.WORKLOADS["toy"], name="toy_whole_pool", cache_slots=32, decode_tokens=24)
+    assert wl.cache_slots == wl.n_layers * wl.n_experts
+    X = synth.decode_inputs(wl)
+    runs = []
+    for la in (1, 0):
+        m, _ = make_moe(wl, lookahead=la)
+        ids, w, y = run_stack(m, wl, X)
+        _, recs = m.stats(trace_cap=1 << 16)
+        if la == 1:
+            points = [(t, l, 0) for t in range(X.shape[0]) for l in range(wl.n_layers)]
+            _check_run(wl, X, ids, w, y, recs, m, points)
+        runs.append((ids, y, trace_tuples(recs)))
+        m.close()
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    assert runs[0][2] == runs[1][2]
+
+
 def test_layer_forward_matches_stack():
     import torch
     wl = synth.WORKLOADS["toy"]
