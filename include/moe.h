@@ -176,7 +176,12 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t step, int32_t layer, const vo
 /* One decode step through all L layers with the configured lookahead.  Layer
  * l reads x_bf16_dev + l * x_layer_stride elements (stride 0: the same input
  * for every layer) and writes y_bf16_dev + l * y_layer_stride.  ids_dev_out
- * ([L][n_tokens][k]) and w_dev_out may be NULL. */
+ * ([L][n_tokens][k]) and w_dev_out may be NULL.  Work is ordered on the
+ * compute stream as seen by the caller.  One-token calls of the hybrid backend,
+ * and one-token offload calls when the cache holds the whole pool (C >= L * E),
+ * run the router and resolve on a library-owned stream that joins the compute
+ * stream before the call returns; layer l+1's copies then start only once layer
+ * l-1's FFN has ended, so the copies stay one layer ahead. */
 moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev, int64_t x_layer_stride,
                              int32_t n_tokens, void* y_bf16_dev, int64_t y_layer_stride,
                              int32_t* ids_dev_out, float* w_dev_out);
