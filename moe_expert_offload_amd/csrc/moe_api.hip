@@ -49,9 +49,9 @@ struct moe_ctx {
     // l+1 run there, so a layer's miss list (the host workers' next task) does not wait behind an
     // FFN that waits for its copies.  Events order the rest: rs_start (call start on cs) before
     // the call's first K1; ffn_done[p] (on cs, after the FFN of the last layer of parity p) before
-    // the copies that may overwrite that layer's slots (the copies of layer l+2); k2_done[p]
-    // before an FFN that reads K2's slot and weight buffers (the one-token FFN takes them as
-    // launch arguments instead); rs_end joins rs back into cs.
+    // the copies that may overwrite that layer's slots (the copies of layer l+2); k2_done[p],
+    // recorded only when needed, before an FFN that reads K2's slot and weight buffers (the
+    // one-token FFN takes them as launch arguments instead); rs_end joins rs back into cs.
     hipStream_t rs = nullptr;
     hipEvent_t rs_start = nullptr, rs_end = nullptr;
     hipEvent_t k2_done[2] = {nullptr, nullptr};
@@ -571,10 +571,13 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         if (c->copy_used[par][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
         if (c->copy_used[par][1]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev2[par], 0));
     }
-    // the single-token kernels take their slots and weights as launch arguments; every other
-    // FFN reads the ones K2 wrote, on the route stream in a route-stream call
-    if (c->rs_active && par < 2 && !(B == 1 && !slots_dev && c->tok0_valid[par]))
+    // the single-token kernels take their slots and weights as launch arguments; any other FFN
+    // reads the ones K2 wrote, on the route stream in a route-stream call: it waits for all the
+    // route stream holds so far (which includes that K2)
+    if (c->rs_active && par < 2 && !(B == 1 && !slots_dev && c->tok0_valid[par])) {
+        HIPCHK(c, hipEventRecord(c->k2_done[par], c->rs));
         HIPCHK(c, hipStreamWaitEvent(c->cs, c->k2_done[par], 0));
+    }
     const bool prof = (c->cfg.flags & MOE_FLAG_PROFILE) != 0;
     ProfSlot ps{};
     if (prof) {
@@ -1023,7 +1026,6 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
         if (n_tokens == 1 && (st = route_stream_begin(c))) return st;
         if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
         if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
-        if (c->rs_active) HIPCHK(c, hipEventRecord(c->k2_done[0], c->rs));
         int nm_of[2] = {0, 0};
         if ((st = stage_misses(c, 0, 0, c->seq, &nm_of[0]))) return st;
         for (int l = 0; l < L; ++l) {
@@ -1033,7 +1035,6 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
                 if ((st = launch_resolve(c, step, l + 1, true, nullptr, n_tokens, np, nullptr, idl(l + 1),
                                          wl(l + 1))))
                     return st;
-                if (c->rs_active) HIPCHK(c, hipEventRecord(c->k2_done[np], c->rs));
                 if ((st = stage_misses(c, l + 1, np, c->seq, &nm_of[np]))) return st;
             }
             if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm_of[par]))) return st;
@@ -1053,7 +1054,6 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     }
     if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
     if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
-    if (c->rs_active) HIPCHK(c, hipEventRecord(c->k2_done[0], c->rs));
     seq_of[0] = c->seq;
     for (int l = 0; l < L; ++l) {
         const int par = l & 1;
@@ -1064,7 +1064,6 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
             if ((st = launch_route(c, l + 1, xl(l + 1), n_tokens))) return st;
             if ((st = launch_resolve(c, step, l + 1, true, nullptr, n_tokens, np, nullptr, idl(l + 1), wl(l + 1))))
                 return st;
-            if (c->rs_active) HIPCHK(c, hipEventRecord(c->k2_done[np], c->rs));
             seq_of[np] = c->seq;
         }
         if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
