@@ -181,7 +181,9 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t step, int32_t layer, const vo
  * and one-token offload calls when the cache holds the whole pool (C >= L * E),
  * run the router and resolve on a library-owned stream that joins the compute
  * stream before the call returns; layer l+1's copies then start only once layer
- * l-1's FFN has ended, so the copies stay one layer ahead. */
+ * l-1's FFN has ended, so the copies stay one layer ahead.  In the whole-pool
+ * case the call also starts a helper host thread that issues those launches
+ * and is joined before the call returns (also on error). */
 moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev, int64_t x_layer_stride,
                              int32_t n_tokens, void* y_bf16_dev, int64_t y_layer_stride,
                              int32_t* ids_dev_out, float* w_dev_out);
