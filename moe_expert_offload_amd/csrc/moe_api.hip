@@ -1085,7 +1085,8 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     std::atomic<bool> quit{false};
     std::atomic<int> helper_st{MOE_OK};
     std::vector<int64_t> seq_layer((size_t)L, 0);
-    std::thread helper([&] {
+    std::thread helper;
+    auto helper_fn = [&] {
         for (int r = 0; r < L; ++r) {
             while (staged.load(std::memory_order_acquire) < r - 1) {
                 if (quit.load(std::memory_order_relaxed)) return;
@@ -1100,13 +1101,18 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
             seq_layer[(size_t)r] = c->seq;
             resolved.store(r + 1, std::memory_order_release);
         }
-    });
+    };
+    try {
+        helper = std::thread(helper_fn);
+    } catch (...) {
+        return set_err(c, MOE_ENOMEM, "could not start the stack call's helper thread");
+    }
     struct Joiner {
         std::thread& t;
         std::atomic<bool>& q;
         ~Joiner() {
             q.store(true, std::memory_order_relaxed);
-            t.join();
+            if (t.joinable()) t.join();
         }
     } joiner{helper, quit};
     for (int l = 0; l < L; ++l) {
