@@ -840,7 +840,12 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     c->order[0] = (int32_t*)(c->state_dev + sp.ord);
     c->order[1] = c->order[0] + C;
     {
-        std::vector<uint8_t> h(sp.tr, 0);
+        std::vector<uint8_t> h;
+        try {
+            h.assign(sp.tr, 0);
+        } catch (...) {
+            return bail(MOE_ENOMEM);
+        }
         memset(h.data() + sp.slot, 0xFF, n_sl * 4);
         memset(h.data() + sp.key, 0xFF, (size_t)C * 4);
         memset(h.data() + sp.stamp, 0xFF, (size_t)C * 8);
@@ -919,18 +924,37 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     int nth = cfg->fill_threads > 0 ? cfg->fill_threads : (int)std::thread::hardware_concurrency();
     nth = std::max(1, std::min<int>(nth, (int)std::min<size_t>(n_sl, 64)));
     std::atomic<size_t> next{0};
+    std::atomic<bool> fill_failed{false};
     auto worker = [&]() {
-        std::vector<uint8_t> tmp(L.blob_bytes);
+        // nothing may throw across the C ABI (nor out of a thread): a failed buffer allocation
+        // stops the fill and is reported below
+        std::vector<uint8_t> tmp;
+        try {
+            tmp.resize(L.blob_bytes);
+        } catch (...) {
+            fill_failed.store(true);
+            return;
+        }
         for (;;) {
             size_t i = next.fetch_add(1);
-            if (i >= n_sl) break;
+            if (i >= n_sl || fill_failed.load(std::memory_order_relaxed)) break;
             fill(user, (int32_t)(i / E), (int32_t)(i % E), tmp.data());
             repack(L, tmp.data(), const_cast<uint8_t*>(c->blob_src(i)));
         }
     };
-    std::vector<std::thread> th;
-    for (int t = 0; t < nth; ++t) th.emplace_back(worker);
-    for (auto& t : th) t.join();
+    {
+        std::vector<std::thread> th;
+        try {
+            th.reserve((size_t)nth);
+            for (int t = 1; t < nth; ++t) th.emplace_back(worker);
+        } catch (...) {
+            // fewer helper threads: the calling thread fills the rest
+        }
+        worker();
+        for (auto& t : th) t.join();
+    }
+    where = "pool fill (host buffer allocation)";
+    if (fill_failed.load()) return bail(MOE_ENOMEM);
 
     if (cfg->policy == MOE_POLICY_STATIC) {
         where = "static split resident fill";
@@ -946,7 +970,13 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     if (cfg->n_shared > 0) {
         const size_t sb = (size_t)Lyr * cfg->n_shared * L.blob_bytes;
         if (hipMalloc(&c->shared_dev, sb) != hipSuccess) return bail(MOE_ENOMEM);
-        std::vector<uint8_t> tmp(L.blob_bytes), packed(L.blob_bytes);
+        std::vector<uint8_t> tmp, packed;
+        try {
+            tmp.resize(L.blob_bytes);
+            packed.resize(L.blob_bytes);
+        } catch (...) {
+            return bail(MOE_ENOMEM);
+        }
         for (int l = 0; l < Lyr; ++l)
             for (int s = 0; s < cfg->n_shared; ++s) {
                 fill(user, l, -1 - s, tmp.data());
