@@ -2,16 +2,19 @@
 
 A step is one decode token through the whole MoE stack (all layers): router + top-k, cache
 resolve, miss copies over PCIe, expert FFNs and combine, with inputs resident in HBM and the
-expert pool in pinned host RAM.  Default workload: the gpt-oss-120b-shaped decode (36 layers x
-128 experts, top-4, H = I = 2880, MXFP4, batch 1, 1862 of 4608 experts cached, AR(1) hidden
-states with rho = 0.9).  W warm-up tokens, then K timed tokens (the cache keeps its state).
+expert pool in host RAM.  Default workload: the DeepSeek-V4-Flash-shaped decode, the largest
+batch-1 shape and the pages' stress case for the miss path (43 layers x 256 experts, top-6,
+H = 4096, I = 2048, MXFP4, batch 1, 1211 of 11008 experts cached (11 %), a 147 GB pool, AR(1)
+hidden states with rho = 0.85).  W warm-up tokens, then K timed tokens (the cache keeps its state).
 
 Prints one JSON line with the decode rate, the expert-FFN kernel roofline (HIP events around
-every K3/K4 launch on the compute stream), the miss rate, the effective and measured
-host-to-device bandwidth, and the CPU oracle timed on a bounded sample on the host cores.
+graph replays of the layer FFNs on the compute stream, and the same kernels timed inside the
+decode loop), the miss rate, the copy path's achieved and measured host-to-device bandwidth, and
+the CPU oracle timed on a bounded sample on the host cores.
 """
 import argparse
 import ctypes
+import dataclasses
 import json
 import os
 import sys
@@ -157,14 +160,20 @@ def run_prefill(m, wl, dev, rounds):
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nb}}
 
 
-def cpu_baseline(wl, W, X, C, budget_s=20.0):
+def cpu_baseline(wl, W, X, C, n_trace, budget_s=20.0):
     """The oracle as it stands, on the host cores: routing, LRU step and FFN of every token of
-    one decode step through every layer, repeated while the budget lasts (at least one step)."""
+    one decode step through every layer, repeated while the budget lasts (at least one step);
+    and, apart, the oracle's routing and LRU trace alone over the first n_trace tokens (every
+    layer), the part of the method that decides ids and slots."""
     import numpy as np
 
     import oracle
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    wtr = dataclasses.replace(wl, cache_slots=C)
+    t0 = time.perf_counter()
+    oracle.decode_trace(wtr, W, X[:n_trace])
+    trace_s = time.perf_counter() - t0
     cache = oracle.Cache(wl.n_layers, wl.n_experts, C)
     B = X.shape[1]
     t0 = time.perf_counter()
@@ -185,7 +194,11 @@ def cpu_baseline(wl, W, X, C, budget_s=20.0):
     return {"value": done * B / dt, "unit": "tok/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
             "kind": "oracle",
             "sample": f"{done} decode step(s) of {B} token(s) x {wl.n_layers} layers of {wl.name}: FP32 router, "
-                      f"top-{wl.top_k}, LRU step, FP64 MXFP4 SwiGLU FFN of the selected experts"}
+                      f"top-{wl.top_k}, LRU step, FP64 MXFP4 SwiGLU FFN of the selected experts",
+            "trace_only_tok_s": round(n_trace * B / trace_s, 2),
+            "trace_only_sample": f"routing (FP32 logits, top-{wl.top_k}, softmax) and the LRU cache step of "
+                                 f"{n_trace} step(s) x {B} token(s) x {wl.n_layers} layers (warm-up + timed "
+                                 "tokens of this run), no FFN"}
 
 
 def main():
@@ -193,7 +206,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=448)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="gptoss120b_shaped")
+    ap.add_argument("--workload", default="dsv4_flash_shaped")
     ap.add_argument("--lookahead", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ffn-rounds", type=int, default=20)
@@ -350,9 +363,27 @@ def main():
             "launches": args.ffn_rounds * len(layers), "layers_timed": len(layers)}
     if B == 1:
         roof["bytes_k3"], roof["bytes_k4"] = ffn_bytes_split(wl)
-    # miss bytes over the whole timed region: a lower bound on the copy path's achieved rate
+    # the same kernels inside the timed decode loop (one layer FFN in seven timed by the library,
+    # with the miss copies streaming beside them), against the same algorithmic bytes
+    n_ffn = c_all["ffn_timed"] - c_warm["ffn_timed"]
+    if n_ffn > 0 and not c["host_experts"]:
+        us_loop = (c_all["ffn_ns"] - c_warm["ffn_ns"]) / n_ffn / 1e3
+        b_loop = ffn_bytes(wl, B, min(B * wl.top_k, wl.n_experts)) if B == 1 else None
+        roof["in_loop"] = {"avg_us": round(us_loop, 2), "launches_timed": n_ffn}
+        if b_loop:
+            g_loop = b_loop / (us_loop * 1e-6) / 1e9
+            roof["in_loop"].update({"achieved": round(g_loop, 1), "frac": round(g_loop / HBM_PEAK_GBS, 4),
+                                    "bytes_per_launch": b_loop})
+    # miss bytes over the time the copy path was busy (per layer step and copy stream, first copy
+    # start to last copy end, merged over both streams), and over the whole timed region (a lower
+    # bound)
     eff = c["h2d_bytes"] / dt / 1e9
-    extra["h2d"] = {"effective_GBps": round(eff, 2), "measured_GBps": round(h2d_meas, 2),
+    busy_ns = c_all["h2d_ns"] - c_warm["h2d_ns"]
+    ach = c["h2d_bytes"] / busy_ns if busy_ns > 0 else None
+    extra["h2d"] = {"achieved_GBps": round(ach, 2) if ach else None,
+                    "achieved_frac_of_measured": round(ach / h2d_meas, 4) if ach else None,
+                    "busy_frac_of_wall": round(busy_ns * 1e-9 / dt, 4),
+                    "effective_GBps": round(eff, 2), "measured_GBps": round(h2d_meas, 2),
                     "measured_64MB_GBps": round(h2d_big, 2), "frac_of_measured": round(eff / h2d_meas, 4),
                     "link": pcie_link(0)}
     extra["pool"] = {"GB": round(wl.pool * m.blob_bytes / 1e9, 2), "pinned_GB": round(pinned_gb, 2),
@@ -395,7 +426,7 @@ def main():
         del src, dst
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, Wr, X, C)
+        cpu = cpu_baseline(wl, Wr, X, C, W_ + K)
     m.close()
     out = {
         "metric": ("decode tok/s per MoE stack at batch 1" if B == 1 else

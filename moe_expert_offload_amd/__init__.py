@@ -25,12 +25,13 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE = 0, -1, -2, -3, -4, -5
+MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE, MOE_EVERIFY = 0, -1, -2, -3, -4, -5, -6
 MOE_FLAG_PROFILE = 1
 MOE_FLAG_PER_TOKEN_FFN = 2
+MOE_FLAG_VERIFY = 4
 MOE_POLICY_LRU, MOE_POLICY_STATIC = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
-           -5: "MOE_ESTATE"}
+           -5: "MOE_ESTATE", -6: "MOE_EVERIFY"}
 
 
 class MoeConfig(ctypes.Structure):
@@ -45,7 +46,8 @@ class MoeCounters(ctypes.Structure):
         "trace_dropped", "ffn_launches", "h2d_bounced", "pool_pinned_bytes")] + [
         ("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double),
         ("host_experts", ctypes.c_uint64), ("host_tasks", ctypes.c_uint64),
-        ("host_busy_ms", ctypes.c_double), ("host_wait_ms", ctypes.c_double)]
+        ("host_busy_ms", ctypes.c_double), ("host_wait_ms", ctypes.c_double),
+        ("h2d_ns", ctypes.c_uint64), ("ffn_ns", ctypes.c_uint64), ("ffn_timed", ctypes.c_uint64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -492,7 +492,14 @@ double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int
     };
     const auto t0 = std::chrono::steady_clock::now();
     std::vector<std::thread> pool;
-    for (int t = 0; t < threads; ++t) pool.emplace_back(run, t);
+    // nothing may throw out of here (the C ABI calls it): a thread that cannot start leaves the
+    // measurement to the ones that did, and the rate counts only their work
+    try {
+        pool.reserve((size_t)threads);
+        for (int t = 0; t < threads; ++t) pool.emplace_back(run, t);
+    } catch (...) {
+    }
+    if (pool.empty()) return 0.0;
     std::this_thread::sleep_for(std::chrono::duration<double>(min_seconds));
     stop.store(true);
     for (auto& th : pool) th.join();

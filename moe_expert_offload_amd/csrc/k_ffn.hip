@@ -97,18 +97,26 @@ __device__ __forceinline__ float karg_w(const FfnArgs& a, int j) {
     return v;
 }
 
-// blob of the token's j-th expert (j >= k: the shared expert)
+// slot of the token's j-th routed expert (j < k)
+__device__ __forceinline__ int expert_slot(const FfnArgs& a, int b, int j) {
+    return a.karg ? karg_slot(a, j) : a.slots[b * a.k + j];
+}
+
+// blob of the token's j-th expert (j >= k: the shared expert).  A slot outside [0, C) is never
+// dereferenced: slot 0 is read instead and the expert's weight is NaN (expert_weight), so every
+// output of the token is NaN.
 __device__ __forceinline__ const uint8_t* expert_blob(const FfnArgs& a, int b, int j) {
     if (j < a.k) {
-        const int slot = a.karg ? karg_slot(a, j) : a.slots[b * a.k + j];
-        return a.arena + (size_t)slot * a.blob_bytes;
+        const int slot = expert_slot(a, b, j);
+        return a.arena + (size_t)((unsigned)slot < (unsigned)a.C ? slot : 0) * a.blob_bytes;
     }
     return a.shared + (size_t)(a.layer * a.n_shared + (j - a.k)) * a.blob_bytes;
 }
 
 __device__ __forceinline__ float expert_weight(const FfnArgs& a, int b, int j) {
     if (j >= a.k) return 1.0f;
-    return a.karg ? karg_w(a, j) : a.w[b * a.k + j];
+    const float w = a.karg ? karg_w(a, j) : a.w[b * a.k + j];
+    return (unsigned)expert_slot(a, b, j) < (unsigned)a.C ? w : __uint_as_float(0x7FC00000u);
 }
 
 constexpr int FFN_THREADS = 256;

@@ -321,6 +321,33 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         else atomicAdd(&s_invalid, 1);
     }
     __syncthreads();
+    if (s_invalid != 0) {
+        // Ids outside [0, E): the step is rejected as a whole and leaves the cache as it was.
+        // Only the count is published (no entries); the victim order is carried over unchanged
+        // into the other order buffer (the next step reads that one); slot table, reverse map,
+        // stamps, clock, counters and trace are not touched; every slot output is -1.
+        if (!stat) {
+#pragma unroll
+            for (int c = 0; c < K2_CPT; ++c)
+                if (p0 + c < C) order_out[p0 + c] = ent[c];
+        }
+        for (int i = tid; i < a.n_ids; i += K2_THREADS) {
+            a.slots[i] = -1;
+            if (a.slots_out) a.slots_out[i] = -1;
+        }
+        if (tid < 64) {
+            if (tid == 0) {
+                a.ml->n_miss = 0;
+                a.ml->n_xfer = 0;
+                a.ml->n_unique = 0;
+                a.ml->n_evict = 0;
+                a.ml->n_invalid = s_invalid;
+            }
+            __threadfence_system();
+            if (tid == 0) __hip_atomic_store(&a.ml->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        return;
+    }
 
     // classify the requested experts (thread e <-> expert e; E <= 1024)
     const bool req = e < E && s_req[e] != 0;

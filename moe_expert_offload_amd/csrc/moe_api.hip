@@ -40,6 +40,11 @@ struct ProfSlot {
     hipEvent_t ev[3];
 };
 
+// a timed interval on the GPU: [ev[0], ev[1]] on one stream
+struct TimedPair {
+    hipEvent_t ev[2];
+};
+
 struct moe_ctx {
     moe_config cfg{};
     Layout lay{};
@@ -104,6 +109,26 @@ struct moe_ctx {
     uint64_t ffn_launches = 0;
     double k3_ms = 0, k4_ms = 0;
     std::vector<ProfSlot> prof_used, prof_free;
+    // Copy-path busy time: one timed pair per copy stream and layer step with copies (before the
+    // first copy, after the last); harvested into intervals on the GPU clock (relative to t_ref)
+    // and merged, so copies overlapping on the two streams count once.
+    hipEvent_t t_ref = nullptr;
+    std::vector<TimedPair> h2d_used, h2d_free;
+    std::vector<std::pair<double, double>> h2d_iv;   // harvested, not yet merged (ms from t_ref)
+    double h2d_iv_end = -1.0;                        // end of the merged busy time so far (ms)
+    double h2d_busy_ms = 0.0;
+    // Sampled FFN timing (every FFN_SAMPLE-th layer FFN; every one under MOE_FLAG_PROFILE)
+    std::vector<TimedPair> ffn_used, ffn_free;
+    uint64_t ffn_count = 0, ffn_timed = 0;
+    double ffn_ms = 0.0;
+    // Debug and failure injection (environment at init): MOE_FAULT=h2d_fail_at=N makes the N-th
+    // host-to-device copy (1-based, over the context's life) fail as a HIP error would, before it
+    // is issued; h2d_corrupt_at=N copies the wrong pool blob for the N-th copy.  MOE_VERIFY=1 (or
+    // MOE_FLAG_VERIFY) reads back every filled slot once its copy has landed and compares it with
+    // its pool blob.
+    uint64_t fault_fail_at = 0, fault_corrupt_at = 0, copies_issued = 0;
+    bool verify = false;
+    std::vector<uint8_t> verify_buf;
     // hybrid backend: part of a step's misses (batches of at most 16 tokens) computed by host workers
     int backend = MOE_BACKEND_OFFLOAD;
     double hyb_bp = 0.0, hyb_bh = 0.0;   // B_P and B_H of the split
@@ -142,7 +167,7 @@ moe_status set_err(moe_ctx* c, moe_status st, const char* fmt, ...) {
     if (c) {
         std::lock_guard<std::mutex> lk(c->err_mu);
         c->err = buf;
-        if (st == MOE_EHIP) c->failed = true;
+        if (st == MOE_EHIP || st == MOE_EVERIFY) c->failed = true;
     }
     return st;
 }
@@ -309,6 +334,9 @@ void free_all(moe_ctx* c) {
     if (c->rs) (void)hipStreamDestroy(c->rs);
     for (auto& p : c->prof_used) for (auto e : p.ev) (void)hipEventDestroy(e);
     for (auto& p : c->prof_free) for (auto e : p.ev) (void)hipEventDestroy(e);
+    for (auto* v : {&c->h2d_used, &c->h2d_free, &c->ffn_used, &c->ffn_free})
+        for (auto& p : *v) for (auto e : p.ev) (void)hipEventDestroy(e);
+    if (c->t_ref) (void)hipEventDestroy(c->t_ref);
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev2) if (e) (void)hipEventDestroy(e);
     if (c->ps2) (void)hipStreamDestroy(c->ps2);
@@ -409,6 +437,75 @@ moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
     c->xh_stride = xs;
     c->hyb_call = true;
     c->hyb_B = B;
+    return MOE_OK;
+}
+
+moe_status get_pair(moe_ctx* c, std::vector<TimedPair>& free_list, TimedPair& p) {
+    if (!free_list.empty()) {
+        p = free_list.back();
+        free_list.pop_back();
+        return MOE_OK;
+    }
+    p.ev[0] = p.ev[1] = nullptr;
+    for (auto& e : p.ev)
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto& f : p.ev)
+                if (f) (void)hipEventDestroy(f);
+            return set_err(c, MOE_EHIP, "timing event creation failed");
+        }
+    return MOE_OK;
+}
+
+constexpr int FFN_SAMPLE = 7;           // one layer FFN in this many is timed (co-prime with layer counts)
+constexpr size_t TIMED_PENDING = 256;   // timed pairs kept before the oldest finished ones are harvested
+
+// Copy-path busy time: intervals of the finished timed pairs (all of them when `all`, which
+// waits), merged into the running union of busy time.  An interval's start is read against
+// t_ref and its length from its own two events (float milliseconds lose precision far from
+// t_ref; the length stays exact).
+moe_status harvest_h2d(moe_ctx* c, bool all) {
+    size_t n = 0;
+    for (; n < c->h2d_used.size(); ++n) {
+        TimedPair& p = c->h2d_used[n];
+        if (!all && hipEventQuery(p.ev[1]) != hipSuccess) break;
+        float t0 = 0.0f, len = 0.0f;
+        HIPCHK(c, hipEventSynchronize(p.ev[1]));
+        HIPCHK(c, hipEventElapsedTime(&t0, c->t_ref, p.ev[0]));
+        HIPCHK(c, hipEventElapsedTime(&len, p.ev[0], p.ev[1]));
+        c->h2d_iv.emplace_back((double)t0, (double)t0 + (double)len);
+        c->h2d_free.push_back(p);
+    }
+    (void)hipGetLastError();  // a not-ready query is not an error
+    c->h2d_used.erase(c->h2d_used.begin(), c->h2d_used.begin() + (ptrdiff_t)n);
+    std::sort(c->h2d_iv.begin(), c->h2d_iv.end());
+    for (const auto& iv : c->h2d_iv) {
+        if (iv.first >= c->h2d_iv_end) {
+            c->h2d_busy_ms += iv.second - iv.first;
+            c->h2d_iv_end = iv.second;
+        } else if (iv.second > c->h2d_iv_end) {
+            c->h2d_busy_ms += iv.second - c->h2d_iv_end;
+            c->h2d_iv_end = iv.second;
+        }
+    }
+    c->h2d_iv.clear();
+    return MOE_OK;
+}
+
+// sampled FFN times of the finished timed pairs (all of them when `all`, which waits)
+moe_status harvest_ffn(moe_ctx* c, bool all) {
+    size_t n = 0;
+    for (; n < c->ffn_used.size(); ++n) {
+        TimedPair& p = c->ffn_used[n];
+        if (!all && hipEventQuery(p.ev[1]) != hipSuccess) break;
+        float ms = 0.0f;
+        HIPCHK(c, hipEventSynchronize(p.ev[1]));
+        HIPCHK(c, hipEventElapsedTime(&ms, p.ev[0], p.ev[1]));
+        c->ffn_ms += ms;
+        ++c->ffn_timed;
+        c->ffn_free.push_back(p);
+    }
+    (void)hipGetLastError();
+    c->ffn_used.erase(c->ffn_used.begin(), c->ffn_used.begin() + (ptrdiff_t)n);
     return MOE_OK;
 }
 
@@ -518,24 +615,56 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         }
     }
     bool used[2] = {false, false};
+    hipStream_t qs[2] = {c->ps, c->ps2};
     int nd = 0;  // direct copies so far: they alternate between the two copy streams
     int ncopy = 0;
+    if (c->h2d_used.size() >= TIMED_PENDING) {
+        moe_status st = harvest_h2d(c, false);
+        if (st) return st;
+    }
+    // the first copy on a stream opens its timed interval (the pair goes to the pending list at
+    // once, so an error return leaks nothing; the context is failed then anyway)
+    auto open_stream = [&](int q) -> moe_status {
+        if (used[q]) return MOE_OK;
+        TimedPair tp{};
+        moe_status st = get_pair(c, c->h2d_free, tp);
+        if (st) return st;
+        if (hipEventRecord(tp.ev[0], qs[q]) != hipSuccess) {
+            c->h2d_free.push_back(tp);
+            return set_err(c, MOE_EHIP, "copy timing event record failed");
+        }
+        c->h2d_used.push_back(tp);
+        used[q] = true;
+        return MOE_OK;
+    };
+    size_t pair_of[2] = {0, 0};
     for (int i = 0; i < nm; ++i) {
         const MissEntry m = ml->e[i];
         if (m.slot < 0) continue;  // computed by the host
         ++ncopy;
         const size_t idx = (size_t)layer * c->cfg.n_experts + m.expert;
         uint8_t* dst = c->arena + (size_t)m.slot * blob;
+        ++c->copies_issued;
+        if (c->fault_fail_at && c->copies_issued == c->fault_fail_at)
+            return set_err(c, MOE_EHIP, "injected failure of host-to-device copy %llu (MOE_FAULT), layer %d expert %d",
+                           (unsigned long long)c->copies_issued, layer, m.expert);
+        const size_t n_sl = (size_t)c->cfg.n_layers * c->cfg.n_experts;
+        const size_t src_idx = (c->fault_corrupt_at && c->copies_issued == c->fault_corrupt_at) ? (idx + 1) % n_sl : idx;
+        const int q = idx < c->n_pin ? (nd++ & 1) : 0;
+        if (!used[q]) {
+            moe_status st = open_stream(q);
+            if (st) return st;
+            pair_of[q] = c->h2d_used.size() - 1;
+        }
         if (idx < c->n_pin) {
-            const int q = nd++ & 1;
-            HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(idx), blob, hipMemcpyHostToDevice, q ? c->ps2 : c->ps));
-            used[q] = true;
+            HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(src_idx), blob, hipMemcpyHostToDevice, qs[q]));
         } else {
-            HIPCHK(c, c->bounce.copy(dst, c->blob_src(idx), blob));  // on the caller's copy stream
+            HIPCHK(c, c->bounce.copy(dst, c->blob_src(src_idx), blob));  // on the caller's copy stream
             ++c->h2d_bounced;
-            used[0] = true;
         }
     }
+    for (int q = 0; q < 2; ++q)
+        if (used[q]) HIPCHK(c, hipEventRecord(c->h2d_used[pair_of[q]].ev[1], qs[q]));
     if (used[0]) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
     if (used[1]) HIPCHK(c, hipEventRecord(c->copy_ev2[par], c->ps2));
     c->copy_used[par][0] = used[0];
@@ -543,6 +672,21 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     c->h2d_bytes += (uint64_t)ncopy * blob;
     c->h2d_copies += (uint64_t)ncopy;
     if (n_miss_out) *n_miss_out = ncopy;
+    if (c->verify && ncopy > 0) {
+        // debug mode: once this step's copies have landed, every filled slot must hold its pool blob
+        HIPCHK(c, hipStreamSynchronize(c->ps));
+        HIPCHK(c, hipStreamSynchronize(c->ps2));
+        if (c->verify_buf.size() != blob) c->verify_buf.assign(blob, 0);
+        for (int i = 0; i < nm; ++i) {
+            const MissEntry m = ml->e[i];
+            if (m.slot < 0) continue;
+            const size_t idx = (size_t)layer * c->cfg.n_experts + m.expert;
+            HIPCHK(c, hipMemcpy(c->verify_buf.data(), c->arena + (size_t)m.slot * blob, blob, hipMemcpyDeviceToHost));
+            if (memcmp(c->verify_buf.data(), c->blob_src(idx), blob) != 0)
+                return set_err(c, MOE_EVERIFY, "slot %d (layer %d, expert %d) differs from its pool blob after its copy",
+                               m.slot, layer, m.expert);
+        }
+    }
     return MOE_OK;
 }
 
@@ -587,6 +731,22 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         moe_status st = get_prof(c, ps);
         if (st) return st;
         HIPCHK(c, hipEventRecord(ps.ev[0], c->cs));
+    }
+    // every FFN_SAMPLE-th layer FFN is timed (on the compute stream, after its copy waits)
+    const bool sampled = !prof && (c->ffn_count++ % FFN_SAMPLE) == 0;
+    TimedPair tp{};
+    if (sampled) {
+        if (c->ffn_used.size() >= TIMED_PENDING) {
+            moe_status st = harvest_ffn(c, false);
+            if (st) return st;
+        }
+        moe_status st = get_pair(c, c->ffn_free, tp);
+        if (st) return st;
+        if (hipEventRecord(tp.ev[0], c->cs) != hipSuccess) {
+            c->ffn_free.push_back(tp);
+            return set_err(c, MOE_EHIP, "FFN timing event record failed");
+        }
+        c->ffn_used.push_back(tp);  // its end is recorded after the launches (destroyed with the context on error)
     }
     if (B > 1 && !(c->cfg.flags & MOE_FLAG_PER_TOKEN_FFN)) {
         GroupArgs g{};
@@ -652,6 +812,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
     f.NBI = c->lay.NBI;
     f.I = c->cfg.inter;
     f.H = c->cfg.hidden;
+    f.C = c->cfg.cache_slots;
     f.karg = (B == 1 && !slots_dev && par < 2 && c->tok0_valid[par]) ? 1 : 0;
     if (f.karg) {
         // the experts in GPU slots, in rank order (hybrid steps leave some to the host)
@@ -673,6 +834,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         HIPCHK(c, hipEventRecord(ps.ev[2], c->cs));
         c->prof_used.push_back(ps);
     }
+    if (sampled) HIPCHK(c, hipEventRecord(tp.ev[1], c->cs));
     if (c->rs_active && par < 2) {
         HIPCHK(c, hipEventRecord(c->ffn_done[par], c->cs));
         c->ffn_done_valid[par] = true;
@@ -873,6 +1035,33 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     for (int p = 0; p < 2; ++p) miss_list(c, p)->seq = -1;
     for (auto& e : c->copy_ev)
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
+    // the reference point of the copy-path timing (the GPU clock is shared by all streams)
+    where = "timing reference";
+    if (hipEventCreate(&c->t_ref) != hipSuccess || hipEventRecord(c->t_ref, c->ps) != hipSuccess)
+        return bail(MOE_EHIP);
+    // debug and failure-injection switches
+    c->verify = (cfg->flags & MOE_FLAG_VERIFY) != 0;
+    if (const char* v = getenv("MOE_VERIFY")) c->verify = c->verify || (v[0] && strcmp(v, "0") != 0);
+    if (const char* f = getenv("MOE_FAULT")) {
+        where = "MOE_FAULT";
+        std::string spec(f);
+        size_t pos = 0;
+        while (pos < spec.size()) {
+            size_t end = spec.find(',', pos);
+            if (end == std::string::npos) end = spec.size();
+            const std::string item = spec.substr(pos, end - pos);
+            unsigned long long n = 0;
+            char tail = 0;
+            if (sscanf(item.c_str(), "h2d_fail_at=%llu%c", &n, &tail) == 1 && n > 0) c->fault_fail_at = n;
+            else if (sscanf(item.c_str(), "h2d_corrupt_at=%llu%c", &n, &tail) == 1 && n > 0) c->fault_corrupt_at = n;
+            else if (!item.empty()) {
+                g_init_err = "moe_init_pool: MOE_FAULT item '" + item + "' is not h2d_fail_at=N or h2d_corrupt_at=N";
+                free_all(c);
+                return MOE_EINVAL;
+            }
+            pos = end + 1;
+        }
+    }
     // a second copy stream (default priority): blob copies alternate between the two, which
     // keeps two DMA queues busy and hides the per-copy overhead of small blobs
     if (hipStreamCreateWithFlags(&c->ps2, hipStreamNonBlocking) != hipSuccess) return bail(MOE_EHIP);
@@ -1185,6 +1374,16 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
     // drain: restart the trace at 0, keep the dropped count
     uint64_t zero2[2] = {0, dropped};
     HIPCHK(c, hipMemcpy(c->cd.trace_head, zero2, sizeof zero2, hipMemcpyHostToDevice));
+    HIPCHK(c, hipStreamSynchronize(c->ps2));
+    {
+        moe_status st = harvest_h2d(c, true);
+        if (!st) st = harvest_ffn(c, true);
+        if (st) return st;
+        // a fresh reference point keeps the interval starts precise (float milliseconds)
+        HIPCHK(c, hipEventRecord(c->t_ref, c->ps));
+        HIPCHK(c, hipEventSynchronize(c->t_ref));
+        c->h2d_iv_end = -1.0;
+    }
     for (auto& p : c->prof_used) {
         float a = 0, b = 0;
         HIPCHK(c, hipEventElapsedTime(&a, p.ev[0], p.ev[1]));
@@ -1213,6 +1412,9 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         out->host_tasks = c->host_tasks;
         out->host_busy_ms = (double)c->hpool.busy_ns() * 1e-6;
         out->host_wait_ms = c->host_wait_ms;
+        out->h2d_ns = (uint64_t)llround(c->h2d_busy_ms * 1e6);
+        out->ffn_ns = (uint64_t)llround(c->ffn_ms * 1e6);
+        out->ffn_timed = c->ffn_timed;
     }
     c->ffn_launches = 0;
     c->k3_ms = c->k4_ms = 0;

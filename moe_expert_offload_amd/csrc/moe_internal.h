@@ -129,6 +129,7 @@ struct FfnArgs {
     const float* yh;        // [B][H] FP32 added before rounding (host-computed experts), or NULL
     size_t blob_bytes, d_codes_off, d_scales_off;
     int k, n_shared, nE, layer, NB, NBI, I, H;
+    int C;                  // slots in the arena: a slot outside [0, C) is never read (NaN output)
     int P1, P2;             // K3 and K4 workgroups per token
     int karg;               // 1: slots and weights of the single token come in kslot/kw
     int32_t kslot[16];

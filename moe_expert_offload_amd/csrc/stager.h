@@ -12,12 +12,11 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
-#include <condition_variable>
 #include <cstddef>
 #include <cstdint>
-#include <mutex>
-#include <thread>
 #include <vector>
+
+#include "copy_team.h"
 
 namespace moe {
 
@@ -29,7 +28,8 @@ public:
     ~BounceRing() { shutdown(); }
 
     // slots pinned buffers of slot_bytes each; threads host threads per copy
-    // (including the caller).  Returns hipSuccess or the failing call's error.
+    // (including the caller).  Returns hipSuccess or the failing call's error
+    // (hipErrorOutOfMemory when a copy thread could not be started).
     hipError_t init(size_t slot_bytes, int slots, int threads, hipStream_t stream);
 
     // Copies `bytes` (<= slot_bytes) from pageable host memory to device memory
@@ -42,9 +42,6 @@ public:
     uint64_t copies() const { return copies_; }
 
 private:
-    void worker(int id);
-    void parallel_memcpy(uint8_t* dst, const uint8_t* src, size_t bytes);
-
     size_t slot_bytes_ = 0;
     std::vector<uint8_t*> slot_;
     std::vector<hipEvent_t> ev_;
@@ -52,17 +49,7 @@ private:
     size_t next_ = 0;
     hipStream_t stream_ = nullptr;
     uint64_t copies_ = 0;
-    // memcpy workers
-    std::vector<std::thread> th_;
-    int n_threads_ = 1;        // memcpy threads including the caller
-    std::mutex mu_;
-    std::condition_variable cv_go_, cv_done_;
-    uint64_t gen_ = 0;
-    int pending_ = 0;
-    bool stop_ = false;
-    uint8_t* job_dst_ = nullptr;
-    const uint8_t* job_src_ = nullptr;
-    size_t job_bytes_ = 0;
+    CopyTeam team_;  // host threads that fill a ring slot together
 };
 
 }  // namespace moe

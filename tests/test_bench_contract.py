@@ -59,3 +59,46 @@ def test_pcie_and_budget_arithmetic():
     assert abs(b.per_token_budget_gb(49.0, 127.0) - 0.38583) < 1e-4
     assert b.decode_rate(100, 11.0, 1.0) == 10.0
     assert b.ffn_flops(synth.WORKLOADS["toy"], 3) == 2 * 3 * 3 * 256 * 512
+
+
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_worked_numbers.txt")
+
+
+def _golden(tag):
+    return [[float(v) for v in line.split()[1:]] for line in open(GOLDEN) if line.split()[:1] == [tag]]
+
+
+def test_decode_rate_reproduces_the_pages_runs():
+    """blog.florigen.ai Qwen3.8-Flash-Next page, speed section: three runs printed as completion
+    tokens, total seconds and time to first token, with their decode rates and mean."""
+    b = _bench()
+    rows = _golden("decode")
+    assert len(rows) == 3
+    rates = []
+    for tokens, total, ttft, printed in rows:
+        r = b.decode_rate(tokens, total, ttft)
+        assert abs(r - printed) < 0.005 + 1e-9, (tokens, total, ttft, r, printed)
+        rates.append(r)
+    (mean,), = _golden("decode_mean")
+    assert abs(sum(rates) / 3 - mean) < 0.005
+
+
+def test_pcie_payload_reproduces_the_pages_link_figures():
+    """Same page, PCIe efficiency section: PCIe 5.0 x8 carries 31.5 GB/s per direction, and
+    the measured 28.9 GB/s is 91.7 % of it."""
+    b = _bench()
+    (gt, lanes, printed), = _golden("pcie")
+    assert abs(b.pcie_payload_gbps(gt, lanes) - printed) < 0.05
+    (meas, link, pct), = _golden("pcie_eff")
+    assert abs(100.0 * meas / b.pcie_payload_gbps(gt, lanes) - pct) < 0.1
+    assert abs(100.0 * meas / link - pct) < 0.1
+
+
+def test_per_token_budget_reproduces_the_pages_ceiling():
+    """pirouter.ai "FreeToken x RTX 5090" page, expert-path section: the per-token transfer
+    ceiling is the link rate over the decode rate (0.39 GB at 127.1 tok/s, 1.53 GB at 32 tok/s)."""
+    b = _bench()
+    rows = _golden("budget")
+    assert len(rows) == 2
+    for link, tok_s, printed in rows:
+        assert abs(b.per_token_budget_gb(link, tok_s) - printed) < 0.005 + 1e-9, (link, tok_s, printed)

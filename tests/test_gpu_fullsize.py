@@ -188,3 +188,32 @@ def test_dsv4_shaped_hybrid_sampled():
         rel, mx, ok = close_enough(y[t, l, 0], r)
         print("hybrid t", t, "l", l, "rel-L2", rel)
         assert ok, (t, l, rel, mx)
+
+
+def test_gptoss_shaped_whole_pool_schedule_sampled():
+    """C = L E = 4608 slots (the whole 60.9 GB pool cached, as auto sizing gives on this GPU): one-token
+    stack calls then resolve on the route stream, launched by a helper host thread, and the host
+    stages layer l+1's copies once layer l-1's FFN has ended.  48 tokens: ids, weights, the whole
+    trace and the final cache state bit-exact with the oracle; outputs at sampled (step, layer)
+    points."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["gptoss120b_shaped"], name="gptoss_whole_pool", cache_slots=36 * 128)
+    T = 48
+    X = synth.decode_inputs(wl)[:T]
+    m, W = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    _, recs = m.stats(trace_cap=1 << 20)
+    state = m.cache_state()
+    m.close()
+    ref = oracle.decode_trace(wl, W, X)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["w"])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    for u, v in zip(state, ref["cache"].state()):
+        np.testing.assert_array_equal(u, v)
+    assert ref["counters"]["evictions"] == 0
+    for (t, l) in [(0, 0), (1, 35), (9, 18), (T // 2, 2), (T - 1, 1), (T - 1, 35)]:
+        r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
+        rel, mx, ok = close_enough(y[t, l, 0], r)
+        print("whole pool t", t, "l", l, "rel-L2", rel)
+        assert ok, (t, l, rel, mx)

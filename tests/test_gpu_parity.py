@@ -91,6 +91,30 @@ def test_whole_pool_cache_route_stream_matches_causal_and_oracle():
     assert runs[0][2] == runs[1][2]
 
 
+def test_whole_pool_schedule_deep_stack_matches_causal_and_oracle():
+    """The whole-pool one-token schedule with 8 layers: the helper thread's resolve of layer r
+    waits until layer r-2's miss list, which it rewrites, has been staged, a gate that only blocks
+    with more than two layers in flight.  Ids, trace, final cache state and outputs equal the causal
+    schedule's bit for bit and the oracle's (outputs within tolerance) over every step."""
+    wl = synth.Workload("whole_pool_l8", 8, 16, 2, 0, 256, 512, 8 * 16, 24, 1, 0.9, seed=21)
+    X = synth.decode_inputs(wl)
+    runs = []
+    for la in (1, 0):
+        m, _ = make_moe(wl, lookahead=la)
+        ids, w, y = run_stack(m, wl, X)
+        _, recs = m.stats(trace_cap=1 << 16)
+        if la == 1:
+            points = [(t, l, 0) for t in range(X.shape[0]) for l in range(wl.n_layers)]
+            _check_run(wl, X, ids, w, y, recs, m, points)
+        runs.append((ids, y, trace_tuples(recs), m.cache_state()))
+        m.close()
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    assert runs[0][2] == runs[1][2]
+    for u, v in zip(runs[0][3], runs[1][3]):
+        np.testing.assert_array_equal(u, v)
+
+
 def test_layer_forward_matches_stack():
     import torch
     wl = synth.WORKLOADS["toy"]
@@ -283,16 +307,80 @@ def test_profile_counters_and_h2d_measurement():
     m.close()
 
 
-def test_out_of_range_ids_are_rejected():
-    """Ids outside [0, E) given to moe_cache_resolve are counted by the resolve kernel (never
-    used as an index) and the call fails with MOE_EINVAL."""
+def test_out_of_range_ids_are_rejected_and_leave_no_trace():
+    """Ids outside [0, E) given to moe_cache_resolve are counted by the resolve kernel (never used
+    as an index) and the whole step is rejected with MOE_EINVAL before any state changes: slot
+    table, reverse map, stamps, counters and trace stay as they were and every slot output is -1.
+    The context keeps working: a run with rejected calls between its steps equals, in ids, trace,
+    cache state and outputs, the oracle run that never saw them."""
     import torch
     import moe_expert_offload_amd as M
-    wl = synth.WORKLOADS["toy"]
+    from gpu_helpers import bf16_to_f32
+    wl = dataclasses.replace(synth.WORKLOADS["toy"], name="toy_reject", decode_tokens=10)
+    X = synth.decode_inputs(wl)  # [T][1][H]: one token per step through the stack
+    W = synth.router_weights(wl)
     m, _ = make_moe(wl, max_tokens=2)
-    ids = torch.tensor([[0, wl.n_experts + 5], [1, 2]], dtype=torch.int32, device=m.device)
-    with pytest.raises(M.MoeError) as ei:
+    dev = m.device
+    xd = torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).to(dev)
+    T, L, H, k = X.shape[0], wl.n_layers, wl.hidden, wl.top_k
+    y = torch.empty((T, L, 1, H), dtype=torch.int16, device=dev)
+    ids = torch.empty((T, L, 1, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, L, 1, k), dtype=torch.float32, device=dev)
+    # the oracle: the same stack steps plus the valid caller-id steps, none of the rejected ones
+    ref_ids, ref_w = oracle.route_batch(W, X.reshape(T, H), k, np.tile(np.arange(L), T), np.repeat(np.arange(T), L))
+    ref_ids, ref_w = ref_ids.reshape(T, L, 1, k), ref_w.reshape(T, L, 1, k)
+    cache = oracle.Cache(L, wl.n_experts, wl.cache_slots)
+    recs_ref = []
+    valid = np.array([[3, 9], [9, 14]], np.int32)
+    bad = {3: np.array([[0, wl.n_experts + 5], [1, 2]], np.int32), 7: np.array([[-1, 4], [7, 7]], np.int32)}
+
+    def drain_and_check():
+        _, recs = m.stats(trace_cap=1 << 12)
+        want = np.concatenate(recs_ref) if recs_ref else np.empty(0, oracle.TRACE_DTYPE)
+        assert trace_tuples(recs) == trace_tuples(want)
+        recs_ref.clear()
+
+    for t in range(T):
+        if t in bad:
+            drain_and_check()
+            before = m.cache_state()
+            c0, _ = m.stats()
+            sl = torch.full((2, k), 123, dtype=torch.int32, device=dev)
+            with pytest.raises(M.MoeError) as ei:
+                with torch.cuda.stream(m.compute_stream):
+                    m.cache_resolve(100 + t, t % L, torch.from_numpy(bad[t]).to(dev), sl)
+            assert ei.value.status == M.MOE_EINVAL
+            m.compute_stream.synchronize()
+            assert np.all(sl.cpu().numpy() == -1)
+            for u, v in zip(before, m.cache_state()):
+                np.testing.assert_array_equal(u, v)
+            c1, recs_mid = m.stats(trace_cap=1 << 10)
+            assert len(recs_mid) == 0
+            assert all(c0[f] == c1[f] for f in ("hits", "misses", "evictions", "resolves", "h2d_copies"))
+            # then a valid caller-id step on the same context
+            sl2 = torch.empty((2, k), dtype=torch.int32, device=dev)
+            with torch.cuda.stream(m.compute_stream):
+                nm = m.cache_resolve(200 + t, (t + 1) % L, torch.from_numpy(valid).to(dev), sl2)
+            m.compute_stream.synchronize()
+            slots_ref, r = cache.step(200 + t, (t + 1) % L, valid)
+            recs_ref.append(r)
+            assert nm == int((r["hit"] == 0).sum())
+            np.testing.assert_array_equal(sl2.cpu().numpy().ravel(), slots_ref)
         with torch.cuda.stream(m.compute_stream):
-            m.cache_resolve(0, 0, ids)
-    assert ei.value.status == M.MOE_EINVAL
+            m.stack_forward(t, xd[t], 0, 1, y[t], H, ids[t], w[t])
+        for l in range(L):
+            _, r = cache.step(t, l, ref_ids[t, l])
+            recs_ref.append(r)
+    m.compute_stream.synchronize()
+    drain_and_check()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.max(np.abs(w.cpu().numpy() - ref_w)) <= 1e-5
+    for u, v in zip(m.cache_state(), cache.state()):
+        np.testing.assert_array_equal(u, v)
+    yf = bf16_to_f32(y)
+    for t in range(T):
+        for l in range(L):
+            r = oracle.moe_output(wl, l, X[t, 0], ref_ids[t, l, 0], ref_w[t, l, 0])
+            rel, mx, ok = close_enough(yf[t, l, 0], r)
+            assert ok, (t, l, rel, mx)
     m.close()
