@@ -230,6 +230,30 @@ moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev,
 moe_status moe_expert_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16_dev, int32_t n_tokens,
                               const int32_t* slots_dev, const float* w_dev, void* y_bf16_dev);
 
+/* Allocation-free variant of moe_expert_forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It needs
+ * no context: the caller passes the shape (cfg: top_k, hidden, inter, n_shared, and cache_slots =
+ * the number of blobs in slot_arena_dev; the other fields are not used), the slot arena (device,
+ * [cache_slots][blob] in the pool's layout, e.g. the arena of a context), the shared expert's blob
+ * (device, pool layout; NULL when n_shared = 0), x_bf16_dev [n_tokens][H], slots_dev and w_dev
+ * [n_tokens][k] and y_bf16_dev [n_tokens][H], and the stream (hipStream_t as void*, NULL = the null
+ * stream).  y = sum_j w_j * FFN(slot_j)(x) + shared(x) with the per-token GEMV kernels (as
+ * moe_expert_forward of a context with MOE_FLAG_PER_TOKEN_FFN, bit for bit); a slot outside
+ * [0, cache_slots) is never read and makes its token's outputs NaN.
+ * The intermediate vectors (n_tokens * (k + n_shared) * inter bf16; at most 16 * 24576 * 2 bytes,
+ * since the down kernel's LDS bounds (k + n_shared) * inter by 24576) live in a static device array
+ * of MOE_NOALLOC_SCRATCH_BYTES (1 MiB) per GPU, held until the process ends; the call allocates and frees
+ * nothing (its first call on a device looks the array's address up).  Every call on one GPU uses
+ * the same array, so calls that overlap on one GPU (different streams, or host threads) race;
+ * order them on one stream.  Errors (message: moe_last_error(NULL)): MOE_EINVAL (shape, null
+ * buffer, n_tokens outside [1, MOE_NOALLOC_MAX_TOKENS], or intermediate vectors larger than the
+ * array), MOE_EHIP (launch failure). */
+#define MOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+#define MOE_NOALLOC_MAX_TOKENS 16
+moe_status moe_expert_forward_noalloc(const moe_config* cfg, const void* slot_arena_dev, const void* shared_blob_dev,
+                                      const void* x_bf16_dev, int32_t n_tokens, const int32_t* slots_dev,
+                                      const float* w_dev, void* y_bf16_dev, void* stream);
+
 typedef struct {
     uint64_t hits, misses, evictions;  /* cache accesses (unique (layer, expert) per step) */
     uint64_t resolves;                 /* layer steps resolved */
@@ -374,8 +398,9 @@ moe_status moe_pack_blob(const moe_config* cfg, const uint8_t* logical, uint8_t*
 
 /* Frees everything the context owns (after synchronising both streams).  NULL is a no-op. */
 void moe_destroy(moe_ctx* ctx);
-/* Text of the context's last error; with ctx = NULL, of the last failed moe_init_pool on the
- * calling thread.  Valid until the next call on the same context / thread. */
+/* Text of the context's last error; with ctx = NULL, of the last failed call without a context
+ * (moe_init_pool, moe_expert_forward_noalloc) on the calling thread.  Valid until the next call on
+ * the same context / thread. */
 const char* moe_last_error(const moe_ctx* ctx);
 
 #ifdef __cplusplus

@@ -94,6 +94,8 @@ _lib.moe_stack_forward.restype = _st
 _lib.moe_stack_forward.argtypes = [_P, _I32, _P, ctypes.c_int64, _I32, _P, ctypes.c_int64, _P, _P]
 _lib.moe_expert_forward.restype = _st
 _lib.moe_expert_forward.argtypes = [_P, _I32, _P, _I32, _P, _P, _P]
+_lib.moe_expert_forward_noalloc.restype = _st
+_lib.moe_expert_forward_noalloc.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _P, _I32, _P, _P, _P, _P]
 _lib.moe_stats.restype = _st
 _lib.moe_stats.argtypes = [_P, ctypes.POINTER(MoeCounters), _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
 _lib.moe_measure_h2d.restype = _st
@@ -108,7 +110,7 @@ _lib.moe_last_error.argtypes = [_P]
 EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_host_expert_batch",
             "moe_hybrid_split",
             "moe_select_backend", "moe_calibrate_backend", "moe_set_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
-            "moe_expert_forward", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
+            "moe_expert_forward", "moe_expert_forward_noalloc", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -213,6 +215,21 @@ def hybrid_split(n_miss: int, pcie_gbps: float, host_gbps: float) -> int:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20
+NOALLOC_MAX_TOKENS = 16
+
+
+def expert_forward_noalloc(cfg: MoeConfig, arena, shared_blob, x, slots, w, y, stream=None):
+    """moe_expert_forward_noalloc: the expert FFN on caller slots with no context and no device
+    allocation (device tensors; stream: a torch stream or None for the current one)."""
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = _lib.moe_expert_forward_noalloc(ctypes.byref(cfg), _ptr(arena), _ptr(shared_blob), _ptr(x), x.shape[0],
+                                         _ptr(slots), _ptr(w), _ptr(y), ctypes.c_void_p(s.cuda_stream))
+    if st:
+        raise MoeError(st, "moe_expert_forward_noalloc: " + _lib.moe_last_error(None).decode())
 
 
 class OffloadMoE:

@@ -155,7 +155,8 @@ struct moe_ctx {
 
 namespace {
 
-// message of the last failed moe_init_pool on this thread (its context no longer exists)
+// message of the last failed call without a context on this thread (moe_init_pool, whose context
+// no longer exists, or moe_expert_forward_noalloc)
 thread_local std::string g_init_err;
 
 moe_status set_err(moe_ctx* c, moe_status st, const char* fmt, ...) {
@@ -879,6 +880,37 @@ moe_status check_call(moe_ctx* c, int n_tokens) {
     return MOE_OK;
 }
 
+// ------------------------------------------------ allocation-free expert FFN --
+// The intermediate vectors of moe_expert_forward_noalloc live in this array (each GPU the library
+// runs on holds its own copy until the process ends).  Host code never uses the array's name as an
+// address: on first use on a device, with that device current, hipGetSymbolAddress gives the
+// device address, which is kept per device and is what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device (nullptr and a message on failure)
+void* scratch_address(int dev, std::string& err) {
+    if (dev < 0 || dev >= kMaxDevices) {
+        err = "device index " + std::to_string(dev) + " outside the library's table";
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            err = std::string("hipGetSymbolAddress of the scratch array failed: ") + hipGetErrorString(e);
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 // ====================================================================== ABI ==
@@ -1356,6 +1388,67 @@ moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t 
     if (layer < 0 || layer >= c->cfg.n_layers || !x || !y || !slots_dev || !w_dev)
         return set_err(c, MOE_EINVAL, "bad layer or buffers");
     return launch_ffn_layer(c, layer, x, n_tokens, 2, y, 0, slots_dev, w_dev);
+}
+
+moe_status moe_expert_forward_noalloc(const moe_config* cfg, const void* arena, const void* shared_blob,
+                                      const void* x, int32_t n_tokens, const int32_t* slots_dev, const float* w_dev,
+                                      void* y, void* stream) {
+    auto fail = [](moe_status st, const std::string& msg) {
+        g_init_err = "moe_expert_forward_noalloc: " + msg;
+        return st;
+    };
+    if (!cfg) return fail(MOE_EINVAL, "null config");
+    // the shape checks of a context; the cache's capacity rule does not apply (no cache here)
+    moe_config shape = *cfg;
+    shape.cache_slots = 0;
+    shape.max_tokens = 1;
+    moe_status st = check_cfg(&shape, true);
+    if (st) return fail(st, "unsupported shape");
+    if (cfg->cache_slots < 1) return fail(MOE_EINVAL, "cache_slots (slots in the arena) must be >= 1");
+    if (!arena || !x || !y || !slots_dev || !w_dev || (cfg->n_shared > 0 && !shared_blob))
+        return fail(MOE_EINVAL, "null buffer");
+    if (n_tokens < 1 || n_tokens > MOE_NOALLOC_MAX_TOKENS)
+        return fail(MOE_EINVAL, "n_tokens " + std::to_string(n_tokens) + " outside [1, " +
+                                    std::to_string(MOE_NOALLOC_MAX_TOKENS) + "]");
+    const int nE = cfg->top_k + cfg->n_shared;
+    const size_t need = (size_t)n_tokens * nE * cfg->inter * 2;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_EINVAL, "intermediate vectors need " + std::to_string(need) + " bytes, more than the " +
+                                    std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES) + "-byte scratch array");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_EHIP, "hipGetDevice failed");
+    }
+    std::string err;
+    void* ptr = scratch_address(dev, err);
+    if (!ptr) return fail(MOE_EHIP, err);
+    const Layout L = make_layout(cfg->hidden, cfg->inter);
+    FfnArgs f{};
+    f.arena = (const uint8_t*)arena;
+    f.shared = (const uint8_t*)shared_blob;
+    f.slots = slots_dev;
+    f.w = w_dev;
+    f.x = (const uint16_t*)x;
+    f.a = (uint16_t*)ptr;
+    f.y = (uint16_t*)y;
+    f.yh = nullptr;
+    f.blob_bytes = L.blob_bytes;
+    f.d_codes_off = L.d_codes_off;
+    f.d_scales_off = L.d_scales_off;
+    f.k = cfg->top_k;
+    f.n_shared = cfg->n_shared;
+    f.nE = nE;
+    f.layer = 0;
+    f.NB = L.NB;
+    f.NBI = L.NBI;
+    f.I = cfg->inter;
+    f.H = cfg->hidden;
+    f.C = cfg->cache_slots;
+    f.karg = 0;
+    const int e = launch_ffn(f, L, n_tokens, stream, nullptr);
+    if (e != 0) return fail(MOE_EHIP, std::string("FFN launch failed: ") + hipGetErrorString((hipError_t)e));
+    return MOE_OK;
 }
 
 moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t cap, size_t* n_out) {

@@ -137,3 +137,32 @@ def test_auto_cache_slots_reports_capacity_shortfall():
     with pytest.raises(M.MoeError) as ei:
         M.auto_cache_slots(cfg, free_bytes=1000)
     assert ei.value.status == -4
+
+
+def test_noalloc_entry_rejects_bad_arguments_before_any_gpu_call():
+    """moe_expert_forward_noalloc checks its arguments on the host first: null buffers, token counts
+    outside [1, 16] and intermediate vectors larger than the static scratch array fail with
+    MOE_EINVAL and a message, with no GPU call."""
+    import ctypes
+    import moe_expert_offload_amd as M
+    lib = M.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails before a launch
+    cfg = M.make_config(1, 16, 2, 256, 512, 0, 8, 16)
+
+    def call(cfg, n_tok, arena=fake, x=fake):
+        return lib.moe_expert_forward_noalloc(ctypes.byref(cfg), arena, None, x, n_tok, fake, fake, fake, None)
+
+    assert call(cfg, 0) == M.MOE_EINVAL
+    assert b"n_tokens" in lib.moe_last_error(None)
+    assert call(cfg, M.NOALLOC_MAX_TOKENS + 1) == M.MOE_EINVAL
+    assert call(cfg, 1, arena=None) == M.MOE_EINVAL
+    assert call(cfg, 1, x=None) == M.MOE_EINVAL
+    shared = M.make_config(1, 16, 2, 256, 512, 1, 8, 16)
+    assert call(shared, 1) == M.MOE_EINVAL  # n_shared = 1 needs the shared blob
+    # the largest shape the kernels take ((k + n_shared) * I/32 * 80 B of LDS <= 60 KiB) at 16
+    # tokens fits the scratch array; one expert more is rejected as a shape
+    assert 16 * 12 * 2048 * 2 <= M.NOALLOC_SCRATCH_BYTES  # k = 11 + shared, I = 2048: the largest shape
+    over = M.make_config(1, 16, 12, 256, 2048, 1, 32, 16)
+    assert call(over, 1) == M.MOE_EINVAL and b"shape" in lib.moe_last_error(None)
+    zero_slots = M.make_config(1, 16, 2, 256, 512, 0, 0, 16)
+    assert call(zero_slots, 1) == M.MOE_EINVAL
