@@ -28,8 +28,9 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 
 # HBM bytes moved per layer FFN launch (k3_gate_up + k4_down, batch 1) from the FETCH_SIZE and
 # WRITE_SIZE counter runs, scaled by a device copy of known size in the same process
-# (profiles/expert_ffn_gptoss120b_shaped_traffic.md).  Set an entry to None when those kernels change.
-FFN_TRAFFIC_BYTES = {"gptoss120b_shaped": 53.69e6}
+# (profiles/expert_ffn_*_traffic.md, profiles/decode_qwen36_*_traffic.md).  Set an entry to None when
+# those kernels change.
+FFN_TRAFFIC_BYTES = {"gptoss120b_shaped": None, "dsv4_flash_shaped": None, "qwen36_35b_a3b_shaped": None}
 
 
 def decode_rate(tokens, total_s, ttft_s):

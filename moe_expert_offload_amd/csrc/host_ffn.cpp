@@ -6,7 +6,7 @@
 // backend's host workers run on their share of the misses.
 //
 // It reads the blob in the pool's layout (the layout the GPU kernels read; see
-// moe_internal.h), in memory order: gate/up tile by tile (16 rows, chunks
+// moe_internal.h), in memory order: gate/up tile by tile (8 rows, chunks
 // ordered by (step, segment, row)), then the down section by 8-row tile.  Every
 // 16-byte chunk holds one 32-element block of one row; element 2i is the low
 // nibble of byte i.  Accumulation is FP32; the intermediate vector is rounded
@@ -82,26 +82,29 @@ float dot_block_scalar(const uint8_t* codes, const float* ev, const float* od) {
     return s;
 }
 
+// gate/up tiles [t_begin, t_end) (kGuRows rows each) in memory order: position q (segment
+// q % kGuSegments, step q / kGuSegments) holds one block of every row of the tile
 void gate_up_scalar(const Layout& L, const uint8_t* blob, const float* xe, const float* xo, float* g, float* u,
                     int t_begin, int t_end) {
-    int b0[16];
-    for (int s = 0; s < 16; ++s) b0[s] = seg_begin(L.NB, 16, s);
+    constexpr int GR = kGuRows, S = kGuSegments;
+    int b0[S];
+    for (int s = 0; s < S; ++s) b0[s] = seg_begin(L.NB, S, s);
     for (int tile = t_begin; tile < t_end; ++tile) {
-        const uint8_t* tb = blob + (size_t)tile * 16 * L.NB * 34;
-        const uint8_t* ub = tb + (size_t)16 * L.NB * 16;
-        const uint8_t* sc = tb + (size_t)16 * L.NB * 32;
-        float ag[16] = {}, au[16] = {};
+        const uint8_t* tb = blob + (size_t)tile * L.gu_tile_bytes;
+        const uint8_t* ub = tb + (size_t)GR * L.NB * 16;
+        const uint8_t* sc = tb + (size_t)GR * L.NB * 32;
+        float ag[GR] = {}, au[GR] = {};
         for (int q = 0; q < L.NB; ++q) {
-            const int blk = b0[q & 15] + (q >> 4);
-            for (int r = 0; r < 16; ++r) {
-                const size_t c = (size_t)q * 16 + r;
+            const int blk = b0[q % S] + q / S;
+            for (int r = 0; r < GR; ++r) {
+                const size_t c = (size_t)q * GR + r;
                 ag[r] += e8m0(sc[c * 2]) * dot_block_scalar(tb + c * 16, xe + blk * 16, xo + blk * 16);
                 au[r] += e8m0(sc[c * 2 + 1]) * dot_block_scalar(ub + c * 16, xe + blk * 16, xo + blk * 16);
             }
         }
-        for (int r = 0; r < 16; ++r) {
-            g[tile * 16 + r] = ag[r];
-            u[tile * 16 + r] = au[r];
+        for (int r = 0; r < GR; ++r) {
+            g[tile * GR + r] = ag[r];
+            u[tile * GR + r] = au[r];
         }
     }
 }
@@ -141,34 +144,33 @@ MOE_AVX512 inline __m512 dot_block_v(const uint8_t* codes, __m512 lut, __m512 ev
 
 MOE_AVX512 void gate_up_avx512(const Layout& L, const uint8_t* blob, const float* xe, const float* xo, float* g,
                                float* u, int t_begin, int t_end) {
+    constexpr int GR = kGuRows, S = kGuSegments;
     const __m512 lut = _mm512_loadu_ps(kE2M1);
-    int b0[16];
-    for (int s = 0; s < 16; ++s) b0[s] = seg_begin(L.NB, 16, s);
+    int b0[S];
+    for (int s = 0; s < S; ++s) b0[s] = seg_begin(L.NB, S, s);
     for (int tile = t_begin; tile < t_end; ++tile) {
-        const uint8_t* tb = blob + (size_t)tile * 16 * L.NB * 34;
-        const uint8_t* sc = tb + (size_t)16 * L.NB * 32;
+        const uint8_t* tb = blob + (size_t)tile * L.gu_tile_bytes;
+        const uint8_t* sc = tb + (size_t)GR * L.NB * 32;
         // gate rows from the gate codes, then up rows from the parallel up codes
         for (int part = 0; part < 2; ++part) {
-            const uint8_t* cb = tb + (size_t)part * 16 * L.NB * 16;
-            __m512 acc[16];
-            for (int r = 0; r < 16; ++r) acc[r] = _mm512_setzero_ps();
+            const uint8_t* cb = tb + (size_t)part * GR * L.NB * 16;
+            __m512 acc[GR];
+            for (int r = 0; r < GR; ++r) acc[r] = _mm512_setzero_ps();
             for (int q = 0; q < L.NB; ++q) {
-                const int blk = b0[q & 15] + (q >> 4);
+                const int blk = b0[q % S] + q / S;
                 const __m512 ev = _mm512_loadu_ps(xe + (size_t)blk * 16);
                 const __m512 od = _mm512_loadu_ps(xo + (size_t)blk * 16);
-                const uint8_t* cq = cb + (size_t)q * 256;
-                const uint8_t* sq = sc + (size_t)q * 32 + part;
+                const uint8_t* cq = cb + (size_t)q * GR * 16;
+                const uint8_t* sq = sc + (size_t)q * GR * 2 + part;
                 _mm_prefetch(reinterpret_cast<const char*>(cq) + kPrefetchBytes, _MM_HINT_T0);
                 _mm_prefetch(reinterpret_cast<const char*>(cq) + kPrefetchBytes + 64, _MM_HINT_T0);
-                _mm_prefetch(reinterpret_cast<const char*>(cq) + kPrefetchBytes + 128, _MM_HINT_T0);
-                _mm_prefetch(reinterpret_cast<const char*>(cq) + kPrefetchBytes + 192, _MM_HINT_T0);
-#pragma GCC unroll 16
-                for (int r = 0; r < 16; ++r)
+#pragma GCC unroll 8
+                for (int r = 0; r < GR; ++r)
                     acc[r] = _mm512_fmadd_ps(dot_block_v(cq + r * 16, lut, ev, od), _mm512_set1_ps(e8m0(sq[r * 2])),
                                              acc[r]);
             }
             float* out = part ? u : g;
-            for (int r = 0; r < 16; ++r) out[tile * 16 + r] = _mm512_reduce_add_ps(acc[r]);
+            for (int r = 0; r < GR; ++r) out[tile * GR + r] = _mm512_reduce_add_ps(acc[r]);
         }
     }
 }
@@ -226,7 +228,7 @@ void activation_blocks(ExpertBuf& e, int b_begin, int b_end) {
 
 // one expert for one token: y += w * down(silu(gate x) * (up x))
 void expert_one(const Layout& L, const uint8_t* blob, float w, const TokenBuf& x, ExpertBuf& e, float* y, bool vec) {
-    gate_up_rows(L, blob, x, e, 0, L.I / 16, vec);
+    gate_up_rows(L, blob, x, e, 0, L.I / kGuRows, vec);
     activation_blocks(e, 0, L.NBI);
     down_rows(L, blob, e, w, y, 0, L.H / 8, vec);
 }
@@ -267,7 +269,8 @@ void host_expert_ffn(const Layout& L, const uint8_t* const* blobs, const float* 
 // Units of work are handed out dynamically (atomic counters), so a slow or
 // descheduled worker delays the task by at most one unit.  Unit sizes aim at
 // about four units per participant and kind, within these bounds.
-constexpr int kGuChunkMax = 4;   // 16-row gate/up tiles per unit (even: whole 32-blocks of a)
+constexpr int kGuTilesPerBlock = 32 / kGuRows;   // gate/up tiles per 32-block of the intermediate vector
+constexpr int kGuChunkMax = 8;   // gate/up tiles per unit (whole 32-blocks of the intermediate vector)
 constexpr int kDChunkMax = 32;   // 8-row output tiles of one entry per unit
 
 inline int unit_size(long items, int participants, int max_chunk) {
@@ -344,9 +347,10 @@ void HostExpertPool::submit(const Layout& L, int n_tok, const uint16_t* const* x
     for (int b = 0; b < task_.ntok; ++b) xbuf_[b].size(L);
     // about four units per participant (workers and the waiting caller) and kind
     const int np = n_ + 1;
-    task_.gu_chunk = std::max(2, unit_size((long)task_.n * (L.I / 16), np, kGuChunkMax) & ~1);
+    task_.gu_chunk = std::max(kGuTilesPerBlock, unit_size((long)task_.n * (L.I / kGuRows), np, kGuChunkMax) /
+                                                     kGuTilesPerBlock * kGuTilesPerBlock);
     task_.d_chunk = unit_size((long)task_.n * (L.H / 8), np, kDChunkMax);
-    task_.gu_per = (L.I / 16 + task_.gu_chunk - 1) / task_.gu_chunk;
+    task_.gu_per = (L.I / kGuRows + task_.gu_chunk - 1) / task_.gu_chunk;
     task_.d_per = (L.H / 8 + task_.d_chunk - 1) / task_.d_chunk;
     task_.gu_step = unit_step(task_.gu_per, np);
     task_.d_step = unit_step(task_.d_per, np);
@@ -393,7 +397,7 @@ void HostExpertPool::work(bool vec) {
         x_done_.fetch_add(1, std::memory_order_release);
     }
     while (x_done_.load(std::memory_order_acquire) < ntok) _mm_pause();
-    const int ngu = L.I / 16, nt8 = L.H / 8;
+    const int ngu = L.I / kGuRows, nt8 = L.H / 8;
     const int gc = task_.gu_chunk, gu_per = task_.gu_per, dc = task_.d_chunk, d_per = task_.d_per;
     const int seg = gu_per + d_per, n_main = n * seg;
     for (int u; (u = main_next_.fetch_add(1, std::memory_order_relaxed)) < n_main;) {
@@ -421,7 +425,7 @@ void HostExpertPool::work(bool vec) {
             const int kk = (int)((long)k * task_.gu_step % gu_per);
             const int t0 = kk * gc, t1 = std::min(ngu, t0 + gc);
             gate_up_rows(L, e.blob, xbuf_[e.tok], ebuf_[j], t0, t1, vec);
-            activation_blocks(ebuf_[j], t0 / 2, t1 / 2);
+            activation_blocks(ebuf_[j], t0 / kGuTilesPerBlock, t1 / kGuTilesPerBlock);
             gu_left_[j].v.fetch_sub(1, std::memory_order_release);
             continue;
         }

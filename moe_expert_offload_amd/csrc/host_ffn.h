@@ -64,8 +64,8 @@ struct HostEntry {
 // each of up to 16 tokens b, y_b[H] (FP32) = sum over the task's entries of
 // token b, in their order, of w * FFN(x_b).  Units are handed out through
 // atomic counters: first one unit per token (x to FP32), then one list that
-// interleaves, entry by entry, (entry, an even number of gate/up tiles) units,
-// which also form the intermediate vector of those rows (two 16-row tiles are
+// interleaves, entry by entry, (entry, a multiple of four gate/up tiles) units,
+// which also form the intermediate vector of those rows (four 8-row tiles are
 // one 32-element block), with the (entry, chunk of output rows) down units of
 // the entry before, which write w * (its rows of the expert's output).  A down
 // unit waits only for its own entry's gate/up units; the participant that
@@ -98,7 +98,7 @@ private:
         int n = 0, ntok = 0;
         const uint16_t* x[kHostMaxTokens] = {};
         float* y[kHostMaxTokens] = {};
-        int gu_chunk = 2, d_chunk = 1;  // 16-row gate/up tiles and 8-row output tiles per unit
+        int gu_chunk = 4, d_chunk = 1;  // 8-row gate/up tiles and 8-row output tiles per unit
         int gu_per = 1, d_per = 1;      // gate/up and down units per entry
         int gu_step = 1, d_step = 1;    // order within an entry: k -> k * step mod count
     };

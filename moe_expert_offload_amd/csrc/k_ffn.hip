@@ -161,21 +161,22 @@ __device__ __forceinline__ void stage_commit(const StageRegs& r, uint4* smem, co
 }
 
 // ---------------------------------------------------------------- phase 1 --
-// one 16-row tile of one expert: compute lane (r = lane&15, s = 4*wave + lane>>4)
+// one 8-row tile of one expert: compute lane (r = lane&7, s = 8*wave + lane>>3);
+// the 32 segments of a row are spread over the 4 waves
 template <int T1>
 __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int unit, int b) {
-    constexpr int S = 16;
-    const int tiles = a.I / 16;
+    constexpr int S = kGuSegments, GR = kGuRows;
+    const int tiles = a.I / GR;
     const int j = __builtin_amdgcn_readfirstlane(unit / tiles), tile = unit - j * tiles;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int NB = a.NB;
     float* red = reinterpret_cast<float*>(smem + NB * 5);
-    const int r = lane & 15, s = w * 4 + (lane >> 4);
+    const int r = lane & 7, s = w * 8 + (lane >> 3);
     const int nb = seg_len(NB, S, s);
     const uint8_t* blob = expert_blob(a, b, j);
-    const uint8_t* tb = blob + (size_t)tile * 16 * NB * 34;
-    const uint8_t* tub = tb + (size_t)16 * NB * 16;
-    const uint8_t* tsc = tb + (size_t)16 * NB * 32;
+    const uint8_t* tb = blob + (size_t)tile * GR * NB * 34;
+    const uint8_t* tub = tb + (size_t)GR * NB * 16;
+    const uint8_t* tsc = tb + (size_t)GR * NB * 32;
 
     float g = 0.0f, u = 0.0f;
     uint4 gc[T1], uc[T1];
@@ -183,13 +184,13 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
     // Steps past this lane's segment re-read its step-0 chunk (a cache hit) and
     // are dropped by a select, so loads and compute are branch-free and the
     // compiler can wait for each step's data separately; an empty segment
-    // (NB < 16) reads the tile's first chunk.
+    // (NB < 32) reads the tile's first chunk.
     const int sv = nb > 0 ? s : 0;
     auto load = [&](int t0) {
 #pragma unroll
         for (int t = 0; t < T1; ++t) {
             const int tt = (t0 + t < nb) ? t0 + t : 0;
-            const size_t c = (size_t)((tt * S + sv) * 16 + r);
+            const size_t c = (size_t)(tt * S + sv) * GR + r;
             gc[t] = ldg16(tb + c * 16);
             uc[t] = ldg16(tub + c * 16);
             sc[t] = *reinterpret_cast<const uint16_t*>(tsc + c * 2);
@@ -218,50 +219,50 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
         load(t0);
         compute(t0);
     }
-    // segments of a row: lanes r, r+16, r+32, r+48 of every compute wave
+    // segments of a row: lanes r + 8i of every compute wave
+    g += __shfl_xor(g, 8);
     g += __shfl_xor(g, 16);
     g += __shfl_xor(g, 32);
+    u += __shfl_xor(u, 8);
     u += __shfl_xor(u, 16);
     u += __shfl_xor(u, 32);
-    if (lane < 16) {
-        red[(w * 16 + r) * 2] = g;
-        red[(w * 16 + r) * 2 + 1] = u;
+    if (lane < GR) {
+        red[(w * GR + r) * 2] = g;
+        red[(w * GR + r) * 2 + 1] = u;
     }
     __syncthreads();
-    if (tid < 16) {
+    if (tid < GR) {
         float gs = 0.0f, us = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-            gs += red[(ww * 16 + tid) * 2];
-            us += red[(ww * 16 + tid) * 2 + 1];
+            gs += red[(ww * GR + tid) * 2];
+            us += red[(ww * GR + tid) * 2 + 1];
         }
         const float act = swiglu(gs, us);
-        a.a[((size_t)b * a.nE + j) * a.I + tile * 16 + tid] = f32_to_bf16(act);
+        a.a[((size_t)b * a.nE + j) * a.I + tile * GR + tid] = f32_to_bf16(act);
     }
 }
 
 // ---------------------------------------------------------------- phase 2 --
-// R8 8-row tiles of the output per workgroup, four waves on each (sub-tile
-// sub = wave/4), all sharing one LDS copy of the token's activations.  Compute
-// lane (r = lane&7, s = 8*(wave%4) + lane>>3); the 32 segments split the
-// combined (expert, I-block) range of the token.  A sub-tile past H/8 (odd
-// H/8) reads tile 0 and writes nothing.
-template <int T2, int R8>
-__device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile16, int b) {
-    constexpr int S = 32;
-    const int tid = threadIdx.x, lane = tid & 63, wf = tid >> 6, w = wf & 3, sub = wf >> 2;
+// One 8-row tile of the output per workgroup of K4_WAVES waves, all sharing one
+// LDS copy of the token's activations.  Compute lane (r = lane&7, s = 8*wave +
+// lane>>3); the 64 segments split the combined (expert, I-block) range of the
+// token, so each lane takes about nE*NBI/64 blocks.
+constexpr int K4_WAVES = 8;
+
+template <int T2>
+__device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile, int b) {
+    constexpr int S = 8 * K4_WAVES;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int NBI = a.NBI, nE = a.nE;
     const int Q = nE * NBI;
     float* red = reinterpret_cast<float*>(smem + Q * 5);
-    const int t8 = tile16 * R8 + sub;
-    const bool tok = t8 < (a.H >> 3);
-    const int tile = tok ? t8 : 0;
     const int r = lane & 7, s = w * 8 + (lane >> 3);
     const int nq = seg_len(Q, S, s), q0 = seg_begin(Q, S, s);
-    // A segment (at most ceil(nE*NBI/32) <= NBI + 1 blocks, as nE <= 32)
+    // A segment (at most ceil(nE*NBI/64) <= NBI + 1 blocks, as nE <= 64)
     // spans at most two experts: j0 from block ib0 for `split` steps, then j0+1
     // from block 0.  Steps past the segment re-read step 0 and are dropped; an
-    // empty segment (Q < 32) reads block 0 of expert 0.
+    // empty segment (Q < 64) reads block 0 of expert 0.
     const int qv = nq > 0 ? q0 : 0;
     const int j0 = qv / NBI, ib0 = qv - (qv / NBI) * NBI;
     const int split = NBI - ib0;
@@ -298,54 +299,45 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
     __builtin_amdgcn_sched_barrier(0);
     load(0);
     __builtin_amdgcn_sched_barrier(0);
-    // the host-computed experts' sum for the rows this thread writes (host-mapped memory: a PCIe
+    // the host-computed experts' sum for the row this thread writes (host-mapped memory: a PCIe
     // round trip), issued behind the weights, which it does not hold up, and used at the end
     float yhv = 0.0f;
-    if (a.yh && tid < 8 * R8) {
-        const int yr = (tile16 * R8 + (tid >> 3)) * 8 + (tid & 7);
-        if (yr < a.H) yhv = a.yh[(size_t)b * a.H + yr];
-    }
-    stage_commit(ar, smem, asrc, Q, S, 4 * 64 * R8);
+    if (a.yh && tid < 8) yhv = a.yh[(size_t)b * a.H + tile * 8 + tid];
+    stage_commit(ar, smem, asrc, Q, S, 64 * K4_WAVES);
     __syncthreads();
     compute(0);
     for (int t0 = T2; t0 < nq; t0 += T2) {
         load(t0);
         compute(t0);
     }
-    // segments of an output row: lanes r + 8*i of every compute wave
+    // segments of an output row: lanes r + 8i of every compute wave
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
-    if (lane < 8) red[(sub * 4 + w) * 8 + r] = acc;
+    if (lane < 8) red[w * 8 + r] = acc;
     __syncthreads();
-    if (tid < 8 * R8) {
-        const int sb = tid >> 3, rr = tid & 7;
+    if (tid < 8) {
         float ys = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) ys += red[(sb * 4 + ww) * 8 + rr];
+        for (int ww = 0; ww < K4_WAVES; ++ww) ys += red[ww * 8 + tid];
         ys += yhv;
-        const int tt8 = tile16 * R8 + sb;
-        if (tt8 < (a.H >> 3)) a.y[(size_t)b * a.H + tt8 * 8 + rr] = f32_to_bf16(ys);
+        a.y[(size_t)b * a.H + tile * 8 + tid] = f32_to_bf16(ys);
     }
 }
 
-// K3: grid (nE * I/16 tiles, B), 256 threads; K4: grid (ceil(H/16), B), 512
-// threads (two 8-row sub-tiles, so 2880-wide outputs take 180 workgroups per
-// token: one round on 256 CUs instead of two uneven ones, and the activations
-// are staged into LDS half as often)
+// K3: grid (nE * I/8 tiles, B), 256 threads; K4: grid (H/8, B), 512 threads
 template <int T1>
 __global__ __launch_bounds__(FFN_THREADS) void k3_gate_up(FfnArgs a) {
     extern __shared__ uint4 smem[];
     ffn_gate_up<T1>(a, smem, blockIdx.x, blockIdx.y);
 }
 
-constexpr int K4_SUBTILES = 2;
-constexpr int K4_THREADS = 4 * 64 * K4_SUBTILES;
+constexpr int K4_THREADS = 64 * K4_WAVES;
 
 template <int T2>
 __global__ __launch_bounds__(K4_THREADS) void k4_down(FfnArgs a) {
     extern __shared__ uint4 smem[];
-    ffn_down<T2, K4_SUBTILES>(a, smem, blockIdx.x, blockIdx.y);
+    ffn_down<T2>(a, smem, blockIdx.x, blockIdx.y);
 }
 
 // a layer step whose experts all ran on the host: y = bf16(yh)
@@ -355,8 +347,8 @@ __global__ __launch_bounds__(256) void k_host_only_out(const float* yh, uint16_t
 }
 
 size_t ffn_lds_bytes(const Layout& L, int nE) {
-    const size_t p1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
-    const size_t p2 = (size_t)nE * L.NBI * 80 + 4 * K4_SUBTILES * 8 * 4;
+    const size_t p1 = (size_t)L.NB * 80 + 4 * kGuRows * 2 * 4;
+    const size_t p2 = (size_t)nE * L.NBI * 80 + K4_WAVES * 8 * 4;
     return p1 > p2 ? p1 : p2;
 }
 
@@ -370,15 +362,19 @@ int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid) {
         hipLaunchKernelGGL(k_host_only_out, dim3((n + 255) / 256), dim3(256), 0, st, a.yh, a.y, n);
         return (int)hipGetLastError();
     }
-    a.P1 = a.nE * (L.I / 16);
-    a.P2 = (L.H / 8 + K4_SUBTILES - 1) / K4_SUBTILES;
+    a.P1 = a.nE * (L.I / kGuRows);
+    a.P2 = L.H / 8;
     const int T1 = L.T3;
-    const int T2 = (a.nE * L.NBI + 31) / 32;
-    const size_t lds1 = (size_t)L.NB * 80 + 4 * 16 * 2 * 4;
-    const size_t lds2 = (size_t)a.nE * L.NBI * 80 + 4 * K4_SUBTILES * 8 * 4;
+    const int T2 = (a.nE * L.NBI + 8 * K4_WAVES - 1) / (8 * K4_WAVES);
+    const size_t lds1 = (size_t)L.NB * 80 + 4 * kGuRows * 2 * 4;
+    const size_t lds2 = (size_t)a.nE * L.NBI * 80 + K4_WAVES * 8 * 4;
     dim3 g1(a.P1, B), g2(a.P2, B), blk(FFN_THREADS), blk2(K4_THREADS);
-    if (T1 <= 2)
+    if (T1 <= 1)
+        hipLaunchKernelGGL(k3_gate_up<1>, g1, blk, lds1, st, a);
+    else if (T1 <= 2)
         hipLaunchKernelGGL(k3_gate_up<2>, g1, blk, lds1, st, a);
+    else if (T1 <= 3)
+        hipLaunchKernelGGL(k3_gate_up<3>, g1, blk, lds1, st, a);
     else if (T1 <= 4)
         hipLaunchKernelGGL(k3_gate_up<4>, g1, blk, lds1, st, a);
     else if (T1 <= 6)
@@ -386,10 +382,16 @@ int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid) {
     else
         hipLaunchKernelGGL(k3_gate_up<8>, g1, blk, lds1, st, a);
     if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
-    if (T2 <= 2)
+    if (T2 <= 1)
+        hipLaunchKernelGGL(k4_down<1>, g2, blk2, lds2, st, a);
+    else if (T2 <= 2)
         hipLaunchKernelGGL(k4_down<2>, g2, blk2, lds2, st, a);
+    else if (T2 <= 3)
+        hipLaunchKernelGGL(k4_down<3>, g2, blk2, lds2, st, a);
     else if (T2 <= 4)
         hipLaunchKernelGGL(k4_down<4>, g2, blk2, lds2, st, a);
+    else if (T2 <= 6)
+        hipLaunchKernelGGL(k4_down<6>, g2, blk2, lds2, st, a);
     else if (T2 <= 8)
         hipLaunchKernelGGL(k4_down<8>, g2, blk2, lds2, st, a);
     else

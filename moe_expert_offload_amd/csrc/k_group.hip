@@ -210,7 +210,9 @@ __device__ __forceinline__ int row_token(const GemmArgs& a, int row) {
 }
 
 // block index of position p of the gate/up section's (step, segment) order
-__device__ __forceinline__ int gu_block(int p, int NB) { return seg_begin(NB, 16, p & 15) + (p >> 4); }
+__device__ __forceinline__ int gu_block(int p, int NB) {
+    return seg_begin(NB, kGuSegments, p % kGuSegments) + p / kGuSegments;
+}
 
 // 8 E2M1 codes (one dword) times the block scale -> 8 bf16 MFMA operand values
 __device__ __forceinline__ bf16x8_t dq8(uint32_t w, float s) {
@@ -316,14 +318,15 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
     const int NB = a.NB;
     const int tile0 = (u.nt * 4 + w) * RT;
     const uint8_t* blob = group_blob(a, u.g_slot);
+    const int r = lane & 15, q = lane >> 4;
+    // a 16-row operand tile is two 8-row gate/up tiles of the blob: rows r < 8 from the first
     const uint8_t* tb[RT];
     bool tok[RT];
 #pragma unroll
     for (int j = 0; j < RT; ++j) {
         tok[j] = tile0 + j < n_tiles;
-        tb[j] = blob + (size_t)(tok[j] ? tile0 + j : 0) * 16 * NB * 34;
+        tb[j] = blob + (size_t)(2 * (tok[j] ? tile0 + j : 0) + (r >> 3)) * kGuRows * NB * 34;
     }
-    const int r = lane & 15, q = lane >> 4;
     __syncthreads();
     Stager<NTT> st;
     stager_init<NTT>(st, s_row, a.x, a.H, a, true);
@@ -345,12 +348,12 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
             for (int i = 0; i < NTT; ++i) f.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + blk * 32);
         }
         const int p = 4 * it + q;
-        const size_t c = (size_t)(p < NB ? p : NB - 1) * 16 + r;
+        const size_t c = (size_t)(p < NB ? p : NB - 1) * kGuRows + (r & 7);
 #pragma unroll
         for (int j = 0; j < RT; ++j) {
             f.gc[j] = ldg16(tb[j] + c * 16);
-            f.uc[j] = ldg16(tb[j] + (size_t)16 * NB * 16 + c * 16);
-            f.sc[j] = *reinterpret_cast<const uint16_t*>(tb[j] + (size_t)16 * NB * 32 + c * 2);
+            f.uc[j] = ldg16(tb[j] + (size_t)kGuRows * NB * 16 + c * 16);
+            f.sc[j] = *reinterpret_cast<const uint16_t*>(tb[j] + (size_t)kGuRows * NB * 32 + c * 2);
         }
     };
     auto step = [&](int it, const GuFrag<NTT, RT>& f, uint4* xb) {

@@ -289,19 +289,20 @@ void repack(const Layout& L, const uint8_t* src, uint8_t* dst) {
     const uint8_t* us = uc + HI / 2;
     const uint8_t* dc = us + HI / 32;
     const uint8_t* ds = dc + HI / 2;
-    const int NB = L.NB, S = L.S3, NBI = L.NBI;
-    for (int tile = 0; tile < L.I / 16; ++tile) {
-        uint8_t* tb = dst + (size_t)tile * 16 * NB * 34;
-        uint8_t* tsc = tb + (size_t)16 * NB * 32;
+    const int NB = L.NB, S = L.S3, NBI = L.NBI, GR = L.GR;
+    for (int tile = 0; tile < L.I / GR; ++tile) {
+        uint8_t* tb = dst + (size_t)tile * L.gu_tile_bytes;
+        uint8_t* tub = tb + (size_t)GR * NB * 16;
+        uint8_t* tsc = tb + (size_t)GR * NB * 32;
         for (int s = 0; s < S; ++s) {
             const int nb = seg_len(NB, S, s), b0 = seg_begin(NB, S, s);
             for (int t = 0; t < nb; ++t) {
-                for (int r = 0; r < 16; ++r) {
-                    const size_t row = (size_t)tile * 16 + r;
+                for (int r = 0; r < GR; ++r) {
+                    const size_t row = (size_t)tile * GR + r;
                     const int blk = b0 + t;
-                    const size_t c = (size_t)((t * S + s) * 16 + r);
+                    const size_t c = (size_t)(t * S + s) * GR + r;
                     memcpy(tb + c * 16, gc + row * (L.H / 2) + (size_t)blk * 16, 16);
-                    memcpy(tb + (size_t)16 * NB * 16 + c * 16, uc + row * (L.H / 2) + (size_t)blk * 16, 16);
+                    memcpy(tub + c * 16, uc + row * (L.H / 2) + (size_t)blk * 16, 16);
                     tsc[c * 2] = gs[row * NB + blk];
                     tsc[c * 2 + 1] = us[row * NB + blk];
                 }

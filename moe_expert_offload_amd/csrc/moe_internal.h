@@ -3,16 +3,17 @@
 // Kernel blob layout (what the pinned pool and the HBM slots hold; same size
 // as the logical blob, 3*H*I*17/32 bytes, a permutation of its bytes):
 //
-//  GU section (gate and up, read by the gate/up phase of the FFN kernel), I/16
-//  tiles of 16 rows each.  One workgroup of 4 waves takes a 16-row tile; a wave
-//  is 16 rows x 4 segments, so a row's NB = H/32 blocks are split into S3 = 16
-//  contiguous segments (segment s: nb(s) = NB/16 + (s < NB%16) blocks starting
-//  at b0(s) = s*(NB/16) + min(s, NB%16)).  Lane (r, s) reads block b0(s)+t at
-//  step t.  Chunk c = (t*S3 + s)*16 + r enumerates the tile's (row, block)
-//  pairs densely in that order:
-//     tile + c*16          : gate codes of (row, block) [16 B]
-//     tile + 16*NB*16 + c*16: up codes of (row, block) [16 B]
-//     tile + 16*NB*32 + c*2 : gate scale byte, up scale byte
+//  GU section (gate and up, read by the gate/up phase of the FFN kernel), I/8
+//  tiles of GR = 8 rows each.  One workgroup of 4 waves takes an 8-row tile; a
+//  wave is 8 rows x 8 segments, so a row's NB = H/32 blocks are split into
+//  S3 = 32 contiguous segments (segment s: nb(s) = NB/32 + (s < NB%32) blocks
+//  starting at b0(s) = s*(NB/32) + min(s, NB%32)).  Lane (r, s) reads block
+//  b0(s)+t at step t.  Position p = t*S3 + s enumerates the tile's blocks (for
+//  p < NB it is a bijection onto them), and chunk c = p*GR + r its (row, block)
+//  pairs, densely in that order:
+//     tile + c*16             : gate codes of (row, block) [16 B]
+//     tile + GR*NB*16 + c*16  : up codes of (row, block) [16 B]
+//     tile + GR*NB*32 + c*2   : gate scale byte, up scale byte
 //  so the 64 lanes of a wave read 1 KB of contiguous gate codes and 1 KB of
 //  contiguous up codes per step.
 //
@@ -32,18 +33,25 @@ namespace moe {
 
 struct Layout {
     int H, I, NB, NBI;     // blocks of 32 along H (gate/up rows) and along I (down rows)
-    int S3, T3;            // gate/up phase: segments per row (16), max steps per lane
+    int GR;                // rows per gate/up tile (8)
+    int S3, T3;            // gate/up phase: segments per row (32), max steps per lane
+    size_t gu_tile_bytes;  // one gate/up tile: GR rows of gate and up codes and scales
     size_t gu_bytes;       // size of the GU section
     size_t d_codes_off;    // offset of the D codes (== gu_bytes)
     size_t d_scales_off;   // offset of the D scales
     size_t blob_bytes;
 };
 
+constexpr int kGuRows = 8;       // rows per gate/up tile
+constexpr int kGuSegments = 32;  // segments per gate/up row
+
 inline Layout make_layout(int H, int I) {
     Layout L;
     L.H = H; L.I = I; L.NB = H / 32; L.NBI = I / 32;
-    L.S3 = 16;
+    L.GR = kGuRows;
+    L.S3 = kGuSegments;
     L.T3 = (L.NB + L.S3 - 1) / L.S3;
+    L.gu_tile_bytes = (size_t)L.GR * L.NB * 34;
     L.gu_bytes = (size_t)I * (size_t)H * 34 / 32;
     L.d_codes_off = L.gu_bytes;
     L.d_scales_off = L.gu_bytes + (size_t)H * (size_t)I / 2;

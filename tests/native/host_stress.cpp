@@ -38,9 +38,9 @@ std::vector<uint8_t> random_blob(const Layout& L, std::mt19937_64& rng) {
     std::vector<uint8_t> b(L.blob_bytes);
     for (auto& v : b) v = (uint8_t)rng();
     const int NB = L.NB, NBI = L.NBI;
-    for (int tile = 0; tile < L.I / 16; ++tile) {
-        uint8_t* tsc = b.data() + (size_t)tile * 16 * NB * 34 + (size_t)16 * NB * 32;
-        for (size_t i = 0; i < (size_t)16 * NB * 2; ++i) tsc[i] = (uint8_t)(123 + rng() % 5);
+    for (int tile = 0; tile < L.I / L.GR; ++tile) {
+        uint8_t* tsc = b.data() + (size_t)tile * L.gu_tile_bytes + (size_t)L.GR * NB * 32;
+        for (size_t i = 0; i < (size_t)L.GR * NB * 2; ++i) tsc[i] = (uint8_t)(123 + rng() % 5);
     }
     uint8_t* ds = b.data() + L.d_scales_off;
     for (size_t i = 0; i < (size_t)L.H * NBI; ++i) ds[i] = (uint8_t)(123 + rng() % 5);
