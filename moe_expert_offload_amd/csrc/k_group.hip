@@ -16,10 +16,10 @@
 //              (distinct experts of the step), appends the shared expert as a
 //              group of all B tokens, and cuts groups into chunks of at most
 //              gm rows (the work unit);
-//  k5_gate_up  per (chunk, 64 intermediate rows): gate and up projections of
-//              the chunk's tokens on the matrix cores, SwiGLU, a (bf16);
-//  k5_down     per (chunk, 64 output rows): down projection, unweighted
-//              expert outputs (fp32) per row;
+//  k5_gate_up  per (chunk, 64*RT intermediate rows): gate and up projections
+//              of the chunk's tokens on the matrix cores, SwiGLU, a (bf16);
+//  k5_down     per (chunk, SPW slices of 64*RT output rows): down projection,
+//              unweighted expert outputs (fp32) per row;
 //  k5_combine  per (token, 1024 outputs): routing-weighted sum over the
 //              token's experts in rank order, plus the shared expert, bf16.
 //
@@ -29,21 +29,23 @@
 // (r = l % 16, q = l / 16) holds weight row r and token r of the tile and the
 // reduction elements 8q..8q+7 of each MFMA.  The reduction order inside an
 // MFMA is free as long as both operands agree, so a k-iteration covers four
-// whole MX blocks of 32 elements: lane group q takes one block, loaded as a
-// single 16-byte chunk of codes plus its scale byte, and MFMA step s (0..3)
-// consumes elements 8s..8s+7 of every lane group's block.  Weights are
+// whole MX blocks of 32 elements, in their natural order (the activations of
+// a token for one iteration are 256 contiguous bytes): lane group q takes
+// block 4*it + q, loaded as a single 16-byte chunk of codes plus its scale
+// byte from that block's position in the repacked blob, and MFMA step s
+// (0..3) consumes elements 8s..8s+7 of every lane group's block.  Weights are
 // dequantised with the gfx950 scaled convert (v_cvt_scalef32_pk_bf16_fp4), the
 // E8M0 block scale folded in (a power of two, so the bf16 value is exact);
-// bf16 x bf16 products are exact in the FP32 accumulator.  Both matrices are
-// read in the same repacked blob layout as the single-token kernels, each
-// wave read a contiguous 1 KB (gate/up) or eight whole 128-byte lines (down).
-// Token activations are staged in LDS per k-iteration (three buffers), one
-// copy shared by the workgroup's four waves.
+// bf16 x bf16 products are exact in the FP32 accumulator.  Token activations
+// are staged in LDS per k-iteration (one copy shared by the workgroup's four
+// waves, in an XOR-swizzled layout that keeps stores and operand reads free of
+// bank conflicts); each wave's weights go straight to registers, two or three
+// k-iterations ahead.
 //
-// blockIdx -> work mapping is XCD-aware: consecutive workgroups go to
-// different XCDs, so the linear index is remapped so that each XCD gets a
-// contiguous range of (chunk, N tile) units, i.e. the N tiles of one chunk
-// (same tokens, L2-resident activations) run on one XCD.
+// blockIdx -> work mapping is XCD-aware: workgroup b runs on XCD b % 8, so the
+// step's units are split into eight contiguous ranges, one per XCD: every XCD
+// gets an equal share, and the N tiles of one chunk (same tokens, so
+// L2-resident activations) run on one XCD.
 #include <hip/hip_runtime.h>
 
 #include "ffn_device.h"
@@ -95,6 +97,25 @@ __device__ __forceinline__ int kg_scan(int v, int* s_wave, int& total) {
     return before + x - v;
 }
 
+// f(i, slots[i]) for every row i < n of this thread (rows tid, tid + 1024, ...),
+// with the slot loads of eight rows in flight at once
+template <typename F>
+__device__ __forceinline__ void for_rows(const int32_t* slots, int n, F&& f) {
+    for (int base = threadIdx.x; base < n; base += KG_THREADS * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * KG_THREADS;
+            v[u] = i < n ? slots[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * KG_THREADS;
+            if (i < n) f(i, v[u]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
     __shared__ uint32_t s_bits[KG_MAXC / 32];
     __shared__ int32_t s_pre[KG_MAXC / 32];
@@ -112,11 +133,10 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
     }
     if (tid == 0) s_invalid = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += KG_THREADS) {
-        const int sl = a.slots[i];
+    for_rows(a.slots, n, [&](int, int sl) {
         if ((unsigned)sl < (unsigned)a.C) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
         else if (!(a.host_rows && sl == -1)) atomicAdd(&s_invalid, 1);  // -1 with host_rows: the host's row
-    }
+    });
     __syncthreads();
     // nw <= 512: one bitmap word per thread; rank of a slot = present slots below it
     const int pc = tid < nw ? __popc(s_bits[tid]) : 0;
@@ -136,12 +156,11 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
         return;
     }
     __syncthreads();
-    for (int i = tid; i < n; i += KG_THREADS) {
-        const int sl = a.slots[i];
-        if (sl < 0) continue;  // a host row
+    for_rows(a.slots, n, [&](int, int sl) {
+        if (sl < 0) return;  // a host row
         const int g = s_pre[sl >> 5] + __popc(s_bits[sl >> 5] & ((1u << (sl & 31)) - 1u));
         atomicAdd(&s_cnt[g], 1);
-    }
+    });
     if (tid < nw) {
         uint32_t bits = s_bits[tid];
         int g = s_pre[tid];
@@ -183,12 +202,11 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
     __syncthreads();
     // rows of a group in any order: every output element depends on its own
     // token only, so the order inside a group does not change any result
-    for (int i = tid; i < n; i += KG_THREADS) {
-        const int sl = a.slots[i];
-        if (sl < 0) continue;  // a host row
+    for_rows(a.slots, n, [&](int i, int sl) {
+        if (sl < 0) return;  // a host row
         const int g = s_pre[sl >> 5] + __popc(s_bits[sl >> 5] & ((1u << (sl & 31)) - 1u));
         a.p.perm[s_off[g] + atomicAdd(&s_cur[g], 1)] = i;
-    }
+    });
     if (tid == 0) {
         a.p.hdr[0] = n_rg + a.n_shared;
         a.p.hdr[1] = n_rch + a.n_shared * sh_nch;
@@ -209,9 +227,21 @@ __device__ __forceinline__ int row_token(const GemmArgs& a, int row) {
     return row < n ? row / a.k : (row - n) % a.B;
 }
 
-// block index of position p of the gate/up section's (step, segment) order
-__device__ __forceinline__ int gu_block(int p, int NB) {
-    return seg_begin(NB, kGuSegments, p % kGuSegments) + p / kGuSegments;
+// position of block b in the gate/up section's (step, segment) order: segment
+// s holds blocks seg_begin(s) .. + seg_len(s) - 1 (the first NB % 32 segments
+// one block longer), block seg_begin(s) + t sits at position t * 32 + s
+__device__ __forceinline__ int gu_pos(int b, int NB) {
+    const int q = NB / kGuSegments, rem = NB % kGuSegments;
+    int s, t;
+    if (b < rem * (q + 1)) {
+        s = b / (q + 1);
+        t = b - s * (q + 1);
+    } else {
+        const int b2 = b - rem * (q + 1);
+        s = rem + b2 / q;
+        t = b2 - (s - rem) * q;
+    }
+    return t * kGuSegments + s;
 }
 
 // 8 E2M1 codes (one dword) times the block scale -> 8 bf16 MFMA operand values
@@ -234,18 +264,24 @@ __device__ __forceinline__ uint32_t word(uint4 v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Work unit of this workgroup: (chunk ci, N tile nt), XCD-aware.  Returns false
-// when the unit is past the step's chunks (the grid is sized for the maximum).
+// Work unit of this workgroup: (chunk ci, N tile nt).  The grid is sized for the
+// most chunks a step can have; the step's own U units are split into 8
+// contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so every XCD
+// gets an equal share and the N tiles of a chunk, which read the same
+// activation rows, run on one XCD's L2.  Returns false for workgroups past the
+// step's units.
 struct Unit {
     int ci, nt, g, nrow, base, g_slot;
 };
 
 __device__ __forceinline__ bool get_unit(const GemmArgs& a, int nt_per_chunk, Unit& u) {
-    const int G = gridDim.x;
-    const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int n_units = a.p.hdr[1] * nt_per_chunk;
+    const int per_xcd = (n_units + 7) >> 3;
+    const int j = blockIdx.x >> 3;
+    const int logical = (blockIdx.x & 7) * per_xcd + j;
+    if (j >= per_xcd || logical >= n_units) return false;
     u.ci = logical / nt_per_chunk;
     u.nt = logical - u.ci * nt_per_chunk;
-    if (u.ci >= a.p.hdr[1]) return false;
     u.g = a.p.chunks[2 * u.ci];
     const int start = a.p.chunks[2 * u.ci + 1];
     const int cnt = a.p.g_cnt[u.g];
@@ -258,14 +294,18 @@ __device__ __forceinline__ bool get_unit(const GemmArgs& a, int nt_per_chunk, Un
 // Activation staging: the chunk's GM token rows x 4 blocks (64 bytes each) per
 // k-iteration, NTT 16-byte pieces per thread.  Piece v = tid + 256*i is
 // (token t = v/16, lane group q = (v/4)%4, step s = v%4): q and s are the same
-// for all of a thread's pieces and t grows by 16 per piece.  LDS: [token][q] in
-// 80-byte cells (5 x 16 B), so the 16 tokens a wave reads at once are spread
-// over the banks.
+// for all of a thread's pieces and t grows by 16 per piece.  LDS holds 16
+// cells of 16 bytes per token, cell (q, s) of token t at t*16 + ((4q+s) xor
+// (t%16)): the 16 lanes that store one token's pieces and the 16 lanes that
+// read piece (q, s) of 16 consecutive tokens for an MFMA operand both touch 16
+// different cells of a 256-byte row, i.e. every LDS bank once.
+__device__ __forceinline__ int x_cell(int t, int q, int s) { return t * 16 + ((4 * q + s) ^ (t & 15)); }
+
 template <int NTT>
 struct Stager {
     const uint16_t* src[NTT];   // row base of the piece's token (row 0 for an empty row)
     uint32_t ok;                // bit i: piece i holds a row of the chunk
-    int q, s, dst0;             // lane group, step, LDS cell of piece 0 (piece i: + 320 i)
+    int q, s, dst0;             // lane group, step, LDS cell of piece 0 (piece i: + 256 i)
 };
 
 template <int NTT>
@@ -274,7 +314,7 @@ __device__ __forceinline__ void stager_init(Stager<NTT>& st, const int* s_row, c
     const int v = threadIdx.x;
     st.q = (v >> 2) & 3;
     st.s = v & 3;
-    st.dst0 = ((v >> 4) * 4 + st.q) * 5 + st.s;
+    st.dst0 = x_cell(v >> 4, st.q, st.s);
     st.ok = 0u;
 #pragma unroll
     for (int i = 0; i < NTT; ++i) {
@@ -290,15 +330,36 @@ __device__ __forceinline__ void stager_init(Stager<NTT>& st, const int* s_row, c
 // DEPTH fragments and LDS buffers are used in turn (the loop is unrolled by
 // DEPTH so each has fixed registers).  Iterations past the end read clamped,
 // in-bounds addresses and are masked.  Loads complete in order, so a step
-// waits only for its own fragment while the later ones stay in flight.  Token
-// tiles past the chunk's rows are skipped (a wave-uniform branch).
+// waits only for its own fragment while the later ones stay in flight; a step
+// refills its fragment after its MFMAs.  The loop is
+// compiled once per count NT of token tiles that hold rows of the chunk (a
+// wave-uniform switch outside it), so its body has no branches: the LDS reads
+// of one MFMA step can overlap the MFMAs of the step before.
+
+template <int N>
+struct IC {
+    static constexpr int value = N;
+};
+
+// f(IC<n>) for the chunk's token-tile count n (1..NTT)
+template <int NTT, typename F>
+__device__ __forceinline__ void with_tiles(int n, F&& f) {
+    if constexpr (NTT == 1) {
+        f(IC<1>{});
+    } else {
+        if (n <= 1) f(IC<1>{});
+        else if (n == 2) f(IC<2>{});
+        else if (n == 3 && NTT > 3) f(IC<3>{});
+        else f(IC<NTT>{});
+    }
+}
 
 // ---------------------------------------------------------- k5_gate_up --
 // RT 16-row tiles of the intermediate dimension per wave (tiles (nt*4 + w)*RT
 // + j), so one LDS read of an activation operand feeds 2*RT MFMAs.
-template <int NTT, int RT>
+template <int NT, int RT>
 struct GuFrag {
-    uint4 xv[NTT];
+    uint4 xv[NT];
     uint4 gc[RT], uc[RT];
     uint32_t sc[RT];
 };
@@ -306,7 +367,7 @@ struct GuFrag {
 template <int NTT, int RT, int DEPTH>
 __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
     constexpr int GM = 16 * NTT;
-    __shared__ uint4 xs[DEPTH][GM * 4 * 5];
+    __shared__ uint4 xs[DEPTH][GM * 16];
     __shared__ int s_row[GM];
     const int n_tiles = a.I >> 4;
     const int nt_per_chunk = (n_tiles + 4 * RT - 1) / (4 * RT);
@@ -340,139 +401,139 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
             accu[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     const int nit = (NB + 3) >> 2;
-    auto issue = [&](int it, GuFrag<NTT, RT>& f) {
-        {
-            const int p = 4 * it + st.q;
-            const int blk = gu_block(p < NB ? p : NB - 1, NB);
+    with_tiles<NTT>(ntt, [&](auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        auto issue = [&](int it, GuFrag<NT, RT>& f) {
+            {
+                const int b = 4 * it + st.q;
+                const int blk = b < NB ? b : NB - 1;
 #pragma unroll
-            for (int i = 0; i < NTT; ++i) f.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + blk * 32);
-        }
-        const int p = 4 * it + q;
-        const size_t c = (size_t)(p < NB ? p : NB - 1) * kGuRows + (r & 7);
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-            f.gc[j] = ldg16(tb[j] + c * 16);
-            f.uc[j] = ldg16(tb[j] + (size_t)kGuRows * NB * 16 + c * 16);
-            f.sc[j] = *reinterpret_cast<const uint16_t*>(tb[j] + (size_t)kGuRows * NB * 32 + c * 2);
-        }
-    };
-    auto step = [&](int it, const GuFrag<NTT, RT>& f, uint4* xb) {
-        const bool pin = (4 * it + st.q) < NB;
-#pragma unroll
-        for (int i = 0; i < NTT; ++i) {
-            const bool ok = pin && ((st.ok >> i) & 1u);
-            xb[st.dst0 + 320 * i] = ok ? f.xv[i] : make_uint4(0u, 0u, 0u, 0u);
-        }
-        const bool pv = (4 * it + q) < NB;
-        float sg[RT], su[RT];
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-            sg[j] = pv && tok[j] ? e8m0(f.sc[j]) : 0.0f;
-            su[j] = pv && tok[j] ? e8m0(f.sc[j] >> 8) : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            bf16x8_t wg[RT], wu[RT];
+                for (int i = 0; i < NT; ++i) f.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + blk * 32);
+            }
+            const int b = 4 * it + q;
+            const size_t c = (size_t)gu_pos(b < NB ? b : NB - 1, NB) * kGuRows + (r & 7);
 #pragma unroll
             for (int j = 0; j < RT; ++j) {
-                wg[j] = dq8(word(f.gc[j], s4), sg[j]);
-                wu[j] = dq8(word(f.uc[j], s4), su[j]);
+                f.gc[j] = ldg16(tb[j] + c * 16);
+                f.uc[j] = ldg16(tb[j] + (size_t)kGuRows * NB * 16 + c * 16);
+                f.sc[j] = *reinterpret_cast<const uint16_t*>(tb[j] + (size_t)kGuRows * NB * 32 + c * 2);
             }
+        };
+        // MFMA step s4 (elements 8*s4.. of each lane group's block) of all NT token tiles
+        auto mma = [&](const bf16x8_t* wg, const bf16x8_t* wu, const uint4* xb, int s4) {
+            bf16x8_t xo[NT];
 #pragma unroll
-            for (int m = 0; m < NTT; ++m) {
-                if (NTT > 1 && m >= ntt) continue;
-                const bf16x8_t xo = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
+            for (int m = 0; m < NT; ++m) xo[m] = as_bf16x8(xb[x_cell(m * 16 + r, q, s4)]);
+#pragma unroll
+            for (int m = 0; m < NT; ++m)
 #pragma unroll
                 for (int j = 0; j < RT; ++j) {
-                    accg[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[j], xo, accg[j][m], 0, 0, 0);
-                    accu[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu[j], xo, accu[j][m], 0, 0, 0);
+                    accg[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[j], xo[m], accg[j][m], 0, 0, 0);
+                    accu[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu[j], xo[m], accu[j][m], 0, 0, 0);
                 }
+        };
+        // one k-iteration on fragment f; `next` refills f with a later iteration's loads
+        auto step = [&](int it, GuFrag<NT, RT>& f, uint4* xb, auto&& next) {
+            const bool pin = (4 * it + st.q) < NB;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const bool ok = pin && ((st.ok >> i) & 1u);
+                xb[st.dst0 + 256 * i] = ok ? f.xv[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            const bool pv = (4 * it + q) < NB;
+            float sg[RT], su[RT];
+#pragma unroll
+            for (int j = 0; j < RT; ++j) {
+                sg[j] = pv && tok[j] ? e8m0(f.sc[j]) : 0.0f;
+                su[j] = pv && tok[j] ? e8m0(f.sc[j] >> 8) : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                bf16x8_t wg[RT], wu[RT];
+#pragma unroll
+                for (int j = 0; j < RT; ++j) {
+                    wg[j] = dq8(word(f.gc[j], s4), sg[j]);
+                    wu[j] = dq8(word(f.uc[j], s4), su[j]);
+                }
+                mma(wg, wu, xb, s4);
+            }
+            next();
+        };
+        if constexpr (DEPTH == 3) {
+            GuFrag<NT, RT> fa, fb, fc;
+            issue(0, fa);
+            issue(1, fb);
+            issue(2, fc);
+            for (int it = 0; it < nit; it += 3) {
+                step(it, fa, xs[0], [&] { issue(it + 3, fa); });
+                step(it + 1, fb, xs[1], [&] { issue(it + 4, fb); });
+                step(it + 2, fc, xs[2], [&] { issue(it + 5, fc); });
+            }
+        } else {
+            GuFrag<NT, RT> fa, fb;
+            issue(0, fa);
+            issue(1, fb);
+            for (int it = 0; it < nit; it += 2) {
+                step(it, fa, xs[0], [&] { issue(it + 2, fa); });
+                step(it + 1, fb, xs[1], [&] { issue(it + 3, fb); });
             }
         }
-    };
-    if constexpr (DEPTH == 3) {
-        GuFrag<NTT, RT> fa, fb, fc;
-        issue(0, fa);
-        issue(1, fb);
-        issue(2, fc);
-        for (int it = 0; it < nit; it += 3) {
-            step(it, fa, xs[0]);
-            issue(it + 3, fa);
-            step(it + 1, fb, xs[1]);
-            issue(it + 4, fb);
-            step(it + 2, fc, xs[2]);
-            issue(it + 5, fc);
-        }
-    } else {
-        GuFrag<NTT, RT> fa, fb;
-        issue(0, fa);
-        issue(1, fb);
-        for (int it = 0; it < nit; it += 2) {
-            step(it, fa, xs[0]);
-            issue(it + 2, fa);
-            step(it + 1, fb, xs[1]);
-            issue(it + 3, fb);
-        }
-    }
+    });
     // lane holds intermediate rows (tile0+j)*16 + 4q + 0..3 of token r of each token tile
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
-        {
-            const int row = s_row[m * 16 + r];
-            if (row >= 0) {
+        const int row = s_row[m * 16 + r];
+        if (row < 0) continue;
 #pragma unroll
-                for (int j = 0; j < RT; ++j) {
-                    if (!tok[j]) continue;
-                    const f32x4_t g = accg[j][m], v = accu[j][m];
-                    const uint32_t lo = (uint32_t)f32_to_bf16(swiglu(g[0], v[0])) |
-                                        ((uint32_t)f32_to_bf16(swiglu(g[1], v[1])) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(swiglu(g[2], v[2])) |
-                                        ((uint32_t)f32_to_bf16(swiglu(g[3], v[3])) << 16);
-                    *reinterpret_cast<uint2*>(a.a + (size_t)row * a.I + (tile0 + j) * 16 + 4 * q) =
-                        make_uint2(lo, hi);
-                }
-            }
+        for (int j = 0; j < RT; ++j) {
+            if (!tok[j]) continue;
+            const f32x4_t g = accg[j][m], v = accu[j][m];
+            const uint32_t lo = (uint32_t)f32_to_bf16(swiglu(g[0], v[0])) |
+                                ((uint32_t)f32_to_bf16(swiglu(g[1], v[1])) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(swiglu(g[2], v[2])) |
+                                ((uint32_t)f32_to_bf16(swiglu(g[3], v[3])) << 16);
+            *reinterpret_cast<uint2*>(a.a + (size_t)row * a.I + (tile0 + j) * 16 + 4 * q) = make_uint2(lo, hi);
         }
     }
 }
 
 // ------------------------------------------------------------- k5_down --
-// RT 16-row tiles of the output per wave (tiles (nt*4 + w)*RT + j); a 16-row
-// tile is two 8-row tiles of the D section.
-template <int NTT, int RT>
+// A slice is 4*RT 16-row tiles of the output, RT per wave (tiles (s*4 + w)*RT
+// + j of slice s); a 16-row tile is two 8-row tiles of the D section.  A
+// workgroup takes SPW consecutive slices of its chunk and runs their
+// k-iterations as one pipeline (the reduction is short, I / 128 iterations, so
+// the loads of the next slice are already in flight when a slice ends), storing
+// each slice's outputs after its last iteration.
+template <int NT, int RT>
 struct DnFrag {
-    uint4 xv[NTT];
+    uint4 xv[NT];
     uint4 dc[RT];
     uint32_t sc[RT];
 };
 
-template <int NTT, int RT, int DEPTH>
+template <int NTT, int RT, int DEPTH, int SPW>
 __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
     constexpr int GM = 16 * NTT;
-    __shared__ uint4 xs[DEPTH][GM * 4 * 5];
+    __shared__ uint4 xs[DEPTH][GM * 16];
     __shared__ int s_row[GM];
     const int n_tiles = a.H >> 4;
-    const int nt_per_chunk = (n_tiles + 4 * RT - 1) / (4 * RT);
+    const int n_slices = (n_tiles + 4 * RT - 1) / (4 * RT);
+    const int nt_per_chunk = (n_slices + SPW - 1) / SPW;
     Unit u;
     if (!get_unit(a, nt_per_chunk, u)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid < GM) s_row[tid] = tid < u.nrow ? a.p.perm[u.base + tid] : -1;
     const int ntt = (u.nrow + 15) >> 4;   // token tiles holding rows of the chunk
     const int NBI = a.NBI;
-    const int tile0 = (u.nt * 4 + w) * RT;
+    const int s0 = u.nt * SPW;                        // first slice
+    const int nsl = min(SPW, n_slices - s0);          // slices of this workgroup
+    const int nit = (NBI + 3) >> 2;                   // k-iterations per slice
+    const int F = nsl * nit;                          // pipeline length
     const int r = lane & 15, q = lane >> 4;
     const uint8_t* blob = group_blob(a, u.g_slot);
-    const uint8_t* dcod[RT];
-    const uint8_t* dsc[RT];
-    bool tok[RT];
-#pragma unroll
-    for (int j = 0; j < RT; ++j) {
-        tok[j] = tile0 + j < n_tiles;
-        const int t8 = 2 * (tok[j] ? tile0 + j : 0) + (r >> 3), rr = r & 7;
-        dcod[j] = blob + a.d_codes_off + ((size_t)t8 * NBI * 8 + rr) * 16;
-        dsc[j] = blob + a.d_scales_off + (size_t)t8 * NBI * 8 + rr;
-    }
+    const uint8_t* dcod0 = blob + a.d_codes_off + (size_t)(r & 7) * 16;
+    const uint8_t* dsc0 = blob + a.d_scales_off + (r & 7);
     __syncthreads();
     Stager<NTT> st;
     stager_init<NTT>(st, s_row, a.a, a.I, a, false);
@@ -482,87 +543,99 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
     for (int j = 0; j < RT; ++j)
 #pragma unroll
         for (int m = 0; m < NTT; ++m) acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nit = (NBI + 3) >> 2;
-    auto issue = [&](int it, DnFrag<NTT, RT>& f) {
-        {
-            const int p = 4 * it + st.q;
+    // tile j of slice s0 + sl (clamped to tile 0 past the output), and whether it is real
+    auto tile_of = [&](int sl, int j) { return ((s0 + sl) * 4 + w) * RT + j; };
+    auto store = [&](int sl) {
+#pragma unroll
+        for (int m = 0; m < NTT; ++m) {
+            const int row = s_row[m * 16 + r];
+#pragma unroll
+            for (int j = 0; j < RT; ++j) {
+                const int t = tile_of(sl, j);
+                if (row >= 0 && t < n_tiles)
+                    *reinterpret_cast<float4*>(a.yp + (size_t)row * a.H + t * 16 + 4 * q) =
+                        make_float4(acc[j][m][0], acc[j][m][1], acc[j][m][2], acc[j][m][3]);
+                acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    with_tiles<NTT>(ntt, [&](auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        // loads of pipeline step f (slice f / nit, k-iteration f % nit); steps
+        // past the end re-read the last one (in bounds, masked in `step`)
+        auto issue = [&](int f, DnFrag<NT, RT>& fr) {
+            const int fc = f < F ? f : F - 1;
+            const int sl = fc / nit, it = fc - sl * nit;
+            {
+                const int p = 4 * it + st.q;
+                const int ib = p < NBI ? p : NBI - 1;
+#pragma unroll
+                for (int i = 0; i < NT; ++i) fr.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + ib * 32);
+            }
+            const int p = 4 * it + q;
             const int ib = p < NBI ? p : NBI - 1;
 #pragma unroll
-            for (int i = 0; i < NTT; ++i) f.xv[i] = *reinterpret_cast<const uint4*>(st.src[i] + ib * 32);
-        }
-        const int p = 4 * it + q;
-        const int ib = p < NBI ? p : NBI - 1;
+            for (int j = 0; j < RT; ++j) {
+                const int t = tile_of(sl, j);
+                const size_t t8 = (size_t)(2 * (t < n_tiles ? t : 0) + (r >> 3)) * NBI * 8;
+                fr.dc[j] = ldg16(dcod0 + (t8 + (size_t)ib * 8) * 16);
+                fr.sc[j] = dsc0[t8 + (size_t)ib * 8];
+            }
+        };
+        auto mma = [&](const bf16x8_t* wd, const uint4* xb, int s4) {
+            bf16x8_t ao[NT];
 #pragma unroll
-        for (int j = 0; j < RT; ++j) {
-            f.dc[j] = ldg16(dcod[j] + (size_t)ib * 8 * 16);
-            f.sc[j] = dsc[j][(size_t)ib * 8];
-        }
-    };
-    auto step = [&](int it, const DnFrag<NTT, RT>& f, uint4* xb) {
-        const bool pin = (4 * it + st.q) < NBI;
+            for (int m = 0; m < NT; ++m) ao[m] = as_bf16x8(xb[x_cell(m * 16 + r, q, s4)]);
 #pragma unroll
-        for (int i = 0; i < NTT; ++i) {
-            const bool ok = pin && ((st.ok >> i) & 1u);
-            xb[st.dst0 + 320 * i] = ok ? f.xv[i] : make_uint4(0u, 0u, 0u, 0u);
-        }
-        const bool pv = (4 * it + q) < NBI;
-        float sd[RT];
-#pragma unroll
-        for (int j = 0; j < RT; ++j) sd[j] = pv && tok[j] ? e8m0(f.sc[j]) : 0.0f;
-        __syncthreads();
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            bf16x8_t wd[RT];
-#pragma unroll
-            for (int j = 0; j < RT; ++j) wd[j] = dq8(word(f.dc[j], s4), sd[j]);
-#pragma unroll
-            for (int m = 0; m < NTT; ++m) {
-                if (NTT > 1 && m >= ntt) continue;
-                const bf16x8_t ao = as_bf16x8(xb[((m * 16 + r) * 4 + q) * 5 + s4]);
+            for (int m = 0; m < NT; ++m)
 #pragma unroll
                 for (int j = 0; j < RT; ++j)
-                    acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd[j], ao, acc[j][m], 0, 0, 0);
+                    acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd[j], ao[m], acc[j][m], 0, 0, 0);
+        };
+        auto step = [&](int f, DnFrag<NT, RT>& fr, uint4* xb, auto&& next) {
+            const bool live = f < F;
+            const int sl = f / nit, it = f - sl * nit;
+            const bool pin = live && (4 * it + st.q) < NBI;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const bool ok = pin && ((st.ok >> i) & 1u);
+                xb[st.dst0 + 256 * i] = ok ? fr.xv[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            const bool pv = live && (4 * it + q) < NBI;
+            float sd[RT];
+#pragma unroll
+            for (int j = 0; j < RT; ++j) sd[j] = pv && tile_of(sl, j) < n_tiles ? e8m0(fr.sc[j]) : 0.0f;
+            __syncthreads();
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                bf16x8_t wd[RT];
+#pragma unroll
+                for (int j = 0; j < RT; ++j) wd[j] = dq8(word(fr.dc[j], s4), sd[j]);
+                mma(wd, xb, s4);
+            }
+            next();
+            if (live && it == nit - 1) store(sl);
+        };
+        if constexpr (DEPTH == 3) {
+            DnFrag<NT, RT> fa, fb, fc;
+            issue(0, fa);
+            issue(1, fb);
+            issue(2, fc);
+            for (int f = 0; f < F; f += 3) {
+                step(f, fa, xs[0], [&] { issue(f + 3, fa); });
+                step(f + 1, fb, xs[1], [&] { issue(f + 4, fb); });
+                step(f + 2, fc, xs[2], [&] { issue(f + 5, fc); });
+            }
+        } else {
+            DnFrag<NT, RT> fa, fb;
+            issue(0, fa);
+            issue(1, fb);
+            for (int f = 0; f < F; f += 2) {
+                step(f, fa, xs[0], [&] { issue(f + 2, fa); });
+                step(f + 1, fb, xs[1], [&] { issue(f + 3, fb); });
             }
         }
-    };
-    if constexpr (DEPTH == 3) {
-        DnFrag<NTT, RT> fa, fb, fc;
-        issue(0, fa);
-        issue(1, fb);
-        issue(2, fc);
-        for (int it = 0; it < nit; it += 3) {
-            step(it, fa, xs[0]);
-            issue(it + 3, fa);
-            step(it + 1, fb, xs[1]);
-            issue(it + 4, fb);
-            step(it + 2, fc, xs[2]);
-            issue(it + 5, fc);
-        }
-    } else {
-        DnFrag<NTT, RT> fa, fb;
-        issue(0, fa);
-        issue(1, fb);
-        for (int it = 0; it < nit; it += 2) {
-            step(it, fa, xs[0]);
-            issue(it + 2, fa);
-            step(it + 1, fb, xs[1]);
-            issue(it + 3, fb);
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < NTT; ++m) {
-        {
-            const int row = s_row[m * 16 + r];
-            if (row >= 0) {
-#pragma unroll
-                for (int j = 0; j < RT; ++j) {
-                    if (!tok[j]) continue;
-                    *reinterpret_cast<float4*>(a.yp + (size_t)row * a.H + (tile0 + j) * 16 + 4 * q) =
-                        make_float4(acc[j][m][0], acc[j][m][1], acc[j][m][2], acc[j][m][3]);
-                }
-            }
-        }
-    }
+    });
 }
 
 // ---------------------------------------------------------- k5_combine --
@@ -610,26 +683,29 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
 
 static int pad8(long v) { return (int)((v + 7) / 8 * 8); }
 
-// row tiles per wave: gate/up and down of prefill-sized chunks (64 rows) take
-// 2 and 4 tiles; single-token-sized chunks (16 rows) keep one for parallelism
-constexpr int RT_GU_BIG = 2, RT_D_BIG = 4;
+// prefill-sized chunks (64 rows): gate/up waves take 2 row tiles with three
+// fragments in flight, down waves 4 row tiles with two, and a down workgroup 3
+// slices of 256 outputs; single-token-sized chunks (16 rows) keep one tile and
+// one slice for parallelism
+constexpr int RT_GU_BIG = 2, RT_D_BIG = 4, SPW_D_BIG = 3;
 
 int launch_grouped_ffn(GroupArgs& g, GemmArgs& m, CombineArgs& c, void* stream, void* ev_mid) {
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(k2g_group, dim3(1), dim3(KG_THREADS), 0, st, g);
     const bool big = m.gm != 16;
-    const int rt1 = big ? RT_GU_BIG : 1, rt2 = big ? RT_D_BIG : 1;
-    const int nt1 = (m.I / 16 + 4 * rt1 - 1) / (4 * rt1), nt2 = (m.H / 16 + 4 * rt2 - 1) / (4 * rt2);
+    const int rt1 = big ? RT_GU_BIG : 1, rt2 = big ? RT_D_BIG : 1, spw = big ? SPW_D_BIG : 1;
+    const int nt1 = (m.I / 16 + 4 * rt1 - 1) / (4 * rt1);
+    const int nt2 = ((m.H / 16 + 4 * rt2 - 1) / (4 * rt2) + spw - 1) / spw;
     const dim3 g1(pad8((long)m.p.max_chunks * nt1)), g2(pad8((long)m.p.max_chunks * nt2));
     if (big)
-        hipLaunchKernelGGL((k5_gate_up<4, RT_GU_BIG, 2>), g1, dim3(K5_THREADS), 0, st, m);
+        hipLaunchKernelGGL((k5_gate_up<4, RT_GU_BIG, 3>), g1, dim3(K5_THREADS), 0, st, m);
     else
         hipLaunchKernelGGL((k5_gate_up<1, 1, 3>), g1, dim3(K5_THREADS), 0, st, m);
     if (ev_mid) (void)hipEventRecord((hipEvent_t)ev_mid, st);
     if (big)
-        hipLaunchKernelGGL((k5_down<4, RT_D_BIG, 2>), g2, dim3(K5_THREADS), 0, st, m);
+        hipLaunchKernelGGL((k5_down<4, RT_D_BIG, 2, SPW_D_BIG>), g2, dim3(K5_THREADS), 0, st, m);
     else
-        hipLaunchKernelGGL((k5_down<1, 1, 3>), g2, dim3(K5_THREADS), 0, st, m);
+        hipLaunchKernelGGL((k5_down<1, 1, 3, 1>), g2, dim3(K5_THREADS), 0, st, m);
     hipLaunchKernelGGL(k5_combine, dim3((c.H + 1023) / 1024, c.B), dim3(256), 0, st, c, m.p.hdr);
     return (int)hipGetLastError();
 }
