@@ -67,13 +67,23 @@ struct moe_ctx {
     bool rs_active = false;     // the current call runs K1/K2 on rs
     std::mutex err_mu;          // set_err may run on a call's helper thread too
     bool rs_host_wait = false;  // ... and the host (not the copy streams) waits for ffn_done
-    uint8_t* pool = nullptr;    // pinned host, blobs [0, n_pin) of [L*E][blob]
+    // The pool's L*E blobs are split between pinned memory (n_pin of them) and pageable memory.
+    // Blob i is pinned iff pin_rank steps at i (pin_rank(i) = floor(i * n_pin / n_blobs)), so
+    // the pinned ones are spread evenly over every layer's experts: a layer's misses mix pinned
+    // blobs (DMA at once) with pageable ones (filled into a bounce slot by the host first), and
+    // the pinned copies keep the link busy during those fills.  A pinned blob sits at
+    // pinned index pin_rank(i), a pageable one at pageable index i - pin_rank(i).
+    uint8_t* pool = nullptr;    // pinned host, n_pin blobs
     size_t pool_bytes = 0;      // whole pool
     size_t n_pin = 0;           // blobs in pinned memory
-    uint8_t* pool_pg = nullptr; // pageable host, blobs [n_pin, L*E)
+    size_t n_blobs = 0;         // L*E
+    uint8_t* pool_pg = nullptr; // pageable host, n_blobs - n_pin blobs
     BounceRing bounce;          // pinned bounce ring for the pageable part
+    size_t pin_rank(size_t i) const { return n_pin == n_blobs ? i : (size_t)((uint64_t)i * n_pin / n_blobs); }
+    bool pinned(size_t i) const { return pin_rank(i + 1) > pin_rank(i); }
     const uint8_t* blob_src(size_t i) const {
-        return i < n_pin ? pool + i * lay.blob_bytes : pool_pg + (i - n_pin) * lay.blob_bytes;
+        const size_t r = pin_rank(i);
+        return pinned(i) ? pool + r * lay.blob_bytes : pool_pg + (i - r) * lay.blob_bytes;
     }
     uint8_t* arena = nullptr;   // caller device memory, [C][blob]
     uint8_t* shared_dev = nullptr;
@@ -640,11 +650,16 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         return MOE_OK;
     };
     size_t pair_of[2] = {0, 0};
+    // pass 0 queues the misses whose blobs are pinned (their DMA starts at once), pass 1 the
+    // pageable ones: the host fills each of those into a bounce slot before its DMA, at about the
+    // DMA's own rate, so the pinned copies queued ahead keep the link busy during the fills
+    for (int pass = 0; pass < 2; ++pass)
     for (int i = 0; i < nm; ++i) {
         const MissEntry m = ml->e[i];
         if (m.slot < 0) continue;  // computed by the host
-        ++ncopy;
         const size_t idx = (size_t)layer * c->cfg.n_experts + m.expert;
+        if (c->pinned(idx) != (pass == 0)) continue;
+        ++ncopy;
         uint8_t* dst = c->arena + (size_t)m.slot * blob;
         ++c->copies_issued;
         if (c->fault_fail_at && c->copies_issued == c->fault_fail_at)
@@ -652,13 +667,13 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
                            (unsigned long long)c->copies_issued, layer, m.expert);
         const size_t n_sl = (size_t)c->cfg.n_layers * c->cfg.n_experts;
         const size_t src_idx = (c->fault_corrupt_at && c->copies_issued == c->fault_corrupt_at) ? (idx + 1) % n_sl : idx;
-        const int q = idx < c->n_pin ? (nd++ & 1) : 0;
+        const int q = c->pinned(idx) ? (nd++ & 1) : 0;
         if (!used[q]) {
             moe_status st = open_stream(q);
             if (st) return st;
             pair_of[q] = c->h2d_used.size() - 1;
         }
-        if (idx < c->n_pin) {
+        if (c->pinned(idx)) {
             HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(src_idx), blob, hipMemcpyHostToDevice, qs[q]));
         } else {
             HIPCHK(c, c->bounce.copy(dst, c->blob_src(src_idx), blob));  // on the caller's copy stream
@@ -1132,6 +1147,7 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
         n_pin = n_pin * 7 / 8;
     }
     c->n_pin = n_pin;
+    c->n_blobs = n_sl;
     if (n_pin < n_sl) {
         if (!c->bounce.ready()) {
             where = "bounce ring allocation";
