@@ -91,8 +91,12 @@ typedef struct {
     int32_t n_shared;       /* always-on shared experts per layer (0 or 1), resident in HBM */
     int32_t cache_slots;    /* C: GPU expert slots; must be >= 2 * min(max_tokens * k, E) */
     int32_t max_tokens;     /* largest n_tokens of any call */
-    int32_t lookahead;      /* moe_stack_forward: 1 = resolve and copy layer l+1 while layer l's
-                               FFN runs; 0 = causal (each layer's copies before its FFN) */
+    int32_t lookahead;      /* moe_stack_forward: 2 = resolve layer l+2 and copy its misses while
+                               layers l and l+1 wait for theirs (LRU policy, offload steps and
+                               cache_slots >= 3 * top_k * n_tokens of the call; otherwise the call
+                               runs with lookahead 1); 1 = resolve and copy layer l+1 while layer
+                               l's FFN runs; 0 = causal (each layer's copies before its FFN).
+                               Every lookahead gives the same ids, slots, trace and outputs */
     int32_t trace_capacity; /* cache trace records kept on the device (0 = none) */
     int32_t fill_threads;   /* host threads calling the fill callback (0 = all cores) */
     int32_t flags;          /* MOE_FLAG_* */
@@ -269,12 +273,16 @@ typedef struct {
     uint64_t host_tasks;               /* hybrid backend: layer steps with a host share */
     double host_busy_ms;               /* ... summed time from a host task's submission to its end */
     double host_wait_ms;               /* ... time the calling thread waited for host tasks */
-    uint64_t h2d_ns;                   /* time the copy path was busy with miss copies: per layer step
-                                          and copy stream, first copy start to last copy end (GPU
-                                          timestamps), merged over both copy streams */
+    uint64_t h2d_ns;                   /* time the copy path was busy with the miss copies of the
+                                          timed calls (one moe_stack_forward, moe_layer_forward or
+                                          moe_cache_resolve call in 7, all its copies): per layer
+                                          step and copy stream, first copy start to last copy end
+                                          (GPU timestamps), merged over both copy streams */
     uint64_t ffn_ns, ffn_timed;        /* summed duration of the timed layer FFNs and their count: one
-                                          layer FFN in 7 is timed (GPU timestamps around its launches,
-                                          after its copy waits) */
+                                          layer FFN in 17 is timed (GPU timestamps around its
+                                          launches, after its copy waits) */
+    uint64_t h2d_timed_bytes;          /* bytes the copies of the timed calls moved:
+                                          h2d_timed_bytes / h2d_ns is the copy path's rate while busy */
 } moe_counters;
 
 typedef struct {
@@ -288,7 +296,7 @@ typedef struct {
  * how misses are made up for: 16 % / 39 % with LRU against 62 % / 89 % with a
  * static split) and the expert transfer bandwidth (pirouter.ai page, section
  * on how 65 GB runs on a 32 GB GPU: 49.0 GB/s over PCIe 5.0 x16), here as
- * h2d_bytes over h2d_ns.  Counters are cumulative over the context's life,
+ * h2d_timed_bytes over h2d_ns.  Counters are cumulative over the context's life,
  * except k3_ms, k4_ms and ffn_launches (MOE_FLAG_PROFILE), which are harvested
  * and reset on every call. */
 moe_status moe_stats(moe_ctx* ctx, moe_counters* out, moe_trace_rec* buf, size_t cap, size_t* n_out);

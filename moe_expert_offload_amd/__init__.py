@@ -47,7 +47,8 @@ class MoeCounters(ctypes.Structure):
         ("k3_ms", ctypes.c_double), ("k4_ms", ctypes.c_double),
         ("host_experts", ctypes.c_uint64), ("host_tasks", ctypes.c_uint64),
         ("host_busy_ms", ctypes.c_double), ("host_wait_ms", ctypes.c_double),
-        ("h2d_ns", ctypes.c_uint64), ("ffn_ns", ctypes.c_uint64), ("ffn_timed", ctypes.c_uint64)]
+        ("h2d_ns", ctypes.c_uint64), ("ffn_ns", ctypes.c_uint64), ("ffn_timed", ctypes.c_uint64),
+        ("h2d_timed_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -265,23 +265,24 @@ __device__ __forceinline__ uint32_t word(uint4 v, int i) {
 }
 
 // Work unit of this workgroup: (chunk ci, N tile nt).  The grid is sized for the
-// most chunks a step can have; the step's own U units are split into 8
-// contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so every XCD
-// gets an equal share and the N tiles of a chunk, which read the same
-// activation rows, run on one XCD's L2.  Returns false for workgroups past the
-// step's units.
+// most chunks a step can have.  Workgroup b runs on XCD b % 8; chunks are dealt
+// to the XCDs in turn and each XCD runs all N tiles of its chunks one after the
+// other (they read the same activation rows, so those stay in that XCD's L2).
+// Chunks go out in reverse plan order: the shared expert's full chunks, the
+// heaviest, start first and the short routed ones fill the tail.  Returns false
+// for workgroups past the step's units.
 struct Unit {
     int ci, nt, g, nrow, base, g_slot;
 };
 
 __device__ __forceinline__ bool get_unit(const GemmArgs& a, int nt_per_chunk, Unit& u) {
-    const int n_units = a.p.hdr[1] * nt_per_chunk;
-    const int per_xcd = (n_units + 7) >> 3;
-    const int j = blockIdx.x >> 3;
-    const int logical = (blockIdx.x & 7) * per_xcd + j;
-    if (j >= per_xcd || logical >= n_units) return false;
-    u.ci = logical / nt_per_chunk;
-    u.nt = logical - u.ci * nt_per_chunk;
+    const int n_chunks = a.p.hdr[1];
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int cl = j / nt_per_chunk;            // this XCD's cl-th chunk
+    const int k = cl * 8 + x;                   // position in the dealt order
+    if (k >= n_chunks) return false;
+    u.ci = n_chunks - 1 - k;
+    u.nt = j - cl * nt_per_chunk;
     u.g = a.p.chunks[2 * u.ci];
     const int start = a.p.chunks[2 * u.ci + 1];
     const int cnt = a.p.g_cnt[u.g];
@@ -681,7 +682,9 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
     *reinterpret_cast<uint2*>(c.y + (size_t)b * c.H + h) = make_uint2(lo, hi);
 }
 
-static int pad8(long v) { return (int)((v + 7) / 8 * 8); }
+// workgroups for max_chunks chunks of nt units each: eight XCDs x the most
+// chunks one XCD is dealt x nt (the mapping of get_unit)
+static int unit_grid(int max_chunks, int nt) { return (max_chunks + 7) / 8 * 8 * nt; }
 
 // prefill-sized chunks (64 rows): gate/up waves take 2 row tiles with three
 // fragments in flight, down waves 4 row tiles with two, and a down workgroup 3
@@ -696,7 +699,7 @@ int launch_grouped_ffn(GroupArgs& g, GemmArgs& m, CombineArgs& c, void* stream, 
     const int rt1 = big ? RT_GU_BIG : 1, rt2 = big ? RT_D_BIG : 1, spw = big ? SPW_D_BIG : 1;
     const int nt1 = (m.I / 16 + 4 * rt1 - 1) / (4 * rt1);
     const int nt2 = ((m.H / 16 + 4 * rt2 - 1) / (4 * rt2) + spw - 1) / spw;
-    const dim3 g1(pad8((long)m.p.max_chunks * nt1)), g2(pad8((long)m.p.max_chunks * nt2));
+    const dim3 g1(unit_grid(m.p.max_chunks, nt1)), g2(unit_grid(m.p.max_chunks, nt2));
     if (big)
         hipLaunchKernelGGL((k5_gate_up<4, RT_GU_BIG, 3>), g1, dim3(K5_THREADS), 0, st, m);
     else

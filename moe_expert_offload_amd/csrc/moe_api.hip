@@ -11,7 +11,9 @@
 // kernel.  With lookahead 1 the next layer's K1/K2 and copies are issued
 // before the current layer's FFN, so its misses load while the current layer
 // computes (ai.holude.com preflight page, section on long prompts: the next
-// layer's experts load over PCIe while the GPU computes the current one).
+// layer's experts load over PCIe while the GPU computes the current one);
+// lookahead 2 resolves two layers ahead, so the copy queue still holds a layer
+// of misses when a layer without misses passes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,6 +46,10 @@ struct ProfSlot {
 struct TimedPair {
     hipEvent_t ev[2];
 };
+
+// Layer parities of the per-layer buffers (K2's slots and weights, miss lists, copy events): a
+// lookahead-2 stack call has the buffers of layers l, l+1 and l+2 in use at once.
+constexpr int NPAR = 3;
 
 struct moe_ctx {
     moe_config cfg{};
@@ -94,10 +100,12 @@ struct moe_ctx {
     int parity = 0;             // which order buffer is current
     // workspace carve
     float* z = nullptr;
-    int32_t* ids[2] = {nullptr, nullptr};
-    float* w[2] = {nullptr, nullptr};
-    int32_t* slots[2] = {nullptr, nullptr};
-    uint16_t* a[3] = {nullptr, nullptr, nullptr};  // [2] serves moe_expert_forward
+    // per layer parity (NPAR: layers l, l+1, l+2 of a lookahead-2 call are in flight at once);
+    // index NPAR of a and copy_used serves moe_expert_forward
+    int32_t* ids[NPAR] = {};
+    float* w[NPAR] = {};
+    int32_t* slots[NPAR] = {};
+    uint16_t* a[NPAR + 1] = {};
     GroupPlanDev gp{};          // grouped path (max_tokens > 1)
     float* yp = nullptr;
     // host-mapped miss lists
@@ -106,14 +114,14 @@ struct moe_ctx {
     int max_unique = 0;
     int static_T = 0;           // static split: transient slots (2 * max distinct experts per step)
     int64_t seq = 0;
-    hipEvent_t copy_ev[2] = {nullptr, nullptr};    // per parity, on the caller's copy stream
+    hipEvent_t copy_ev[NPAR] = {};                  // per parity, on the caller's copy stream
     hipStream_t ps2 = nullptr;                      // second copy stream (library-owned)
-    hipEvent_t copy_ev2[2] = {nullptr, nullptr};    // per parity, on ps2
-    bool copy_used[3][2] = {};                      // per parity: copies went to ps / ps2
+    hipEvent_t copy_ev2[NPAR] = {};                 // per parity, on ps2
+    bool copy_used[NPAR + 1][2] = {};               // per parity: copies went to ps / ps2
     // token 0's slots and weights of the last miss list read per parity
-    int32_t tok0_slot[2][16] = {};
-    float tok0_w[2][16] = {};
-    bool tok0_valid[2] = {false, false};
+    int32_t tok0_slot[NPAR][16] = {};
+    float tok0_w[NPAR][16] = {};
+    bool tok0_valid[NPAR] = {};
     // host counters
     uint64_t h2d_bytes = 0, h2d_copies = 0, h2d_bounced = 0;
     uint64_t ffn_launches = 0;
@@ -127,6 +135,8 @@ struct moe_ctx {
     std::vector<std::pair<double, double>> h2d_iv;   // harvested, not yet merged (ms from t_ref)
     double h2d_iv_end = -1.0;                        // end of the merged busy time so far (ms)
     double h2d_busy_ms = 0.0;
+    uint64_t h2d_calls = 0, h2d_timed_bytes = 0;     // calls that stage misses; bytes of the timed copies
+    bool h2d_timing = false;                         // the current call's copies are timed
     // Sampled FFN timing (every FFN_SAMPLE-th layer FFN; every one under MOE_FLAG_PROFILE)
     std::vector<TimedPair> ffn_used, ffn_free;
     uint64_t ffn_count = 0, ffn_timed = 0;
@@ -215,7 +225,7 @@ moe_status check_cfg(const moe_config* c, bool allow_auto = false) {
         c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
         c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 0 ||
-        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 1 || c->trace_capacity < 0 ||
+        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 2 || c->trace_capacity < 0 ||
         c->pinned_mb < 0 || c->policy < 0 || c->policy > 1)
         return MOE_EINVAL;
     // the down kernel stages every selected expert's intermediate vector in LDS
@@ -269,10 +279,10 @@ WsPlan plan_workspace(const moe_config& c) {
     const size_t nE = k + (size_t)c.n_shared;
     size_t off = 0;
     p.z = off;     off = align_up(off + B * E * 4, 256);
-    p.ids = off;   off = align_up(off + 2 * B * k * 4, 256);
-    p.w = off;     off = align_up(off + 2 * B * k * 4, 256);
-    p.slots = off; off = align_up(off + 2 * B * k * 4, 256);
-    p.a = off;     off = align_up(off + 3 * B * nE * (size_t)c.inter * 2, 256);
+    p.ids = off;   off = align_up(off + NPAR * B * k * 4, 256);
+    p.w = off;     off = align_up(off + NPAR * B * k * 4, 256);
+    p.slots = off; off = align_up(off + NPAR * B * k * 4, 256);
+    p.a = off;     off = align_up(off + (NPAR + 1) * B * nE * (size_t)c.inter * 2, 256);
     p.grp = p.yp = off;
     p.max_groups = p.max_chunks = 0;
     if (B > 1) {
@@ -468,7 +478,14 @@ moe_status get_pair(moe_ctx* c, std::vector<TimedPair>& free_list, TimedPair& p)
     return MOE_OK;
 }
 
-constexpr int FFN_SAMPLE = 7;           // one layer FFN in this many is timed (co-prime with layer counts)
+// Sampling of the GPU-timed counters (two event records each, a few µs of host time, so not on
+// every layer step): one layer FFN in FFN_SAMPLE (co-prime with the workloads' layer counts, so
+// every layer is sampled), and every copy of one call in H2D_SAMPLE (moe_stack_forward,
+// moe_layer_forward and moe_cache_resolve calls; whole calls, so that the union of the timed
+// intervals carries no bytes of untimed copies, apart from the few that overlap the first and
+// last layer steps of a call)
+constexpr int FFN_SAMPLE = 17;
+constexpr int H2D_SAMPLE = 7;
 constexpr size_t TIMED_PENDING = 256;   // timed pairs kept before the oldest finished ones are harvested
 
 // Copy-path busy time: intervals of the finished timed pairs (all of them when `all`, which
@@ -626,18 +643,23 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
             HIPCHK(c, hipStreamWaitEvent(c->ps2, c->ffn_done[par], 0));
         }
     }
-    bool used[2] = {false, false};
+    bool used[2] = {false, false}, timed_q[2] = {false, false};
     hipStream_t qs[2] = {c->ps, c->ps2};
     int nd = 0;  // direct copies so far: they alternate between the two copy streams
     int ncopy = 0;
+    const bool timed = nm > 0 && c->h2d_timing;
     if (c->h2d_used.size() >= TIMED_PENDING) {
         moe_status st = harvest_h2d(c, false);
         if (st) return st;
     }
-    // the first copy on a stream opens its timed interval (the pair goes to the pending list at
-    // once, so an error return leaks nothing; the context is failed then anyway)
+    size_t pair_of[2] = {0, 0};
+    // the first copy on a stream marks it used and, in a sampled step, opens its timed interval
+    // (the pair goes to the pending list at once, so an error return leaks nothing; the context
+    // is failed then anyway)
     auto open_stream = [&](int q) -> moe_status {
         if (used[q]) return MOE_OK;
+        used[q] = true;
+        if (!timed) return MOE_OK;
         TimedPair tp{};
         moe_status st = get_pair(c, c->h2d_free, tp);
         if (st) return st;
@@ -646,10 +668,10 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
             return set_err(c, MOE_EHIP, "copy timing event record failed");
         }
         c->h2d_used.push_back(tp);
-        used[q] = true;
+        pair_of[q] = c->h2d_used.size() - 1;
+        timed_q[q] = true;
         return MOE_OK;
     };
-    size_t pair_of[2] = {0, 0};
     // pass 0 queues the misses whose blobs are pinned (their DMA starts at once), pass 1 the
     // pageable ones: the host fills each of those into a bounce slot before its DMA, at about the
     // DMA's own rate, so the pinned copies queued ahead keep the link busy during the fills
@@ -667,11 +689,13 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
                            (unsigned long long)c->copies_issued, layer, m.expert);
         const size_t n_sl = (size_t)c->cfg.n_layers * c->cfg.n_experts;
         const size_t src_idx = (c->fault_corrupt_at && c->copies_issued == c->fault_corrupt_at) ? (idx + 1) % n_sl : idx;
-        const int q = c->pinned(idx) ? (nd++ & 1) : 0;
+        // a pool with a pageable part: pageable misses on the caller's copy stream (each DMA waits
+        // for its host fill), pinned ones on the second stream, where they run while the fills
+        // hold the first; an all-pinned pool alternates its copies over both streams
+        const int q = !c->pinned(idx) ? 0 : (c->n_pin < c->n_blobs ? 1 : (nd++ & 1));
         if (!used[q]) {
             moe_status st = open_stream(q);
             if (st) return st;
-            pair_of[q] = c->h2d_used.size() - 1;
         }
         if (c->pinned(idx)) {
             HIPCHK(c, hipMemcpyAsync(dst, c->blob_src(src_idx), blob, hipMemcpyHostToDevice, qs[q]));
@@ -681,7 +705,8 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         }
     }
     for (int q = 0; q < 2; ++q)
-        if (used[q]) HIPCHK(c, hipEventRecord(c->h2d_used[pair_of[q]].ev[1], qs[q]));
+        if (timed_q[q]) HIPCHK(c, hipEventRecord(c->h2d_used[pair_of[q]].ev[1], qs[q]));
+    if (timed) c->h2d_timed_bytes += (uint64_t)ncopy * blob;
     if (used[0]) HIPCHK(c, hipEventRecord(c->copy_ev[par], c->ps));
     if (used[1]) HIPCHK(c, hipEventRecord(c->copy_ev2[par], c->ps2));
     c->copy_used[par][0] = used[0];
@@ -731,7 +756,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
         c->host_has[par] = false;
         yh = c->yh + (size_t)layer * kHostMaxTokens * c->cfg.hidden;
     }
-    if (n_miss > 0 && par < 2) {
+    if (n_miss > 0 && par < NPAR) {
         if (c->copy_used[par][0]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev[par], 0));
         if (c->copy_used[par][1]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_ev2[par], 0));
     }
@@ -830,7 +855,7 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
     f.I = c->cfg.inter;
     f.H = c->cfg.hidden;
     f.C = c->cfg.cache_slots;
-    f.karg = (B == 1 && !slots_dev && par < 2 && c->tok0_valid[par]) ? 1 : 0;
+    f.karg = (B == 1 && !slots_dev && par < NPAR && c->tok0_valid[par]) ? 1 : 0;
     if (f.karg) {
         // the experts in GPU slots, in rank order (hybrid steps leave some to the host)
         int kk = 0;
@@ -1015,12 +1040,12 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     uint8_t* ws = (uint8_t*)workspace_dev;
     const size_t Bk = (size_t)cfg->max_tokens * cfg->top_k;
     c->z = (float*)(ws + wp.z);
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < NPAR; ++p) {
         c->ids[p] = (int32_t*)(ws + wp.ids) + p * Bk;
         c->w[p] = (float*)(ws + wp.w) + p * Bk;
         c->slots[p] = (int32_t*)(ws + wp.slots) + p * Bk;
     }
-    for (int p = 0; p < 3; ++p) c->a[p] = (uint16_t*)(ws + wp.a) + (size_t)p * cfg->max_tokens * c->nE * cfg->inter;
+    for (int p = 0; p <= NPAR; ++p) c->a[p] = (uint16_t*)(ws + wp.a) + (size_t)p * cfg->max_tokens * c->nE * cfg->inter;
     if (cfg->max_tokens > 1) {
         int32_t* g = (int32_t*)(ws + wp.grp);
         c->gp.max_groups = wp.max_groups;
@@ -1076,11 +1101,11 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
     where = "miss list allocation";
     c->max_unique = (int)std::min<int64_t>((int64_t)cfg->max_tokens * cfg->top_k, E);
     c->ml_stride = align_up(sizeof(MissList) + sizeof(MissEntry) * (size_t)c->max_unique, 256);
-    if (hipHostMalloc((void**)&c->ml_mem, 2 * c->ml_stride, hipHostMallocMapped | hipHostMallocCoherent) !=
+    if (hipHostMalloc((void**)&c->ml_mem, NPAR * c->ml_stride, hipHostMallocMapped | hipHostMallocCoherent) !=
         hipSuccess)
         return bail(MOE_ENOMEM);
-    memset(c->ml_mem, 0, 2 * c->ml_stride);
-    for (int p = 0; p < 2; ++p) miss_list(c, p)->seq = -1;
+    memset(c->ml_mem, 0, NPAR * c->ml_stride);
+    for (int p = 0; p < NPAR; ++p) miss_list(c, p)->seq = -1;
     for (auto& e : c->copy_ev)
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return bail(MOE_EHIP);
     // the reference point of the copy-path timing (the GPU clock is shared by all streams)
@@ -1233,6 +1258,7 @@ moe_status moe_cache_resolve(moe_ctx* c, int32_t step, int32_t layer, const int3
                              int32_t n_tokens, int32_t* slots_dev, int32_t* n_miss_out) {
     moe_status st = check_call(c, n_tokens);
     if (st) return st;
+    c->h2d_timing = (c->h2d_calls++ % H2D_SAMPLE) == 0;
     if (layer < 0 || layer >= c->cfg.n_layers || !ids_dev) return set_err(c, MOE_EINVAL, "bad layer or ids");
     st = launch_resolve(c, step, layer, false, ids_dev, n_tokens, 0, slots_dev, nullptr, nullptr);
     if (st) return st;
@@ -1251,6 +1277,7 @@ moe_status moe_layer_forward(moe_ctx* c, int32_t step, int32_t layer, const void
                              void* y, int32_t* ids_out, float* w_out) {
     moe_status st = check_call(c, n_tokens);
     if (st) return st;
+    c->h2d_timing = (c->h2d_calls++ % H2D_SAMPLE) == 0;
     if (layer < 0 || layer >= c->cfg.n_layers || !x || !y) return set_err(c, MOE_EINVAL, "bad layer or buffers");
     if ((st = hyb_begin(c, x, 0, 1, n_tokens))) return st;
     if ((st = launch_route(c, layer, x, n_tokens))) return st;
@@ -1264,6 +1291,7 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
                              void* y, int64_t ys, int32_t* ids_out, float* w_out) {
     moe_status st = check_call(c, n_tokens);
     if (st) return st;
+    c->h2d_timing = (c->h2d_calls++ % H2D_SAMPLE) == 0;
     if (!x || !y) return set_err(c, MOE_EINVAL, "null buffers");
     const int L = c->cfg.n_layers;
     const size_t kB = (size_t)n_tokens * c->cfg.top_k;
@@ -1321,6 +1349,43 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     // another 1 % at gpt-oss shape, 10 % at Qwen3.6 shape).
     RouteStreamGuard guard{c};
     const bool whole_pool = n_tokens == 1 && (int64_t)c->cfg.cache_slots >= (int64_t)L * c->cfg.n_experts;
+    // Lookahead 2 (LRU, C >= 3 k B): K1/K2 of layer l+2 are enqueued before layer l's FFN, so
+    // they run right after layer l-1's FFN and the copies of two layers are queued while a
+    // layer's FFN waits for its own.  When layer l's copies are issued the FFNs of layers l-2
+    // and l-1 may still be pending.  The step's victims are the least recently used slots outside
+    // its own hits; the slots touched by the two previous steps (at most 2 k B) are more recent
+    // than every slot they did not touch, and the step's hits and misses number at most k B, so
+    // with C >= 3 k B every victim was last used three or more steps back, by an FFN that has
+    // finished (stream order: layer l's resolve runs after layer l-3's FFN).  The resolve
+    // sequence, and so every result, is the same as with lookahead 1 or 0.
+    const bool la2 = c->cfg.lookahead == 2 && !whole_pool && c->cfg.policy == MOE_POLICY_LRU &&
+                     (int64_t)c->cfg.cache_slots >= 3 * (int64_t)c->cfg.top_k * n_tokens;
+    if (la2) {
+        int64_t seq_par[NPAR] = {};
+        if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
+        if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
+        seq_par[0] = c->seq;
+        if (L > 1) {
+            if ((st = launch_route(c, 1, xl(1), n_tokens))) return st;
+            if ((st = launch_resolve(c, step, 1, true, nullptr, n_tokens, 1, nullptr, idl(1), wl(1)))) return st;
+            seq_par[1] = c->seq;
+        }
+        for (int l = 0; l < L; ++l) {
+            const int par = l % NPAR;
+            int nm = 0;
+            if ((st = stage_misses(c, l, par, seq_par[par], &nm))) return st;
+            if (l + 2 < L) {
+                const int np = (l + 2) % NPAR;
+                if ((st = launch_route(c, l + 2, xl(l + 2), n_tokens))) return st;
+                if ((st = launch_resolve(c, step, l + 2, true, nullptr, n_tokens, np, nullptr, idl(l + 2),
+                                         wl(l + 2))))
+                    return st;
+                seq_par[np] = c->seq;
+            }
+            if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
+        }
+        return MOE_OK;
+    }
     if (!whole_pool) {
         if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
         if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
@@ -1404,7 +1469,7 @@ moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t 
     if (st) return st;
     if (layer < 0 || layer >= c->cfg.n_layers || !x || !y || !slots_dev || !w_dev)
         return set_err(c, MOE_EINVAL, "bad layer or buffers");
-    return launch_ffn_layer(c, layer, x, n_tokens, 2, y, 0, slots_dev, w_dev);
+    return launch_ffn_layer(c, layer, x, n_tokens, NPAR, y, 0, slots_dev, w_dev);
 }
 
 moe_status moe_expert_forward_noalloc(const moe_config* cfg, const void* arena, const void* shared_blob,
@@ -1525,6 +1590,7 @@ moe_status moe_stats(moe_ctx* c, moe_counters* out, moe_trace_rec* buf, size_t c
         out->h2d_ns = (uint64_t)llround(c->h2d_busy_ms * 1e6);
         out->ffn_ns = (uint64_t)llround(c->ffn_ms * 1e6);
         out->ffn_timed = c->ffn_timed;
+        out->h2d_timed_bytes = c->h2d_timed_bytes;
     }
     c->ffn_launches = 0;
     c->k3_ms = c->k4_ms = 0;

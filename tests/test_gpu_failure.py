@@ -154,20 +154,24 @@ def test_bad_fault_spec_is_rejected_at_init():
 
 
 def test_copy_and_ffn_timing_counters():
-    """h2d_ns: the copy path's busy time (merged over both copy streams); ffn_ns / ffn_timed: one
-    layer FFN in seven timed.  Both filled without MOE_FLAG_PROFILE."""
+    """h2d_ns / h2d_timed_bytes: the copy path's busy time (merged over both copy streams) and the
+    bytes moved in it, over every copy of one stack call in seven; ffn_ns / ffn_timed: one layer
+    FFN in 17 timed.  Both filled without MOE_FLAG_PROFILE."""
     wl = dataclasses.replace(synth.WORKLOADS["toy"], cache_slots=4)
-    X = synth.decode_inputs(wl)[:21]
+    X = synth.decode_inputs(wl)[:40]
     m, _ = make_moe(wl)
     run_stack(m, wl, X)
     cnt, _ = m.stats()
     launches = X.shape[0] * wl.n_layers
-    assert cnt["ffn_timed"] == (launches + 6) // 7
+    assert cnt["ffn_timed"] == (launches + 16) // 17
     assert cnt["ffn_ns"] > 0 and cnt["ffn_ns"] / cnt["ffn_timed"] < 5e6
     assert cnt["h2d_copies"] > 0 and cnt["h2d_ns"] > 0
-    gbps = cnt["h2d_bytes"] / cnt["h2d_ns"]
+    assert 0 < cnt["h2d_timed_bytes"] < cnt["h2d_bytes"]
+    assert cnt["h2d_timed_bytes"] % wl.blob_bytes == 0
+    gbps = cnt["h2d_timed_bytes"] / cnt["h2d_ns"]
     assert 0.05 < gbps < 80.0, gbps
     # cumulative: a second stats call without work reports the same figures
     cnt2, _ = m.stats()
-    assert (cnt2["h2d_ns"], cnt2["ffn_ns"], cnt2["ffn_timed"]) == (cnt["h2d_ns"], cnt["ffn_ns"], cnt["ffn_timed"])
+    keys = ("h2d_ns", "h2d_timed_bytes", "ffn_ns", "ffn_timed")
+    assert tuple(cnt2[k] for k in keys) == tuple(cnt[k] for k in keys)
     m.close()

@@ -60,13 +60,45 @@ def test_toy_decode_all_outputs():
 def test_lookahead_and_causal_are_bitwise_equal():
     wl = synth.WORKLOADS["toy"]
     X = synth.decode_inputs(wl)[:24]
-    m1, _ = make_moe(wl, lookahead=1)
-    _, _, y1 = run_stack(m1, wl, X)
-    m1.close()
-    m0, _ = make_moe(wl, lookahead=0)
-    _, _, y0 = run_stack(m0, wl, X)
-    m0.close()
-    np.testing.assert_array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    ys = []
+    for la in (2, 1, 0):
+        m, _ = make_moe(wl, lookahead=la)
+        _, _, y = run_stack(m, wl, X)
+        m.close()
+        ys.append(y)
+    for y in ys[1:]:
+        np.testing.assert_array_equal(ys[0].view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_lookahead2_deep_stack_at_its_cache_bound_matches_causal_and_oracle(B):
+    """Lookahead 2 enqueues the resolve of layer l+2 before layer l's FFN, so layer l+2's copies can
+    land while the FFNs of layers l and l+1 are still pending; the library takes it when
+    C >= 3 k B, where a step's LRU victims are always older than the two steps before it.  Eight
+    layers at exactly C = 3 k B (evictions on almost every step), B tokens per step: ids, weights,
+    trace, final cache state and outputs equal the causal schedule's bit for bit and the oracle's
+    (outputs within tolerance, every step and layer)."""
+    k = 2
+    wl = synth.Workload(f"la2_l8_b{B}", 8, 16, k, 0, 256, 512, 3 * k * B, 24, B, 0.9, seed=23)
+    X = synth.decode_inputs(wl)
+    runs = []
+    for la in (2, 0):
+        m, _ = make_moe(wl, lookahead=la)
+        ids, w, y = run_stack(m, wl, X)
+        _, recs = m.stats(trace_cap=1 << 16)
+        if la == 2:
+            points = [(t, l, b) for t in range(X.shape[0]) for l in range(wl.n_layers) for b in range(B)]
+            ref = oracle.decode_trace(wl, synth.router_weights(wl), X)
+            assert ref["counters"]["evictions"] > X.shape[0] * wl.n_layers // 2
+            _check_run(wl, X, ids, w, y, recs, m, points, ref=ref)
+        runs.append((ids, w, y, trace_tuples(recs), m.cache_state()))
+        m.close()
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    np.testing.assert_array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32))
+    assert runs[0][3] == runs[1][3]
+    for u, v in zip(runs[0][4], runs[1][4]):
+        np.testing.assert_array_equal(u, v)
 
 
 def test_whole_pool_cache_route_stream_matches_causal_and_oracle():
