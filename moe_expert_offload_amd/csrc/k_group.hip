@@ -19,7 +19,8 @@
 //  k5_gate_up  per (chunk, 64*RT intermediate rows): gate and up projections
 //              of the chunk's tokens on the matrix cores, SwiGLU, a (bf16);
 //  k5_down     per (chunk, SPW slices of 64*RT output rows): down projection,
-//              unweighted expert outputs (fp32) per row;
+//              unweighted expert outputs per row, rounded to bf16 (halves the
+//              bytes that k5_down writes and k5_combine reads back);
 //  k5_combine  per (token, 1024 outputs): routing-weighted sum over the
 //              token's experts in rank order, plus the shared expert, bf16.
 //
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
     const int nit = (NB + 3) >> 2;
     with_tiles<NTT>(ntt, [&](auto nt_c) {
         constexpr int NT = decltype(nt_c)::value;
-        auto issue = [&](int it, GuFrag<NT, RT>& f) {
+        auto issue = [&](int it, GuFrag<NT, RT>& f) __attribute__((always_inline)) {
             {
                 const int b = 4 * it + st.q;
                 const int blk = b < NB ? b : NB - 1;
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
             }
         };
         // MFMA step s4 (elements 8*s4.. of each lane group's block) of all NT token tiles
-        auto mma = [&](const bf16x8_t* wg, const bf16x8_t* wu, const uint4* xb, int s4) {
+        auto mma = [&](const bf16x8_t* wg, const bf16x8_t* wu, const uint4* xb, int s4) __attribute__((always_inline)) {
             bf16x8_t xo[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) xo[m] = as_bf16x8(xb[x_cell(m * 16 + r, q, s4)]);
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_gate_up(GemmArgs a) {
                 }
         };
         // one k-iteration on fragment f; `next` refills f with a later iteration's loads
-        auto step = [&](int it, GuFrag<NT, RT>& f, uint4* xb, auto&& next) {
+        auto step = [&](int it, GuFrag<NT, RT>& f, uint4* xb, auto&& next) __attribute__((always_inline)) {
             const bool pin = (4 * it + st.q) < NB;
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
@@ -546,16 +547,18 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
         for (int m = 0; m < NTT; ++m) acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // tile j of slice s0 + sl (clamped to tile 0 past the output), and whether it is real
     auto tile_of = [&](int sl, int j) { return ((s0 + sl) * 4 + w) * RT + j; };
-    auto store = [&](int sl) {
+    auto store = [&](int sl) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < NTT; ++m) {
             const int row = s_row[m * 16 + r];
 #pragma unroll
             for (int j = 0; j < RT; ++j) {
                 const int t = tile_of(sl, j);
+                const f32x4_t v = acc[j][m];
+                const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
                 if (row >= 0 && t < n_tiles)
-                    *reinterpret_cast<float4*>(a.yp + (size_t)row * a.H + t * 16 + 4 * q) =
-                        make_float4(acc[j][m][0], acc[j][m][1], acc[j][m][2], acc[j][m][3]);
+                    *reinterpret_cast<uint2*>(a.yp + (size_t)row * a.H + t * 16 + 4 * q) = make_uint2(lo, hi);
                 acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
         constexpr int NT = decltype(nt_c)::value;
         // loads of pipeline step f (slice f / nit, k-iteration f % nit); steps
         // past the end re-read the last one (in bounds, masked in `step`)
-        auto issue = [&](int f, DnFrag<NT, RT>& fr) {
+        auto issue = [&](int f, DnFrag<NT, RT>& fr) __attribute__((always_inline)) {
             const int fc = f < F ? f : F - 1;
             const int sl = fc / nit, it = fc - sl * nit;
             {
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
                 fr.sc[j] = dsc0[t8 + (size_t)ib * 8];
             }
         };
-        auto mma = [&](const bf16x8_t* wd, const uint4* xb, int s4) {
+        auto mma = [&](const bf16x8_t* wd, const uint4* xb, int s4) __attribute__((always_inline)) {
             bf16x8_t ao[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) ao[m] = as_bf16x8(xb[x_cell(m * 16 + r, q, s4)]);
@@ -593,7 +596,7 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
                 for (int j = 0; j < RT; ++j)
                     acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd[j], ao[m], acc[j][m], 0, 0, 0);
         };
-        auto step = [&](int f, DnFrag<NT, RT>& fr, uint4* xb, auto&& next) {
+        auto step = [&](int f, DnFrag<NT, RT>& fr, uint4* xb, auto&& next) __attribute__((always_inline)) {
             const bool live = f < F;
             const int sl = f / nit, it = f - sl * nit;
             const bool pin = live && (4 * it + st.q) < NBI;
@@ -640,6 +643,13 @@ __global__ __launch_bounds__(K5_THREADS, 2) void k5_down(GemmArgs a) {
 }
 
 // ---------------------------------------------------------- k5_combine --
+// outputs h .. h+3 of expert-output row `row` (bf16) as floats
+__device__ __forceinline__ float4 yp4(const CombineArgs& c, int row, int h) {
+    const uint2 v = *reinterpret_cast<const uint2*>(c.yp + (size_t)row * c.H + h);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                       __uint_as_float(v.y & 0xFFFF0000u));
+}
+
 // grid (ceil(H / 1024), B), 256 threads, 4 outputs per thread
 __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* hdr) {
     const int b = blockIdx.y;
@@ -654,7 +664,7 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
             const int row = b * c.k + j;
             if (c.host_rows && c.slots[row] < 0) continue;  // computed by the host
             const float wj = c.w[row];
-            const float4 v = *reinterpret_cast<const float4*>(c.yp + (size_t)row * c.H + h);
+            const float4 v = yp4(c, row, h);
             acc.x += wj * v.x;
             acc.y += wj * v.y;
             acc.z += wj * v.z;
@@ -662,7 +672,7 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
         }
         for (int s = 0; s < c.n_shared; ++s) {
             const int row = c.B * c.k + s * c.B + b;
-            const float4 v = *reinterpret_cast<const float4*>(c.yp + (size_t)row * c.H + h);
+            const float4 v = yp4(c, row, h);
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;

@@ -107,7 +107,7 @@ struct moe_ctx {
     int32_t* slots[NPAR] = {};
     uint16_t* a[NPAR + 1] = {};
     GroupPlanDev gp{};          // grouped path (max_tokens > 1)
-    float* yp = nullptr;
+    uint16_t* yp = nullptr;     // bf16 expert outputs, one row per (token, expert)
     // host-mapped miss lists
     uint8_t* ml_mem = nullptr;
     size_t ml_stride = 0;
@@ -294,7 +294,7 @@ WsPlan plan_workspace(const moe_config& c) {
         p.grp = off;
         off = align_up(off + 4 * 4 + 3 * (size_t)p.max_groups * 4 + 2 * (size_t)p.max_chunks * 4 +
                            B * nE * 4, 256);
-        p.yp = off;    off = align_up(off + B * nE * (size_t)c.hidden * 4, 256);
+        p.yp = off;    off = align_up(off + B * nE * (size_t)c.hidden * 2, 256);
     }
     p.total = off;
     return p;
@@ -1056,7 +1056,7 @@ moe_status moe_init_pool(const moe_config* cfg, moe_fill_fn fill, void* user,
         c->gp.g_cnt = c->gp.g_off + wp.max_groups;
         c->gp.chunks = c->gp.g_cnt + wp.max_groups;
         c->gp.perm = c->gp.chunks + 2 * (size_t)wp.max_chunks;
-        c->yp = (float*)(ws + wp.yp);
+        c->yp = (uint16_t*)(ws + wp.yp);
     }
 
     // device cache state

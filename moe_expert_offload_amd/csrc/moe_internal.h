@@ -173,14 +173,14 @@ struct GemmArgs {
     const uint8_t* shared;  // [L][n_shared] blobs
     const uint16_t* x;      // [B][H] (gate/up input)
     uint16_t* a;            // [B*nE][I] bf16, rows = row ids
-    float* yp;              // [B*nE][H] fp32, rows = row ids (unweighted expert outputs)
+    uint16_t* yp;           // [B*nE][H] bf16, rows = row ids (unweighted expert outputs)
     size_t blob_bytes, d_codes_off, d_scales_off;
     int B, k, n_shared, layer, H, I, NB, NBI, gm;
     int nt;                 // N tiles (of 64 output rows) per chunk
 };
 
 struct CombineArgs {
-    const float* yp;
+    const uint16_t* yp;     // [B*nE][H] bf16 expert outputs
     const float* w;         // [B][k]
     const int32_t* slots;   // [B][k]
     uint16_t* y;            // [B][H] bf16
