@@ -42,6 +42,33 @@ __device__ __forceinline__ float fold8(uint4 wv, uint4 xv, float p) {
     return p;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The xor butterfly over the 64 lanes: p + (p of lane ^ d) for d = 32, 16, 8, 4, 2, 1, in that
+// order, so every lane ends with the same sum.  The partner values come from the gfx950 lane
+// swaps (d = 32, 16) and DPP (d = 8: rotate a row of 16 by 8; d = 4: mirror each half-row, then
+// reverse each quad; d = 2, 1: quad permutes): register moves instead of LDS round trips.  A
+// lane adds its own value and its partner's in whichever order the swap returns them, which
+// gives the same bits since IEEE addition is commutative.
+__device__ __forceinline__ float xor_butterfly(float p) {
+    {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+        p = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+        p = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    p = p + dpp_f32<0x128>(p);                      // row_ror:8
+    p = p + dpp_f32<0x1B>(dpp_f32<0x141>(p));       // row_half_mirror, then quad_perm(3,2,1,0)
+    p = p + dpp_f32<0x4E>(p);                       // quad_perm(2,3,0,1)
+    p = p + dpp_f32<0xB1>(p);                       // quad_perm(1,0,3,2)
+    return p;
+}
+
 // order-preserving 64-bit key: larger logit first, then lower expert index
 __device__ __forceinline__ uint64_t topk_key(float z, int e) {
     uint32_t u = __float_as_uint(z + 0.0f);  // -0 -> +0
@@ -91,17 +118,20 @@ __global__ __launch_bounds__(64) void k1_logits(K1Args a) {
         for (int i = 0; i < K1_BATCH; ++i)
             if (g0 + 64 * i < ng) p = fold8(wv[i], xv[i], p);
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+    p = xor_butterfly(p);
     if (lane == 0) a.z[(size_t)b * a.E + e] = p;
 }
 
 // Many tokens (a prefill chunk, more than 16): a workgroup of 4 waves takes 16
 // experts x 16 tokens; each wave keeps its 4 experts' router rows in registers
 // (G groups of 8 bf16 per lane: lane l holds groups g = l + 64 i, i < G) and
-// walks the 16 tokens, so each router row is read once per token tile instead
-// of once per token.  Every logit is still lane l's fold over its groups in increasing g,
-// then the xor butterfly: the same bits as k1_logits.
+// walks the 16 tokens two at a time, so each router row is read once per token
+// tile instead of once per token.  Every logit is still lane l's fold over its
+// groups in increasing g (a group past the row leaves the fold unchanged), then
+// the xor butterfly: the same bits as k1_logits.  The rows stay packed bf16
+// across the token loop (converted at each use): converted once they would take
+// 4 x G x 8 fp32 registers and leave one wave per SIMD.  Lanes 0..7 collect the
+// 8 logits of a token pair and store them together.
 constexpr int K1T_EXP = 4, K1T_TOK = 16;
 
 template <int G>
@@ -111,6 +141,9 @@ __global__ __launch_bounds__(256) void k1_logits_tiled(K1Args a) {
     const int b0 = blockIdx.y * K1T_TOK;
     const int ng = a.H >> 3;
     uint4 wr[K1T_EXP][G];
+    bool gv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) gv[i] = lane + 64 * i < ng;
 #pragma unroll
     for (int j = 0; j < K1T_EXP; ++j) {
         const int e = e0 + j < a.E ? e0 + j : a.E - 1;
@@ -121,8 +154,8 @@ __global__ __launch_bounds__(256) void k1_logits_tiled(K1Args a) {
             wr[j][i] = *reinterpret_cast<const uint4*>(W + (size_t)(g < ng ? g : 0) * 8);
         }
     }
-    // the next token's activations are loaded while the current one is folded
-    auto load_x = [&](int b, uint4* xv) {
+    // the next token pair's activations are loaded while the current pair is folded
+    auto load_x = [&](int b, uint4* xv) __attribute__((always_inline)) {
         const uint16_t* x = a.x + (size_t)(b < a.B ? b : a.B - 1) * a.H;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -130,26 +163,40 @@ __global__ __launch_bounds__(256) void k1_logits_tiled(K1Args a) {
             xv[i] = *reinterpret_cast<const uint4*>(x + (size_t)(g < ng ? g : 0) * 8);
         }
     };
-    auto logits = [&](int b, const uint4* xv) {
+    float out = 0.0f;   // lane k < 8: logit of (token k / 4, expert k % 4) of the current pair
+    auto logits = [&](int t, const uint4* xv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < K1T_EXP; ++j)
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                asm volatile("" : "+v"(wr[j][i].x), "+v"(wr[j][i].y), "+v"(wr[j][i].z), "+v"(wr[j][i].w));
 #pragma unroll
         for (int j = 0; j < K1T_EXP; ++j) {
             float p = 0.0f;
 #pragma unroll
-            for (int i = 0; i < G; ++i)
-                if (lane + 64 * i < ng) p = fold8(wr[j][i], xv[i], p);
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
-            if (lane == 0 && e0 + j < a.E && b < a.B) a.z[(size_t)b * a.E + e0 + j] = p;
+            for (int i = 0; i < G; ++i) {
+                const float q = fold8(wr[j][i], xv[i], p);
+                p = gv[i] ? q : p;
+            }
+            p = xor_butterfly(p);
+            out = lane == (t & 1) * K1T_EXP + j ? p : out;
+        }
+    };
+    auto store_pair = [&](int t) __attribute__((always_inline)) {
+        if (lane < 2 * K1T_EXP) {
+            const int b = b0 + t + lane / K1T_EXP, e = e0 + lane % K1T_EXP;
+            if (b < a.B && e < a.E) a.z[(size_t)b * a.E + e] = out;
         }
     };
     uint4 xa[G], xb[G];
     load_x(b0, xa);
     load_x(b0 + 1, xb);
     for (int t = 0; t < K1T_TOK; t += 2) {
-        logits(b0 + t, xa);
+        logits(t, xa);
         load_x(b0 + t + 2, xa);
-        logits(b0 + t + 1, xb);
+        logits(t + 1, xb);
         load_x(b0 + t + 3, xb);
+        store_pair(t);
     }
 }
 
