@@ -121,6 +121,23 @@ __device__ __forceinline__ float expert_weight(const FfnArgs& a, int b, int j) {
 
 constexpr int FFN_THREADS = 256;
 
+// v + (v of lane ^ 8), then ^ 16, then ^ 32: the sum of a row's segments held by lanes r + 8i.
+// Partners come from DPP (rotate a row of 16 by 8) and the gfx950 lane swaps instead of LDS
+// round trips; each step adds the same two values as a shuffle would (in either order, which
+// gives the same bits).
+__device__ __forceinline__ float sum_lanes_8_16_32(float v) {
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return v;
+}
+
 // Activations are staged into LDS in lds_pos() order, one 64-byte block (32
 // bf16 values) per thread and step, in two halves around the weight loads:
 // stage_first() loads a thread's first block into registers; the caller then
@@ -220,12 +237,8 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
         compute(t0);
     }
     // segments of a row: lanes r + 8i of every compute wave
-    g += __shfl_xor(g, 8);
-    g += __shfl_xor(g, 16);
-    g += __shfl_xor(g, 32);
-    u += __shfl_xor(u, 8);
-    u += __shfl_xor(u, 16);
-    u += __shfl_xor(u, 32);
+    g = sum_lanes_8_16_32(g);
+    u = sum_lanes_8_16_32(u);
     if (lane < GR) {
         red[(w * GR + r) * 2] = g;
         red[(w * GR + r) * 2 + 1] = u;
@@ -311,9 +324,7 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
         compute(t0);
     }
     // segments of an output row: lanes r + 8i of every compute wave
-    acc += __shfl_xor(acc, 8);
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
+    acc = sum_lanes_8_16_32(acc);
     if (lane < 8) red[w * 8 + r] = acc;
     __syncthreads();
     if (tid < 8) {

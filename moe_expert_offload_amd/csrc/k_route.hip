@@ -82,13 +82,42 @@ __device__ __forceinline__ float topk_key_logit(uint64_t key) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
+// lane permutations inside a row of 16 lanes (DPP)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+    const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+    return o > v ? o : v;
+}
+
+// the larger of a lane's value and its partner's after a lane swap: each lane gets its own value
+// and its partner's back as the swap's two results, in either order
+__device__ __forceinline__ uint64_t max_swapped_u64(uint32_t lo0, uint32_t hi0, uint32_t lo1, uint32_t hi1) {
+    const uint64_t a = ((uint64_t)hi0 << 32) | lo0, b = ((uint64_t)hi1 << 32) | lo1;
+    return a > b ? a : b;
+}
+
+// maximum over the wave, in every lane, in register moves only: DPP inside each row of 16, then
+// the gfx950 lane swaps across rows (16) and halves (32).  A maximum does not depend on the order
+// in which values meet, so any exchange pattern gives the same result.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, d);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
+    v = max_dpp_u64<0xB1>(v);   // quad_perm(1,0,3,2): lane ^ 1
+    v = max_dpp_u64<0x4E>(v);   // quad_perm(2,3,0,1): lane ^ 2
+    v = max_dpp_u64<0x141>(v);  // row_half_mirror: the other quad of each 8
+    v = max_dpp_u64<0x140>(v);  // row_mirror: the other 8 of each 16
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_swapped_u64(lo[0], hi[0], lo[1], hi[1]);
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_swapped_u64(lo[0], hi[0], lo[1], hi[1]);
     }
     return v;
 }
@@ -257,10 +286,10 @@ __device__ void wave_topk(const K2Args& a, int b, int32_t* s_ids = nullptr, floa
     }
     // softmax over the k selected logits (FP32); lane j holds rank j
     float zj = lane < a.k ? topk_key_logit(my_key) : 0.0f;
-    float z0 = __shfl(zj, 0);
+    float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), 0));
     float ej = lane < a.k ? expf(zj - z0) : 0.0f;
     float den = 0.0f;
-    for (int j = 0; j < a.k; ++j) den += __shfl(ej, j);
+    for (int j = 0; j < a.k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej), j));
     if (lane < a.k) {
         float wj = ej / den;
         size_t o = (size_t)b * a.k + lane;
@@ -554,34 +583,6 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
 // most k order entries are hit slots and the nm victims (the first nm non-hit
 // entries) are among the first k entries of the order.
 
-// lane permutations inside a row of 16 lanes (DPP)
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
-    const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
-    return o > v ? o : v;
-}
-
-// maximum over the wave, in every lane
-__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
-    v = max_dpp_u64<0xB1>(v);   // quad_perm(1,0,3,2): lane ^ 1
-    v = max_dpp_u64<0x4E>(v);   // quad_perm(2,3,0,1): lane ^ 2
-    v = max_dpp_u64<0x141>(v);  // row_half_mirror: the other quad of each 8
-    v = max_dpp_u64<0x140>(v);  // row_mirror: the other 8 of each 16
-#pragma unroll
-    for (int d = 16; d <= 32; d <<= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, d);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 __device__ __forceinline__ int lane_i32(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
 __device__ __forceinline__ float lane_f32(float v, int j) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const
                     best = key[c];
                     bc = c;
                 }
-            const uint64_t wbest = wave_max_u64_dpp(best);
+            const uint64_t wbest = wave_max_u64(best);
             if (bc >= 0 && best == wbest) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
