@@ -224,6 +224,21 @@ moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev,
                              int32_t n_tokens, void* y_bf16_dev, int64_t y_layer_stride,
                              int32_t* ids_dev_out, float* w_dev_out);
 
+/* Router logits of one layer.
+ * Passage: pirouter.ai "FreeToken x RTX 5090 -- 120B MoE が 127 tok/s、その請求書", section on
+ * the mechanism: the router picks the experts a token uses and the cache follows that choice.
+ * The pages fix neither the logit precision nor the summation order; the library computes
+ * z[t][e] = sum_i x[t][i] * W[e][i] in FP32 in one fixed order (element i goes to lane
+ * (i / 8) mod 64, each lane adds its products in increasing i, then an xor butterfly over the
+ * 64 lanes, d = 32, 16, ..., 1), the same kernels and bits behind the top-k of
+ * moe_layer_forward and moe_stack_forward (one kernel up to 16 tokens, a tiled one above).
+ * x_bf16_dev [n_tokens][H] bf16 (device); z_f32_dev_out [n_tokens][E] float (device, owned by
+ * the caller), enqueued on the compute stream.  Nothing in the cache changes.
+ * Errors: MOE_EINVAL (layer outside [0, L), NULL buffers, n_tokens outside [1, max_tokens]),
+ * MOE_ESTATE (after a sticky failure), MOE_EHIP (launch failure). */
+moe_status moe_router_logits(moe_ctx* ctx, int32_t layer, const void* x_bf16_dev, int32_t n_tokens,
+                             float* z_f32_dev_out);
+
 /* Expert FFN of one layer with caller-resolved slots (e.g. from moe_cache_resolve):
  * y = sum_j w_j * FFN(slot_j)(x) + shared(x), on the compute stream (the same
  * kernels as moe_layer_forward for that token count).  slots_dev [n_tokens][k]

@@ -95,6 +95,8 @@ _lib.moe_stack_forward.restype = _st
 _lib.moe_stack_forward.argtypes = [_P, _I32, _P, ctypes.c_int64, _I32, _P, ctypes.c_int64, _P, _P]
 _lib.moe_expert_forward.restype = _st
 _lib.moe_expert_forward.argtypes = [_P, _I32, _P, _I32, _P, _P, _P]
+_lib.moe_router_logits.restype = _st
+_lib.moe_router_logits.argtypes = [_P, _I32, _P, _I32, _P]
 _lib.moe_expert_forward_noalloc.restype = _st
 _lib.moe_expert_forward_noalloc.argtypes = [ctypes.POINTER(MoeConfig), _P, _P, _P, _I32, _P, _P, _P, _P]
 _lib.moe_stats.restype = _st
@@ -111,7 +113,7 @@ _lib.moe_last_error.argtypes = [_P]
 EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_host_expert_batch",
             "moe_hybrid_split",
             "moe_select_backend", "moe_calibrate_backend", "moe_set_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
-            "moe_expert_forward", "moe_expert_forward_noalloc", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
+            "moe_expert_forward", "moe_expert_forward_noalloc", "moe_router_logits", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -319,6 +321,10 @@ class OffloadMoE:
     def expert_forward(self, layer, x, slots, w, y):
         self._check(_lib.moe_expert_forward(self.ctx, layer, _ptr(x), x.shape[0], _ptr(slots), _ptr(w), _ptr(y)),
                     "moe_expert_forward")
+
+    def router_logits(self, layer, x, z):
+        """z [n][E] float32 device tensor <- the layer's router logits of x [n][H] (moe_router_logits)."""
+        self._check(_lib.moe_router_logits(self.ctx, layer, _ptr(x), x.shape[0], _ptr(z)), "moe_router_logits")
 
     def set_backend(self, backend, pcie_gbps=0.0, host_gbps=0.0, host_threads=1):
         """backend "offload" or "hybrid" (moe_set_backend)."""

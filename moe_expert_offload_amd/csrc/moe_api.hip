@@ -1273,6 +1273,21 @@ moe_status moe_cache_resolve(moe_ctx* c, int32_t step, int32_t layer, const int3
     return MOE_OK;
 }
 
+moe_status moe_router_logits(moe_ctx* c, int32_t layer, const void* x, int32_t n_tokens, float* z_out) {
+    moe_status st = check_call(c, n_tokens);
+    if (st) return st;
+    if (layer < 0 || layer >= c->cfg.n_layers || !x || !z_out) return set_err(c, MOE_EINVAL, "bad layer or buffers");
+    K1Args a{};
+    a.W = c->router_dev + (size_t)layer * c->cfg.n_experts * c->cfg.hidden;
+    a.x = (const uint16_t*)x;
+    a.z = z_out;
+    a.E = c->cfg.n_experts;
+    a.H = c->cfg.hidden;
+    a.B = n_tokens;
+    LAUNCHCHK(c, launch_k1(a, c->cs));
+    return MOE_OK;
+}
+
 moe_status moe_layer_forward(moe_ctx* c, int32_t step, int32_t layer, const void* x, int32_t n_tokens,
                              void* y, int32_t* ids_out, float* w_out) {
     moe_status st = check_call(c, n_tokens);
