@@ -151,81 +151,118 @@ __global__ __launch_bounds__(64) void k1_logits(K1Args a) {
     if (lane == 0) a.z[(size_t)b * a.E + e] = p;
 }
 
-// Many tokens (a prefill chunk, more than 16): a workgroup of 4 waves takes 16
-// experts x 16 tokens; each wave keeps its 4 experts' router rows in registers
-// (G groups of 8 bf16 per lane: lane l holds groups g = l + 64 i, i < G) and
-// walks the 16 tokens two at a time, so each router row is read once per token
-// tile instead of once per token.  Every logit is still lane l's fold over its
-// groups in increasing g (a group past the row leaves the fold unchanged), then
-// the xor butterfly: the same bits as k1_logits.  The rows stay packed bf16
-// across the token loop (converted at each use): converted once they would take
-// 4 x G x 8 fp32 registers and leave one wave per SIMD.  Lanes 0..7 collect the
-// 8 logits of a token pair and store them together.
-constexpr int K1T_EXP = 4, K1T_TOK = 16;
+// Many tokens (a prefill chunk, more than 16): a workgroup of 4 waves takes 8
+// experts x 16 tokens.  Each wave keeps its 2 experts' router rows in registers
+// as FP32 (lane l holds groups g = l + 64 i, i < G, of 8 elements each); the
+// workgroup converts each token pair's activations once to FP32 and stages them
+// in LDS (the 8 elements of a group as two 16-byte planes, so a wave's reads of
+// one plane are 64 consecutive 16-byte cells), double-buffered with one barrier
+// per pair.  Every logit is still lane l's fold over its groups in increasing g
+// (a group past the row leaves the fold unchanged), then the xor butterfly: the
+// same bits as k1_logits (bf16 -> FP32 is exact, and the products are exact in
+// FP32 either way).  Lanes 0..3 store a token pair's 4 logits.
+constexpr int K1T_EXPW = 2, K1T_WAVES = 4, K1T_TOK = 16;
 
 template <int G>
-__global__ __launch_bounds__(256) void k1_logits_tiled(K1Args a) {
+__global__ __launch_bounds__(64 * K1T_WAVES) void k1_logits_tiled(K1Args a) {
+    constexpr int NT = 64 * K1T_WAVES, GMAX = 64 * G;
+    constexpr int UPT = (2 * GMAX + NT - 1) / NT;    // staging units (8 activations) per thread and pair
+    __shared__ float4 xs[2][2][2][GMAX];             // [buffer][token of the pair][plane][group]
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int e0 = (blockIdx.x * 4 + w) * K1T_EXP;
+    const int e0 = (blockIdx.x * K1T_WAVES + w) * K1T_EXPW;
     const int b0 = blockIdx.y * K1T_TOK;
     const int ng = a.H >> 3;
-    uint4 wr[K1T_EXP][G];
+    float wf[K1T_EXPW][G][8];
     bool gv[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) gv[i] = lane + 64 * i < ng;
 #pragma unroll
-    for (int j = 0; j < K1T_EXP; ++j) {
+    for (int j = 0; j < K1T_EXPW; ++j) {
         const int e = e0 + j < a.E ? e0 + j : a.E - 1;
         const uint16_t* W = a.W + (size_t)e * a.H;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int g = lane + 64 * i;
-            wr[j][i] = *reinterpret_cast<const uint4*>(W + (size_t)(g < ng ? g : 0) * 8);
+            const uint4 v = *reinterpret_cast<const uint4*>(W + (size_t)(g < ng ? g : 0) * 8);
+            wf[j][i][0] = bf16lo(v.x);
+            wf[j][i][1] = bf16hi(v.x);
+            wf[j][i][2] = bf16lo(v.y);
+            wf[j][i][3] = bf16hi(v.y);
+            wf[j][i][4] = bf16lo(v.z);
+            wf[j][i][5] = bf16hi(v.z);
+            wf[j][i][6] = bf16lo(v.w);
+            wf[j][i][7] = bf16hi(v.w);
         }
     }
-    // the next token pair's activations are loaded while the current pair is folded
-    auto load_x = [&](int b, uint4* xv) __attribute__((always_inline)) {
-        const uint16_t* x = a.x + (size_t)(b < a.B ? b : a.B - 1) * a.H;
+    // staging unit u < 2 ng of a pair: token u / ng of the pair, group u % ng
+    uint4 sv[UPT];
+    auto load_pair = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int g = lane + 64 * i;
-            xv[i] = *reinterpret_cast<const uint4*>(x + (size_t)(g < ng ? g : 0) * 8);
+        for (int k = 0; k < UPT; ++k) {
+            const int u = threadIdx.x + NT * k;
+            const int tp = u >= ng ? 1 : 0, g = u - tp * ng;
+            const int b = b0 + t + tp;
+            const uint16_t* x = a.x + (size_t)(b < a.B ? b : a.B - 1) * a.H;
+            sv[k] = *reinterpret_cast<const uint4*>(x + (size_t)(u < 2 * ng ? g : 0) * 8);
         }
     };
-    float out = 0.0f;   // lane k < 8: logit of (token k / 4, expert k % 4) of the current pair
-    auto logits = [&](int t, const uint4* xv) __attribute__((always_inline)) {
+    auto store_pair = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < K1T_EXP; ++j)
+        for (int k = 0; k < UPT; ++k) {
+            const int u = threadIdx.x + NT * k;
+            const int tp = u >= ng ? 1 : 0, g = u - tp * ng;
+            if (u < 2 * ng) {
+                xs[buf][tp][0][g] = make_float4(bf16lo(sv[k].x), bf16hi(sv[k].x), bf16lo(sv[k].y), bf16hi(sv[k].y));
+                xs[buf][tp][1][g] = make_float4(bf16lo(sv[k].z), bf16hi(sv[k].z), bf16lo(sv[k].w), bf16hi(sv[k].w));
+            }
+        }
+    };
+    auto logits = [&](int t, int buf) __attribute__((always_inline)) {
+        float out = 0.0f;   // lane k < 4: logit of (token t + k / 2, expert e0 + k % 2)
 #pragma unroll
-            for (int i = 0; i < G; ++i)
-                asm volatile("" : "+v"(wr[j][i].x), "+v"(wr[j][i].y), "+v"(wr[j][i].z), "+v"(wr[j][i].w));
+        for (int tp = 0; tp < 2; ++tp) {
+            float p[K1T_EXPW];
 #pragma unroll
-        for (int j = 0; j < K1T_EXP; ++j) {
-            float p = 0.0f;
+            for (int j = 0; j < K1T_EXPW; ++j) p[j] = 0.0f;
 #pragma unroll
             for (int i = 0; i < G; ++i) {
-                const float q = fold8(wr[j][i], xv[i], p);
-                p = gv[i] ? q : p;
+                const int g = gv[i] ? lane + 64 * i : 0;
+                const float4 lo = xs[buf][tp][0][g], hi = xs[buf][tp][1][g];
+#pragma unroll
+                for (int j = 0; j < K1T_EXPW; ++j) {
+                    float q = p[j];
+                    q = fmaf(wf[j][i][0], lo.x, q);
+                    q = fmaf(wf[j][i][1], lo.y, q);
+                    q = fmaf(wf[j][i][2], lo.z, q);
+                    q = fmaf(wf[j][i][3], lo.w, q);
+                    q = fmaf(wf[j][i][4], hi.x, q);
+                    q = fmaf(wf[j][i][5], hi.y, q);
+                    q = fmaf(wf[j][i][6], hi.z, q);
+                    q = fmaf(wf[j][i][7], hi.w, q);
+                    p[j] = gv[i] ? q : p[j];
+                }
             }
-            p = xor_butterfly(p);
-            out = lane == (t & 1) * K1T_EXP + j ? p : out;
+#pragma unroll
+            for (int j = 0; j < K1T_EXPW; ++j) {
+                const float z = xor_butterfly(p[j]);
+                out = lane == tp * K1T_EXPW + j ? z : out;
+            }
         }
-    };
-    auto store_pair = [&](int t) __attribute__((always_inline)) {
-        if (lane < 2 * K1T_EXP) {
-            const int b = b0 + t + lane / K1T_EXP, e = e0 + lane % K1T_EXP;
+        if (lane < 2 * K1T_EXPW) {
+            const int b = b0 + t + lane / K1T_EXPW, e = e0 + lane % K1T_EXPW;
             if (b < a.B && e < a.E) a.z[(size_t)b * a.E + e] = out;
         }
     };
-    uint4 xa[G], xb[G];
-    load_x(b0, xa);
-    load_x(b0 + 1, xb);
+    load_pair(0);
+    store_pair(0);
+    load_pair(2);
+    __syncthreads();
     for (int t = 0; t < K1T_TOK; t += 2) {
-        logits(t, xa);
-        load_x(b0 + t + 2, xa);
-        logits(t + 1, xb);
-        load_x(b0 + t + 3, xb);
-        store_pair(t);
+        logits(t, (t >> 1) & 1);
+        // pair t + 2 goes to the buffer read one pair ago (every wave has passed the barrier since)
+        if (t + 2 < K1T_TOK) store_pair(((t >> 1) + 1) & 1);
+        if (t + 4 < K1T_TOK) load_pair(t + 4);
+        __syncthreads();
     }
 }
 
@@ -233,15 +270,16 @@ int launch_k1(const K1Args& a, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     const int G = (a.H / 8 + 63) / 64;  // groups per lane (H <= 4096: G <= 8)
     if (a.B > K1T_TOK && G <= 8) {
-        const dim3 grid((a.E + 4 * K1T_EXP - 1) / (4 * K1T_EXP), (a.B + K1T_TOK - 1) / K1T_TOK);
+        const int epw = K1T_WAVES * K1T_EXPW;   // experts per workgroup
+        const dim3 grid((a.E + epw - 1) / epw, (a.B + K1T_TOK - 1) / K1T_TOK);
         if (G <= 2)
-            hipLaunchKernelGGL(k1_logits_tiled<2>, grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k1_logits_tiled<2>, grid, dim3(64 * K1T_WAVES), 0, st, a);
         else if (G <= 4)
-            hipLaunchKernelGGL(k1_logits_tiled<4>, grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k1_logits_tiled<4>, grid, dim3(64 * K1T_WAVES), 0, st, a);
         else if (G <= 6)
-            hipLaunchKernelGGL(k1_logits_tiled<6>, grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k1_logits_tiled<6>, grid, dim3(64 * K1T_WAVES), 0, st, a);
         else
-            hipLaunchKernelGGL(k1_logits_tiled<8>, grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k1_logits_tiled<8>, grid, dim3(64 * K1T_WAVES), 0, st, a);
     } else {
         hipLaunchKernelGGL(k1_logits, dim3(a.E, a.B), dim3(64), 0, st, a);
     }
