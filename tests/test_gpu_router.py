@@ -3,7 +3,8 @@ canonical summation order, bit for bit.
 
 Both router kernels are covered: the one-wave-per-(expert, token) kernel (1 and 16 tokens) and
 the tiled kernel (more than 16 tokens).  The hidden sizes fill every lane's groups exactly (256,
-3072, 4096) or leave a partial last group (2880: 360 groups of 8 over 64 lanes; 800: 100 groups).
+3072, 4096) or leave a partial last group (2880: 360 groups of 8 over 64 lanes; 800: 100; 3584:
+448, so the tiled kernel's eighth group of every lane is past the row; 1056: 132).
 All-zero activations make every product zero.  Ids being bit-exact does not show that the logits
 are: a change in the order of the additions moves a logit by an ulp, which almost never changes
 a top-k choice."""
@@ -25,6 +26,8 @@ CASES = [
     synth.Workload("router_3072_e512", 1, 512, 10, 1, 3072, 256, 480, 1, 1, 0.9, prefill_tokens=24, seed=33),
     synth.Workload("router_4096", 2, 256, 6, 0, 4096, 256, 288, 1, 1, 0.9, prefill_tokens=24, seed=34),
     synth.Workload("router_800", 2, 24, 3, 1, 800, 96, 48, 1, 1, 0.85, prefill_tokens=24, seed=35),
+    synth.Workload("router_3584", 2, 64, 4, 0, 3584, 128, 128, 1, 1, 0.9, prefill_tokens=24, seed=36),
+    synth.Workload("router_1056", 2, 48, 2, 0, 1056, 64, 96, 1, 1, 0.9, prefill_tokens=24, seed=37),
 ]
 
 
