@@ -78,4 +78,6 @@ def test_matrix_core_kernels_fit_two_waves_per_simd(tmp_path):
     mm = {n: r for n, r in ks.items() if "k5_gate_up" in n or "k5_down" in n}
     assert mm
     for n, r in mm.items():
-        assert r["vgpr"] + r["agpr"] <= 256, (n, r)
+        # on this target the metadata's vgpr_count is the whole unified register block of a wave
+        # (architected VGPRs and AGPRs together; agpr_count is its AGPR part)
+        assert r["agpr"] <= r["vgpr"] <= 256, (n, r)
