@@ -91,12 +91,13 @@ typedef struct {
     int32_t n_shared;       /* always-on shared experts per layer (0 or 1), resident in HBM */
     int32_t cache_slots;    /* C: GPU expert slots; must be >= 2 * min(max_tokens * k, E) */
     int32_t max_tokens;     /* largest n_tokens of any call */
-    int32_t lookahead;      /* moe_stack_forward: 2 = resolve layer l+2 and copy its misses while
-                               layers l and l+1 wait for theirs (LRU policy, offload steps and
-                               cache_slots >= 3 * top_k * n_tokens of the call; otherwise the call
-                               runs with lookahead 1); 1 = resolve and copy layer l+1 while layer
-                               l's FFN runs; 0 = causal (each layer's copies before its FFN).
-                               Every lookahead gives the same ids, slots, trace and outputs */
+    int32_t lookahead;      /* moe_stack_forward: D = 2 or 3 resolves layer l+D and copies its
+                               misses while layers l .. l+D-1 wait for theirs (LRU policy, offload
+                               steps and cache_slots >= (D + 1) * top_k * n_tokens of the call; a
+                               call whose cache is smaller takes the deepest D that fits, else
+                               lookahead 1); 1 = resolve and copy layer l+1 while layer l's FFN
+                               runs; 0 = causal (each layer's copies before its FFN).  Every
+                               lookahead gives the same ids, slots, trace and outputs */
     int32_t trace_capacity; /* cache trace records kept on the device (0 = none) */
     int32_t fill_threads;   /* host threads calling the fill callback (0 = all cores) */
     int32_t flags;          /* MOE_FLAG_* */

@@ -12,8 +12,8 @@
 // before the current layer's FFN, so its misses load while the current layer
 // computes (ai.holude.com preflight page, section on long prompts: the next
 // layer's experts load over PCIe while the GPU computes the current one);
-// lookahead 2 resolves two layers ahead, so the copy queue still holds a layer
-// of misses when a layer without misses passes.
+// lookahead 2 or 3 resolves that many layers ahead, so the copy queue still
+// holds layers of misses when a layer without misses passes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -48,8 +48,8 @@ struct TimedPair {
 };
 
 // Layer parities of the per-layer buffers (K2's slots and weights, miss lists, copy events): a
-// lookahead-2 stack call has the buffers of layers l, l+1 and l+2 in use at once.
-constexpr int NPAR = 3;
+// lookahead-3 stack call has the buffers of layers l .. l+3 in use at once.
+constexpr int NPAR = 4;
 
 struct moe_ctx {
     moe_config cfg{};
@@ -100,7 +100,7 @@ struct moe_ctx {
     int parity = 0;             // which order buffer is current
     // workspace carve
     float* z = nullptr;
-    // per layer parity (NPAR: layers l, l+1, l+2 of a lookahead-2 call are in flight at once);
+    // per layer parity (NPAR: layers l .. l+3 of a lookahead-3 call are in flight at once);
     // index NPAR of a and copy_used serves moe_expert_forward
     int32_t* ids[NPAR] = {};
     float* w[NPAR] = {};
@@ -225,7 +225,7 @@ moe_status check_cfg(const moe_config* c, bool allow_auto = false) {
         c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
         c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 0 ||
-        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 2 || c->trace_capacity < 0 ||
+        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 3 || c->trace_capacity < 0 ||
         c->pinned_mb < 0 || c->policy < 0 || c->policy > 1)
         return MOE_EINVAL;
     // the down kernel stages every selected expert's intermediate vector in LDS
@@ -1364,36 +1364,38 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     // another 1 % at gpt-oss shape, 10 % at Qwen3.6 shape).
     RouteStreamGuard guard{c};
     const bool whole_pool = n_tokens == 1 && (int64_t)c->cfg.cache_slots >= (int64_t)L * c->cfg.n_experts;
-    // Lookahead 2 (LRU, C >= 3 k B): K1/K2 of layer l+2 are enqueued before layer l's FFN, so
-    // they run right after layer l-1's FFN and the copies of two layers are queued while a
-    // layer's FFN waits for its own.  When layer l's copies are issued the FFNs of layers l-2
-    // and l-1 may still be pending.  The step's victims are the least recently used slots outside
-    // its own hits; the slots touched by the two previous steps (at most 2 k B) are more recent
-    // than every slot they did not touch, and the step's hits and misses number at most k B, so
-    // with C >= 3 k B every victim was last used three or more steps back, by an FFN that has
-    // finished (stream order: layer l's resolve runs after layer l-3's FFN).  The resolve
-    // sequence, and so every result, is the same as with lookahead 1 or 0.
-    const bool la2 = c->cfg.lookahead == 2 && !whole_pool && c->cfg.policy == MOE_POLICY_LRU &&
-                     (int64_t)c->cfg.cache_slots >= 3 * (int64_t)c->cfg.top_k * n_tokens;
-    if (la2) {
+    // Lookahead D = 2 or 3 (LRU, C >= (D + 1) k B): K1/K2 of layer l+D are enqueued before layer
+    // l's FFN, so they run right after layer l-1's FFN and the copies of D layers are queued while
+    // a layer's FFN waits for its own.  When layer l's copies are issued the FFNs of layers l-D ..
+    // l-1 may still be pending.  The step's victims are the least recently used slots outside its
+    // own hits; the slots touched by the D previous steps (at most D k B) are more recent than
+    // every slot they did not touch, and the step's hits and misses number at most k B, so with
+    // C >= (D + 1) k B every victim was last used D + 1 or more steps back, by an FFN that has
+    // finished (stream order: layer l's resolve runs after layer l-D-1's FFN, and its copies are
+    // issued once the host has read its miss list).  A layer's buffers (ids, weights, slots, miss
+    // list, copy events) are reused D + 1 layers later, after that layer's FFN in stream order.
+    // The resolve sequence, and so every result, is the same as with lookahead 1 or 0.  A call
+    // whose cache is too small for the configured depth takes the deepest one that fits.
+    int depth = 0;
+    if (!whole_pool && c->cfg.policy == MOE_POLICY_LRU)
+        for (int d = std::min(c->cfg.lookahead, NPAR - 1); d >= 2 && !depth; --d)
+            if ((int64_t)c->cfg.cache_slots >= (int64_t)(d + 1) * c->cfg.top_k * n_tokens) depth = d;
+    if (depth >= 2) {
         int64_t seq_par[NPAR] = {};
-        if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
-        if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
-        seq_par[0] = c->seq;
-        if (L > 1) {
-            if ((st = launch_route(c, 1, xl(1), n_tokens))) return st;
-            if ((st = launch_resolve(c, step, 1, true, nullptr, n_tokens, 1, nullptr, idl(1), wl(1)))) return st;
-            seq_par[1] = c->seq;
+        for (int l = 0; l < depth && l < L; ++l) {
+            if ((st = launch_route(c, l, xl(l), n_tokens))) return st;
+            if ((st = launch_resolve(c, step, l, true, nullptr, n_tokens, l, nullptr, idl(l), wl(l)))) return st;
+            seq_par[l] = c->seq;
         }
         for (int l = 0; l < L; ++l) {
             const int par = l % NPAR;
             int nm = 0;
             if ((st = stage_misses(c, l, par, seq_par[par], &nm))) return st;
-            if (l + 2 < L) {
-                const int np = (l + 2) % NPAR;
-                if ((st = launch_route(c, l + 2, xl(l + 2), n_tokens))) return st;
-                if ((st = launch_resolve(c, step, l + 2, true, nullptr, n_tokens, np, nullptr, idl(l + 2),
-                                         wl(l + 2))))
+            if (l + depth < L) {
+                const int np = (l + depth) % NPAR;
+                if ((st = launch_route(c, l + depth, xl(l + depth), n_tokens))) return st;
+                if ((st = launch_resolve(c, step, l + depth, true, nullptr, n_tokens, np, nullptr, idl(l + depth),
+                                         wl(l + depth))))
                     return st;
                 seq_par[np] = c->seq;
             }

@@ -72,6 +72,16 @@ def test_null_context_calls_fail_cleanly():
     L.moe_destroy(None)
 
 
+def test_lookahead_up_to_three_layers_is_accepted():
+    import moe_expert_offload_amd as M
+    for la in (0, 1, 2, 3):
+        M.query_sizes(_cfg(lookahead=la))
+    for la in (-1, 4):
+        with pytest.raises(M.MoeError) as e:
+            M.query_sizes(_cfg(lookahead=la))
+        assert e.value.status == M.MOE_EINVAL
+
+
 def test_grouped_workspace_grows_with_max_tokens():
     """Batches of tokens need the grouped plan and the per-row expert outputs in the workspace."""
     import moe_expert_offload_amd as M

@@ -61,7 +61,7 @@ def test_lookahead_and_causal_are_bitwise_equal():
     wl = synth.WORKLOADS["toy"]
     X = synth.decode_inputs(wl)[:24]
     ys = []
-    for la in (2, 1, 0):
+    for la in (3, 2, 1, 0):
         m, _ = make_moe(wl, lookahead=la)
         _, _, y = run_stack(m, wl, X)
         m.close()
@@ -70,23 +70,23 @@ def test_lookahead_and_causal_are_bitwise_equal():
         np.testing.assert_array_equal(ys[0].view(np.uint32), y.view(np.uint32))
 
 
-@pytest.mark.parametrize("B", [1, 4])
-def test_lookahead2_deep_stack_at_its_cache_bound_matches_causal_and_oracle(B):
-    """Lookahead 2 enqueues the resolve of layer l+2 before layer l's FFN, so layer l+2's copies can
-    land while the FFNs of layers l and l+1 are still pending; the library takes it when
-    C >= 3 k B, where a step's LRU victims are always older than the two steps before it.  Eight
-    layers at exactly C = 3 k B (evictions on almost every step), B tokens per step: ids, weights,
-    trace, final cache state and outputs equal the causal schedule's bit for bit and the oracle's
-    (outputs within tolerance, every step and layer)."""
+@pytest.mark.parametrize("D,B", [(2, 1), (2, 4), (3, 1), (3, 4)])
+def test_deep_lookahead_stack_at_its_cache_bound_matches_causal_and_oracle(D, B):
+    """Lookahead D (2 or 3) enqueues the resolve of layer l+D before layer l's FFN, so layer
+    l+D's copies can land while the FFNs of layers l .. l+D-1 are still pending; the library
+    takes it when C >= (D + 1) k B, where a step's LRU victims are always older than the D steps
+    before it.  Eight layers at exactly C = (D + 1) k B (evictions on almost every step), B tokens
+    per step: ids, weights, trace, final cache state and outputs equal the causal schedule's bit
+    for bit and the oracle's (outputs within tolerance, every step and layer)."""
     k = 2
-    wl = synth.Workload(f"la2_l8_b{B}", 8, 16, k, 0, 256, 512, 3 * k * B, 24, B, 0.9, seed=23)
+    wl = synth.Workload(f"la{D}_l8_b{B}", 8, 16, k, 0, 256, 512, (D + 1) * k * B, 24, B, 0.9, seed=23)
     X = synth.decode_inputs(wl)
     runs = []
-    for la in (2, 0):
+    for la in (D, 0):
         m, _ = make_moe(wl, lookahead=la)
         ids, w, y = run_stack(m, wl, X)
         _, recs = m.stats(trace_cap=1 << 16)
-        if la == 2:
+        if la == D:
             points = [(t, l, b) for t in range(X.shape[0]) for l in range(wl.n_layers) for b in range(B)]
             ref = oracle.decode_trace(wl, synth.router_weights(wl), X)
             assert ref["counters"]["evictions"] > X.shape[0] * wl.n_layers // 2
@@ -99,6 +99,24 @@ def test_lookahead2_deep_stack_at_its_cache_bound_matches_causal_and_oracle(B):
     assert runs[0][3] == runs[1][3]
     for u, v in zip(runs[0][4], runs[1][4]):
         np.testing.assert_array_equal(u, v)
+
+
+def test_lookahead3_with_a_cache_for_two_layers_ahead_matches_causal():
+    """Configured lookahead 3 but C = 3 k B: the call runs two layers ahead (the deepest that
+    fits) and still equals the causal schedule bit for bit."""
+    k, B = 2, 2
+    wl = synth.Workload("la3_c3kb", 6, 16, k, 0, 256, 512, 3 * k * B, 16, B, 0.9, seed=29)
+    X = synth.decode_inputs(wl)
+    runs = []
+    for la in (3, 0):
+        m, _ = make_moe(wl, lookahead=la)
+        ids, w, y = run_stack(m, wl, X)
+        _, recs = m.stats(trace_cap=1 << 16)
+        runs.append((ids, w, y, trace_tuples(recs)))
+        m.close()
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32))
+    assert runs[0][3] == runs[1][3]
 
 
 def test_whole_pool_cache_route_stream_matches_causal_and_oracle():
