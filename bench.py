@@ -208,7 +208,7 @@ def main():
     ap.add_argument("--steps", type=int, default=448)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="dsv4_flash_shaped")
-    ap.add_argument("--lookahead", type=int, default=3, choices=(0, 1, 2, 3))
+    ap.add_argument("--lookahead", type=int, default=7, choices=tuple(range(8)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ffn-rounds", type=int, default=20)
     ap.add_argument("--calib-copy", action="store_true",

@@ -91,7 +91,7 @@ typedef struct {
     int32_t n_shared;       /* always-on shared experts per layer (0 or 1), resident in HBM */
     int32_t cache_slots;    /* C: GPU expert slots; must be >= 2 * min(max_tokens * k, E) */
     int32_t max_tokens;     /* largest n_tokens of any call */
-    int32_t lookahead;      /* moe_stack_forward: D = 2 or 3 resolves layer l+D and copies its
+    int32_t lookahead;      /* moe_stack_forward: D = 2 .. 7 resolves layer l+D and copies its
                                misses while layers l .. l+D-1 wait for theirs (LRU policy, offload
                                steps and cache_slots >= (D + 1) * top_k * n_tokens of the call; a
                                call whose cache is smaller takes the deepest D that fits, else

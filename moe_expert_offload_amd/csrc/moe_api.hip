@@ -12,8 +12,8 @@
 // before the current layer's FFN, so its misses load while the current layer
 // computes (ai.holude.com preflight page, section on long prompts: the next
 // layer's experts load over PCIe while the GPU computes the current one);
-// lookahead 2 or 3 resolves that many layers ahead, so the copy queue still
-// holds layers of misses when a layer without misses passes.
+// lookahead D = 2 .. 7 resolves that many layers ahead, so the copy queue
+// still holds layers of misses when layers without misses pass.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -48,8 +48,8 @@ struct TimedPair {
 };
 
 // Layer parities of the per-layer buffers (K2's slots and weights, miss lists, copy events): a
-// lookahead-3 stack call has the buffers of layers l .. l+3 in use at once.
-constexpr int NPAR = 4;
+// lookahead-7 stack call has the buffers of layers l .. l+7 in use at once.
+constexpr int NPAR = 8;
 
 struct moe_ctx {
     moe_config cfg{};
@@ -100,7 +100,7 @@ struct moe_ctx {
     int parity = 0;             // which order buffer is current
     // workspace carve
     float* z = nullptr;
-    // per layer parity (NPAR: layers l .. l+3 of a lookahead-3 call are in flight at once);
+    // per layer parity (NPAR: layers l .. l+7 of a lookahead-7 call are in flight at once);
     // index NPAR of a and copy_used serves moe_expert_forward
     int32_t* ids[NPAR] = {};
     float* w[NPAR] = {};
@@ -111,6 +111,7 @@ struct moe_ctx {
     // host-mapped miss lists
     uint8_t* ml_mem = nullptr;
     size_t ml_stride = 0;
+    uint64_t copy_rr = 0;  // pinned copies issued so far (all-pinned pools): picks their copy stream
     int max_unique = 0;
     int static_T = 0;           // static split: transient slots (2 * max distinct experts per step)
     int64_t seq = 0;
@@ -225,7 +226,7 @@ moe_status check_cfg(const moe_config* c, bool allow_auto = false) {
         c->top_k > 16 || c->top_k > c->n_experts || c->hidden < 32 || c->hidden % 32 ||
         c->hidden > 16384 || c->inter < 32 || c->inter % 32 || c->inter > 16384 ||
         c->n_shared < 0 || c->n_shared > 1 || c->max_tokens < 1 || c->cache_slots < 0 ||
-        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 3 || c->trace_capacity < 0 ||
+        c->cache_slots > MAX_CACHE_SLOTS || c->lookahead < 0 || c->lookahead > 7 || c->trace_capacity < 0 ||
         c->pinned_mb < 0 || c->policy < 0 || c->policy > 1)
         return MOE_EINVAL;
     // the down kernel stages every selected expert's intermediate vector in LDS
@@ -645,7 +646,6 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
     }
     bool used[2] = {false, false}, timed_q[2] = {false, false};
     hipStream_t qs[2] = {c->ps, c->ps2};
-    int nd = 0;  // direct copies so far: they alternate between the two copy streams
     int ncopy = 0;
     const bool timed = nm > 0 && c->h2d_timing;
     if (c->h2d_used.size() >= TIMED_PENDING) {
@@ -691,8 +691,9 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
         const size_t src_idx = (c->fault_corrupt_at && c->copies_issued == c->fault_corrupt_at) ? (idx + 1) % n_sl : idx;
         // a pool with a pageable part: pageable misses on the caller's copy stream (each DMA waits
         // for its host fill), pinned ones on the second stream, where they run while the fills
-        // hold the first; an all-pinned pool alternates its copies over both streams
-        const int q = !c->pinned(idx) ? 0 : (c->n_pin < c->n_blobs ? 1 : (nd++ & 1));
+        // hold the first; an all-pinned pool alternates its copies over both streams, counted
+        // across calls, so that steps with one miss each do not all queue on the first
+        const int q = !c->pinned(idx) ? 0 : (c->n_pin < c->n_blobs ? 1 : (int)(c->copy_rr++ & 1));
         if (!used[q]) {
             moe_status st = open_stream(q);
             if (st) return st;
@@ -1364,7 +1365,7 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     // another 1 % at gpt-oss shape, 10 % at Qwen3.6 shape).
     RouteStreamGuard guard{c};
     const bool whole_pool = n_tokens == 1 && (int64_t)c->cfg.cache_slots >= (int64_t)L * c->cfg.n_experts;
-    // Lookahead D = 2 or 3 (LRU, C >= (D + 1) k B): K1/K2 of layer l+D are enqueued before layer
+    // Lookahead D = 2 .. 7 (LRU, C >= (D + 1) k B): K1/K2 of layer l+D are enqueued before layer
     // l's FFN, so they run right after layer l-1's FFN and the copies of D layers are queued while
     // a layer's FFN waits for its own.  When layer l's copies are issued the FFNs of layers l-D ..
     // l-1 may still be pending.  The step's victims are the least recently used slots outside its

@@ -12,7 +12,7 @@ def bf16_to_f32(t):
     return t.view(torch.bfloat16).float().cpu().numpy()
 
 
-def make_moe(wl, lookahead=3, trace_capacity=1 << 20, flags=0, max_tokens=None, cache_slots=None, pinned_mb=0,
+def make_moe(wl, lookahead=7, trace_capacity=1 << 20, flags=0, max_tokens=None, cache_slots=None, pinned_mb=0,
              policy=0):
     import moe_expert_offload_amd as M
     cfg = M.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.n_shared,

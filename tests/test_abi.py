@@ -72,11 +72,11 @@ def test_null_context_calls_fail_cleanly():
     L.moe_destroy(None)
 
 
-def test_lookahead_up_to_three_layers_is_accepted():
+def test_lookahead_up_to_seven_layers_is_accepted():
     import moe_expert_offload_amd as M
-    for la in (0, 1, 2, 3):
+    for la in range(8):
         M.query_sizes(_cfg(lookahead=la))
-    for la in (-1, 4):
+    for la in (-1, 8):
         with pytest.raises(M.MoeError) as e:
             M.query_sizes(_cfg(lookahead=la))
         assert e.value.status == M.MOE_EINVAL

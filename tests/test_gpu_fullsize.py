@@ -1,7 +1,7 @@
 """Full-size parity on every workload shape: gpt-oss-120b (36 x 128 experts, H = I = 2880, top-4,
 1862 of 4608 experts cached, the full 60.9 GB pool in pinned host RAM), Qwen3.6-35B-A3B,
 DeepSeek-V4-Flash (a 147 GB pool, partly pageable) and Qwen3.8-Flash-Next (prefill and 16-request
-decode), in the launch configuration the benchmark times (lookahead 3), with the offload and the
+decode), in the launch configuration the benchmark times (lookahead 7), with the offload and the
 hybrid backends.  Routing ids and the cache trace are checked bit-exactly for every step run;
 outputs at sampled (step, layer[, token]) points."""
 import numpy as np
@@ -141,7 +141,7 @@ def test_other_shapes_sampled(name, T, points):
     """The Qwen3.6-shaped (40 x 256 experts, top-8 + shared, 17.1 GB pool, 3789 slots) and the
     DeepSeek-V4-Flash-shaped (43 x 256, top-6, H = 4096, I = 2048, 147 GB pool, 1211 slots; the
     pool's unpinned part goes through the bounce ring) workloads at full size, in the benchmark's
-    launch configuration (batch 1, lookahead 3): ids, weights and the whole trace bit-exact for
+    launch configuration (batch 1, lookahead 7): ids, weights and the whole trace bit-exact for
     every step run, outputs at sampled (step, layer) points."""
     wl = synth.WORKLOADS[name]
     X = synth.decode_inputs(wl)[:T]

@@ -61,7 +61,7 @@ def test_lookahead_and_causal_are_bitwise_equal():
     wl = synth.WORKLOADS["toy"]
     X = synth.decode_inputs(wl)[:24]
     ys = []
-    for la in (3, 2, 1, 0):
+    for la in (7, 3, 2, 1, 0):
         m, _ = make_moe(wl, lookahead=la)
         _, _, y = run_stack(m, wl, X)
         m.close()
@@ -70,16 +70,17 @@ def test_lookahead_and_causal_are_bitwise_equal():
         np.testing.assert_array_equal(ys[0].view(np.uint32), y.view(np.uint32))
 
 
-@pytest.mark.parametrize("D,B", [(2, 1), (2, 4), (3, 1), (3, 4)])
+@pytest.mark.parametrize("D,B", [(2, 1), (2, 4), (3, 1), (3, 4), (5, 2), (7, 1), (7, 2)])
 def test_deep_lookahead_stack_at_its_cache_bound_matches_causal_and_oracle(D, B):
-    """Lookahead D (2 or 3) enqueues the resolve of layer l+D before layer l's FFN, so layer
+    """Lookahead D (2 .. 7) enqueues the resolve of layer l+D before layer l's FFN, so layer
     l+D's copies can land while the FFNs of layers l .. l+D-1 are still pending; the library
     takes it when C >= (D + 1) k B, where a step's LRU victims are always older than the D steps
-    before it.  Eight layers at exactly C = (D + 1) k B (evictions on almost every step), B tokens
+    before it.  max(8, 2 D) layers at exactly C = (D + 1) k B (evictions on most steps), B tokens
     per step: ids, weights, trace, final cache state and outputs equal the causal schedule's bit
     for bit and the oracle's (outputs within tolerance, every step and layer)."""
     k = 2
-    wl = synth.Workload(f"la{D}_l8_b{B}", 8, 16, k, 0, 256, 512, (D + 1) * k * B, 24, B, 0.9, seed=23)
+    L = max(8, 2 * D)
+    wl = synth.Workload(f"la{D}_l{L}_b{B}", L, 16, k, 0, 256, 512, (D + 1) * k * B, 24, B, 0.9, seed=23)
     X = synth.decode_inputs(wl)
     runs = []
     for la in (D, 0):
@@ -101,14 +102,16 @@ def test_deep_lookahead_stack_at_its_cache_bound_matches_causal_and_oracle(D, B)
         np.testing.assert_array_equal(u, v)
 
 
-def test_lookahead3_with_a_cache_for_two_layers_ahead_matches_causal():
-    """Configured lookahead 3 but C = 3 k B: the call runs two layers ahead (the deepest that
-    fits) and still equals the causal schedule bit for bit."""
+@pytest.mark.parametrize("la_cfg,fits", [(3, 2), (7, 4)])
+def test_deep_lookahead_with_a_smaller_cache_runs_the_deepest_that_fits(la_cfg, fits):
+    """Configured lookahead la_cfg but C = (fits + 1) k B: the call runs `fits` layers ahead (the
+    deepest that fits) and still equals the causal schedule bit for bit."""
     k, B = 2, 2
-    wl = synth.Workload("la3_c3kb", 6, 16, k, 0, 256, 512, 3 * k * B, 16, B, 0.9, seed=29)
+    wl = synth.Workload(f"la{la_cfg}_c{fits + 1}kb", 10, 16, k, 0, 256, 512, (fits + 1) * k * B, 16, B, 0.9,
+                        seed=29)
     X = synth.decode_inputs(wl)
     runs = []
-    for la in (3, 0):
+    for la in (la_cfg, 0):
         m, _ = make_moe(wl, lookahead=la)
         ids, w, y = run_stack(m, wl, X)
         _, recs = m.stats(trace_cap=1 << 16)
