@@ -343,6 +343,36 @@ def test_pageable_pool_part_through_bounce_ring():
     m.close()
 
 
+@pytest.mark.parametrize("B", [1, 2])
+def test_deep_lookahead_with_a_pageable_pool_part_matches_causal_and_oracle(B):
+    """A pool about half pageable with lookahead 7 (C = 16 k B): pinned misses on the second copy
+    stream, pageable ones through the bounce ring on the first, seven layers of them queued.  Ids,
+    weights, trace, cache state, copy counts and outputs equal the causal schedule's bit for bit
+    and the oracle's (outputs within tolerance)."""
+    k, L = 2, 12
+    wl = synth.Workload(f"la7_pageable_b{B}", L, 16, k, 0, 256, 512, 16 * k * B, 24, B, 0.9, seed=41)
+    X = synth.decode_inputs(wl)
+    pinned_mb = (wl.pool * wl.blob_bytes // 2) >> 20
+    runs = []
+    for la in (7, 0):
+        m, _ = make_moe(wl, lookahead=la, pinned_mb=pinned_mb)
+        ids, w, y = run_stack(m, wl, X)
+        cnt, recs = m.stats(trace_cap=1 << 16)
+        assert 0 < cnt["h2d_bounced"] < cnt["h2d_copies"], cnt
+        if la == 7:
+            points = [(t, l, b) for t in range(X.shape[0]) for l in range(L) for b in range(B)]
+            _check_run(wl, X, ids, w, y, recs, m, points)
+        runs.append((ids, w, y, trace_tuples(recs), m.cache_state(), cnt["h2d_copies"], cnt["h2d_bounced"]))
+        m.close()
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    np.testing.assert_array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32))
+    assert runs[0][3] == runs[1][3]
+    for u, v in zip(runs[0][4], runs[1][4]):
+        np.testing.assert_array_equal(u, v)
+    assert runs[0][5:] == runs[1][5:]
+
+
 def test_profile_counters_and_h2d_measurement():
     """MOE_FLAG_PROFILE times every layer FFN with HIP events; moe_measure_h2d returns a plausible
     copy-path bandwidth (PCIe: between 1 and 70 GB/s)."""
