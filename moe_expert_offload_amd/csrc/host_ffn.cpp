@@ -513,4 +513,81 @@ double host_expert_rate(const Layout& L, const uint8_t* const* blobs, int n, int
     return (double)total * (double)L.blob_bytes / dt;
 }
 
+HostTaskQueue::~HostTaskQueue() { stop(); }
+
+bool HostTaskQueue::start(HostExpertPool* pool) {
+    stop();
+    pool_ = pool;
+    quit_ = false;
+    try {
+        th_ = std::thread(&HostTaskQueue::run, this);
+    } catch (...) {
+        return false;
+    }
+    return true;
+}
+
+void HostTaskQueue::stop() {
+    if (!th_.joinable()) return;
+    {
+        std::lock_guard<std::mutex> lk(mu_);
+        quit_ = true;
+    }
+    cv_push_.notify_all();
+    th_.join();
+}
+
+uint64_t HostTaskQueue::push(const Layout& L, int n_tok, const uint16_t* const* x, float* const* y,
+                             const HostEntry* e, int n) {
+    Item it;
+    it.L = L;
+    it.n_tok = std::max(0, std::min(n_tok, kHostMaxTokens));
+    it.n = std::max(0, std::min(n, kHostMaxEntries));
+    for (int b = 0; b < it.n_tok; ++b) {
+        it.x[b] = x[b];
+        it.y[b] = y[b];
+    }
+    std::copy(e, e + it.n, it.e);
+    {
+        std::lock_guard<std::mutex> lk(mu_);
+        q_.push_back(it);
+    }
+    cv_push_.notify_one();
+    return ++pushed_;
+}
+
+bool HostTaskQueue::wait(uint64_t seq, double timeout_s) {
+    if (done() >= seq) return true;
+    // a system-clock deadline: the wait then maps to pthread_cond_timedwait, which thread checkers
+    // follow (a steady-clock wait maps to pthread_cond_clockwait, which older ones do not)
+    const auto deadline = std::chrono::system_clock::now() +
+                          std::chrono::duration_cast<std::chrono::system_clock::duration>(
+                              std::chrono::duration<double>(timeout_s));
+    std::unique_lock<std::mutex> lk(mu_);
+    return cv_done_.wait_until(lk, deadline, [&] { return done() >= seq; });
+}
+
+// the dispatcher: one task at a time on the pool (this thread works on it too), in push order;
+// on stop the queued tasks still run, so every waiter is released
+void HostTaskQueue::run() {
+    for (;;) {
+        Item it;
+        {
+            std::unique_lock<std::mutex> lk(mu_);
+            cv_push_.wait(lk, [&] { return quit_ || !q_.empty(); });
+            if (q_.empty()) return;
+            it = q_.front();
+            q_.pop_front();
+        }
+        pool_->submit(it.L, it.n_tok, it.x, it.y, it.e, it.n);
+        pool_->wait();
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            const uint64_t d = done_.fetch_add(1, std::memory_order_acq_rel) + 1;
+            if (mirror_) __atomic_store_n(mirror_, d, __ATOMIC_RELEASE);
+        }
+        cv_done_.notify_all();
+    }
+}
+
 }  // namespace moe

@@ -3,6 +3,7 @@
 #include <atomic>
 #include <chrono>
 #include <condition_variable>
+#include <deque>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -127,6 +128,47 @@ private:
     std::atomic<bool> quit_{false};
     std::mutex mu_;
     std::condition_variable cv_;
+};
+
+// Tasks of several layer steps queued ahead of their FFNs: a dispatcher thread
+// runs them on a HostExpertPool one after another, in push order, and counts
+// the finished ones, so a waiter can wait for one task without holding up the
+// pushing thread.  Pushed x and y must stay valid until that task is done.
+class HostTaskQueue {
+public:
+    ~HostTaskQueue();
+    bool start(HostExpertPool* pool);  // false if the thread could not be started; numbers go on
+    void stop();                       // runs the queued tasks, then joins the thread
+    bool running() const { return th_.joinable(); }
+    // queues a task (arguments as HostExpertPool::submit); returns its number: 1, 2, ... over the
+    // queue's whole life (a restart keeps counting)
+    uint64_t push(const Layout& L, int n_tok, const uint16_t* const* x, float* const* y, const HostEntry* e, int n);
+    // true once task `seq` (and every task before it) is done; false after timeout_s
+    bool wait(uint64_t seq, double timeout_s);
+    uint64_t pushed() const { return pushed_; }
+    uint64_t done() const { return done_.load(std::memory_order_acquire); }
+    // also store the count of finished tasks at *p after each task (memory the GPU reads); set
+    // while the thread is stopped
+    void set_mirror(uint64_t* p) { mirror_ = p; }
+
+private:
+    struct Item {
+        Layout L{};
+        int n_tok = 0, n = 0;
+        const uint16_t* x[kHostMaxTokens] = {};
+        float* y[kHostMaxTokens] = {};
+        HostEntry e[kHostMaxEntries] = {};
+    };
+    void run();
+    HostExpertPool* pool_ = nullptr;
+    std::thread th_;
+    std::deque<Item> q_;
+    uint64_t pushed_ = 0;               // the pushing thread's count
+    std::atomic<uint64_t> done_{0};
+    uint64_t* mirror_ = nullptr;
+    bool quit_ = false;
+    std::mutex mu_;
+    std::condition_variable cv_push_, cv_done_;
 };
 
 }  // namespace moe

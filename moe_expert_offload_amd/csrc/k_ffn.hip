@@ -357,6 +357,27 @@ __global__ __launch_bounds__(256) void k_host_only_out(const float* yh, uint16_t
     if (i < n) y[i] = f32_to_bf16(yh[i]);
 }
 
+// Waits, in one lane, until the host-mapped count of finished host tasks `done` reaches `seq`
+// (the hybrid backend's host task of the layer whose FFN follows), reading it at most max_polls
+// times with a sleep between reads.  At the limit it sets *late and returns: the wave always exits.
+__global__ __launch_bounds__(64) void k_wait_host(const uint64_t* done, uint64_t seq, uint32_t max_polls,
+                                                  uint32_t* late) {
+    if (threadIdx.x != 0) return;
+    uint32_t n = 0;
+    while (__hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq) {
+        if (++n >= max_polls) {
+            __hip_atomic_store(late, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(64);
+    }
+}
+
+int launch_wait_host(const uint64_t* done, uint64_t seq, uint32_t max_polls, uint32_t* late, void* stream) {
+    hipLaunchKernelGGL(k_wait_host, dim3(1), dim3(64), 0, (hipStream_t)stream, done, seq, max_polls, late);
+    return (int)hipGetLastError();
+}
+
 size_t ffn_lds_bytes(const Layout& L, int nE) {
     const size_t p1 = (size_t)L.NB * 80 + 4 * kGuRows * 2 * 4;
     const size_t p2 = (size_t)nE * L.NBI * 80 + K4_WAVES * 8 * 4;

@@ -156,8 +156,13 @@ struct moe_ctx {
     HostExpertPool hpool;
     hipStream_t xs_stream = nullptr;     // device-to-host copies of the hidden states
     hipEvent_t xs_start = nullptr, xs_done = nullptr;
-    uint16_t* xh = nullptr;              // pinned host copy of the call's hidden states
-    size_t xh_cap = 0;
+    uint16_t* xh = nullptr;              // pinned host copy of the call's hidden states (one of xh_buf)
+    // two buffers used by calls in turn: host tasks a call queued may still read its buffer
+    // while the next call fills the other
+    uint16_t* xh_buf[2] = {nullptr, nullptr};
+    size_t xh_cap_buf[2] = {0, 0};
+    int xh_cur = 0;
+    uint64_t xh_last_seq[2] = {0, 0};    // the last queued host task that reads each buffer
     int64_t xh_stride = 0;
     bool xh_pending = false;
     bool hyb_call = false;               // the current call runs hybrid steps
@@ -169,6 +174,15 @@ struct moe_ctx {
     int host_running = -1;               // parity of the host task in flight, -1: none
     uint64_t host_tasks = 0;
     double host_wait_ms = 0.0;           // time the calling thread waited for host tasks
+    // hybrid steps of a stack call with a lookahead of two or more layers queue their host tasks
+    // here; before a layer's FFN a one-wave kernel on the compute stream waits until the queue's
+    // count of finished tasks (mirrored in host-mapped memory) reaches that layer's task, so the
+    // calling thread stages the next layers meanwhile
+    HostTaskQueue hq;
+    bool hq_mode = false;                // the current call queues its host tasks
+    uint64_t host_seq[NPAR] = {};        // per parity: the queued task its FFN adds (0: none)
+    uint64_t* hq_flag = nullptr;         // host-mapped: [0] finished tasks, [1] low word: a wait timed out
+    uint64_t* hq_flag_dev = nullptr;     // its device address
     double spin_timeout_s = 60.0;
     bool failed = false;
     std::string err;
@@ -363,12 +377,15 @@ void free_all(moe_ctx* c) {
     for (auto e : c->copy_ev) if (e) (void)hipEventDestroy(e);
     for (auto e : c->copy_ev2) if (e) (void)hipEventDestroy(e);
     if (c->ps2) (void)hipStreamDestroy(c->ps2);
+    c->hq.stop();
     c->hpool.stop();
+    if (c->hq_flag) (void)hipHostFree(c->hq_flag);
     if (c->xs_stream) (void)hipStreamSynchronize(c->xs_stream);
     if (c->xs_start) (void)hipEventDestroy(c->xs_start);
     if (c->xs_done) (void)hipEventDestroy(c->xs_done);
     if (c->xs_stream) (void)hipStreamDestroy(c->xs_stream);
-    if (c->xh) (void)hipHostFree(c->xh);
+    for (auto* b : c->xh_buf)
+        if (b) (void)hipHostFree(b);
     if (c->yh) (void)hipHostFree(c->yh);
     c->bounce.shutdown();
     if (c->pool) (void)hipHostFree(c->pool);
@@ -434,6 +451,8 @@ moe_status launch_resolve(moe_ctx* c, int step, int layer, bool routed, const in
 // with the LRU policy run hybrid steps (batches through the grouped FFN path).
 moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
     c->hyb_call = false;
+    c->hq_mode = false;
+    for (auto& q : c->host_seq) q = 0;
     // a call that returned early can leave a host task running or a host sum unclaimed
     if (c->host_running >= 0) {
         c->hpool.wait();
@@ -444,14 +463,20 @@ moe_status hyb_begin(moe_ctx* c, const void* x, int64_t xs, int layers, int B) {
         (B > 1 && (c->cfg.flags & MOE_FLAG_PER_TOKEN_FFN)))
         return MOE_OK;
     const size_t bytes = ((size_t)(layers - 1) * (size_t)xs + (size_t)B * c->cfg.hidden) * 2;
-    if (bytes > c->xh_cap) {
-        if (c->xh) HIPCHK(c, hipHostFree(c->xh));
-        c->xh = nullptr;
-        c->xh_cap = 0;
-        if (hipHostMalloc((void**)&c->xh, bytes, 0) != hipSuccess)
+    const int i = c->xh_cur ^ 1;
+    if (c->xh_last_seq[i] && !c->hq.wait(c->xh_last_seq[i], c->spin_timeout_s))
+        return set_err(c, MOE_EHIP, "timed out waiting for the host tasks of an earlier call");
+    c->xh_last_seq[i] = 0;
+    if (bytes > c->xh_cap_buf[i]) {
+        if (c->xh_buf[i]) HIPCHK(c, hipHostFree(c->xh_buf[i]));
+        c->xh_buf[i] = nullptr;
+        c->xh_cap_buf[i] = 0;
+        if (hipHostMalloc((void**)&c->xh_buf[i], bytes, 0) != hipSuccess)
             return set_err(c, MOE_ENOMEM, "pinned buffer of %zu bytes for the hidden states", bytes);
-        c->xh_cap = bytes;
+        c->xh_cap_buf[i] = bytes;
     }
+    c->xh_cur = i;
+    c->xh = c->xh_buf[i];
     HIPCHK(c, hipEventRecord(c->xs_start, c->cs));
     HIPCHK(c, hipStreamWaitEvent(c->xs_stream, c->xs_start, 0));
     HIPCHK(c, hipMemcpyAsync(c->xh, x, bytes, hipMemcpyDeviceToHost, c->xs_stream));
@@ -598,14 +623,6 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
                     ent[nh++] = {c->blob_src((size_t)layer * E + e), ml->w_all[i], i / k};
             }
         }
-        if (c->host_running >= 0) {
-            // one task at a time: the previous layer's host experts finish first (their sums
-            // stay in their own parity's buffers for that layer's FFN)
-            const auto tw = std::chrono::steady_clock::now();
-            c->hpool.wait();
-            c->host_wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
-            c->host_running = -1;
-        }
         const uint16_t* xs[kHostMaxTokens];
         float* ys[kHostMaxTokens];
         const size_t H = c->cfg.hidden;
@@ -613,9 +630,28 @@ moe_status stage_misses(moe_ctx* c, int layer, int par, int64_t seq, int* n_miss
             xs[b] = c->xh + (size_t)layer * c->xh_stride + (size_t)b * H;
             ys[b] = c->yh + ((size_t)layer * kHostMaxTokens + b) * H;
         }
-        c->hpool.submit(c->lay, B, xs, ys, ent, nh);
-        c->host_running = par;
-        c->host_has[par] = true;
+        if (c->hq_mode) {
+            // queued: the dispatcher runs it after the tasks before it; the FFN waits for it
+            const uint64_t sq = c->hq.push(c->lay, B, xs, ys, ent, nh);
+            c->host_seq[par] = sq;
+            c->xh_last_seq[c->xh_cur] = sq;
+        } else {
+            // the pool is used directly: tasks still queued by an earlier call finish first
+            if (c->hq.done() < c->hq.pushed() && !c->hq.wait(c->hq.pushed(), c->spin_timeout_s))
+                return set_err(c, MOE_EHIP, "timed out waiting for queued host tasks");
+            if (c->host_running >= 0) {
+                // one task at a time: the previous layer's host experts finish first (their sums
+                // stay in their own parity's buffers for that layer's FFN)
+                const auto tw = std::chrono::steady_clock::now();
+                c->hpool.wait();
+                c->host_wait_ms +=
+                    std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - tw).count();
+                c->host_running = -1;
+            }
+            c->hpool.submit(c->lay, B, xs, ys, ent, nh);
+            c->host_running = par;
+            c->host_has[par] = true;
+        }
         ++c->host_tasks;
     }
     const size_t blob = c->lay.blob_bytes;
@@ -755,6 +791,16 @@ moe_status launch_ffn_layer(moe_ctx* c, int layer, const void* x, int B, int par
             c->host_running = -1;
         }
         c->host_has[par] = false;
+        yh = c->yh + (size_t)layer * kHostMaxTokens * c->cfg.hidden;
+    }
+    if (par < NPAR && c->host_seq[par]) {
+        // a queued host task: the compute stream waits for it (the calling thread does not); the
+        // wait reads the count about every 2 us or more, so max_polls covers the time limit
+        const double polls = std::min(4.0e9, c->spin_timeout_s * 5.0e5);
+        if (launch_wait_host(c->hq_flag_dev, c->host_seq[par], (uint32_t)polls,
+                             reinterpret_cast<uint32_t*>(c->hq_flag_dev + 1), c->cs) != (int)hipSuccess)
+            return set_err(c, MOE_EHIP, "launch of the host-task wait failed");
+        c->host_seq[par] = 0;
         yh = c->yh + (size_t)layer * kHostMaxTokens * c->cfg.hidden;
     }
     if (n_miss > 0 && par < NPAR) {
@@ -917,6 +963,8 @@ struct RouteStreamGuard {
 moe_status check_call(moe_ctx* c, int n_tokens) {
     if (!c) return MOE_EINVAL;
     if (c->failed) return MOE_ESTATE;
+    if (c->hq_flag && __atomic_load_n(reinterpret_cast<uint32_t*>(c->hq_flag + 1), __ATOMIC_ACQUIRE))
+        return set_err(c, MOE_EHIP, "a queued host task did not finish within %g s", c->spin_timeout_s);
     if (n_tokens < 1 || n_tokens > c->cfg.max_tokens)
         return set_err(c, MOE_EINVAL, "n_tokens %d outside [1, %d]", n_tokens, c->cfg.max_tokens);
     return MOE_OK;
@@ -1326,6 +1374,51 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
         }
         return MOE_OK;
     }
+    const bool whole_pool = n_tokens == 1 && (int64_t)c->cfg.cache_slots >= (int64_t)L * c->cfg.n_experts;
+    // Lookahead D = 2 .. 7 (LRU, C >= (D + 1) k B): K1/K2 of layer l+D are enqueued before layer
+    // l's FFN, so they run right after layer l-1's FFN and the copies of D layers are queued while
+    // a layer's FFN waits for its own.  When layer l's copies are issued the FFNs of layers l-D ..
+    // l-1 may still be pending.  The step's victims are the least recently used slots outside its
+    // own hits; the slots touched by the D previous steps (at most D k B) are more recent than
+    // every slot they did not touch, and the step's hits and misses number at most k B, so with
+    // C >= (D + 1) k B every victim was last used D + 1 or more steps back, by an FFN that has
+    // finished (stream order: layer l's resolve runs after layer l-D-1's FFN, and its copies are
+    // issued once the host has read its miss list).  A layer's buffers (ids, weights, slots, miss
+    // list, copy events) are reused D + 1 layers later, after that layer's FFN in stream order.
+    // The resolve sequence, and so every result, is the same as with lookahead 1 or 0.  A call
+    // whose cache is too small for the configured depth takes the deepest one that fits.
+    // Hybrid steps take the same pipeline: their host tasks are queued (HostTaskQueue) and the
+    // compute stream waits for each layer's task before its FFN, so host tasks and copies both
+    // run up to D layers ahead.
+    int depth = 0;
+    if ((c->hyb_call || !whole_pool) && c->cfg.policy == MOE_POLICY_LRU)
+        for (int d = std::min(c->cfg.lookahead, NPAR - 1); d >= 2 && !depth; --d)
+            if ((int64_t)c->cfg.cache_slots >= (int64_t)(d + 1) * c->cfg.top_k * n_tokens) depth = d;
+    if (depth >= 2) {
+        int64_t seq_par[NPAR] = {};
+        c->hq_mode = c->hyb_call;
+        for (int l = 0; l < depth && l < L; ++l) {
+            if ((st = launch_route(c, l, xl(l), n_tokens))) return st;
+            if ((st = launch_resolve(c, step, l, true, nullptr, n_tokens, l, nullptr, idl(l), wl(l)))) return st;
+            seq_par[l] = c->seq;
+        }
+        for (int l = 0; l < L; ++l) {
+            const int par = l % NPAR;
+            int nm = 0;
+            if ((st = stage_misses(c, l, par, seq_par[par], &nm))) return st;
+            if (l + depth < L) {
+                const int np = (l + depth) % NPAR;
+                if ((st = launch_route(c, l + depth, xl(l + depth), n_tokens))) return st;
+                if ((st = launch_resolve(c, step, l + depth, true, nullptr, n_tokens, np, nullptr, idl(l + depth),
+                                         wl(l + depth))))
+                    return st;
+                seq_par[np] = c->seq;
+            }
+            if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
+        }
+        c->hq_mode = false;
+        return MOE_OK;
+    }
     // lookahead 1: K1/K2 of layer l+1 and its copies are issued before layer l's FFN
     int64_t seq_of[2] = {0, 0};
     if (c->hyb_call) {
@@ -1364,46 +1457,6 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t step, const void* x, int64_t xs
     // short copies), while with the whole pool cached it gained 6 % (and the helper thread below
     // another 1 % at gpt-oss shape, 10 % at Qwen3.6 shape).
     RouteStreamGuard guard{c};
-    const bool whole_pool = n_tokens == 1 && (int64_t)c->cfg.cache_slots >= (int64_t)L * c->cfg.n_experts;
-    // Lookahead D = 2 .. 7 (LRU, C >= (D + 1) k B): K1/K2 of layer l+D are enqueued before layer
-    // l's FFN, so they run right after layer l-1's FFN and the copies of D layers are queued while
-    // a layer's FFN waits for its own.  When layer l's copies are issued the FFNs of layers l-D ..
-    // l-1 may still be pending.  The step's victims are the least recently used slots outside its
-    // own hits; the slots touched by the D previous steps (at most D k B) are more recent than
-    // every slot they did not touch, and the step's hits and misses number at most k B, so with
-    // C >= (D + 1) k B every victim was last used D + 1 or more steps back, by an FFN that has
-    // finished (stream order: layer l's resolve runs after layer l-D-1's FFN, and its copies are
-    // issued once the host has read its miss list).  A layer's buffers (ids, weights, slots, miss
-    // list, copy events) are reused D + 1 layers later, after that layer's FFN in stream order.
-    // The resolve sequence, and so every result, is the same as with lookahead 1 or 0.  A call
-    // whose cache is too small for the configured depth takes the deepest one that fits.
-    int depth = 0;
-    if (!whole_pool && c->cfg.policy == MOE_POLICY_LRU)
-        for (int d = std::min(c->cfg.lookahead, NPAR - 1); d >= 2 && !depth; --d)
-            if ((int64_t)c->cfg.cache_slots >= (int64_t)(d + 1) * c->cfg.top_k * n_tokens) depth = d;
-    if (depth >= 2) {
-        int64_t seq_par[NPAR] = {};
-        for (int l = 0; l < depth && l < L; ++l) {
-            if ((st = launch_route(c, l, xl(l), n_tokens))) return st;
-            if ((st = launch_resolve(c, step, l, true, nullptr, n_tokens, l, nullptr, idl(l), wl(l)))) return st;
-            seq_par[l] = c->seq;
-        }
-        for (int l = 0; l < L; ++l) {
-            const int par = l % NPAR;
-            int nm = 0;
-            if ((st = stage_misses(c, l, par, seq_par[par], &nm))) return st;
-            if (l + depth < L) {
-                const int np = (l + depth) % NPAR;
-                if ((st = launch_route(c, l + depth, xl(l + depth), n_tokens))) return st;
-                if ((st = launch_resolve(c, step, l + depth, true, nullptr, n_tokens, np, nullptr, idl(l + depth),
-                                         wl(l + depth))))
-                    return st;
-                seq_par[np] = c->seq;
-            }
-            if ((st = launch_ffn_layer(c, l, xl(l), n_tokens, par, yl(l), nm))) return st;
-        }
-        return MOE_OK;
-    }
     if (!whole_pool) {
         if ((st = launch_route(c, 0, xl(0), n_tokens))) return st;
         if ((st = launch_resolve(c, step, 0, true, nullptr, n_tokens, 0, nullptr, idl(0), wl(0)))) return st;
@@ -1718,7 +1771,10 @@ moe_status moe_set_backend(moe_ctx* c, int32_t backend, double pcie_gbps, double
         c->host_running = -1;
     }
     c->host_has[0] = c->host_has[1] = false;
+    if (c->hq.done() < c->hq.pushed() && !c->hq.wait(c->hq.pushed(), c->spin_timeout_s))
+        return set_err(c, MOE_EHIP, "timed out waiting for queued host tasks");
     if (backend == MOE_BACKEND_OFFLOAD) {
+        c->hq.stop();
         c->hpool.stop();
         c->backend = MOE_BACKEND_OFFLOAD;
         return MOE_OK;
@@ -1739,6 +1795,17 @@ moe_status moe_set_backend(moe_ctx* c, int32_t backend, double pcie_gbps, double
     }
     if (c->hpool.workers() != host_threads && !c->hpool.start(host_threads))
         return set_err(c, MOE_ENOMEM, "could not start %d host workers", host_threads);
+    if (!c->hq_flag) {
+        if (hipHostMalloc((void**)&c->hq_flag, 256, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
+            return set_err(c, MOE_ENOMEM, "host-mapped word for the host-task count");
+        memset(c->hq_flag, 0, 256);
+        HIPCHK(c, hipHostGetDevicePointer((void**)&c->hq_flag_dev, c->hq_flag, 0));
+    }
+    if (!c->hq.running()) {
+        __atomic_store_n(c->hq_flag, c->hq.done(), __ATOMIC_RELEASE);
+        c->hq.set_mirror(c->hq_flag);
+        if (!c->hq.start(&c->hpool)) return set_err(c, MOE_ENOMEM, "could not start the host task dispatcher");
+    }
     c->backend = MOE_BACKEND_HYBRID;
     c->hyb_bp = pcie_gbps;
     c->hyb_bh = host_gbps;

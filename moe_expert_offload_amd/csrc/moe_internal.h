@@ -194,6 +194,8 @@ int launch_k1(const K1Args& a, void* stream);
 int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void* stream);
 int launch_ffn(FfnArgs& a, const Layout& L, int B, void* stream, void* ev_mid);
 size_t ffn_lds_bytes(const Layout& L, int nE);
+// one wave that waits until *done >= seq (host-mapped), at most max_polls reads, else sets *late
+int launch_wait_host(const uint64_t* done, uint64_t seq, uint32_t max_polls, uint32_t* late, void* stream);
 int grouped_max_groups(int B, int k, int E, int n_shared);
 int grouped_max_chunks(int B, int k, int E, int n_shared, int gm);
 int grouped_gm(int B);

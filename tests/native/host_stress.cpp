@@ -6,13 +6,17 @@
 //  - host_expert_ffn (the calibration kernel) on 1 and 4 threads against a plain reference of the
 //    same arithmetic within FP32 rounding;
 //  - CopyTeam (the bounce ring's pageable-to-pinned copy): ragged sizes on teams of 1 to 5
-//    threads, restarted, every copy checked byte for byte.
+//    threads, restarted, every copy checked byte for byte;
+//  - HostTaskQueue (host tasks of several layer steps queued ahead): tasks pushed in bursts by one
+//    thread and waited for by another, out of order and with a time limit, the queue stopped
+//    with tasks still queued; every result must equal the 1-worker pool's bit for bit.
 // Prints "host stress ok" and exits 0 when every check passes.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <random>
+#include <thread>
 #include <vector>
 
 #include "copy_team.h"
@@ -152,12 +156,91 @@ void copy_rounds() {
     }
 }
 
+void queue_rounds() {
+    const Layout L = make_layout(256, 128);
+    std::mt19937_64 rng(11);
+    std::vector<std::vector<uint8_t>> blobs;
+    for (int i = 0; i < 8; ++i) blobs.push_back(random_blob(L, rng));
+    const int ntask = 12, ntok = 3;
+    std::normal_distribution<float> nd(0.0f, 1.0f);
+    std::vector<std::vector<uint16_t>> x(ntask * ntok, std::vector<uint16_t>(L.H));
+    for (auto& v : x)
+        for (auto& e : v) e = bf16_bits(nd(rng));
+    // task t: token b takes (t + b) % 3 + 1 experts
+    std::vector<std::vector<HostEntry>> ent(ntask);
+    for (int t = 0; t < ntask; ++t)
+        for (int b = 0; b < ntok; ++b)
+            for (int j = 0; j <= (t + b) % 3; ++j)
+                ent[t].push_back({blobs[(t * 3 + b + j) % blobs.size()].data(), 0.25f * (float)(j + 1), b});
+    auto ptrs = [&](int t, std::vector<std::vector<float>>& y, const uint16_t** xs, float** ys) {
+        for (int b = 0; b < ntok; ++b) {
+            xs[b] = x[t * ntok + b].data();
+            ys[b] = y[t * ntok + b].data();
+        }
+    };
+    std::vector<std::vector<float>> ref(ntask * ntok, std::vector<float>(L.H, -1.0f));
+    {
+        HostExpertPool p1;
+        CHECK(p1.start(1), "pool start(1)");
+        for (int t = 0; t < ntask; ++t) {
+            const uint16_t* xs[kHostMaxTokens];
+            float* ys[kHostMaxTokens];
+            ptrs(t, ref, xs, ys);
+            p1.submit(L, ntok, xs, ys, ent[t].data(), (int)ent[t].size());
+            p1.wait();
+        }
+    }
+    for (int workers : {2, 4}) {
+        HostExpertPool pool;
+        CHECK(pool.start(workers), "pool start(%d)", workers);
+        HostTaskQueue q;
+        for (int round = 0; round < 3; ++round) {
+            CHECK(q.start(&pool), "queue start");  // restarts the thread; task numbers keep counting
+            const uint64_t base = q.pushed();
+            CHECK(q.done() == base, "a stopped queue has run every task pushed to it");
+            std::vector<std::vector<float>> y(ntask * ntok, std::vector<float>(L.H, -1.0f));
+            std::vector<uint64_t> seq(ntask, 0);
+            // a waiter thread waits for the tasks out of order while this thread pushes them in bursts
+            std::atomic<int> pushed{0};
+            std::thread waiter([&] {
+                for (int t : {3, 1, 7, 11}) {
+                    while (pushed.load(std::memory_order_acquire) <= t) std::this_thread::yield();
+                    CHECK(q.wait(seq[t], 30.0), "task %d not done in time", t);
+                    CHECK(q.done() >= seq[t], "done count below task %d", t);
+                }
+            });
+            for (int t = 0; t < ntask; ++t) {
+                const uint16_t* xs[kHostMaxTokens];
+                float* ys[kHostMaxTokens];
+                ptrs(t, y, xs, ys);
+                seq[t] = q.push(L, ntok, xs, ys, ent[t].data(), (int)ent[t].size());
+                CHECK(seq[t] == base + (uint64_t)t + 1, "task numbers run on by one");
+                pushed.store(t + 1, std::memory_order_release);
+                if (t % 4 == 3) std::this_thread::sleep_for(std::chrono::microseconds(200));
+            }
+            waiter.join();
+            if (round == 2) {
+                q.stop();  // with tasks possibly still queued: they run before the thread ends
+                CHECK(q.done() == base + (uint64_t)ntask, "stop left %llu of %d tasks undone",
+                      (unsigned long long)(base + ntask - q.done()), ntask);
+            } else {
+                CHECK(q.wait(seq[ntask - 1], 30.0), "last task not done in time");
+            }
+            for (int i = 0; i < ntask * ntok; ++i)
+                CHECK(memcmp(y[i].data(), ref[i].data(), L.H * sizeof(float)) == 0,
+                      "queued task %d token %d differs from the 1-worker pool", i / ntok, i % ntok);
+        }
+        pool.stop();
+    }
+}
+
 }  // namespace
 
 int main() {
     pool_rounds();
     ffn_threads();
     copy_rounds();
+    queue_rounds();
     if (g_fail) {
         fprintf(stderr, "%d check(s) failed\n", g_fail);
         return 1;

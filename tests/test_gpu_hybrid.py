@@ -121,6 +121,42 @@ def test_hybrid_is_bitwise_independent_of_workers_and_lookahead():
         np.testing.assert_array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+# caches of at least 8 k B slots: stack calls run seven layers ahead, the host tasks queued
+WIDE_DEEP = synth.Workload("hyb_2880_deep", 6, 16, 4, 0, 2880, 2880, 32, 10, 1, 0.7, seed=57)
+SHARED_DEEP = synth.Workload("hyb_shared_deep", 6, 32, 8, 1, 2048, 512, 64, 12, 1, 0.8, seed=58)
+BATCH4_DEEP = synth.Workload("hyb_b4_deep", 6, 32, 4, 1, 512, 256, 128, 10, 4, 0.8, seed=59)
+
+
+@pytest.mark.parametrize("split", SPLITS[:3], ids=[f"{a}_{b}" for a, b in SPLITS[:3]])
+@pytest.mark.parametrize("wl", [WIDE_DEEP, SHARED_DEEP, BATCH4_DEEP], ids=lambda w: w.name)
+def test_hybrid_with_queued_host_tasks_matches_oracle(wl, split):
+    """Lookahead 7: the host tasks of up to seven layer steps are queued ahead of their FFNs, and
+    the compute stream waits for each layer's task.  Same bar as the other hybrid tests."""
+    X = synth.decode_inputs(wl)
+    m, W = _hybrid(wl, split)
+    ids, w, y = run_stack(m, wl, X)
+    c, worst = _check(wl, X, W, m, ids, w, y, split)
+    print(wl.name, split, c, "worst rel-L2 %.2e" % worst)
+    assert c["host"] > 0
+    m.close()
+
+
+@pytest.mark.parametrize("wl", [WIDE_DEEP, BATCH4_DEEP], ids=lambda w: w.name)
+def test_queued_host_tasks_are_bitwise_equal_to_lookahead_1_and_0(wl):
+    X = synth.decode_inputs(wl)
+    outs = []
+    for threads, la in ((4, 7), (9, 7), (4, 3), (1, 1), (4, 0)):
+        m, _ = _hybrid(wl, (26.7, 45.5), threads=threads, lookahead=la)
+        ids, w, y = run_stack(m, wl, X)
+        outs.append((ids, y, m.cache_state()))
+        m.close()
+    for ids, y, st in outs[1:]:
+        np.testing.assert_array_equal(ids, outs[0][0])
+        np.testing.assert_array_equal(y.view(np.uint32), outs[0][1].view(np.uint32))
+        for u, v in zip(st, outs[0][2]):
+            np.testing.assert_array_equal(u, v)
+
+
 @pytest.mark.parametrize("wl", [SHARED, BATCH4], ids=lambda w: w.name)
 def test_hybrid_layer_forward_matches_stack_and_pageable_pool(wl):
     import torch
