@@ -214,13 +214,16 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t step, int32_t layer, const vo
  * l reads x_bf16_dev + l * x_layer_stride elements (stride 0: the same input
  * for every layer) and writes y_bf16_dev + l * y_layer_stride.  ids_dev_out
  * ([L][n_tokens][k]) and w_dev_out may be NULL.  Work is ordered on the
- * compute stream as seen by the caller.  One-token calls of the hybrid backend,
- * and one-token offload calls when the cache holds the whole pool (C >= L * E),
- * run the router and resolve on a library-owned stream that joins the compute
- * stream before the call returns; layer l+1's copies then start only once layer
- * l-1's FFN has ended, so the copies stay one layer ahead.  In the whole-pool
- * case the call also starts a helper host thread that issues those launches
- * and is joined before the call returns (also on error). */
+ * compute stream as seen by the caller.  One-token calls of the hybrid backend
+ * that run one layer ahead, and one-token offload calls when the cache holds
+ * the whole pool (C >= L * E), run the router and resolve on a library-owned
+ * stream that joins the compute stream before the call returns; layer l+1's
+ * copies then start only once layer l-1's FFN has ended, so the copies stay one
+ * layer ahead.  In the whole-pool case the call also starts a helper host
+ * thread that issues those launches and is joined before the call returns
+ * (also on error).  Hybrid calls that run two or more layers ahead can return
+ * while their queued host tasks still run (the FFNs that need them wait on the
+ * compute stream); the tasks read the library's own host copy of x. */
 moe_status moe_stack_forward(moe_ctx* ctx, int32_t step, const void* x_bf16_dev, int64_t x_layer_stride,
                              int32_t n_tokens, void* y_bf16_dev, int64_t y_layer_stride,
                              int32_t* ids_dev_out, float* w_dev_out);
@@ -373,7 +376,12 @@ moe_status moe_calibrate_backend(moe_ctx* ctx, int32_t host_threads, double host
  *   host once per call.  Steps of more tokens, steps run with
  *   MOE_FLAG_PER_TOKEN_FFN and more than one token, and moe_cache_resolve
  *   transfer every miss.  The workers spin between tasks and sleep after
- *   20 ms idle.
+ *   20 ms idle.  In moe_stack_forward calls that run D >= 2 layers ahead (see
+ *   moe_config.lookahead) the host tasks are queued: a dispatcher thread runs
+ *   them in layer order, and before each layer's FFN a one-wave kernel on the
+ *   compute stream waits (at most about the library's 60 s limit, else the
+ *   next call fails with MOE_EHIP) until that layer's task has finished, so
+ *   host tasks and copies both run up to D layers ahead of the FFNs.
  * Needs the LRU policy.  Synchronises the compute stream.
  * Errors: MOE_EINVAL (backend, bandwidths <= 0, threads outside 1..256,
  * static policy), MOE_ENOMEM, MOE_ESTATE, MOE_EHIP. */
