@@ -21,7 +21,8 @@ BATCH16 = synth.Workload("hyb_b16_k8", 3, 64, 8, 0, 1024, 512, 130, 8, 16, 0.8, 
 BATCH8W = synth.Workload("hyb_b8_2880", 2, 16, 4, 1, 2880, 2880, 32, 6, 8, 0.7, seed=55)
 
 # (B_P, B_H): every miss on the host (q = round(m / 40) = 0 for m < 20), the pages' calibration
-# (q = 0.59 m), this box's measured ratio (q = 0.19 m), and no spare host bandwidth (offload)
+# (q = 0.59 m), a ratio measured on an MI355X host with 16 EPYC cores (q = 0.19 m), and no spare
+# host bandwidth (offload)
 SPLITS = [(10.0, 400.0), (26.7, 45.5), (56.0, 290.0), (50.0, 50.0)]
 
 
