@@ -117,6 +117,46 @@ def time_ffn_pass(m, x, layers, slots, w, y, rounds):
     return e0.elapsed_time(e1) * 1e3 / (rounds * L)
 
 
+def time_read_pass(m, byte_counts, n_layers, rounds):
+    """Mean time (us) per layer of plain streaming reads (moe_hbm_read): one launch per entry of
+    byte_counts, for each of n_layers layers from its own region of the slot arena (consecutive
+    layers read different bytes, as the FFN's layers read different slots), captured as one HIP
+    graph and replayed `rounds` times between two events on the compute stream."""
+    import torch
+
+    import moe_expert_offload_amd as M
+    cs = m.compute_stream
+    counts = [b // 16 * 16 for b in byte_counts]
+    stride = (sum(counts) + 4095) // 4096 * 4096
+    total = m.arena.numel()
+    n_regions = max(1, (total - stride) // stride + 1) if total >= stride else 0
+    if not n_regions:
+        return None
+
+    def one_pass():
+        for i in range(n_layers):
+            o = (i % n_regions) * stride
+            for b in counts:
+                M.hbm_read(m.arena, o, b, cs)
+                o += b
+
+    with torch.cuda.stream(cs):
+        one_pass()
+    cs.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        one_pass()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        graph.replay()
+        e0.record(cs)
+        for _ in range(rounds):
+            graph.replay()
+        e1.record(cs)
+    cs.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (rounds * n_layers)
+
+
 def run_prefill(m, wl, dev, rounds):
     """The prefill chunk: one step of all its tokens through every layer (cold cache), then the
     last layer's grouped expert FFN on the chunk timed alone (its experts are all resident)."""
@@ -364,6 +404,17 @@ def main():
             "launches": args.ffn_rounds * len(layers), "layers_timed": len(layers)}
     if B == 1:
         roof["bytes_k3"], roof["bytes_k4"] = ffn_bytes_split(wl)
+        # the plain-read floor of the same byte counts on this GPU: two launches (k3's bytes, then
+        # k4's) and one launch of both, per layer, replayed like the FFN
+        two = time_read_pass(m, [roof["bytes_k3"], roof["bytes_k4"]], len(layers), args.ffn_rounds)
+        one = time_read_pass(m, [roof["bytes_k3"] + roof["bytes_k4"]], len(layers), args.ffn_rounds)
+        if two and one:
+            fb = roof["bytes_k3"] + roof["bytes_k4"]
+            roof["plain_read"] = {
+                "kernel": "moe_hbm_read: 16-byte nontemporal loads, 8 per lane, one round, from the slot arena",
+                "two_launches_us": round(two, 2), "two_launches_frac": round(fb / (two * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "one_launch_us": round(one, 2), "one_launch_frac": round(fb / (one * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "ffn_frac_of_two_launches": round(two / ffn_us, 4)}
     # the same kernels inside the timed decode loop (one layer FFN in 17 timed by the library,
     # with the miss copies streaming beside them), against the same algorithmic bytes
     n_ffn = c_all["ffn_timed"] - c_warm["ffn_timed"]

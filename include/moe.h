@@ -327,6 +327,22 @@ moe_status moe_stats(moe_ctx* ctx, moe_counters* out, moe_trace_rec* buf, size_t
  * miss stager does; returns GB/s (1e9).  Leaves the cache untouched. */
 moe_status moe_measure_h2d(moe_ctx* ctx, size_t bytes_per_copy, int32_t n_copies, double* gbps_out);
 
+/* Plain streaming read of device memory, the HBM counterpart of moe_measure_h2d:
+ * one kernel launch on `stream` (a hipStream_t; NULL is the null stream) that
+ * loads every 16-byte word of [buf_dev, buf_dev + bytes) once, with the same
+ * nontemporal 16-byte loads as the expert FFN kernels, eight per lane, all in
+ * flight at once, and keeps nothing but a sink word.  Timed over the byte counts
+ * of the FFN's two kernels, it is the floor an HBM-bound launch of that size
+ * reaches on this GPU, the reference for the FFN's own time.  The pages treat
+ * VRAM as the fast side whose bandwidth serves the cache hits (pirouter.ai
+ * "FreeToken × RTX 5090" page, section on how 65 GB runs on a 32 GB GPU:
+ * 1-1.8 TB/s against PCIe's tens of GB/s).  buf_dev: device memory, 16-byte
+ * aligned, owned by the caller; bytes: a multiple of 16.  No context; allocates
+ * nothing; stream-ordered, so it can be captured in a graph.
+ * Errors: MOE_EINVAL (null or unaligned buffer, bytes 0 or not a multiple of 16),
+ * MOE_EHIP (launch). */
+moe_status moe_hbm_read(const void* buf_dev, size_t bytes, void* stream);
+
 /* Reads back the cache state (host buffers, each may be NULL): slot_of
  * [L*E], key_of [C], stamp [C].  Synchronises the compute stream. */
 moe_status moe_cache_state(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, int64_t* stamp);

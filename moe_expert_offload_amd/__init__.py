@@ -103,6 +103,8 @@ _lib.moe_stats.restype = _st
 _lib.moe_stats.argtypes = [_P, ctypes.POINTER(MoeCounters), _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
 _lib.moe_measure_h2d.restype = _st
 _lib.moe_measure_h2d.argtypes = [_P, ctypes.c_size_t, _I32, ctypes.POINTER(ctypes.c_double)]
+_lib.moe_hbm_read.restype = _st
+_lib.moe_hbm_read.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.moe_cache_state.restype = _st
 _lib.moe_cache_state.argtypes = [_P, _P, _P, _P]
 _lib.moe_destroy.restype = None
@@ -113,7 +115,7 @@ _lib.moe_last_error.argtypes = [_P]
 EXPORTED = ("moe_query_sizes", "moe_auto_cache_slots", "moe_pack_blob", "moe_host_expert_ffn", "moe_host_expert_batch",
             "moe_hybrid_split",
             "moe_select_backend", "moe_calibrate_backend", "moe_set_backend", "moe_init_pool", "moe_cache_resolve", "moe_layer_forward", "moe_stack_forward",
-            "moe_expert_forward", "moe_expert_forward_noalloc", "moe_router_logits", "moe_stats", "moe_measure_h2d", "moe_cache_state", "moe_destroy", "moe_last_error")
+            "moe_expert_forward", "moe_expert_forward_noalloc", "moe_router_logits", "moe_stats", "moe_measure_h2d", "moe_hbm_read", "moe_cache_state", "moe_destroy", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -233,6 +235,18 @@ def expert_forward_noalloc(cfg: MoeConfig, arena, shared_blob, x, slots, w, y, s
                                          _ptr(slots), _ptr(w), _ptr(y), ctypes.c_void_p(s.cuda_stream))
     if st:
         raise MoeError(st, "moe_expert_forward_noalloc: " + _lib.moe_last_error(None).decode())
+
+
+def hbm_read(buf, offset, nbytes, stream=None):
+    """moe_hbm_read: one streaming-read launch over nbytes of the device tensor buf from byte
+    offset (stream: a torch stream or None for the current one)."""
+    import torch
+    if offset < 0 or offset + nbytes > buf.numel() * buf.element_size():
+        raise MoeError(MOE_EINVAL, "moe_hbm_read: range outside the buffer")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = _lib.moe_hbm_read(ctypes.c_void_p(buf.data_ptr() + offset), nbytes, ctypes.c_void_p(s.cuda_stream))
+    if st:
+        raise MoeError(st, "moe_hbm_read")
 
 
 class OffloadMoE:

@@ -72,6 +72,16 @@ def test_null_context_calls_fail_cleanly():
     L.moe_destroy(None)
 
 
+def test_hbm_read_rejects_bad_ranges_before_any_launch():
+    import moe_expert_offload_amd as M
+    L = M.lib()
+    assert L.moe_hbm_read(None, 16, None) == M.MOE_EINVAL
+    # fake device addresses: rejected on alignment or size alone, never dereferenced
+    assert L.moe_hbm_read(ctypes.c_void_p(0x1000), 0, None) == M.MOE_EINVAL
+    assert L.moe_hbm_read(ctypes.c_void_p(0x1000), 24, None) == M.MOE_EINVAL
+    assert L.moe_hbm_read(ctypes.c_void_p(0x1008), 16, None) == M.MOE_EINVAL
+
+
 def test_lookahead_up_to_seven_layers_is_accepted():
     import moe_expert_offload_amd as M
     for la in range(8):
