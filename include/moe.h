@@ -89,7 +89,7 @@ typedef struct {
     int32_t hidden;         /* H, multiple of 32, <= 16384 */
     int32_t inter;          /* I, multiple of 32, <= 16384 */
     int32_t n_shared;       /* always-on shared experts per layer (0 or 1), resident in HBM */
-    int32_t cache_slots;    /* C: GPU expert slots; must be >= 2 * min(max_tokens * k, E) */
+    int32_t cache_slots;    /* C: GPU expert slots, <= 32768; must be >= 2 * min(max_tokens * k, E) */
     int32_t max_tokens;     /* largest n_tokens of any call */
     int32_t lookahead;      /* moe_stack_forward: D = 2 .. 7 resolves layer l+D and copies its
                                misses while layers l .. l+D-1 wait for theirs (LRU policy, offload
@@ -130,7 +130,7 @@ moe_status moe_query_sizes(const moe_config* cfg, size_t* blob_bytes, size_t* ar
  *     C * blob + the library's own device bytes at C (cache state, router
  *     weights, shared experts; each rounded to 2 MiB) + reserve_bytes
  *     <= free_bytes,
- * capped at n_layers * n_experts (the whole pool) and at 16384 slots.
+ * capped at n_layers * n_experts (the whole pool) and at 32768 slots.
  * free_bytes: device bytes free; 0 = ask the runtime (hipMemGetInfo on the
  * current device).  reserve_bytes: kept free for the caller (KV cache,
  * activations, allocator slack).  Allocates nothing.

@@ -58,7 +58,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KG_THREADS = 1024;
-constexpr int KG_MAXC = 16384;   // cache slots
+constexpr int KG_MAXC = 32768;   // cache slots
+static_assert(KG_MAXC / 32 <= KG_THREADS, "the grouping kernel ranks slots with one bitmap word per thread");
 constexpr int KG_MAXG = 1024;    // routed groups (distinct experts <= E <= 1024)
 constexpr int K5_THREADS = 256;
 
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(KG_THREADS) void k2g_group(GroupArgs a) {
         else if (!(a.host_rows && sl == -1)) atomicAdd(&s_invalid, 1);  // -1 with host_rows: the host's row
     });
     __syncthreads();
-    // nw <= 512: one bitmap word per thread; rank of a slot = present slots below it
+    // nw <= KG_MAXC / 32 = 1024: one bitmap word per thread; rank of a slot = present slots below it
     const int pc = tid < nw ? __popc(s_bits[tid]) : 0;
     int n_rg;
     const int pre = kg_scan(pc, s_wave, n_rg);

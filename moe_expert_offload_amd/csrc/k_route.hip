@@ -344,8 +344,7 @@ __device__ void wave_topk(const K2Args& a, int b, int32_t* s_ids = nullptr, floa
 
 constexpr int K2_THREADS = 1024;
 constexpr int K2_MAXE = 1024;
-constexpr int K2_MAXC = 16384;
-constexpr int K2_CPT = K2_MAXC / K2_THREADS;  // order entries per thread
+constexpr int K2_MAXC = 32768;               // cache slots the resolve kernels address
 constexpr int K2_IDS_LDS = 1024;              // ids of a step kept in LDS up to this many
 
 // exclusive prefix count of a 0/1 flag over the 1024 threads, in thread order
@@ -388,12 +387,14 @@ __device__ __forceinline__ int block_scan(int v, int* s_wave, int& total) {
     return before + x - v;
 }
 
+// CPT: order entries per thread (C <= 1024 CPT); compiled for 16 and 32
+template <int CPT>
 __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t* order_in,
                                                          int32_t* order_out) {
     __shared__ int32_t s_req[K2_MAXE];     // requested flag, then final slot per expert
     __shared__ int32_t s_miss_e[K2_MAXE];  // misses by rank
     __shared__ int32_t s_victim[K2_MAXE];  // victims by rank
-    __shared__ uint32_t s_hitbits[K2_MAXC / 32];
+    __shared__ uint32_t s_hitbits[CPT * K2_THREADS / 32];
     __shared__ int s_wave[K2_THREADS / 64];
     __shared__ int s_evict, s_invalid;
     __shared__ int32_t s_ids[K2_IDS_LDS];
@@ -409,10 +410,10 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
     // trace head.
     const int e = tid;
     const int v_pre = (!stat && e < E) ? a.c.slot_of[l * E + e] : -1;
-    int ent[K2_CPT];
-    const int p0 = tid * K2_CPT;
+    int ent[CPT];
+    const int p0 = tid * CPT;
 #pragma unroll
-    for (int c = 0; c < K2_CPT; ++c) ent[c] = (!stat && p0 + c < C) ? order_in[p0 + c] : -1;
+    for (int c = 0; c < CPT; ++c) ent[c] = (!stat && p0 + c < C) ? order_in[p0 + c] : -1;
     const int64_t clock0 = *a.c.clock;
     const int64_t trace_base = (int64_t)a.c.trace_head[0];
 
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         // stamps, clock, counters and trace are not touched; every slot output is -1.
         if (!stat) {
 #pragma unroll
-            for (int c = 0; c < K2_CPT; ++c)
+            for (int c = 0; c < CPT; ++c)
                 if (p0 + c < C) order_out[p0 + c] = ent[c];
         }
         for (int i = tid; i < a.n_ids; i += K2_THREADS) {
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         // the first q of them are this step's victims
         int kept = 0;
 #pragma unroll
-        for (int c = 0; c < K2_CPT; ++c) {
+        for (int c = 0; c < CPT; ++c) {
             const int sl = ent[c];
             if (sl >= 0) {
                 const bool is_hit = (s_hitbits[sl >> 5] >> (sl & 31)) & 1u;
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_resolve(K2Args a, const int32_t
         int nkept;
         int kr = block_scan(kept, s_wave, nkept);
 #pragma unroll
-        for (int c = 0; c < K2_CPT; ++c) {
+        for (int c = 0; c < CPT; ++c) {
             if (ent[c] < 0) continue;
             if (kr < q) s_victim[kr] = ent[c];
             else order_out[kr - q] = ent[c];
@@ -627,13 +628,15 @@ __device__ __forceinline__ float lane_f32(float v, int j) {
 }
 
 constexpr int K2T_WAVES = 16;
+static_assert(K2T_WAVES * 64 * 32 == K2_MAXC && 32 * K2_THREADS == K2_MAXC,
+              "the largest resolve specialisations address K2_MAXC slots");
 
 // NC: logit candidates per lane (E <= 64 NC); NI: order entries per lane (C <= 16 * 64 NI)
 template <int NC, int NI>
 __global__ __launch_bounds__(K2T_WAVES * 64) void k2_resolve_tok(K2Args a, const int32_t* order_in,
                                                                  int32_t* order_out) {
     __shared__ int32_t s_slot[64 * NC];          // this layer's slot-table entries
-    __shared__ uint32_t s_hbits[K2_MAXC / 32];   // hit slots
+    __shared__ uint32_t s_hbits[K2T_WAVES * 64 * NI / 32];   // hit slots
     __shared__ int32_t s_vict[16], s_vkey[16];   // victims and their occupants, by miss rank
     __shared__ int s_cnt[K2T_WAVES];
     __shared__ uint64_t s_vmask;                 // order positions (< k) taken as victims
@@ -836,8 +839,10 @@ void launch_k2_tok(const K2Args& a, const int32_t* order_in, int32_t* order_out,
         hipLaunchKernelGGL((k2_resolve_tok<NC, 4>), g, b, 0, st, a, order_in, order_out);
     else if (per_wave <= 64 * 8)
         hipLaunchKernelGGL((k2_resolve_tok<NC, 8>), g, b, 0, st, a, order_in, order_out);
-    else
+    else if (per_wave <= 64 * 16)
         hipLaunchKernelGGL((k2_resolve_tok<NC, 16>), g, b, 0, st, a, order_in, order_out);
+    else
+        hipLaunchKernelGGL((k2_resolve_tok<NC, 32>), g, b, 0, st, a, order_in, order_out);
 }
 
 // top-k + softmax of many tokens, one wave per token, ahead of the resolve
@@ -849,13 +854,21 @@ __global__ __launch_bounds__(256) void k2_topk(K2Args a) {
 
 constexpr int K2_FUSED_TOPK_MAX = 16;  // up to this many tokens the resolve kernel routes them itself
 
+// the general resolve, compiled for the cache size
+void launch_k2_general(const K2Args& a, const int32_t* order_in, int32_t* order_out, hipStream_t st) {
+    if (a.C <= 16 * K2_THREADS)
+        hipLaunchKernelGGL(k2_resolve<16>, dim3(1), dim3(K2_THREADS), 0, st, a, order_in, order_out);
+    else
+        hipLaunchKernelGGL(k2_resolve<32>, dim3(1), dim3(K2_THREADS), 0, st, a, order_in, order_out);
+}
+
 int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     if (a.z && a.B > K2_FUSED_TOPK_MAX) {
         hipLaunchKernelGGL(k2_topk, dim3((a.B + 3) / 4), dim3(256), 0, st, a);
         K2Args r = a;
         r.z = nullptr;  // resolve the ids just written
-        hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, st, r, order_in, order_out);
+        launch_k2_general(r, order_in, order_out, st);
     } else if (a.z && a.B == 1 && a.n_ids == a.k && a.policy == 0) {
         // one routed token: the wave-level resolve
         if (a.E <= 128)
@@ -867,7 +880,7 @@ int launch_k2(const K2Args& a, const int32_t* order_in, int32_t* order_out, void
         else
             launch_k2_tok<16>(a, order_in, order_out, st);
     } else {
-        hipLaunchKernelGGL(k2_resolve, dim3(1), dim3(K2_THREADS), 0, st, a, order_in, order_out);
+        launch_k2_general(a, order_in, order_out, st);
     }
     return (int)hipGetLastError();
 }

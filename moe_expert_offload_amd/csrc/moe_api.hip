@@ -224,7 +224,7 @@ moe_status set_err(moe_ctx* c, moe_status st, const char* fmt, ...) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int MAX_CACHE_SLOTS = 16384;  // the resolve and grouping kernels' slot capacity
+constexpr int MAX_CACHE_SLOTS = 32768;  // the resolve and grouping kernels' slot capacity
 constexpr int MAX_EXPERTS = 1024;       // experts per layer the resolve kernel handles
 
 // distinct experts one layer step can request; the cache needs twice that (one layer in flight

@@ -48,7 +48,7 @@ def test_query_sizes_and_blob_size():
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=100), -1), (dict(inter=48), -1), (dict(top_k=17), -1), (dict(top_k=20, n_experts=16), -1),
     (dict(n_experts=2000), -1), (dict(n_shared=2), -1), (dict(max_tokens=0), -1),
-    (dict(cache_slots=3), -4), (dict(max_tokens=4, cache_slots=15), -4), (dict(cache_slots=20000), -1),
+    (dict(cache_slots=3), -4), (dict(max_tokens=4, cache_slots=15), -4), (dict(cache_slots=32769), -1),
     (dict(pinned_mb=-1), -1),
 ])
 def test_config_rejected(kw, status):
@@ -121,10 +121,14 @@ def test_auto_cache_slots_caps_at_the_pool_and_kernel_limit():
     assert M.auto_cache_slots(_cfg(cache_slots=0), free_bytes=1 << 40) == 2 * 16
     # gpt-oss-120b shape: the 60.9 GB pool fits in 288 GB of HBM whole
     assert M.auto_cache_slots(_cfg(**GPTOSS), free_bytes=288 * 10**9) == 36 * 128
-    # 48 x 512 keys exceed the 16384 slots the resolve kernel addresses
+    # Qwen3.8 shape: the 48 x 512 keys (92 GB) fit whole, under the 32768 slots the resolve kernels
+    # address
     q38 = dict(n_layers=48, n_experts=512, top_k=10, hidden=3072, inter=768, n_shared=1, cache_slots=0,
                max_tokens=2048)
-    assert M.auto_cache_slots(_cfg(**q38), free_bytes=288 * 10**9) == 16384
+    assert M.auto_cache_slots(_cfg(**q38), free_bytes=288 * 10**9) == 48 * 512
+    # 80 x 512 small experts: the kernel limit
+    many = dict(q38, n_layers=80, hidden=256, inter=256)
+    assert M.auto_cache_slots(_cfg(**many), free_bytes=288 * 10**9) == 32768
 
 
 def test_auto_cache_slots_is_the_largest_that_fits():

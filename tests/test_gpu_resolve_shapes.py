@@ -1,6 +1,7 @@
 """Decode parity at the resolve kernels' size limits: expert counts up to 1024, k = 16 and cache
-sizes up to 16384 slots, so that every specialisation of the one-token resolve (logit candidates
-per lane, order entries per lane) runs, with evictions where the pool exceeds the cache.
+sizes up to 32768 slots, so that every specialisation of the one-token resolve (logit candidates
+per lane, order entries per lane) and of the general resolve (order entries per thread) runs,
+with evictions where the pool exceeds the cache.
 
 Bit-exact: ids, trace records and the final cache state.  Outputs (sampled vectors) within
 relative L2 5e-3 and max|diff| 1e-2 * max|ref|."""
@@ -19,6 +20,13 @@ SHAPES = [
     synth.Workload("e512_c4500", 24, 512, 10, 1, 96, 64, 4500, 96, 1, 0.6, seed=32),
     synth.Workload("e1024_k16_c16384", 3, 1024, 16, 0, 64, 64, 16384, 24, 1, 0.85, seed=33),
     synth.Workload("e1024_k16_c1200", 4, 1024, 16, 1, 128, 96, 1200, 64, 1, 0.7, seed=34),
+    # beyond 16384 slots: 32 order entries per lane, with evictions (24,576 keys, 17,000 slots)
+    synth.Workload("e1024_k16_c17000", 24, 1024, 16, 0, 64, 64, 17000, 128, 1, 0.3, seed=35),
+    synth.Workload("e1024_k16_c32768", 3, 1024, 16, 0, 64, 64, 32768, 24, 1, 0.85, seed=37),
+]
+# batches take the general resolve (and the grouping kernel): 32 order entries per thread
+BATCHED = [
+    synth.Workload("e1024_k16_c17000_b4", 24, 1024, 16, 0, 64, 64, 17000, 48, 4, 0.3, seed=36),
 ]
 
 
@@ -45,5 +53,31 @@ def test_one_token_resolve_at_size_limits(wl):
             r = oracle.moe_output(wl, l, X[t, 0], ref["ids"][t, l, 0], ref["w"][t, l, 0])
             rel, mx, ok = close_enough(y[t, l, 0], r)
             assert ok, (t, l, rel, mx)
+    print(wl.name, "hits", cnt["hits"], "misses", cnt["misses"], "evictions", cnt["evictions"])
+    m.close()
+
+
+@pytest.mark.parametrize("wl", BATCHED, ids=[w.name for w in BATCHED])
+def test_batched_resolve_beyond_16384_slots(wl):
+    X = synth.decode_inputs(wl)
+    m, W = make_moe(wl)
+    ids, w, y = run_stack(m, wl, X)
+    cnt, recs = m.stats(trace_cap=1 << 22)
+    ref = oracle.decode_trace(wl, W, X)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["w"])) <= 1e-5
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    for u, v in zip(m.cache_state(), ref["cache"].state()):
+        np.testing.assert_array_equal(u, v)
+    c = ref["counters"]
+    assert (cnt["hits"], cnt["misses"], cnt["evictions"]) == (c["hits"], c["misses"], c["evictions"])
+    assert c["evictions"] > 0
+    T, B = X.shape[0], X.shape[1]
+    for t in sorted({0, T // 2, T - 1}):
+        for l in (0, wl.n_layers // 2, wl.n_layers - 1):
+            for b in range(B):
+                r = oracle.moe_output(wl, l, X[t, b], ref["ids"][t, l, b], ref["w"][t, l, b])
+                rel, mx, ok = close_enough(y[t, l, b], r)
+                assert ok, (t, l, b, rel, mx)
     print(wl.name, "hits", cnt["hits"], "misses", cnt["misses"], "evictions", cnt["evictions"])
     m.close()
