@@ -119,6 +119,44 @@ __device__ __forceinline__ float expert_weight(const FfnArgs& a, int b, int j) {
     return (unsigned)expert_slot(a, b, j) < (unsigned)a.C ? w : __uint_as_float(0x7FC00000u);
 }
 
+// Blob and combine weight of the token's experts j0 and j1 for one down-kernel lane (per-lane j:
+// the lane's segment may start in one expert and end in the next).  Same values as expert_blob and
+// expert_weight; from device memory the two slots and two weights are four independent loads
+// issued together (one memory latency before the weight loads, instead of one per value).
+struct LaneExperts {
+    const uint8_t* blob0;
+    const uint8_t* blob1;
+    float w0, w1;
+};
+
+__device__ __forceinline__ LaneExperts lane_experts(const FfnArgs& a, int b, int j0, int j1) {
+    int s0, s1;
+    float w0, w1;
+    if (a.karg) {
+        s0 = karg_slot(a, j0);
+        s1 = karg_slot(a, j1);
+        w0 = karg_w(a, j0);
+        w1 = karg_w(a, j1);
+    } else {
+        const int32_t* sp = a.slots + b * a.k;
+        const float* wp = a.w + b * a.k;
+        const int i0 = j0 < a.k ? j0 : 0, i1 = j1 < a.k ? j1 : 0;
+        s0 = sp[i0];
+        s1 = sp[i1];
+        w0 = wp[i0];
+        w1 = wp[i1];
+    }
+    auto blob = [&](int j, int sl) {
+        if (j < a.k) return a.arena + (size_t)((unsigned)sl < (unsigned)a.C ? sl : 0) * a.blob_bytes;
+        return a.shared + (size_t)(a.layer * a.n_shared + (j - a.k)) * a.blob_bytes;
+    };
+    auto weight = [&](int j, int sl, float w) {
+        if (j >= a.k) return 1.0f;
+        return (unsigned)sl < (unsigned)a.C ? w : __uint_as_float(0x7FC00000u);
+    };
+    return LaneExperts{blob(j0, s0), blob(j1, s1), weight(j0, s0, w0), weight(j1, s1, w1)};
+}
+
 constexpr int FFN_THREADS = 256;
 
 // v + (v of lane ^ 8), then ^ 16, then ^ 32: the sum of a row's segments held by lanes r + 8i.
@@ -280,9 +318,10 @@ __device__ __forceinline__ void ffn_down(const FfnArgs& a, uint4* smem, int tile
     const int j0 = qv / NBI, ib0 = qv - (qv / NBI) * NBI;
     const int split = NBI - ib0;
     const int j1 = j0 + 1 < nE ? j0 + 1 : j0;
-    const uint8_t* base0 = expert_blob(a, b, j0);
-    const uint8_t* base1 = expert_blob(a, b, j1);
-    const float cw0 = expert_weight(a, b, j0), cw1 = expert_weight(a, b, j1);
+    const LaneExperts le = lane_experts(a, b, j0, j1);
+    const uint8_t* base0 = le.blob0;
+    const uint8_t* base1 = le.blob1;
+    const float cw0 = le.w0, cw1 = le.w1;
     const int sv = nq > 0 ? s : 0;
     uint4 dc[T2];
     uint32_t sc[T2];
