@@ -228,6 +228,11 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
     float* red = reinterpret_cast<float*>(smem + NB * 5);
     const int r = lane & 7, s = w * 8 + (lane >> 3);
     const int nb = seg_len(NB, S, s);
+    // The activations' staging loads go out first: they do not depend on the expert's slot, whose
+    // scalar load (from device memory when the caller passed the slots there) overlaps them.
+    const uint4* xsrc = reinterpret_cast<const uint4*>(a.x + (size_t)b * a.H);
+    const StageRegs xr = stage_first(xsrc, NB);
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* blob = expert_blob(a, b, j);
     const uint8_t* tb = blob + (size_t)tile * GR * NB * 34;
     const uint8_t* tub = tb + (size_t)GR * NB * 16;
@@ -262,9 +267,6 @@ __device__ __forceinline__ void ffn_gate_up(const FfnArgs& a, uint4* smem, int u
             u += (t0 + t < nb) ? pu : 0.0f;
         }
     };
-    const uint4* xsrc = reinterpret_cast<const uint4*>(a.x + (size_t)b * a.H);
-    const StageRegs xr = stage_first(xsrc, NB);
-    __builtin_amdgcn_sched_barrier(0);
     load(0);
     __builtin_amdgcn_sched_barrier(0);
     stage_commit(xr, smem, xsrc, NB, S, FFN_THREADS);
