@@ -30,7 +30,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 # WRITE_SIZE counter runs, scaled by a device copy of known size in the same process
 # (profiles/expert_ffn_*_traffic.md, profiles/decode_qwen36_*_traffic.md).  Set an entry to None when
 # those kernels change.
-FFN_TRAFFIC_BYTES = {"gptoss120b_shaped": 53769175, "dsv4_flash_shaped": 80816211, "qwen36_35b_a3b_shaped": 15421113}
+FFN_TRAFFIC_BYTES = {"gptoss120b_shaped": 53743002, "dsv4_flash_shaped": 80790742, "qwen36_35b_a3b_shaped": 15382205}
 
 
 def decode_rate(tokens, total_s, ttft_s):
