@@ -661,15 +661,25 @@ __global__ __launch_bounds__(256) void k5_combine(CombineArgs c, const int32_t* 
         acc = make_float4(__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
                           __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u));
     } else {
-        for (int j = 0; j < c.k; ++j) {
-            const int row = b * c.k + j;
-            if (c.host_rows && c.slots[row] < 0) continue;  // computed by the host
-            const float wj = c.w[row];
-            const float4 v = yp4(c, row, h);
-            acc.x += wj * v.x;
-            acc.y += wj * v.y;
-            acc.z += wj * v.z;
-            acc.w += wj * v.w;
+        // every rank's loads are issued before the first sum (k <= 16), which then runs in rank order
+        // (raw bf16 pairs are kept until the sums, so no load waits for the one before it)
+        uint2 raw[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (j < c.k) raw[j] = *reinterpret_cast<const uint2*>(c.yp + (size_t)(b * c.k + j) * c.H + h);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < c.k) {
+                const int row = b * c.k + j;
+                if (c.host_rows && c.slots[row] < 0) continue;  // computed by the host
+                const float wj = c.w[row];
+                const float4 v = make_float4(__uint_as_float(raw[j].x << 16), __uint_as_float(raw[j].x & 0xFFFF0000u),
+                                             __uint_as_float(raw[j].y << 16), __uint_as_float(raw[j].y & 0xFFFF0000u));
+                acc.x += wj * v.x;
+                acc.y += wj * v.y;
+                acc.z += wj * v.z;
+                acc.w += wj * v.w;
+            }
         }
         for (int s = 0; s < c.n_shared; ++s) {
             const int row = c.B * c.k + s * c.B + b;
