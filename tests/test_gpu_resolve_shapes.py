@@ -81,3 +81,37 @@ def test_batched_resolve_beyond_16384_slots(wl):
                 assert ok, (t, l, b, rel, mx)
     print(wl.name, "hits", cnt["hits"], "misses", cnt["misses"], "evictions", cnt["evictions"])
     m.close()
+
+
+def test_static_split_beyond_16384_slots():
+    """MOE_POLICY_STATIC with 17,000 slots (the general resolve's 32-entries-per-thread build):
+    16,968 resident keys from init, every other access streamed into the 32 transient slots.
+    ids, trace, counters and the resident table against the oracle's static split; outputs at
+    sampled steps."""
+    import moe_expert_offload_amd as M
+    from gpu_helpers import run_steps
+    wl = synth.Workload("e1024_k16_c17000_static", 24, 1024, 16, 0, 64, 64, 17000, 32, 1, 0.3, seed=38)
+    X = synth.decode_inputs(wl)
+    steps = [X[t] for t in range(X.shape[0])]
+    T = 2 * min(wl.top_k, wl.n_experts)
+    m, W = make_moe(wl, max_tokens=1, policy=M.MOE_POLICY_STATIC)
+    ids, w, y = run_steps(m, wl, steps)
+    cnt, recs = m.stats(trace_cap=1 << 22)
+    ref = oracle.run_trace(wl, W, steps, static_transient=T)
+    for t in range(len(steps)):
+        np.testing.assert_array_equal(ids[t], ref["ids"][t])
+    assert trace_tuples(recs) == trace_tuples(ref["trace"])
+    rc = ref["counters"]
+    assert (cnt["hits"], cnt["misses"], cnt["evictions"]) == (rc["hits"], rc["misses"], rc["evictions"])
+    slot_of, key_of, _ = m.cache_state()
+    r_slot, r_key = ref["cache"].state()
+    np.testing.assert_array_equal(slot_of, r_slot)
+    np.testing.assert_array_equal(key_of, r_key)
+    assert cnt["misses"] > 0 and cnt["hits"] > 0
+    for t in (0, len(steps) // 2, len(steps) - 1):
+        for l in (0, wl.n_layers - 1):
+            r = oracle.moe_output(wl, l, steps[t][0], ref["ids"][t][l, 0], ref["w"][t][l, 0])
+            rel, mx, ok = close_enough(y[t][l, 0], r)
+            assert ok, (t, l, rel, mx)
+    print(wl.name, "hits", cnt["hits"], "misses", cnt["misses"], "evictions", cnt["evictions"])
+    m.close()
